@@ -1,0 +1,197 @@
+/*
+ * Oracle for the batch-invariant GEMM family and RMSNorm: a plain, slow,
+ * fp64 CPU implementation of what each operation computes.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; it consumes the same stored
+ * inputs (bf16 bit patterns, NVFP4 code and scale bytes) and nothing else.
+ *
+ * Every function returns the exact-up-to-fp64-rounding value of the plain
+ * definition, never an emulation of a GPU kernel:
+ *   - products of two bf16 values are exact in fp64 (8 + 8 significand bits);
+ *   - sums are accumulated sequentially in ascending k in fp64;
+ *   - nothing is rounded to fp32 or bf16.
+ * Alongside y it returns sum_k |a_k * b_k|, the scale the tolerance uses.
+ *
+ * Sources (the pages' own wording is not reproduced here):
+ *   - "NVFP4 CUTLASS batch invariant mode" (vLLM PR #39912 summary page),
+ *     section "key source snippets", unit test test_nvfp4_gemm_batch_invariance:
+ *     a is [m,k], b is [n,k], k = 2 * packed_k, out = alpha * (a . b^T) with
+ *     alpha = 1 / (global_scale_a * global_scale_b).  This fixes the operand
+ *     orientation y = A . B^T used for every GEMM here.
+ *   - "[Core] Disable fuse_allreduce_rms under VLLM_BATCH_INVARIANT" (vLLM
+ *     PR #51292), section Purpose: RMSNorm is the row reduction fused after
+ *     the all-reduce.  The pages name it without a formula; the definition
+ *     used is the standard one, y = x * gamma / sqrt(mean(x^2) + eps).
+ *   - NVFP4 element and scale encodings are named by the pages but not
+ *     spelled out; the decoders below follow the OCP 8-bit floating point
+ *     (E4M3, "fn" variant: no infinities, one NaN pattern per sign) and the
+ *     OCP Microscaling FP4 E2M1 definitions.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <string.h>
+
+/* bf16 bit pattern -> value: bf16 is the top half of an IEEE binary32. */
+static double bf16_value(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* FP4 E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
+ * Exponent field 0 is subnormal: value = mantissa * 2^(1-1) * 0.5. */
+static double e2m1_value(unsigned code) {
+    unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* FP8 E4M3 (fn): bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa.
+ * Exponent field 0 is subnormal: m/8 * 2^-6.  S.1111.111 is NaN; there is no
+ * infinity, so S.1111.110 = 448 is the largest finite magnitude. */
+static double e4m3_value(unsigned code) {
+    unsigned s = (code >> 7) & 1u, e = (code >> 3) & 15u, m = code & 7u;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m / 8.0, -6);
+    else mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* Exported decoders so the tests can pin them exhaustively. */
+double oracle_e2m1_value(uint32_t code) { return e2m1_value(code & 15u); }
+double oracle_e4m3_value(uint32_t code) { return e4m3_value(code & 255u); }
+double oracle_bf16_value(uint32_t bits) { return bf16_value((uint16_t)bits); }
+
+/* Element k of an NVFP4 row: codes hold two elements per byte, element 2j in
+ * the low nibble of byte j and element 2j+1 in the high nibble; one E4M3
+ * scale covers 16 consecutive elements.  value = e2m1(code) * e4m3(scale). */
+static double nvfp4_elem(const uint8_t *codes, const uint8_t *scales, int64_t k) {
+    unsigned byte = codes[k >> 1];
+    unsigned code = (k & 1) ? (byte >> 4) : (byte & 15u);
+    return e2m1_value(code) * e4m3_value(scales[k >> 4]);
+}
+
+/*
+ * GEMM: Y[r][j] = sum_{k<K} A[i][k] * B[j][k], i = rows[r] (or r when rows is
+ * NULL), for j < N.  A is bf16 [M,K] with row stride lda, B is bf16 [N,K]
+ * with row stride ldb.  Y and S are dense [nrows, N]; S gets sum_k |a*b|.
+ */
+void oracle_gemm(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                 int64_t M, int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                 double *Y, double *S) {
+    if (!rows) nrows = M;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t r = 0; r < nrows; r++) {
+        for (int64_t j = 0; j < N; j++) {
+            int64_t i = rows ? rows[r] : r;
+            const uint16_t *a = A + i * lda, *b = B + j * ldb;
+            double y = 0.0, s = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = bf16_value(a[k]) * bf16_value(b[k]);
+                y += p;
+                s += fabs(p);
+            }
+            Y[r * N + j] = y;
+            S[r * N + j] = s;
+        }
+    }
+}
+
+/*
+ * BMM: for each head h, Y[h][i][j] = sum_{k<K} A[h][i][k] * B[h][k][j].
+ * A is bf16 [batch,M,K] (head stride sA, row stride lda), B is bf16
+ * [batch,K,N] (head stride sB, row stride ldb over k).  Y, S dense
+ * [batch,M,N].
+ */
+void oracle_bmm(const uint16_t *A, int64_t sA, int64_t lda, const uint16_t *B, int64_t sB,
+                int64_t ldb, int64_t batch, int64_t M, int64_t N, int64_t K, double *Y,
+                double *S) {
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int64_t h = 0; h < batch; h++) {
+        for (int64_t i = 0; i < M; i++) {
+            for (int64_t j = 0; j < N; j++) {
+                const uint16_t *a = A + h * sA + i * lda;
+                const uint16_t *b = B + h * sB + j;
+                double y = 0.0, s = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    double p = bf16_value(a[k]) * bf16_value(b[k * ldb]);
+                    y += p;
+                    s += fabs(p);
+                }
+                Y[(h * M + i) * N + j] = y;
+                S[(h * M + i) * N + j] = s;
+            }
+        }
+    }
+}
+
+/*
+ * NVFP4 weight GEMM: Y[r][j] = alpha * sum_{k<K} a(i,k) * w(j,k).
+ *   w(j,k) = e2m1(W code) * e4m3(W scale), W codes [N, K/2] and W scales
+ *   [N, K/16], both dense.
+ *   a_fmt 0: a(i,k) = bf16 A[i*lda + k].
+ *   a_fmt 1: a(i,k) is the NVFP4 element k of row i: codes at A + i*lda/2
+ *            bytes, scales at A_scales + i*lda/16 bytes.
+ * alpha is the fp32 argument, widened to fp64 and applied once.
+ * S gets |alpha| * sum_k |a * w|.
+ */
+void oracle_nvfp4_gemm(const void *A, const uint8_t *A_scales, int a_fmt, int64_t lda,
+                       const uint8_t *W, const uint8_t *W_scales, float alpha, int64_t M,
+                       int64_t N, int64_t K, const int64_t *rows, int64_t nrows, double *Y,
+                       double *S) {
+    if (!rows) nrows = M;
+    double al = (double)alpha;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t r = 0; r < nrows; r++) {
+        for (int64_t j = 0; j < N; j++) {
+            int64_t i = rows ? rows[r] : r;
+            const uint8_t *wc = W + j * (K / 2), *ws = W_scales + j * (K / 16);
+            double y = 0.0, s = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double a;
+                if (a_fmt == 0)
+                    a = bf16_value(((const uint16_t *)A)[i * lda + k]);
+                else
+                    a = nvfp4_elem((const uint8_t *)A + i * (lda / 2), A_scales + i * (lda / 16), k);
+                double p = a * nvfp4_elem(wc, ws, k);
+                y += p;
+                s += fabs(p);
+            }
+            Y[r * N + j] = al * y;
+            S[r * N + j] = fabs(al) * s;
+        }
+    }
+}
+
+/*
+ * RMSNorm: Y[r][h] = x[i][h] * gamma[h] / sqrt((1/H) * sum_h' x[i][h']^2 + eps).
+ * X bf16 [M,H] row stride ldx, gamma bf16 [H], eps the fp32 argument widened.
+ * Y dense [nrows, H].
+ */
+void oracle_rmsnorm(const uint16_t *X, int64_t ldx, const uint16_t *gamma, float eps,
+                    int64_t M, int64_t H, const int64_t *rows, int64_t nrows, double *Y) {
+    if (!rows) nrows = M;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t i = rows ? rows[r] : r;
+        const uint16_t *x = X + i * ldx;
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            double v = bf16_value(x[h]);
+            ss += v * v;
+        }
+        double denom = sqrt(ss / (double)H + (double)eps);
+        for (int64_t h = 0; h < H; h++)
+            Y[r * H + h] = bf16_value(x[h]) * bf16_value(gamma[h]) / denom;
+    }
+}
+
+/* Number of OpenMP threads the oracle will use (for reporting). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,53 @@
+"""Shared test helpers: bf16 decoding of results, the tolerance, comparisons.
+
+The tolerance for the GEMM family is |y - y_ref| <= ulp_bf16(y_ref) +
+1e-3 * sum_k |a_k b_k|; for RMSNorm the same form with one product term,
+|y - y_ref| <= ulp_bf16(y_ref) + 1e-3 * |y_ref|.
+"""
+import numpy as np
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits).view(np.uint16) if np.asarray(bits).dtype == np.int16 else np.asarray(bits, np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def ulp_bf16(y) -> np.ndarray:
+    """Spacing of bf16 at |y|: 2^(max(floor(log2|y|), -126) - 7); 2^-133 at 0."""
+    a = np.abs(np.asarray(y, np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(a > 0, np.maximum(e, -126.0), -126.0)
+    return np.exp2(e - 7.0)
+
+
+def tol_excess(y_gpu_bits, y_ref, s, rel=1e-3):
+    """max over elements of |y - y_ref| - (ulp(y_ref) + rel*s); <= 0 passes."""
+    y = bf16_to_f64(y_gpu_bits)
+    err = np.abs(y - y_ref)
+    bound = ulp_bf16(y_ref) + rel * np.asarray(s, np.float64)
+    if err.size == 0:
+        return -1.0
+    return float(np.max(err - bound))
+
+
+def assert_within_tol(y_gpu_bits, y_ref, s, what=""):
+    y = bf16_to_f64(y_gpu_bits)
+    assert y.shape == np.shape(y_ref), (what, y.shape, np.shape(y_ref))
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    err = np.abs(y - y_ref)
+    bound = ulp_bf16(y_ref) + 1e-3 * np.asarray(s, np.float64)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; first at {tuple(idx)}: "
+            f"gpu={y[tuple(idx)]!r} ref={y_ref[tuple(idx)]!r} bound={bound[tuple(idx)]!r}")
+
+
+def rne_bf16_of_exact(y_exact) -> np.ndarray:
+    """bf16 bits of exactly representable-in-fp32 values, rounded to nearest even."""
+    f = np.asarray(y_exact, np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(y_exact, np.float64)), "not exact in fp32"
+    u = f.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

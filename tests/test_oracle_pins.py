@@ -1,0 +1,344 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test ties one oracle function to something independent: hand-worked
+examples (tests/golden/worked_examples.txt), a published format table
+(tests/golden/e2m1_ocp_mx.txt), a library routine (torch's float8/bfloat16
+conversions, numpy integer matmul), exact rational brute force
+(fractions.Fraction), closed forms and invariants.  They are chosen so that a
+plausible slip in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, a misplaced scale or nibble) fails at least one.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_deterministic_bi_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _parse_matrix(txt):
+    return [[float(v) for v in row.split(",")] for row in txt.split(";")]
+
+
+def _worked():
+    out = {}
+    with open(os.path.join(GOLDEN, "worked_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, rest = [p.strip() for p in line.split(":", 1)]
+            lhs, rhs = [p.strip() for p in rest.split("=>")]
+            args = dict(tok.split("=", 1) for tok in lhs.split())
+            out[name] = (args, rhs)
+    return out
+
+
+WORKED = _worked()
+
+
+def bits(values):
+    return inputs.to_bf16_bits(np.asarray(values, np.float64))
+
+
+def torch_bf16_value(b):
+    t = torch.from_numpy(np.asarray(b, np.uint16).astype(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_bf16_decode_matches_torch_exhaustive():
+    allbits = np.arange(65536, dtype=np.uint32)
+    ours = np.array([oracle.bf16_value(int(b)) for b in allbits[::97]])
+    ref = torch_bf16_value(allbits[::97].astype(np.uint16))
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.all(both_nan | (ours == ref))
+    # a few hand-checked patterns (IEEE binary32 upper halves)
+    assert oracle.bf16_value(0x3F80) == 1.0
+    assert oracle.bf16_value(0xC000) == -2.0
+    assert oracle.bf16_value(0x4049) == 3.140625
+    assert oracle.bf16_value(0x0001) == 2.0 ** -133
+    assert oracle.bf16_value(0x7F7F) == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_e2m1_decode_matches_ocp_table():
+    table = {}
+    with open(os.path.join(GOLDEN, "e2m1_ocp_mx.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                c, v = line.split()
+                table[int(c, 16)] = float(v)
+    assert len(table) == 16
+    for c, v in table.items():
+        got = oracle.e2m1_value(c)
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), (c, got, v)
+
+
+def test_e4m3_decode_matches_torch_exhaustive():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        got = oracle.e4m3_value(c)
+        if np.isnan(ref[c]):
+            assert np.isnan(got), c
+        else:
+            assert got == ref[c], (c, got, ref[c])
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0xB8) == -1.0
+
+
+def test_nvfp4_products_exact_in_bf16():
+    """Every e2m1 x e4m3 product (4096 of them) is a bf16 value: <= 6
+    significant bits, magnitudes in [2^-10, 2688]."""
+    for q in range(16):
+        for s in range(256):
+            if s in (0x7F, 0xFF):
+                continue
+            v = oracle.e2m1_value(q) * oracle.e4m3_value(s)
+            b = inputs.to_bf16_bits(np.array([v]))
+            assert torch_bf16_value(b)[0] == v, (q, s, v)
+            if v != 0:
+                assert 2.0 ** -10 <= abs(v) <= 2688.0
+
+
+# ---------------------------------------------------------------- GEMM
+
+def test_gemm_worked_examples():
+    for name in ("gemm_orient", "gemm_small"):
+        args, rhs = WORKED[name]
+        A = bits(_parse_matrix(args["A"]))
+        B = bits(_parse_matrix(args["B"]))
+        y, s = oracle.gemm(A, B)
+        assert np.array_equal(y, np.array(_parse_matrix(rhs))), name
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 33, 544), (1, 256, 512), (5, 3, 12288)])
+def test_gemm_integer_exact(M, N, K):
+    A = inputs.randint_bf16((M, K), -3, 3, tag=(1, M, N, K))
+    B = inputs.randint_bf16((N, K), -3, 3, tag=(2, M, N, K))
+    Ai = torch_bf16_value(A).astype(np.int64)
+    Bi = torch_bf16_value(B).astype(np.int64)
+    y, s = oracle.gemm(A, B)
+    assert np.array_equal(y, (Ai @ Bi.T).astype(np.float64))
+    assert np.array_equal(s, (np.abs(Ai) @ np.abs(Bi).T).astype(np.float64))
+
+
+def test_gemm_bruteforce_fraction():
+    M, N, K = 3, 4, 37
+    A = inputs.randn_bf16((M, K), tag=(3,))
+    B = inputs.randn_bf16((N, K), tag=(4,))
+    av, bv = torch_bf16_value(A), torch_bf16_value(B)
+    y, s = oracle.gemm(A, B)
+    u = 2.0 ** -53
+    gamma = K * u / (1 - K * u)
+    for i in range(M):
+        for j in range(N):
+            exact = sum(Fraction(av[i, k]) * Fraction(bv[j, k]) for k in range(K))
+            sabs = sum(abs(Fraction(av[i, k]) * Fraction(bv[j, k])) for k in range(K))
+            assert abs(Fraction(y[i, j]) - exact) <= Fraction(gamma) * sabs
+            assert abs(Fraction(s[i, j]) - sabs) <= Fraction(gamma) * sabs
+            fs = math.fsum(float(av[i, k]) * float(bv[j, k]) for k in range(K))
+            assert abs(y[i, j] - fs) <= gamma * float(sabs)
+
+
+def test_gemm_identity_and_one_hot():
+    K = 64
+    A = inputs.randn_bf16((9, K), tag=(5,))
+    I = bits(np.eye(K))
+    y, _ = oracle.gemm(A, I)
+    assert np.array_equal(y, torch_bf16_value(A))
+    B = inputs.randn_bf16((17, K), tag=(6,))
+    for k in (0, 13, K - 1):
+        e = np.zeros((1, K))
+        e[0, k] = 1.0
+        y, _ = oracle.gemm(bits(e), B)
+        assert np.array_equal(y[0], torch_bf16_value(B)[:, k])
+
+
+def test_gemm_rows_and_permutation():
+    A = inputs.randn_bf16((23, 96), tag=(7,))
+    B = inputs.randn_bf16((11, 96), tag=(8,))
+    y, s = oracle.gemm(A, B)
+    perm = inputs.rng(12345, 9).permutation(23)
+    yp, sp = oracle.gemm(A[perm], B)
+    assert np.array_equal(yp, y[perm]) and np.array_equal(sp, s[perm])
+    rows = [22, 0, 5, 5]
+    yr, sr = oracle.gemm(A, B, rows=rows)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(sr, s[rows])
+
+
+def test_gemm_power_of_two_scaling():
+    A = inputs.randn_bf16((4, 128), tag=(10,))
+    B = inputs.randn_bf16((6, 128), tag=(11,))
+    y, _ = oracle.gemm(A, B)
+    y8, _ = oracle.gemm(bits(torch_bf16_value(A) * 8), B)
+    assert np.array_equal(y8, 8 * y)
+
+
+# ---------------------------------------------------------------- BMM
+
+def test_bmm_worked_example():
+    args, rhs = WORKED["bmm_two_heads"]
+    A = bits([_parse_matrix(h) for h in args["A"].split("|")])
+    B = bits([_parse_matrix(h) for h in args["B"].split("|")])
+    y, _ = oracle.bmm(A, B)
+    want = np.array([_parse_matrix(h) for h in rhs.split("|")])
+    assert np.array_equal(y, want)
+
+
+def test_bmm_integer_exact():
+    H, M, K, N = 5, 7, 128, 40
+    A = inputs.randint_bf16((H, M, K), -3, 3, tag=(12,))
+    B = inputs.randint_bf16((H, K, N), -3, 3, tag=(13,))
+    Ai, Bi = torch_bf16_value(A).astype(np.int64), torch_bf16_value(B).astype(np.int64)
+    y, s = oracle.bmm(A, B)
+    assert np.array_equal(y, np.matmul(Ai, Bi).astype(np.float64))
+    assert np.array_equal(s, np.matmul(np.abs(Ai), np.abs(Bi)).astype(np.float64))
+
+
+# ---------------------------------------------------------------- NVFP4
+
+def _decode_nvfp4_independent(codes, scales, K):
+    """Decode with the OCP golden table and torch's float8_e4m3fn."""
+    table = {}
+    with open(os.path.join(GOLDEN, "e2m1_ocp_mx.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                c, v = line.split()
+                table[int(c, 16)] = float(v)
+    lut = np.array([table[c] for c in range(16)])
+    R = codes.shape[0]
+    q = np.empty((R, K), np.int64)
+    q[:, 0::2] = codes & 15
+    q[:, 1::2] = codes >> 4
+    sv = torch.from_numpy(scales.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return lut[q] * np.repeat(sv, 16, axis=1)
+
+
+def test_nvfp4_nibble_order_worked_example():
+    K = 16
+    W = np.zeros((1, K // 2), np.uint8)
+    W[0, 0] = 0x21
+    Ws = np.full((1, 1), 0x40, np.uint8)
+    for k, want in ((0, 1.0), (1, 2.0), (2, 0.0)):
+        e = np.zeros((1, K))
+        e[0, k] = 1.0
+        y, s = oracle.nvfp4_gemm(bits(e), None, W, Ws, 1.0, K)
+        assert y[0, 0] == want and s[0, 0] == abs(want)
+
+
+@pytest.mark.parametrize("a_fmt", ["bf16", "nvfp4"])
+def test_nvfp4_exact_pow2(a_fmt):
+    M, N, K = 6, 21, 256
+    W, Ws = inputs.random_nvfp4_pow2((N, K), tag=(14,))
+    if a_fmt == "bf16":
+        A = inputs.randint_bf16((M, K), -3, 3, tag=(15,))
+        As = None
+        a_val = torch_bf16_value(A)
+    else:
+        A, As = inputs.random_nvfp4_pow2((M, K), tag=(16,))
+        a_val = _decode_nvfp4_independent(A, As, K)
+    w_val = _decode_nvfp4_independent(W, Ws, K)
+    want = a_val @ w_val.T  # exact: dyadic values with few bits
+    for alpha in (1.0, 0.25, -2.0):
+        y, s = oracle.nvfp4_gemm(A, As, W, Ws, alpha, K)
+        assert np.array_equal(y, alpha * want)
+        assert np.array_equal(s, abs(alpha) * (np.abs(a_val) @ np.abs(w_val).T))
+
+
+def test_nvfp4_gaussian_vs_dequantised_gemm_bound():
+    """Quantised weights: the oracle equals the exact dot of decoded values."""
+    M, N, K = 2, 5, 64
+    x = inputs.rng(12345, 17).standard_normal((N, K)) * 0.02
+    g = inputs.nvfp4_global_scale(x)
+    W, Ws = inputs.nvfp4_quantize(x, g)
+    A = inputs.randn_bf16((M, K), tag=(18,))
+    w_val = _decode_nvfp4_independent(W, Ws, K)
+    a_val = torch_bf16_value(A)
+    alpha = float(np.float32(1.0 / g))
+    y, s = oracle.nvfp4_gemm(A, None, W, Ws, alpha, K)
+    for i in range(M):
+        for j in range(N):
+            exact = alpha * sum(Fraction(a_val[i, k]) * Fraction(w_val[j, k]) for k in range(K))
+            assert abs(Fraction(y[i, j]) - exact) <= Fraction(1e-13) * (1 + abs(exact))
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+@pytest.mark.parametrize("name", ["rmsnorm_34", "rmsnorm_ones", "rmsnorm_single"])
+def test_rmsnorm_worked_examples(name):
+    args, rhs = WORKED[name]
+    x = bits([[float(v) for v in args["x"].split(",")]])
+    gam = bits([float(v) for v in args["gamma"].split(",")])
+    y = oracle.rmsnorm(x, gam, float(args["eps"]))
+    want = np.array([float(v) for v in rhs.split(",")])
+    assert np.allclose(y[0], want, rtol=1e-15, atol=0), (y, want)
+
+
+def test_rmsnorm_closed_forms():
+    H = 512
+    gam = inputs.uniform_bf16((H,), 0.5, 1.5, tag=(19,))
+    gv = torch_bf16_value(gam)
+    eps = 1e-6
+    e32 = float(np.float32(eps))
+    rows = np.stack([
+        np.zeros(H),                                   # zero row -> 0
+        np.full(H, 0.75),                              # constant row
+        np.where(np.arange(H) % 3 == 0, -4.0, 4.0),    # +-2^p row
+    ])
+    y = oracle.rmsnorm(bits(rows), gam, eps)
+    assert np.array_equal(y[0], np.zeros(H))
+    assert np.allclose(y[1], gv * 0.75 / math.sqrt(0.75 ** 2 + e32), rtol=1e-15)
+    assert np.allclose(y[2], np.sign(rows[2]) * gv * 4 / math.sqrt(16 + e32), rtol=1e-15)
+
+
+def test_rmsnorm_scale_invariance_and_rows():
+    X = inputs.randn_bf16((9, 256), tag=(20,))
+    gam = inputs.uniform_bf16((256,), 0.5, 1.5, tag=(21,))
+    y = oracle.rmsnorm(X, gam, 0.0)
+    y4 = oracle.rmsnorm(bits(torch_bf16_value(X) * 4), gam, 0.0)
+    assert np.array_equal(y, y4)
+    yr = oracle.rmsnorm(X, gam, 1e-6, rows=[8, 1])
+    yf = oracle.rmsnorm(X, gam, 1e-6)
+    assert np.array_equal(yr, yf[[8, 1]])
+
+
+# ---------------------------------------------------------------- generators
+
+def test_bf16_rounding_matches_torch():
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 257.0, 259.0, -3.3, 1e-40, 6.1e4])
+    ours = inputs.to_bf16_bits(vals)
+    ref = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    x = inputs.rng(12345, 22).standard_normal(10000)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(inputs.to_bf16_bits(x), ref)
+
+
+def test_generators_deterministic():
+    a = inputs.randn_bf16((4, 8), tag=(1, 2))
+    b = inputs.randn_bf16((4, 8), tag=(1, 2))
+    c = inputs.randn_bf16((4, 8), tag=(1, 3))
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+
+
+def test_quantiser_row_local_and_error_bound():
+    x = inputs.rng(12345, 23).standard_normal((8, 64)) * 0.02
+    g = inputs.nvfp4_global_scale(x)
+    W, Ws = inputs.nvfp4_quantize(x, g)
+    for i in range(8):
+        Wi, Wsi = inputs.nvfp4_quantize(x[i:i + 1], g)
+        assert np.array_equal(Wi[0], W[i]) and np.array_equal(Wsi[0], Ws[i])
+    dec = _decode_nvfp4_independent(W, Ws, 64) / float(g)
+    # each element within half an e2m1 step of its block scale (plus scale rounding)
+    blk_amax = np.repeat(np.abs(x).reshape(8, 4, 16).max(axis=2), 16, axis=1)
+    assert np.all(np.abs(dec - x) <= blk_amax * 0.25 + 1e-12)
