@@ -1,0 +1,288 @@
+"""Benchmark of the batch-invariant hot path on one MI355X.
+
+One step = one pass of every operation of the path over one batch of
+synthetic, seeded inputs already resident in HBM, shaped like a Qwen3-8B
+decoder layer's linear layers at M tokens (default M = 2048):
+    RMSNorm(H=4096) -> qkv GEMM (N=6144, K=4096) -> MLA-absorbed BMM
+    (128 heads, [M_b,128] . [128,512], M_b = min(M, 1024)) -> o_proj GEMM
+    (4096, 4096) -> RMSNorm -> gate_up GEMM (24576, 4096) -> down GEMM
+    (4096, 12288) -> NVFP4 gate_up GEMM (W[24576,4096] e2m1 + e4m3/16).
+Activations ~ N(0,1), weights ~ N(0,0.02), rounded to bf16; the NVFP4
+weight is the host quantisation of N(0,0.02) values; gamma ~ U(0.5,1.5).
+
+Prints one JSON line.  `value` is the step's GEMM-family TFLOP/s (all
+flops of the step over the measured step time).  `roofline` is for the
+dominant kernel (the bf16 gate_up GEMM), its duration measured with HIP
+events on the stream it is launched on.  `sweep` adds per-op figures at
+M = 1 and 16 (HBM GB/s, with >= 1 GiB of rotating weight copies so the
+256 MB last-level cache cannot serve them) and at the step's M.
+`invariance` counts bitwise checks of small-M rows against the step's rows.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--m", type=int, default=2048, help="tokens per step")
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    p.add_argument("--only-step", action="store_true",
+                   help="run the timed steps only (for profiler runs)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the batch-invariant path here is single-GPU "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from invariant_deterministic_bi_amd import binding as B
+    from invariant_deterministic_bi_amd import inputs
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    M = args.m
+    Mb = min(M, 1024)
+    H, Nqkv, No, Ngu, Kdn, heads, dk, dn = 4096, 6144, 4096, 24576, 12288, 128, 128, 512
+    eps = 1e-6
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t0 = time.time()
+    log(f"generating inputs M={M}")
+    host = {
+        "X": inputs.randn_bf16((M, H), 1.0, tag=(1,)),
+        "X2": inputs.randn_bf16((M, H), 1.0, tag=(2,)),
+        "g1": inputs.uniform_bf16((H,), 0.5, 1.5, tag=(3,)),
+        "g2": inputs.uniform_bf16((H,), 0.5, 1.5, tag=(4,)),
+        "Wqkv": inputs.randn_bf16((Nqkv, H), 0.02, tag=(5,)),
+        "Amla": inputs.randn_bf16((heads, Mb, dk), 1.0, tag=(6,)),
+        "Bmla": inputs.randn_bf16((heads, dk, dn), 1.0, tag=(7,)),
+        "Ao": inputs.randn_bf16((M, H), 1.0, tag=(8,)),
+        "Wo": inputs.randn_bf16((No, H), 0.02, tag=(9,)),
+        "Wgu": inputs.randn_bf16((Ngu, H), 0.02, tag=(10,)),
+        "Adn": inputs.randn_bf16((M, Kdn), 1.0, tag=(11,)),
+        "Wdn": inputs.randn_bf16((H, Kdn), 0.02, tag=(12,)),
+    }
+    w4_real = inputs.rng(12345, 13).standard_normal((Ngu, H)).astype(np.float32) * np.float32(0.02)
+    g4 = inputs.nvfp4_global_scale(w4_real)
+    host["W4"], host["W4s"] = inputs.nvfp4_quantize(w4_real, g4)
+    del w4_real
+    alpha4 = float(np.float32(1.0) / g4)
+    t = {k: d(v) for k, v in host.items()}
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    out = {
+        "Xn": torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+        "Xn2": torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+        "Yqkv": torch.empty((M, Nqkv), dtype=torch.bfloat16, device=dev),
+        "Ymla": torch.empty((heads, Mb, dn), dtype=torch.bfloat16, device=dev),
+        "Yo": torch.empty((M, No), dtype=torch.bfloat16, device=dev),
+        "Ygu": torch.empty((M, Ngu), dtype=torch.bfloat16, device=dev),
+        "Ydn": torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+        "Y4": torch.empty((M, Ngu), dtype=torch.bfloat16, device=dev),
+    }
+    flops = {
+        "qkv": 2.0 * M * Nqkv * H, "bmm": 2.0 * heads * Mb * dn * dk, "o_proj": 2.0 * M * No * H,
+        "gate_up": 2.0 * M * Ngu * H, "down": 2.0 * M * H * Kdn, "nvfp4_gate_up": 2.0 * M * Ngu * H,
+    }
+    total_flops = sum(flops.values())
+    ev = []
+
+    def step(timed=False):
+        B.bi_rmsnorm(t["X"], t["g1"], eps, out["Xn"])
+        B.bi_gemm(out["Xn"], t["Wqkv"], out["Yqkv"])
+        B.bi_bmm(t["Amla"], t["Bmla"], out["Ymla"])
+        B.bi_gemm(t["Ao"], t["Wo"], out["Yo"])
+        B.bi_rmsnorm(t["X2"], t["g2"], eps, out["Xn2"])
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        B.bi_gemm(out["Xn2"], t["Wgu"], out["Ygu"])
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+        B.bi_gemm(t["Adn"], t["Wdn"], out["Ydn"])
+        B.bi_nvfp4_gemm(out["Xn2"], t["W4"], t["W4s"], alpha4, out["Y4"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timed=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gu_tflops = flops["gate_up"] / (gu_ms * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; gate_up {gu_ms * 1e3:.1f} us "
+        f"{gu_tflops:.1f} TFLOP/s")
+    if args.only_step:
+        print(json.dumps({"metric": "step", "ms_per_step": ms_per_step, "value": value,
+                          "gate_up_us": gu_ms * 1e3}), flush=True)
+        return
+
+    result = {
+        "metric": "batch-invariant GEMM TFLOP/s & GB/s vs M, % roofline; bitwise-invariance pass %",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, bf16; NVFP4 by host quantisation)",
+        "config": {"workload": f"Qwen3-8B-shaped decoder-layer linears at M={M} tokens: rmsnorm(4096), "
+                               f"qkv 6144x4096, MLA BMM 128x[{Mb},128]x[128,512], o_proj 4096x4096, "
+                               f"rmsnorm, gate_up 24576x4096, down 4096x12288, NVFP4 gate_up 24576x4096",
+                   "M": M, "global_batch": M, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "bi_gemm gate_up N=24576 K=4096",
+                     "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "per_launch_flops": flops["gate_up"], "avg_launch_us": round(gu_ms * 1e3, 2)},
+    }
+
+    # ---------------------------------------------------------------- sweep
+    if not args.no_sweep:
+        sweep = []
+        inv_checked = inv_passed = 0
+        specs = [("qkv", t["Wqkv"], out["Xn"], out["Yqkv"], H),
+                 ("o_proj", t["Wo"], t["Ao"], out["Yo"], H),
+                 ("gate_up", t["Wgu"], out["Xn2"], out["Ygu"], H),
+                 ("down", t["Wdn"], t["Adn"], out["Ydn"], Kdn)]
+        for name, W, Afull, Yfull, K in specs:
+            N = W.shape[0]
+            ref16 = Yfull[:16].clone()
+            ncopy = max(2, int(np.ceil((1 << 30) / (W.numel() * 2))))
+            copies = [W] + [W.clone() for _ in range(ncopy - 1)]
+            for m in (1, 16):
+                A = Afull[:m]
+                Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+                for c in copies:
+                    B.bi_gemm(A, c, Y)
+                torch.cuda.synchronize()
+                reps = 20 * ncopy
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for r in range(reps):
+                    B.bi_gemm(A, copies[r % ncopy], Y)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                byt = 2.0 * (m * K + N * K + m * N)
+                gbs = byt / (us * 1e-6) / 1e9
+                sweep.append({"op": name, "N": N, "K": K, "M": m, "us": round(us, 2),
+                              "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "TFLOP/s": round(2.0 * m * N * K / (us * 1e-6) / 1e12, 3)})
+                inv_checked += 1
+                inv_passed += int(torch.equal(Y, ref16[:m]))
+            del copies
+            torch.cuda.empty_cache()
+        # per-op figures at the step's M (one launch each, weights cold in the
+        # cache only as far as the step's own rotation makes them)
+        for name, fn, fl in [
+            ("qkv", lambda: B.bi_gemm(out["Xn"], t["Wqkv"], out["Yqkv"]), flops["qkv"]),
+            ("o_proj", lambda: B.bi_gemm(t["Ao"], t["Wo"], out["Yo"]), flops["o_proj"]),
+            ("gate_up", lambda: B.bi_gemm(out["Xn2"], t["Wgu"], out["Ygu"]), flops["gate_up"]),
+            ("down", lambda: B.bi_gemm(t["Adn"], t["Wdn"], out["Ydn"]), flops["down"]),
+            ("nvfp4_gate_up", lambda: B.bi_nvfp4_gemm(out["Xn2"], t["W4"], t["W4s"], alpha4, out["Y4"]),
+             flops["nvfp4_gate_up"]),
+            ("bmm", lambda: B.bi_bmm(t["Amla"], t["Bmla"], out["Ymla"]), flops["bmm"]),
+        ]:
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 10
+            tf = fl / (us * 1e-6) / 1e12
+            sweep.append({"op": name, "M": M if name != "bmm" else Mb, "us": round(us, 2),
+                          "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        # run-to-run: the step's outputs are identical over repeats
+        snap = {k: v.clone() for k, v in out.items()}
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        for k in out:
+            inv_checked += 1
+            inv_passed += int(torch.equal(out[k], snap[k]))
+        result["sweep"] = sweep
+        result["invariance"] = {"checked": inv_checked, "passed": inv_passed,
+                                "pass_pct": round(100.0 * inv_passed / max(1, inv_checked), 2)}
+
+    # ---------------------------------------------------------------- oracle
+    if not args.no_cpu_baseline:
+        import oracle
+
+        def oracle_rows(r):
+            rows = np.arange(r)
+            done = 0.0
+            oracle.rmsnorm(host["X"], host["g1"], eps, rows=rows)
+            for Wk, Ak, N, K in [("Wqkv", "X", Nqkv, H), ("Wo", "Ao", No, H),
+                                 ("Wgu", "X2", Ngu, H), ("Wdn", "Adn", H, Kdn)]:
+                oracle.gemm(host[Ak], host[Wk], rows=rows)
+                done += 2.0 * r * N * K
+            oracle.bmm(host["Amla"][:, :r], host["Bmla"])
+            done += 2.0 * heads * r * dn * dk
+            oracle.nvfp4_gemm(host["X2"], None, host["W4"], host["W4s"], alpha4, H, rows=rows)
+            done += 2.0 * r * Ngu * H
+            return done
+
+        tc = time.perf_counter()
+        f1 = oracle_rows(1)
+        dt1 = time.perf_counter() - tc
+        r = int(max(1, min(M, args.cpu_seconds / max(dt1, 1e-3))))
+        log(f"oracle: 1 row {dt1:.2f}s; timing {r} rows")
+        tc = time.perf_counter()
+        fr = oracle_rows(r)
+        dtr = time.perf_counter() - tc
+        result["cpu_baseline"] = {
+            "value": round(fr / dtr / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dtr, 2),
+            "sample": f"first {r} of {M} rows of every op of the step (BMM: {r} rows per head), "
+                      f"fp64 oracle, {fr / 1e9:.1f} GFLOP"}
+        log(f"oracle {fr / dtr / 1e9:.2f} GFLOP/s on {oracle.num_threads()} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/*
+ * bi.h -- batch-invariant GEMM family and RMSNorm for AMD MI355X (gfx950).
+ *
+ * Contract shared by every entry point:
+ *   - Output row i is a function of input row i (and the weights) only: it is
+ *     bitwise identical whether computed with M = 1, with the full batch, or
+ *     with the rows in any order, and identical from run to run.  This is the
+ *     property the vLLM-Ascend "Batch Invariance" guide states in its opening
+ *     section (output independent of batch size and request order), which
+ *     the vLLM PR #39912 summary page checks row by row (section "key source
+ *     snippets", test_nvfp4_gemm_batch_invariance) and the vLLM PR #51292 page
+ *     checks run to run (section "Test Plan": 8 identical runs, 1 distinct
+ *     output).
+ *   - How each output is computed depends on the operation and on (N, K)
+ *     (H for RMSNorm) only, never on M: one tile shape, one MFMA instruction,
+ *     one ascending K order, no split-K, no stream-K, no atomics.  M changes
+ *     only the number of tiles and the tail masks.  The PR #39912 page calls
+ *     the M-bucketed kernel configurations the thing batch-invariant mode must
+ *     avoid (section "implementation breakdown": only the default config with
+ *     a persistent scheduler), and the PR #51292 page names size-gated kernel
+ *     selection as the bug class (root-cause comment).
+ *   - There is no mode switch and no environment variable: invariance is
+ *     unconditional (the PR #39912 page lists a cached mode flag as a risk,
+ *     section "risks and impact").
+ *
+ * Memory and streams:
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or keeps device memory, and keeps no per-call
+ *     state; calls are thread-safe.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.  Kernel faults surface at
+ *     the caller's next synchronisation.
+ *   - bf16 data is passed as raw 16-bit patterns; all strides are in elements.
+ *
+ * Errors (returned as bi_status, never by aborting):
+ *   - BI_ERR_NULL: a required pointer is NULL (pointers are not required
+ *     when M == 0, which is a valid no-op).
+ *   - BI_ERR_SHAPE: a negative M, a non-positive N/K/H/batch, a leading
+ *     dimension smaller than its row, or a K/H that is not a multiple of 8
+ *     (of 32 for NVFP4).
+ *   - BI_ERR_ALIGN: a pointer not 16-byte aligned, or a leading dimension or
+ *     batch stride that is not a multiple of 8 elements (of 32 for NVFP4 A).
+ *   - BI_ERR_ALIAS: the output range overlaps an input range.
+ *   - BI_ERR_UNSUPPORTED: no plan for this shape (e.g. an index that would
+ *     overflow 32 bits inside a kernel).  There is never a silent fallback to
+ *     a non-invariant path: the fail-loud rule of the PR #51292 review thread.
+ *   - BI_ERR_HIP: the HIP runtime refused the launch or a device query.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bi_status {
+    BI_OK = 0,
+    BI_ERR_NULL = 1,
+    BI_ERR_SHAPE = 2,
+    BI_ERR_ALIGN = 3,
+    BI_ERR_ALIAS = 4,
+    BI_ERR_UNSUPPORTED = 5,
+    BI_ERR_HIP = 6
+} bi_status;
+
+typedef enum bi_a_format {
+    BI_A_BF16 = 0,  /* A is bf16 [M,K] */
+    BI_A_NVFP4 = 1  /* A is NVFP4: codes [M,K/2] + E4M3 scales [M,K/16] */
+} bi_a_format;
+
+typedef enum bi_op {
+    BI_OP_GEMM = 0,
+    BI_OP_BMM = 1,
+    BI_OP_NVFP4_GEMM = 2,
+    BI_OP_RMSNORM = 3
+} bi_op;
+
+/*
+ * The fixed recipe for one (op, N, K) -- or (op, H) for RMSNorm.  Every
+ * field is a function of op and the shape key only.
+ *   GEMM family: output tile bm x bn, bk columns of K staged per step through
+ *   LDS, `waves` wavefronts per workgroup, MFMA block mfma_m x mfma_n x mfma_k
+ *   (bf16 inputs, fp32 accumulation), K visited in ascending chunks of
+ *   mfma_k, `lds_stages` LDS buffers.
+ *   RMSNorm: `threads` threads per row, each summing `chunks_per_thread`
+ *   16-byte chunks of the row; bm = bn = bk = 0.
+ */
+typedef struct bi_plan {
+    int32_t op;
+    int32_t bm, bn, bk;
+    int32_t mfma_m, mfma_n, mfma_k;
+    int32_t waves;
+    int32_t lds_stages;
+    int32_t threads;
+    int32_t chunks_per_thread;
+    int32_t reserved[5];
+} bi_plan;
+
+/*
+ * Launch options for the *_ex entry points.  They change only which
+ * workgroup computes which tile (or row), never how any output element is
+ * computed, so results are bitwise identical for every value -- that is what
+ * the grid-override invariance test checks.
+ *   max_workgroups: cap on the persistent grid (0 = the library's default,
+ *   a small multiple of the device's compute-unit count).
+ */
+typedef struct bi_launch_opts {
+    int32_t max_workgroups;
+    int32_t reserved[7];
+} bi_launch_opts;
+
+/*
+ * bi_gemm: Y = A . B^T, bf16 in, fp32 accumulation, bf16 out (round to
+ * nearest even).  Operand orientation as in the unit test of the vLLM PR
+ * #39912 summary page (section "key source snippets": a [m,k], b [n,k],
+ * out [m,n]); the dense bf16 case of the batch-invariant GEMM family.
+ *   A: bf16 [M,K], row stride lda >= K.
+ *   B: bf16 [N,K], row stride ldb >= K (the weight; rows are output columns).
+ *   Y: bf16 [M,N], row stride ldy >= N; must not overlap A or B.
+ *   Y[i][j] = bf16_rne( fp32 MFMA chain over k ascending of A[i][k]*B[j][k] ).
+ */
+bi_status bi_gemm(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
+                  int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * bi_bmm: per head h < batch, Y[h] = A[h] . B[h], the batched GEMM the vLLM
+ * batch-invariance tracking issue lists as a performance item (page
+ * "[Feature]: Batch Invariant Feature and Performance Optimization", TODO
+ * "BMM optimization").  Heads are independent; each head's rows obey the
+ * row contract above, and a head's output does not depend on which other
+ * heads are in the call.
+ *   A: bf16 [batch,M,K], head stride sA, row stride lda >= K.
+ *   B: bf16 [batch,K,N] (K rows of N), head stride sB, row stride ldb >= N.
+ *   Y: bf16 [batch,M,N], head stride sY, row stride ldy >= N.
+ */
+bi_status bi_bmm(const void *A, int64_t sA, int64_t lda, const void *B, int64_t sB,
+                 int64_t ldb, void *Y, int64_t sY, int64_t ldy, int64_t batch, int64_t M,
+                 int64_t N, int64_t K, void *stream);
+
+/*
+ * bi_nvfp4_gemm: Y = alpha * (A . W^T) with W in NVFP4, the operation of
+ * cutlass_scaled_fp4_mm in the vLLM PR #39912 unit test (summary page,
+ * section "key source snippets"; alpha = 1 / (global scale of A * global
+ * scale of W), or 1 / global scale of W when A is bf16).
+ *   W: codes uint8 [N,K/2], dense; element 2j of a row in the low nibble of
+ *      byte j, element 2j+1 in the high nibble; each nibble an FP4 E2M1 code.
+ *   W_scales: uint8 [N,K/16], dense; one FP8 E4M3 (fn) scale per 16
+ *      consecutive elements of a row.
+ *   A (a_fmt == BI_A_BF16): bf16 [M,K], row stride lda elements; A_scales
+ *      unused (may be NULL).
+ *   A (a_fmt == BI_A_NVFP4): codes uint8 [M,K/2] with row stride lda/2 bytes,
+ *      A_scales uint8 [M,K/16] with row stride lda/16 bytes; lda % 32 == 0.
+ *   Y: bf16 [M,N], row stride ldy.  K % 32 == 0.
+ *   Each weight element is decoded exactly to bf16 (e2m1 value * e4m3 scale
+ *   has at most 6 significant bits); the product with alpha is one fp32
+ *   multiply in the epilogue, then bf16 round-to-nearest-even.  With
+ *   alpha == 1 the result is bitwise that of bi_gemm on the decoded weights.
+ */
+bi_status bi_nvfp4_gemm(const void *A, const void *A_scales, int a_fmt, int64_t lda,
+                        const void *W, const void *W_scales, float alpha, void *Y,
+                        int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * bi_rmsnorm: Y[i][h] = bf16_rne( x[i][h] * r_i * gamma[h] ),
+ * r_i = rsqrt( (1/H) * sum_h x[i][h]^2 + eps ), fp32 arithmetic.  RMSNorm is
+ * the row reduction fused after the tensor-parallel all-reduce on the vLLM
+ * PR #51292 page (section "Purpose").  The sum over a row has one fixed order
+ * for a given H: per-thread strided partial sums, a 64-lane butterfly, then
+ * the wave partials in wave order.
+ *   X: bf16 [M,H], row stride ldx.  gamma: bf16 [H].  Y: bf16 [M,H], row
+ *   stride ldy (may equal X for an in-place update; any other overlap is
+ *   BI_ERR_ALIAS).  H % 8 == 0 and H <= 32768.
+ */
+bi_status bi_rmsnorm(const void *X, int64_t ldx, const void *gamma, float eps, void *Y,
+                     int64_t ldy, int64_t M, int64_t H, void *stream);
+
+/* The *_ex variants take launch options (may be NULL = defaults). */
+bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
+                     int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream,
+                     const bi_launch_opts *opts);
+bi_status bi_bmm_ex(const void *A, int64_t sA, int64_t lda, const void *B, int64_t sB,
+                    int64_t ldb, void *Y, int64_t sY, int64_t ldy, int64_t batch, int64_t M,
+                    int64_t N, int64_t K, void *stream, const bi_launch_opts *opts);
+bi_status bi_nvfp4_gemm_ex(const void *A, const void *A_scales, int a_fmt, int64_t lda,
+                           const void *W, const void *W_scales, float alpha, void *Y,
+                           int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream,
+                           const bi_launch_opts *opts);
+bi_status bi_rmsnorm_ex(const void *X, int64_t ldx, const void *gamma, float eps, void *Y,
+                        int64_t ldy, int64_t M, int64_t H, void *stream,
+                        const bi_launch_opts *opts);
+
+/*
+ * bi_plan_query: the recipe the library uses for (op, N, K); for
+ * BI_OP_RMSNORM pass H as N and 0 as K.  There is deliberately no M
+ * argument: the recipe cannot depend on it.  Returns BI_ERR_SHAPE or
+ * BI_ERR_UNSUPPORTED for keys the matching entry point would reject.
+ * Host-only; makes no HIP call.
+ */
+bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out);
+
+/* Static, human-readable name of a status code. */
+const char *bi_status_str(bi_status s);
+
+/* Library version string (static). */
+const char *bi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

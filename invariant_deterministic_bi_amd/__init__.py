@@ -1,7 +1,21 @@
 """Batch-invariant GEMM family and RMSNorm for AMD MI355X (gfx950).
 
 The operations run in hand-written HIP kernels inside ``libbi.so`` behind a
-C ABI (``include/bi.h``); this package only marshals arguments to it.  The
-binding is loaded on first use and raises if the library is missing: there is
-no CPU fallback.
+C ABI (``include/bi.h``); ``binding`` only marshals arguments to it, under the
+same names (``bi_gemm``, ``bi_bmm``, ``bi_nvfp4_gemm``, ``bi_rmsnorm``).  The
+binding is imported on first use and raises if the library is missing: there
+is no CPU fallback.  ``inputs`` (seeded synthetic inputs, NVFP4 host
+quantiser) does not need the library.
 """
+
+_BINDING_NAMES = {
+    "bi_gemm", "bi_bmm", "bi_nvfp4_gemm", "bi_rmsnorm", "plan_query", "status_str", "version",
+    "BiError", "lib",
+}
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,226 @@
+"""ctypes binding of libbi (include/bi.h): argument marshalling only.
+
+Each function takes torch tensors (device memory) or raw integers, passes
+pointers, strides and the current HIP stream to the C entry point of the same
+name, and raises ``BiError`` on a non-zero status.  Every step of the
+computation runs in libbi's HIP kernels; if the library is missing this
+module raises on load -- there is no fallback.
+
+torch is imported before the library is opened so that libbi binds to the HIP
+runtime torch has already loaded (one runtime per process, so torch's
+streams and allocations are valid inside libbi).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbi.so")
+
+BI_OK, BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_ALIGN, BI_ERR_ALIAS, BI_ERR_UNSUPPORTED, BI_ERR_HIP = range(7)
+BI_A_BF16, BI_A_NVFP4 = 0, 1
+BI_OP_GEMM, BI_OP_BMM, BI_OP_NVFP4_GEMM, BI_OP_RMSNORM = range(4)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class BiPlan(ctypes.Structure):
+    _fields_ = [("op", _i32), ("bm", _i32), ("bn", _i32), ("bk", _i32), ("mfma_m", _i32),
+                ("mfma_n", _i32), ("mfma_k", _i32), ("waves", _i32), ("lds_stages", _i32),
+                ("threads", _i32), ("chunks_per_thread", _i32), ("reserved", _i32 * 5)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+class BiLaunchOpts(ctypes.Structure):
+    _fields_ = [("max_workgroups", _i32), ("reserved", _i32 * 7)]
+
+
+class BiError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+
+
+_lib = None
+
+_SIGS = {
+    "bi_gemm": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
+    "bi_gemm_ex": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p],
+    "bi_bmm": [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p],
+    "bi_bmm_ex": [_p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p],
+    "bi_nvfp4_gemm": [_p, _p, ctypes.c_int, _i64, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64,
+                      _i64, _p],
+    "bi_nvfp4_gemm_ex": [_p, _p, ctypes.c_int, _i64, _p, _p, ctypes.c_float, _p, _i64, _i64,
+                         _i64, _i64, _p, _p],
+    "bi_rmsnorm": [_p, _i64, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p],
+    "bi_rmsnorm_ex": [_p, _i64, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p],
+    "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libbi (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"libbi.so not found at {LIB_PATH}: build it with "
+            "`python -m invariant_deterministic_bi_amd.build` (there is no CPU fallback)")
+    l = ctypes.CDLL(LIB_PATH)
+    for name, args in _SIGS.items():
+        f = getattr(l, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    l.bi_status_str.argtypes = [ctypes.c_int]
+    l.bi_status_str.restype = ctypes.c_char_p
+    l.bi_version.argtypes = []
+    l.bi_version.restype = ctypes.c_char_p
+    _lib = l
+    return l
+
+
+def status_str(status: int) -> str:
+    return lib().bi_status_str(int(status)).decode()
+
+
+def version() -> str:
+    return lib().bi_version().decode()
+
+
+def plan_query(op: int, N: int, K: int) -> dict:
+    pl = BiPlan()
+    st = lib().bi_plan_query(int(op), int(N), int(K), ctypes.byref(pl))
+    if st != BI_OK:
+        raise BiError(st, "bi_plan_query")
+    return pl.as_dict()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _opts(max_workgroups):
+    if not max_workgroups:
+        return None
+    o = BiLaunchOpts()
+    o.max_workgroups = int(max_workgroups)
+    return ctypes.byref(o)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check2d(t, name, dtypes=(torch.bfloat16, torch.int16, torch.uint16)):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along the last dimension")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not accepted")
+
+
+def _raise(st, what):
+    if st != BI_OK:
+        raise BiError(st, what)
+
+
+def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0):
+    """Y[M,N] = A[M,K] . B[N,K]^T (bf16); allocates Y with torch if not given."""
+    _check2d(A, "A")
+    _check2d(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _check2d(Y, "Y")
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be [M, N]")
+    st = lib().bi_gemm_ex(_ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(Y), Y.stride(0),
+                          M, N, K, _stream(stream), _opts(max_workgroups))
+    _raise(st, "bi_gemm")
+    return Y
+
+
+def bi_bmm(A, B, Y=None, *, stream=None, max_workgroups=0):
+    """Y[h] = A[h] . B[h] for A [H,M,K], B [H,K,N] (bf16)."""
+    if A.dim() != 3 or B.dim() != 3 or A.stride(2) != 1 or B.stride(2) != 1:
+        raise ValueError("A and B must be 3-D with unit stride along the last dimension")
+    H, M, K = A.shape
+    H2, K2, N = B.shape
+    if H != H2 or K != K2:
+        raise ValueError("A [H,M,K] and B [H,K,N] disagree")
+    if Y is None:
+        Y = torch.empty((H, M, N), dtype=torch.bfloat16, device=A.device)
+    if tuple(Y.shape) != (H, M, N) or Y.stride(2) != 1:
+        raise ValueError("Y must be [H, M, N] with unit last stride")
+    st = lib().bi_bmm_ex(_ptr(A), A.stride(0), A.stride(1), _ptr(B), B.stride(0), B.stride(1),
+                         _ptr(Y), Y.stride(0), Y.stride(1), H, M, N, K, _stream(stream),
+                         _opts(max_workgroups))
+    _raise(st, "bi_bmm")
+    return Y
+
+
+def bi_nvfp4_gemm(A, W, W_scales, alpha, Y=None, *, A_scales=None, K=None, stream=None,
+                  max_workgroups=0):
+    """Y[M,N] = alpha * A . W^T with NVFP4 W (codes [N,K/2] uint8, scales [N,K/16] uint8).
+
+    A is bf16 [M,K] when A_scales is None, else NVFP4 codes [M,K/2] with
+    scales [M,K/16].
+    """
+    N = W.shape[0]
+    if K is None:
+        K = W.shape[1] * 2
+    if tuple(W.shape) != (N, K // 2) or tuple(W_scales.shape) != (N, K // 16):
+        raise ValueError("W must be [N,K/2] and W_scales [N,K/16]")
+    if not (W.is_contiguous() and W_scales.is_contiguous()):
+        raise ValueError("W and W_scales must be dense")
+    M = A.shape[0]
+    if A_scales is None:
+        _check2d(A, "A")
+        if A.shape[1] != K:
+            raise ValueError("A must be [M,K]")
+        a_fmt, lda = BI_A_BF16, A.stride(0)
+    else:
+        if A.dim() != 2 or A.stride(1) != 1 or A.shape[1] != K // 2:
+            raise ValueError("NVFP4 A must be [M,K/2] with unit last stride")
+        if tuple(A_scales.shape) != (M, K // 16) or A_scales.stride(1) != 1:
+            raise ValueError("A_scales must be [M,K/16]")
+        if A_scales.stride(0) * 8 != A.stride(0):
+            raise ValueError("A and A_scales row strides must describe the same lda")
+        a_fmt, lda = BI_A_NVFP4, A.stride(0) * 2
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=W.device)
+    _check2d(Y, "Y")
+    st = lib().bi_nvfp4_gemm_ex(_ptr(A), _ptr(A_scales), a_fmt, lda, _ptr(W), _ptr(W_scales),
+                                float(alpha), _ptr(Y), Y.stride(0), M, N, K, _stream(stream),
+                                _opts(max_workgroups))
+    _raise(st, "bi_nvfp4_gemm")
+    return Y
+
+
+def bi_rmsnorm(X, gamma, eps, Y=None, *, stream=None, max_workgroups=0):
+    """Y[M,H] = X * rsqrt(mean(X^2) + eps) * gamma, row by row (bf16)."""
+    _check2d(X, "X")
+    M, H = X.shape
+    if gamma.dim() != 1 or gamma.shape[0] != H or not gamma.is_contiguous():
+        raise ValueError("gamma must be a dense [H] vector")
+    if Y is None:
+        Y = torch.empty((M, H), dtype=torch.bfloat16, device=X.device)
+    _check2d(Y, "Y")
+    st = lib().bi_rmsnorm_ex(_ptr(X), X.stride(0), _ptr(gamma), float(eps), _ptr(Y), Y.stride(0),
+                             M, H, _stream(stream), _opts(max_workgroups))
+    _raise(st, "bi_rmsnorm")
+    return Y

@@ -1,0 +1,311 @@
+// C-ABI layer of libbi: argument validation, the (op, N, K) -> recipe table,
+// persistent-grid sizing and kernel launch.  Declarations and the contract
+// are in include/bi.h.
+//
+// Nothing here looks at M except to size the grid, mask tails and validate
+// pointers: the recipe comes from bi_plan_query(op, N, K), which has no M
+// argument.  This is the batch-invariant kernel-selection rule: the vLLM PR
+// #39912 summary page (section "implementation breakdown") pins the default
+// config instead of the M-bucketed ones, and the vLLM PR #51292 page's
+// root-cause comment names size-gated selection as the failure mode.
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/bi.h"
+#include "bi_internal.h"
+
+namespace {
+
+using bi::GemmArgs;
+using bi::GemmRecipe;
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Half-open byte range of a [rows, cols] matrix with row stride ld elements of
+// esize bytes (esize_num/esize_den to allow half-byte NVFP4 codes).
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range mat_range(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t num, int64_t den) {
+    Range r;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    const int64_t elems = rows > 0 ? (rows - 1) * ld + cols : 0;
+    r.hi = r.lo + static_cast<uintptr_t>((elems * num + den - 1) / den);
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+// Compute-unit count of the current device, cached per device ordinal.
+std::atomic<int> g_cu_count[64];
+
+bi_status device_cus(int *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BI_ERR_HIP;
+    if (dev >= 0 && dev < 64) {
+        const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return BI_OK;
+        }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return BI_ERR_HIP;
+    if (dev >= 0 && dev < 64) g_cu_count[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return BI_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Recipe table.  Variants index the compiled tile shapes in gemm.hip:
+//   0: 128 x 128, 1: 128 x 64, 2: 64 x 64.
+// ---------------------------------------------------------------------------
+struct VariantShape {
+    int bm, bn;
+};
+constexpr VariantShape kVariants[] = {{128, 128}, {128, 64}, {64, 64}};
+
+int gemm_variant(int op, int64_t N, int64_t K) {
+    (void)K;
+    if (op == BI_OP_BMM) return 2;
+    if (N <= 1024) return 2;
+    if (N >= 8192) return 0;
+    return 1;
+}
+
+void fill_gemm_plan(int op, int variant, bi_plan *out) {
+    std::memset(out, 0, sizeof *out);
+    out->op = op;
+    out->bm = kVariants[variant].bm;
+    out->bn = kVariants[variant].bn;
+    out->bk = 64;
+    out->mfma_m = 16;
+    out->mfma_n = 16;
+    out->mfma_k = 32;
+    out->waves = 4;
+    out->lds_stages = 2;
+    out->threads = 256;
+    out->chunks_per_thread = 0;
+}
+
+// RMSNorm: T threads per row, CPT 16-byte chunks per thread, from H alone.
+bool rms_shape(int64_t H, int *T, int *cpt) {
+    if (H <= 0 || H % 8 != 0 || H > 32768) return false;
+    const int64_t chunks = H / 8;
+    *T = chunks <= 128 ? 64 : 256;
+    const int64_t need = (chunks + *T - 1) / *T;
+    int c = 1;
+    while (c < need) c *= 2;
+    *cpt = c;
+    return true;
+}
+
+int default_grid(int tiles, int cus, const bi_launch_opts *opts, int per_cu) {
+    int cap = cus * per_cu;
+    if (opts && opts->max_workgroups > 0) cap = opts->max_workgroups;
+    return tiles < cap ? tiles : cap;
+}
+
+bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *stream,
+                   const bi_launch_opts *opts) {
+    const int variant = gemm_variant(op, in.N, in.K);
+    GemmRecipe r{kVariants[variant].bm, kVariants[variant].bn, variant};
+    GemmArgs a = in;
+    a.tiles_m = static_cast<int>((a.M + r.bm - 1) / r.bm);
+    a.tiles_n = static_cast<int>((a.N + r.bn - 1) / r.bn);
+    const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n * a.batch;
+    if (tiles > kI32Max) return BI_ERR_UNSUPPORTED;
+    a.num_tiles = static_cast<int>(tiles);
+    int cus = 0;
+    bi_status st = device_cus(&cus);
+    if (st != BI_OK) return st;
+    const int grid = default_grid(a.num_tiles, cus, opts, 2);
+    hipError_t e = bi::launch_gemm(a_mode, b_mode, r, a, grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bi_status_str(bi_status s) {
+    switch (s) {
+        case BI_OK: return "BI_OK";
+        case BI_ERR_NULL: return "BI_ERR_NULL: a required pointer is NULL";
+        case BI_ERR_SHAPE: return "BI_ERR_SHAPE: invalid sizes or leading dimensions";
+        case BI_ERR_ALIGN: return "BI_ERR_ALIGN: pointer or stride not 16-byte aligned";
+        case BI_ERR_ALIAS: return "BI_ERR_ALIAS: output overlaps an input";
+        case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: no batch-invariant plan for this shape";
+        case BI_ERR_HIP: return "BI_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown bi_status";
+}
+
+const char *bi_version(void) { return "bi 0.1.0 gfx950"; }
+
+bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
+    if (!out) return BI_ERR_NULL;
+    switch (op) {
+        case BI_OP_GEMM:
+        case BI_OP_BMM:
+        case BI_OP_NVFP4_GEMM: {
+            if (N <= 0 || K <= 0) return BI_ERR_SHAPE;
+            if (op == BI_OP_NVFP4_GEMM ? (K % 32 != 0) : (K % 8 != 0)) return BI_ERR_SHAPE;
+            if (op == BI_OP_BMM && N % 8 != 0) return BI_ERR_SHAPE;
+            if (N > kI32Max || K > kI32Max) return BI_ERR_UNSUPPORTED;
+            fill_gemm_plan(op, gemm_variant(op, N, K), out);
+            return BI_OK;
+        }
+        case BI_OP_RMSNORM: {
+            int T = 0, cpt = 0;
+            if (!rms_shape(N, &T, &cpt)) return N > 32768 && N % 8 == 0 ? BI_ERR_UNSUPPORTED : BI_ERR_SHAPE;
+            std::memset(out, 0, sizeof *out);
+            out->op = op;
+            out->threads = T;
+            out->waves = T / 64;
+            out->chunks_per_thread = cpt;
+            return BI_OK;
+        }
+    }
+    return BI_ERR_UNSUPPORTED;
+}
+
+bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y, int64_t ldy,
+                     int64_t M, int64_t N, int64_t K, void *stream, const bi_launch_opts *opts) {
+    if (M < 0 || N <= 0 || K <= 0 || K % 8 != 0) return BI_ERR_SHAPE;
+    if (lda < K || ldb < K || ldy < N) return BI_ERR_SHAPE;
+    if (M > kI32Max || N > kI32Max || K > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M == 0) return BI_OK;
+    if (!A || !B || !Y) return BI_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(Y) || lda % 8 || ldb % 8) return BI_ERR_ALIGN;
+    const Range ry = mat_range(Y, M, N, ldy, 2, 1);
+    if (overlap(ry, mat_range(A, M, K, lda, 2, 1)) || overlap(ry, mat_range(B, N, K, ldb, 2, 1)))
+        return BI_ERR_ALIAS;
+    GemmArgs a{};
+    a.A = A; a.B = B; a.Y = Y;
+    a.lda = lda; a.ldb = ldb; a.ldy = ldy;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.batch = 1;
+    a.alpha = 1.0f;
+    return run_gemm(bi::OPND_BF16_ROWS, bi::OPND_BF16_ROWS, BI_OP_GEMM, a, stream, opts);
+}
+
+bi_status bi_gemm(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y, int64_t ldy,
+                  int64_t M, int64_t N, int64_t K, void *stream) {
+    return bi_gemm_ex(A, lda, B, ldb, Y, ldy, M, N, K, stream, nullptr);
+}
+
+bi_status bi_bmm_ex(const void *A, int64_t sA, int64_t lda, const void *B, int64_t sB, int64_t ldb,
+                    void *Y, int64_t sY, int64_t ldy, int64_t batch, int64_t M, int64_t N, int64_t K,
+                    void *stream, const bi_launch_opts *opts) {
+    if (M < 0 || N <= 0 || K <= 0 || batch <= 0 || K % 8 != 0 || N % 8 != 0) return BI_ERR_SHAPE;
+    if (lda < K || ldb < N || ldy < N) return BI_ERR_SHAPE;
+    if (batch > 1 && (sA < (M > 0 ? (M - 1) * lda + K : 0) || sB < (K - 1) * ldb + N ||
+                      sY < (M > 0 ? (M - 1) * ldy + N : 0) || sA < 0 || sB < 0 || sY < 0))
+        return BI_ERR_SHAPE;
+    if (M > kI32Max || N > kI32Max || K > kI32Max || batch > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M == 0) return BI_OK;
+    if (!A || !B || !Y) return BI_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(Y) || lda % 8 || ldb % 8 || sA % 8 || sB % 8 ||
+        sY % 8)
+        return BI_ERR_ALIGN;
+    // Whole-tensor spans (head strides are >= the per-head extent, checked above).
+    const Range ra = mat_range(A, 1, (batch - 1) * sA + (M - 1) * lda + K, 0, 2, 1);
+    const Range rb = mat_range(B, 1, (batch - 1) * sB + (K - 1) * ldb + N, 0, 2, 1);
+    const Range ry2 = mat_range(Y, 1, (batch - 1) * sY + (M - 1) * ldy + N, 0, 2, 1);
+    if (overlap(ry2, ra) || overlap(ry2, rb)) return BI_ERR_ALIAS;
+    GemmArgs a{};
+    a.A = A; a.B = B; a.Y = Y;
+    a.lda = lda; a.ldb = ldb; a.ldy = ldy;
+    a.sA = sA; a.sB = sB; a.sY = sY;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.batch = (int)batch;
+    a.alpha = 1.0f;
+    return run_gemm(bi::OPND_BF16_ROWS, bi::OPND_BF16_KN, BI_OP_BMM, a, stream, opts);
+}
+
+bi_status bi_bmm(const void *A, int64_t sA, int64_t lda, const void *B, int64_t sB, int64_t ldb,
+                 void *Y, int64_t sY, int64_t ldy, int64_t batch, int64_t M, int64_t N, int64_t K,
+                 void *stream) {
+    return bi_bmm_ex(A, sA, lda, B, sB, ldb, Y, sY, ldy, batch, M, N, K, stream, nullptr);
+}
+
+bi_status bi_nvfp4_gemm_ex(const void *A, const void *A_scales, int a_fmt, int64_t lda,
+                           const void *W, const void *W_scales, float alpha, void *Y, int64_t ldy,
+                           int64_t M, int64_t N, int64_t K, void *stream,
+                           const bi_launch_opts *opts) {
+    if (a_fmt != BI_A_BF16 && a_fmt != BI_A_NVFP4) return BI_ERR_SHAPE;
+    if (M < 0 || N <= 0 || K <= 0 || K % 32 != 0) return BI_ERR_SHAPE;
+    if (lda < K || ldy < N) return BI_ERR_SHAPE;
+    if (M > kI32Max || N > kI32Max || K > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M == 0) return BI_OK;
+    if (!A || !W || !W_scales || !Y || (a_fmt == BI_A_NVFP4 && !A_scales)) return BI_ERR_NULL;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(W_scales) || !aligned16(Y)) return BI_ERR_ALIGN;
+    if (a_fmt == BI_A_NVFP4 && (!aligned16(A_scales) || lda % 32)) return BI_ERR_ALIGN;
+    if (a_fmt == BI_A_BF16 && lda % 8) return BI_ERR_ALIGN;
+    const Range ry = mat_range(Y, M, N, ldy, 2, 1);
+    if (overlap(ry, mat_range(W, N, K, K, 1, 2)) || overlap(ry, mat_range(W_scales, N, K, K, 1, 16)))
+        return BI_ERR_ALIAS;
+    if (a_fmt == BI_A_BF16) {
+        if (overlap(ry, mat_range(A, M, K, lda, 2, 1))) return BI_ERR_ALIAS;
+    } else {
+        if (overlap(ry, mat_range(A, M, K, lda, 1, 2)) || overlap(ry, mat_range(A_scales, M, K, lda, 1, 16)))
+            return BI_ERR_ALIAS;
+    }
+    GemmArgs a{};
+    a.A = A; a.A_scales = A_scales; a.B = W; a.B_scales = W_scales; a.Y = Y;
+    a.lda = lda; a.ldb = K; a.ldy = ldy;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.batch = 1;
+    a.alpha = alpha;
+    a.use_alpha = 1;
+    const int am = a_fmt == BI_A_BF16 ? bi::OPND_BF16_ROWS : bi::OPND_NVFP4_ROWS;
+    return run_gemm(am, bi::OPND_NVFP4_ROWS, BI_OP_NVFP4_GEMM, a, stream, opts);
+}
+
+bi_status bi_nvfp4_gemm(const void *A, const void *A_scales, int a_fmt, int64_t lda, const void *W,
+                        const void *W_scales, float alpha, void *Y, int64_t ldy, int64_t M,
+                        int64_t N, int64_t K, void *stream) {
+    return bi_nvfp4_gemm_ex(A, A_scales, a_fmt, lda, W, W_scales, alpha, Y, ldy, M, N, K, stream,
+                            nullptr);
+}
+
+bi_status bi_rmsnorm_ex(const void *X, int64_t ldx, const void *gamma, float eps, void *Y,
+                        int64_t ldy, int64_t M, int64_t H, void *stream,
+                        const bi_launch_opts *opts) {
+    int T = 0, cpt = 0;
+    if (M < 0 || H <= 0 || H % 8 != 0) return BI_ERR_SHAPE;
+    if (ldx < H || ldy < H) return BI_ERR_SHAPE;
+    if (!rms_shape(H, &T, &cpt)) return BI_ERR_UNSUPPORTED;
+    if (M > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M == 0) return BI_OK;
+    if (!X || !gamma || !Y) return BI_ERR_NULL;
+    if (!aligned16(X) || !aligned16(gamma) || !aligned16(Y) || ldx % 8 || ldy % 8) return BI_ERR_ALIGN;
+    const Range ry = mat_range(Y, M, H, ldy, 2, 1);
+    const Range rx = mat_range(X, M, H, ldx, 2, 1);
+    const bool in_place = (X == Y && ldx == ldy);
+    if ((!in_place && overlap(ry, rx)) || overlap(ry, mat_range(gamma, 1, H, H, 2, 1)))
+        return BI_ERR_ALIAS;
+    int cus = 0;
+    bi_status st = device_cus(&cus);
+    if (st != BI_OK) return st;
+    bi::RmsArgs a{};
+    a.X = X; a.gamma = gamma; a.Y = Y;
+    a.ldx = ldx; a.ldy = ldy;
+    a.M = (int)M; a.H = (int)H; a.eps = eps;
+    const int grid = default_grid((int)M, cus, opts, 16);
+    hipError_t e = bi::launch_rmsnorm(T, cpt, a, grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+bi_status bi_rmsnorm(const void *X, int64_t ldx, const void *gamma, float eps, void *Y, int64_t ldy,
+                     int64_t M, int64_t H, void *stream) {
+    return bi_rmsnorm_ex(X, ldx, gamma, eps, Y, ldy, M, H, stream, nullptr);
+}
+
+}  // extern "C"

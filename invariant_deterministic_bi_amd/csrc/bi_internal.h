@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel
+// translation units (gemm.hip, rmsnorm.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+// Operand storage modes of the GEMM mainloop.
+enum OperandMode : int {
+    OPND_BF16_ROWS = 0,  // bf16 [rows, K], K contiguous (GEMM A and B, BMM A)
+    OPND_BF16_KN = 1,    // bf16 [K, cols], cols contiguous (BMM B)
+    OPND_NVFP4_ROWS = 2  // e2m1 codes [rows, K/2] + e4m3 scales [rows, K/16]
+};
+
+// Tile recipe selected from (op, N, K).  `variant` indexes the compiled
+// kernel instantiation that implements (bm, bn).
+struct GemmRecipe {
+    int bm, bn;
+    int variant;
+};
+
+struct GemmArgs {
+    const void *A;        // operand A base
+    const void *A_scales; // NVFP4 A scales (mode OPND_NVFP4_ROWS)
+    const void *B;
+    const void *B_scales;
+    void *Y;
+    int64_t lda, sA;      // A row stride (elements), head stride (elements)
+    int64_t ldb, sB;
+    int64_t ldy, sY;
+    int M, N, K, batch;
+    int tiles_m, tiles_n;
+    int num_tiles;
+    float alpha;
+    int use_alpha;
+};
+
+// Launchers; they return hipSuccess or the launch error.
+hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmArgs &args,
+                       int grid, hipStream_t stream);
+
+struct RmsArgs {
+    const void *X;
+    const void *gamma;
+    void *Y;
+    int64_t ldx, ldy;
+    int M, H;
+    float eps;
+};
+
+hipError_t launch_rmsnorm(int threads, int chunks_per_thread, const RmsArgs &args, int grid,
+                          hipStream_t stream);
+
+}  // namespace bi

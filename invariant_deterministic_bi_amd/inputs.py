@@ -71,7 +71,8 @@ def randint_bf16(shape, lo: int, hi: int, seed: int = BASE_SEED, tag=(0,)) -> np
 # here: g = 448 * 6 / amax|X| (maps the tensor's largest magnitude onto the
 # largest product of an E4M3 scale and an E2M1 value); per 16-element block,
 # scale s = E4M3_RNE(min(amax_blk * g / 6, 448)); element code
-# q = E2M1_RNE(x * g / s), saturating at +-6, ties to even, q = 0 when s = 0.
+# q = E2M1_RNE(|x| * (g / s)) with the sign of x, saturating at 6, ties to
+# even, q = 0 when s = 0.
 # The GEMM consumes only the stored codes, so this choice cannot move parity.
 # --------------------------------------------------------------------------
 
@@ -115,27 +116,45 @@ def nvfp4_global_scale(x) -> np.float32:
     return np.float32(1.0) if amax == 0.0 else np.float32(448.0 * 6.0 / amax)
 
 
+def _e2m1_rne_code(t: np.ndarray) -> np.ndarray:
+    """E2M1 magnitude code (0..7) nearest to t >= 0, ties to the even code,
+    saturating at 6.  The decision points are the midpoints between adjacent
+    magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; at a midpoint the even code wins,
+    hence '>' where the lower neighbour is even and '>=' where the upper is."""
+    mids = ((0.25, False), (0.75, True), (1.25, False), (1.75, True),
+            (2.5, False), (3.5, True), (5.0, False))
+    code = np.zeros(t.shape, np.uint8)
+    for m, upper_even in mids:
+        code += (t >= m) if upper_even else (t > m)
+    return code
+
+
 def nvfp4_quantize(x, global_scale) -> tuple[np.ndarray, np.ndarray]:
     """Quantise real values x [R, K] (K % 16 == 0) with a given global scale.
 
     Returns (codes uint8 [R, K/2], scales uint8 [R, K/16]).  Each row depends
     only on itself and the global scale, so quantising a row alone with the
     same global scale gives the same bytes as quantising it inside a batch.
+    Large inputs are processed in row blocks to bound host memory.
     """
-    x = np.asarray(x, np.float64)
+    x = np.asarray(x)
     R, K = x.shape
     assert K % 16 == 0
     g = float(np.float32(global_scale))
-    blk = x.reshape(R, K // 16, 16)
-    amax = np.max(np.abs(blk), axis=2)
-    s_code = _round_to_table(np.minimum(amax * g / 6.0, 448.0), _E4M3)
-    s_val = _E4M3[s_code]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        t = np.where(s_val[..., None] > 0, np.abs(blk) * g / s_val[..., None], 0.0)
-    q = _round_to_table(t, _E2M1)
-    q = np.where(np.signbit(blk) & (q != 0), q | 8, q).reshape(R, K)
-    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
-    return codes, s_code.astype(np.uint8)
+    codes = np.empty((R, K // 2), np.uint8)
+    scales = np.empty((R, K // 16), np.uint8)
+    step = max(1, (1 << 22) // K)
+    for r0 in range(0, R, step):
+        blk = np.asarray(x[r0:r0 + step], np.float64).reshape(-1, K // 16, 16)
+        amax = np.max(np.abs(blk), axis=2)
+        s_code = _round_to_table(np.minimum(amax * g / 6.0, 448.0), _E4M3)
+        s_val = _E4M3[s_code]
+        inv = np.where(s_val > 0, g / np.where(s_val > 0, s_val, 1.0), 0.0)
+        q = _e2m1_rne_code(np.abs(blk) * inv[..., None])
+        q = np.where(np.signbit(blk) & (q != 0), q | np.uint8(8), q).reshape(-1, K)
+        codes[r0:r0 + step] = q[:, 0::2] | (q[:, 1::2] << np.uint8(4))
+        scales[r0:r0 + step] = s_code.astype(np.uint8)
+    return codes, scales
 
 
 def random_nvfp4_pow2(shape, seed: int = BASE_SEED, tag=(0,), exp_range=(-3, 3)):

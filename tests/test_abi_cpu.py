@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, plans are keyed on (op, N, K) only, and argument validation
+rejects bad calls before anything is launched.
+
+Every call below is rejected by validation or is an M == 0 no-op, so no
+kernel is ever launched (fake addresses are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from invariant_deterministic_bi_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "bi.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.lib()
+    names = header_functions()
+    assert {"bi_gemm", "bi_bmm", "bi_nvfp4_gemm", "bi_rmsnorm", "bi_plan_query",
+            "bi_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libbi.so does not export {n}"
+
+
+def test_status_strings():
+    for s in range(7):
+        assert B.status_str(s)
+    assert "UNSUPPORTED" in B.status_str(B.BI_ERR_UNSUPPORTED)
+    assert B.version().startswith("bi ")
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (6144, 4096), (4096, 4096), (24576, 4096),
+                                 (4096, 12288), (200, 544)])
+def test_plan_is_fixed_per_NK(N, K):
+    p = B.plan_query(B.BI_OP_GEMM, N, K)
+    assert p["mfma_m"] == 16 and p["mfma_n"] == 16 and p["mfma_k"] == 32
+    assert p["bm"] > 0 and p["bn"] > 0 and p["bk"] == 64
+    # the same key always gives the same plan
+    assert p == B.plan_query(B.BI_OP_GEMM, N, K)
+
+
+def test_nvfp4_plan_uses_the_bf16_recipe():
+    # same MFMA instruction and K order as the bf16 GEMM for the same (N, K)
+    g = B.plan_query(B.BI_OP_GEMM, 24576, 4096)
+    f = B.plan_query(B.BI_OP_NVFP4_GEMM, 24576, 4096)
+    for k in ("mfma_m", "mfma_n", "mfma_k", "bk"):
+        assert g[k] == f[k]
+
+
+def test_plan_query_rejects():
+    with pytest.raises(B.BiError) as e:
+        B.plan_query(B.BI_OP_GEMM, 256, 12)
+    assert e.value.status == B.BI_ERR_SHAPE
+    with pytest.raises(B.BiError) as e:
+        B.plan_query(B.BI_OP_NVFP4_GEMM, 256, 48)
+    assert e.value.status == B.BI_ERR_SHAPE
+    with pytest.raises(B.BiError) as e:
+        B.plan_query(B.BI_OP_RMSNORM, 4100, 0)
+    assert e.value.status == B.BI_ERR_SHAPE
+    with pytest.raises(B.BiError) as e:
+        B.plan_query(B.BI_OP_RMSNORM, 65536, 0)
+    assert e.value.status == B.BI_ERR_UNSUPPORTED
+    with pytest.raises(B.BiError):
+        B.plan_query(99, 256, 512)
+
+
+def test_rmsnorm_plan():
+    p = B.plan_query(B.BI_OP_RMSNORM, 512, 0)
+    assert p["threads"] == 64 and p["chunks_per_thread"] == 1
+    p = B.plan_query(B.BI_OP_RMSNORM, 4096, 0)
+    assert p["threads"] == 256 and p["chunks_per_thread"] == 2
+
+
+A0, B0, Y0 = 0x10000, 0x200000, 0x4000000   # fake, 16-byte aligned, disjoint
+
+
+def gemm(A=A0, lda=512, Bp=B0, ldb=512, Y=Y0, ldy=256, M=4, N=256, K=512):
+    return B.lib().bi_gemm(A, lda, Bp, ldb, Y, ldy, M, N, K, None)
+
+
+def test_gemm_validation():
+    assert gemm(M=-1) == B.BI_ERR_SHAPE
+    assert gemm(K=12, lda=16, ldb=16) == B.BI_ERR_SHAPE
+    assert gemm(lda=256) == B.BI_ERR_SHAPE
+    assert gemm(ldy=100) == B.BI_ERR_SHAPE
+    assert gemm(N=0) == B.BI_ERR_SHAPE
+    assert gemm(A=0) == B.BI_ERR_NULL
+    assert gemm(Y=0) == B.BI_ERR_NULL
+    assert gemm(A=A0 + 2) == B.BI_ERR_ALIGN
+    assert gemm(lda=516) == B.BI_ERR_ALIGN
+    assert gemm(Y=A0 + 16) == B.BI_ERR_ALIAS
+    assert gemm(Y=B0 + 4096) == B.BI_ERR_ALIAS
+    # M == 0 is a no-op, even with NULL pointers
+    assert gemm(M=0, A=0, Bp=0, Y=0) == B.BI_OK
+
+
+def test_bmm_validation():
+    f = B.lib().bi_bmm
+    # A [2,4,128], B [2,128,512], Y [2,4,512]
+    ok = dict(A=A0, sA=512, lda=128, B=B0, sB=65536, ldb=512, Y=Y0, sY=2048, ldy=512,
+              batch=2, M=4, N=512, K=128)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["A"], a["sA"], a["lda"], a["B"], a["sB"], a["ldb"], a["Y"], a["sY"], a["ldy"],
+                 a["batch"], a["M"], a["N"], a["K"], None)
+    assert call(N=500, ldb=500, ldy=500) == B.BI_ERR_SHAPE
+    assert call(batch=0) == B.BI_ERR_SHAPE
+    assert call(sA=100) == B.BI_ERR_SHAPE
+    assert call(Y=0) == B.BI_ERR_NULL
+    assert call(Y=B0 + 16) == B.BI_ERR_ALIAS
+    assert call(M=0, A=0, B=0, Y=0) == B.BI_OK
+
+
+def test_nvfp4_validation():
+    f = B.lib().bi_nvfp4_gemm
+
+    def call(A=A0, As=0, fmt=0, lda=4096, W=B0, Ws=B0 + 0x1000000, alpha=1.0, Y=Y0, ldy=256,
+             M=4, N=256, K=4096):
+        return f(A, As, fmt, lda, W, Ws, alpha, Y, ldy, M, N, K, None)
+    assert call(K=4080, lda=4080) == B.BI_ERR_SHAPE
+    assert call(fmt=7) == B.BI_ERR_SHAPE
+    assert call(fmt=1) == B.BI_ERR_NULL           # NVFP4 A needs scales
+    assert call(Ws=0) == B.BI_ERR_NULL
+    assert call(fmt=1, As=0x3000000, lda=4104) == B.BI_ERR_ALIGN
+    assert call(Y=B0 + 64) == B.BI_ERR_ALIAS
+    assert call(M=0, A=0, W=0, Ws=0, Y=0) == B.BI_OK
+
+
+def test_rmsnorm_validation():
+    f = B.lib().bi_rmsnorm
+
+    def call(X=A0, ldx=4096, g=B0, eps=1e-6, Y=Y0, ldy=4096, M=4, H=4096):
+        return f(X, ldx, g, eps, Y, ldy, M, H, None)
+    assert call(H=4100, ldx=4104, ldy=4104) == B.BI_ERR_SHAPE
+    assert call(H=65536, ldx=65536, ldy=65536) == B.BI_ERR_UNSUPPORTED
+    assert call(g=0) == B.BI_ERR_NULL
+    assert call(Y=A0 + 32) == B.BI_ERR_ALIAS      # partial overlap with X
+    assert call(Y=B0) == B.BI_ERR_ALIAS           # overlaps gamma
+    assert call(M=0, X=0, g=0, Y=0) == B.BI_OK

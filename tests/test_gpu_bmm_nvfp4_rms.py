@@ -1,0 +1,179 @@
+"""GPU parity and invariance tests of bi_bmm, bi_nvfp4_gemm and bi_rmsnorm."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_deterministic_bi_amd import inputs
+from invariant_deterministic_bi_amd import binding as B
+from harness import assert_within_tol, rne_bf16_of_exact, bf16_to_f64, ulp_bf16
+from gpu_util import dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+# ----------------------------------------------------------------- BMM
+
+
+def test_bmm_mla_shape_parity_and_invariance():
+    """128 heads, per head A[M,128] . B[128,512]; M in {1,16,128,1024}."""
+    H, K, N, Mmax = 128, 128, 512, 1024
+    A = inputs.randn_bf16((H, Mmax, K), tag=(100,))
+    W = inputs.randn_bf16((H, K, N), tag=(101,))
+    Ad, Wd = dev(A), dev(W)
+    note("bmm M=1024")
+    yfull = host(B.bi_bmm(Ad, Wd))
+    heads = [0, 5, 127]
+    ref, s = oracle.bmm(A[heads][:, :64], W[heads])
+    assert_within_tol(yfull[heads][:, :64], ref, s, "bmm heads rows 0..63")
+    for M in (1, 16, 128):
+        note(f"bmm M={M}")
+        y = host(B.bi_bmm(Ad[:, :M].contiguous(), Wd))
+        assert np.array_equal(y, yfull[:, :M]), f"M={M}"
+        # strided head views (no copy) must agree too
+        y2 = host(B.bi_bmm(Ad[:, :M], Wd))
+        assert np.array_equal(y2, yfull[:, :M])
+    g = inputs.rng(12345, 102)
+    for trial in range(3):            # head subsets and row permutations
+        hs = np.sort(g.choice(H, size=[1, 7, 33][trial], replace=False))
+        rows = g.permutation(Mmax)[:[16, 129, 5][trial]]
+        sub = Ad[torch.from_numpy(hs).cuda()][:, torch.from_numpy(rows).cuda()].contiguous()
+        note(f"bmm subset trial {trial}")
+        y = host(B.bi_bmm(sub, Wd[torch.from_numpy(hs).cuda()].contiguous()))
+        assert np.array_equal(y, yfull[hs][:, rows])
+
+
+def test_bmm_integer_exact_and_ragged():
+    H, M, K, N = 6, 70, 136, 200
+    A = inputs.randint_bf16((H, M, K), -3, 3, tag=(110,))
+    W = inputs.randint_bf16((H, K, N), -3, 3, tag=(111,))
+    ref, _ = oracle.bmm(A, W)
+    note("bmm integer ragged")
+    y = host(B.bi_bmm(dev(A), dev(W)))
+    assert np.array_equal(y, rne_bf16_of_exact(ref))
+    An = inputs.randn_bf16((H, M, K), tag=(112,))
+    Wn = inputs.randn_bf16((H, K, N), tag=(113,))
+    ref, s = oracle.bmm(An, Wn)
+    y = host(B.bi_bmm(dev(An), dev(Wn)))
+    assert_within_tol(y, ref, s, "bmm ragged gaussian")
+
+
+# ----------------------------------------------------------------- NVFP4
+
+def _nvfp4_weights(N, K, tag):
+    x = inputs.rng(12345, *tag).standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
+    g = inputs.nvfp4_global_scale(x)
+    W, Ws = inputs.nvfp4_quantize(x, g)
+    return W, Ws, g
+
+
+def test_nvfp4_integer_exact_pow2():
+    M, N, K = 40, 200, 512
+    W, Ws = inputs.random_nvfp4_pow2((N, K), tag=(120,))
+    A = inputs.randint_bf16((M, K), -3, 3, tag=(121,))
+    ref, _ = oracle.nvfp4_gemm(A, None, W, Ws, 1.0, K)
+    note("nvfp4 integer pow2")
+    y = host(B.bi_nvfp4_gemm(dev(A), dev(W), dev(Ws), 1.0))
+    assert np.array_equal(y, rne_bf16_of_exact(ref))
+    Aq, Aqs = inputs.random_nvfp4_pow2((M, K), tag=(122,))
+    ref, _ = oracle.nvfp4_gemm(Aq, Aqs, W, Ws, 0.5, K)
+    y = host(B.bi_nvfp4_gemm(dev(Aq), dev(W), dev(Ws), 0.5, A_scales=dev(Aqs)))
+    assert np.array_equal(y, rne_bf16_of_exact(ref))
+
+
+def test_nvfp4_equals_bf16_gemm_on_decoded_weights():
+    """alpha == 1: bitwise the bf16 GEMM of the exactly decoded weights."""
+    M, N, K = 96, 4096, 4096
+    W, Ws, g = _nvfp4_weights(N, K, (123,))
+    A = inputs.randn_bf16((M, K), tag=(124,))
+    # decode with the oracle's decoders (test side), round (exactly) to bf16
+    lut = np.array([oracle.e2m1_value(c) for c in range(16)])
+    sv = np.array([oracle.e4m3_value(c) if c not in (0x7F, 0xFF) else 0.0 for c in range(256)])
+    q = np.empty((N, K), np.int64)
+    q[:, 0::2] = W & 15
+    q[:, 1::2] = W >> 4
+    wdec = inputs.to_bf16_bits(lut[q] * np.repeat(sv[Ws], 16, axis=1))
+    note("nvfp4 vs bf16 gemm")
+    y4 = host(B.bi_nvfp4_gemm(dev(A), dev(W), dev(Ws), 1.0))
+    yb = host(B.bi_gemm(dev(A), dev(wdec)))
+    assert np.array_equal(y4, yb)
+
+
+def test_nvfp4_config_parity_and_invariance():
+    """W[24576,4096] quantised from N(0,0.02); A bf16 N(0,1), M up to 4096."""
+    N, K, Mmax = 24576, 4096, 4096
+    W, Ws, g = _nvfp4_weights(N, K, (125,))
+    alpha = float(np.float32(1.0) / g)
+    A = inputs.randn_bf16((Mmax, K), tag=(126,))
+    Ad, Wd, Wsd = dev(A), dev(W), dev(Ws)
+    note("nvfp4 M=4096")
+    yfull = host(B.bi_nvfp4_gemm(Ad, Wd, Wsd, alpha))
+    rows = np.array([0, 1, 2, 1000, Mmax - 1])
+    ref, s = oracle.nvfp4_gemm(A, None, W, Ws, alpha, K, rows=rows)
+    assert_within_tol(yfull[rows], ref, s, "nvfp4 sampled rows")
+    for M in (1, 2, 4, 16, 64, 256, 1024):
+        note(f"nvfp4 M={M}")
+        y = host(B.bi_nvfp4_gemm(Ad[:M], Wd, Wsd, alpha))
+        assert np.array_equal(y, yfull[:M]), f"M={M}"
+
+
+def test_nvfp4_activation_rows_quantised_alone():
+    """W4A4: a row quantised alone with the batch's global scale gives the
+    same codes, hence the same output row."""
+    N, K, M = 2048, 4096, 64
+    W, Ws, gw = _nvfp4_weights(N, K, (127,))
+    x = inputs.rng(12345, 128).standard_normal((M, K)).astype(np.float32)
+    ga = inputs.nvfp4_global_scale(x)
+    Aq, Aqs = inputs.nvfp4_quantize(x, ga)
+    alpha = float(np.float32(1.0) / (ga * gw))
+    note("nvfp4 W4A4 full")
+    yfull = host(B.bi_nvfp4_gemm(dev(Aq), dev(W), dev(Ws), alpha, A_scales=dev(Aqs)))
+    ref, s = oracle.nvfp4_gemm(Aq, Aqs, W, Ws, alpha, K, rows=[0, 31, 63])
+    assert_within_tol(yfull[[0, 31, 63]], ref, s, "w4a4 rows")
+    for i in (0, 17, 63):
+        qi, si = inputs.nvfp4_quantize(x[i:i + 1], ga)
+        yi = host(B.bi_nvfp4_gemm(dev(qi), dev(W), dev(Ws), alpha, A_scales=dev(si)))
+        assert np.array_equal(yi[0], yfull[i]), f"row {i}"
+
+
+# ----------------------------------------------------------------- RMSNorm
+
+
+@pytest.mark.parametrize("H,Mmax", [(512, 64), (4096, 2048), (1000, 33), (8, 5), (12288, 100)])
+def test_rmsnorm_parity_and_invariance(H, Mmax):
+    X = inputs.randn_bf16((Mmax, H), tag=(130, H))
+    gam = inputs.uniform_bf16((H,), 0.5, 1.5, tag=(131, H))
+    eps = 1e-6
+    ref = oracle.rmsnorm(X, gam, eps)
+    Xd, gd = dev(X), dev(gam)
+    note(f"rmsnorm H={H} M={Mmax}")
+    y = host(B.bi_rmsnorm(Xd, gd, eps))
+    assert_within_tol(y, ref, np.abs(ref), f"rmsnorm H={H}")
+    for M in sorted({1, 2, 7, Mmax // 2}):
+        yM = host(B.bi_rmsnorm(Xd[:M], gd, eps))
+        assert np.array_equal(yM, y[:M])
+    perm = inputs.rng(12345, 132).permutation(Mmax)
+    yp = host(B.bi_rmsnorm(Xd[torch.from_numpy(perm).cuda()].contiguous(), gd, eps))
+    assert np.array_equal(yp, y[perm])
+    for mw in (1, 3, 1000):
+        assert np.array_equal(host(B.bi_rmsnorm(Xd, gd, eps, max_workgroups=mw)), y)
+    outs = {host(B.bi_rmsnorm(Xd, gd, eps)).tobytes() for _ in range(8)}
+    assert len(outs) == 1
+
+
+def test_rmsnorm_closed_forms_and_inplace():
+    H = 4096
+    gam = inputs.uniform_bf16((H,), 0.5, 1.5, tag=(133,))
+    rows = np.stack([np.zeros(H), np.where(np.arange(H) % 5 == 0, -8.0, 8.0),
+                     np.full(H, 0.25)])
+    X = inputs.to_bf16_bits(rows)
+    note("rmsnorm closed forms")
+    y = host(B.bi_rmsnorm(dev(X), dev(gam), 1e-6))
+    assert not bf16_to_f64(y[0]).any()
+    gv = bf16_to_f64(gam)
+    assert np.array_equal(bf16_to_f64(y[1]), np.sign(rows[1]) * gv)   # +-2^p row -> +-gamma
+    assert np.array_equal(bf16_to_f64(y[2]), gv)                       # constant row, eps << ulp
+    Xr = inputs.randn_bf16((64, H), tag=(134,))
+    Xd = dev(Xr)
+    ref = host(B.bi_rmsnorm(Xd, dev(gam), 1e-6))
+    B.bi_rmsnorm(Xd, dev(gam), 1e-6, Xd)      # in place
+    assert np.array_equal(host(Xd), ref)

@@ -1,0 +1,198 @@
+"""GPU parity and batch-invariance tests of bi_gemm (through the C ABI).
+
+Parity: the HIP result against the fp64 oracle, element by element, within
+|y - y_ref| <= ulp_bf16(y_ref) + 1e-3 * sum_k |a_k b_k|; bit-exact where the
+inputs make every fp32 partial sum exact (small integers).
+Invariance (bitwise, GPU against GPU): every M of a sweep against the largest
+M (prefix rows), singletons, row permutations, gathered subsets at shifted
+base addresses, 8 repeated runs, and persistent-grid overrides.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_deterministic_bi_amd import inputs
+from invariant_deterministic_bi_amd import binding as B
+from harness import assert_within_tol, rne_bf16_of_exact, bf16_to_f64
+from gpu_util import dev, host, note, loaded_hip_runtimes
+
+pytestmark = pytest.mark.gpu
+
+
+def gemm(A, Bw, **kw):
+    return B.bi_gemm(A, Bw, **kw)
+
+
+def test_one_hip_runtime_and_torch_stream():
+    a = dev(inputs.randn_bf16((4, 64), tag=(900,)))
+    b = dev(inputs.randn_bf16((16, 64), tag=(901,)))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = gemm(a, b, stream=s)
+    s.synchronize()
+    libs = loaded_hip_runtimes()
+    assert len(libs) == 1, libs
+    ref, _ = oracle.gemm(host(a), host(b))
+    assert np.abs(bf16_to_f64(host(y)) - ref).max() < 1e-1
+
+
+def test_tiny_config_parity_and_invariance():
+    """A[M,512] . B[256,512]^T, N(0,1) inputs, M in {1,3,7,16,64}."""
+    K, N = 512, 256
+    A = inputs.randn_bf16((64, K), tag=(1,))
+    W = inputs.randn_bf16((N, K), tag=(2,))
+    ref, s = oracle.gemm(A, W)
+    Ad, Wd = dev(A), dev(W)
+    note("gemm tiny M=64")
+    y64 = host(gemm(Ad, Wd))
+    assert_within_tol(y64, ref, s, "tiny M=64")
+    for M in (1, 3, 7, 16):
+        note(f"gemm tiny M={M}")
+        yM = host(gemm(Ad[:M], Wd))
+        assert np.array_equal(yM, y64[:M]), f"prefix rows differ at M={M}"
+    for i in range(64):
+        yi = host(gemm(Ad[i:i + 1], Wd))
+        assert np.array_equal(yi[0], y64[i]), f"row {i} differs between M=1 and M=64"
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 200, 544), (7, 4096, 4096), (64, 6144, 4096),
+                                   (33, 4096, 12288), (300, 256, 512)])
+def test_integer_exact(M, N, K):
+    """Entries in {-3..3}: every partial sum is an exact fp32 integer, so the
+    output must be bf16_rne(exact sum) bit for bit (sums above 256 exercise
+    the ties of round-to-nearest-even)."""
+    A = inputs.randint_bf16((M, K), -3, 3, tag=(10, M, N, K))
+    W = inputs.randint_bf16((N, K), -3, 3, tag=(11, M, N, K))
+    ref, _ = oracle.gemm(A, W)
+    note(f"gemm integer M={M} N={N} K={K}")
+    y = host(gemm(dev(A), dev(W)))
+    assert np.array_equal(y, rne_bf16_of_exact(ref))
+
+
+def test_rne_ties():
+    """Row sums that sit exactly halfway between two bf16 values."""
+    K = 1024
+    sums = np.array([257, 259, 261, 263, -257, -259, 514, 518, 522, -514, 1028, 1036, 1, 0, 255, 511])
+    A = np.zeros((len(sums), K))
+    for i, v in enumerate(sums):     # spread |v| over ones, sign on all of them
+        n = abs(int(v))
+        A[i, :min(n, K)] = np.sign(v)
+        if n > K:
+            A[i, :n - K] = 2 * np.sign(v)
+    W = np.ones((16, K))
+    Ab, Wb = inputs.to_bf16_bits(A), inputs.to_bf16_bits(W)
+    ref, _ = oracle.gemm(Ab, Wb)
+    note("gemm rne ties")
+    y = host(gemm(dev(Ab), dev(Wb)))
+    assert np.array_equal(y, rne_bf16_of_exact(ref))
+
+
+def test_ragged_parity_and_tails():
+    M, N, K = 129, 200, 544          # tails in every dimension
+    A = inputs.randn_bf16((M, K), tag=(20,))
+    W = inputs.randn_bf16((N, K), tag=(21,))
+    ref, s = oracle.gemm(A, W)
+    note("gemm ragged 129x200x544")
+    y = host(gemm(dev(A), dev(W)))
+    assert_within_tol(y, ref, s, "ragged")
+
+
+def test_identity_and_scaling():
+    for K in (512, 4096):
+        A = inputs.randn_bf16((37, K), tag=(30, K))
+        I = inputs.to_bf16_bits(np.eye(K))
+        note(f"gemm identity K={K}")
+        y = host(gemm(dev(A), dev(I)))
+        assert np.array_equal(y, A)
+    A = inputs.randn_bf16((50, 1024), tag=(31,))
+    W = inputs.randn_bf16((384, 1024), tag=(32,))
+    Ad, Wd = dev(A), dev(W)
+    y = host(gemm(Ad, Wd))
+    for p in (-3, 4):
+        note(f"gemm scale 2^{p}")
+        y2 = host(gemm(Ad * (2.0 ** p), Wd))
+        assert np.array_equal(bf16_to_f64(y2), bf16_to_f64(y) * 2.0 ** p)
+
+
+QWEN = [(6144, 4096, 2048), (4096, 4096, 2048), (24576, 4096, 2048), (4096, 12288, 8192)]
+
+
+@pytest.mark.parametrize("N,K,Mmax", QWEN)
+def test_linear_shapes_sweep(N, K, Mmax):
+    """Qwen3-8B-shaped linears: parity on sampled rows at M_max, and every M
+    of the sweep (powers of two, plus 7, 129, 1000 for the long-K case)
+    bitwise equal to the prefix of the M_max result."""
+    A = inputs.randn_bf16((Mmax, K), 1.0, tag=(40, N, K))
+    W = inputs.randn_bf16((N, K), 0.02, tag=(41, N, K))
+    Ad, Wd = dev(A), dev(W)
+    note(f"gemm N={N} K={K} M={Mmax}")
+    yfull = host(gemm(Ad, Wd))
+    rows = np.unique(np.concatenate([[0, 1, Mmax - 1], inputs.rng(12345, 42, N).integers(0, Mmax, 5)]))
+    ref, s = oracle.gemm(A, W, rows=rows)
+    assert_within_tol(yfull[rows], ref, s, f"N={N} K={K} sampled rows")
+    Ms = [1 << i for i in range(Mmax.bit_length()) if (1 << i) < Mmax]
+    if K == 12288:
+        Ms += [7, 129, 1000]
+    for M in Ms:
+        note(f"gemm N={N} K={K} prefix M={M}")
+        y = host(gemm(Ad[:M], Wd))
+        assert np.array_equal(y, yfull[:M]), f"M={M} prefix differs"
+    # small-M parity directly as well
+    ref1, s1 = oracle.gemm(A[:4], W)
+    assert_within_tol(yfull[:4], ref1, s1, f"N={N} K={K} rows 0..3")
+
+
+def test_permutations_subsets_repeats_grid():
+    N, K, M = 4096, 4096, 512
+    A = inputs.randn_bf16((M, K), tag=(50,))
+    W = inputs.randn_bf16((N, K), 0.02, tag=(51,))
+    Ad, Wd = dev(A), dev(W)
+    note("gemm invariance base")
+    y = host(gemm(Ad, Wd))
+    g = inputs.rng(12345, 52)
+    for trial in range(2):
+        perm = g.permutation(M)
+        note(f"gemm permutation {trial}")
+        yp = host(gemm(Ad[torch.from_numpy(perm).cuda()].contiguous(), Wd))
+        assert np.array_equal(yp, y[perm])
+    perm = g.permutation(M)[:77]           # odd M
+    yp = host(gemm(Ad[torch.from_numpy(perm).cuda()].contiguous(), Wd))
+    assert np.array_equal(yp, y[perm])
+    for off in (8, 24, 1000):              # subsets in fresh buffers at shifted bases
+        sub = np.sort(g.choice(M, size=45, replace=False))
+        buf = torch.zeros((off + 45 * K,), dtype=torch.bfloat16, device="cuda")
+        view = buf[off:].view(45, K)
+        view.copy_(Ad[torch.from_numpy(sub).cuda()])
+        note(f"gemm subset off={off}")
+        ys = host(gemm(view, Wd))
+        assert np.array_equal(ys, y[sub])
+    outs = set()
+    for r in range(8):
+        note(f"gemm repeat {r}")
+        outs.add(host(gemm(Ad, Wd)).tobytes())
+    assert len(outs) == 1, f"{len(outs)} distinct outputs over 8 runs"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for mw in (1, 7, cus, 4 * cus):
+        note(f"gemm grid override {mw}")
+        yg = host(gemm(Ad, Wd, max_workgroups=mw))
+        assert np.array_equal(yg, y), f"grid {mw} differs"
+
+
+def test_empty_and_strided():
+    A = inputs.randn_bf16((16, 520), tag=(60,))
+    W = inputs.randn_bf16((136, 520), tag=(61,))
+    Ad, Wd = dev(A), dev(W)
+    y0 = torch.empty((0, 136), dtype=torch.bfloat16, device="cuda")
+    B.bi_gemm(Ad[:0], Wd, y0)
+    # strided views: K=512 inside rows of 520
+    y = host(gemm(Ad[:, :512], Wd[:, :512]))
+    ref, s = oracle.gemm(A[:, :512], W[:, :512])
+    assert_within_tol(y, ref, s, "strided")
+    # output with a leading dimension larger than N
+    ybig = torch.zeros((16, 144), dtype=torch.bfloat16, device="cuda")
+    B.bi_gemm(Ad[:, :512], Wd[:, :512], ybig[:, :136])
+    yb = host(ybig)
+    assert np.array_equal(yb[:, :136], y)
+    assert not yb[:, 136:].any()
