@@ -41,8 +41,9 @@
  *   - BI_ERR_ALIGN: a pointer not 16-byte aligned, or a leading dimension or
  *     batch stride that is not a multiple of 8 elements (of 32 for NVFP4 A).
  *   - BI_ERR_ALIAS: the output range overlaps an input range.
- *   - BI_ERR_UNSUPPORTED: no plan for this shape (e.g. an index that would
- *     overflow 32 bits inside a kernel).  There is never a silent fallback to
+ *   - BI_ERR_UNSUPPORTED: no plan for this shape (an index that would
+ *     overflow 32 bits inside a kernel: a dimension above 2^31-1, a leading
+ *     dimension of 2^22 elements or more).  There is never a silent fallback to
  *     a non-invariant path: the fail-loud rule of the PR #51292 review thread.
  *   - BI_ERR_HIP: the HIP runtime refused the launch or a device query.
  */
@@ -99,16 +100,21 @@ typedef struct bi_plan {
 } bi_plan;
 
 /*
- * Launch options for the *_ex entry points.  They change only which
- * workgroup computes which tile (or row), never how any output element is
+ * Launch options for the *_ex entry points.  They change only which lanes
+ * and workgroups compute which outputs, never how any output element is
  * computed, so results are bitwise identical for every value -- that is what
- * the grid-override invariance test checks.
+ * the grid- and tile-override invariance tests check.  They exist for those
+ * tests and for tuning sweeps; production calls pass NULL.
  *   max_workgroups: cap on the persistent grid (0 = the library's default,
- *   a small multiple of the device's compute-unit count).
+ *     the device's compute-unit count times the tiles one unit holds).
+ *   tile_variant: GEMM family only; 0 = the plan's tile shape, v > 0 = the
+ *     compiled tile shape v-1 (see bi_tile_shape).  BI_ERR_SHAPE if out of
+ *     range.
  */
 typedef struct bi_launch_opts {
     int32_t max_workgroups;
-    int32_t reserved[7];
+    int32_t tile_variant;
+    int32_t reserved[6];
 } bi_launch_opts;
 
 /*
@@ -199,6 +205,14 @@ bi_status bi_rmsnorm_ex(const void *X, int64_t ldx, const void *gamma, float eps
  * Host-only; makes no HIP call.
  */
 bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out);
+
+/*
+ * bi_tile_shape: describe compiled tile shape v (0-based) of the GEMM
+ * mainloop: out->bm, bn, bk, waves, lds_stages and the MFMA block are filled,
+ * out->op is -1.  Returns BI_ERR_SHAPE when v is out of range, and
+ * BI_ERR_NULL for a NULL out.  Host-only.
+ */
+bi_status bi_tile_shape(int v, bi_plan *out);
 
 /* Static, human-readable name of a status code. */
 const char *bi_status_str(bi_status s);

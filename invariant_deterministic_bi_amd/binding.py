@@ -39,7 +39,7 @@ class BiPlan(ctypes.Structure):
 
 
 class BiLaunchOpts(ctypes.Structure):
-    _fields_ = [("max_workgroups", _i32), ("reserved", _i32 * 7)]
+    _fields_ = [("max_workgroups", _i32), ("tile_variant", _i32), ("reserved", _i32 * 6)]
 
 
 class BiError(RuntimeError):
@@ -62,6 +62,7 @@ _SIGS = {
     "bi_rmsnorm": [_p, _i64, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p],
     "bi_rmsnorm_ex": [_p, _i64, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
+    "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
 }
 
 
@@ -103,6 +104,18 @@ def plan_query(op: int, N: int, K: int) -> dict:
     return pl.as_dict()
 
 
+def tile_shapes() -> list:
+    """The compiled GEMM tile shapes (index v is tile_variant v+1)."""
+    out = []
+    v = 0
+    while True:
+        pl = BiPlan()
+        if lib().bi_tile_shape(v, ctypes.byref(pl)) != BI_OK:
+            return out
+        out.append(pl.as_dict())
+        v += 1
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -111,11 +124,12 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _opts(max_workgroups):
-    if not max_workgroups:
+def _opts(max_workgroups=0, tile_variant=0):
+    if not max_workgroups and not tile_variant:
         return None
     o = BiLaunchOpts()
     o.max_workgroups = int(max_workgroups)
+    o.tile_variant = int(tile_variant)
     return ctypes.byref(o)
 
 
@@ -135,7 +149,7 @@ def _raise(st, what):
         raise BiError(st, what)
 
 
-def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0):
+def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
     """Y[M,N] = A[M,K] . B[N,K]^T (bf16); allocates Y with torch if not given."""
     _check2d(A, "A")
     _check2d(B, "B")
@@ -149,12 +163,12 @@ def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0):
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y must be [M, N]")
     st = lib().bi_gemm_ex(_ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(Y), Y.stride(0),
-                          M, N, K, _stream(stream), _opts(max_workgroups))
+                          M, N, K, _stream(stream), _opts(max_workgroups, tile_variant))
     _raise(st, "bi_gemm")
     return Y
 
 
-def bi_bmm(A, B, Y=None, *, stream=None, max_workgroups=0):
+def bi_bmm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
     """Y[h] = A[h] . B[h] for A [H,M,K], B [H,K,N] (bf16)."""
     if A.dim() != 3 or B.dim() != 3 or A.stride(2) != 1 or B.stride(2) != 1:
         raise ValueError("A and B must be 3-D with unit stride along the last dimension")
@@ -168,13 +182,13 @@ def bi_bmm(A, B, Y=None, *, stream=None, max_workgroups=0):
         raise ValueError("Y must be [H, M, N] with unit last stride")
     st = lib().bi_bmm_ex(_ptr(A), A.stride(0), A.stride(1), _ptr(B), B.stride(0), B.stride(1),
                          _ptr(Y), Y.stride(0), Y.stride(1), H, M, N, K, _stream(stream),
-                         _opts(max_workgroups))
+                         _opts(max_workgroups, tile_variant))
     _raise(st, "bi_bmm")
     return Y
 
 
 def bi_nvfp4_gemm(A, W, W_scales, alpha, Y=None, *, A_scales=None, K=None, stream=None,
-                  max_workgroups=0):
+                  max_workgroups=0, tile_variant=0):
     """Y[M,N] = alpha * A . W^T with NVFP4 W (codes [N,K/2] uint8, scales [N,K/16] uint8).
 
     A is bf16 [M,K] when A_scales is None, else NVFP4 codes [M,K/2] with
@@ -206,7 +220,7 @@ def bi_nvfp4_gemm(A, W, W_scales, alpha, Y=None, *, A_scales=None, K=None, strea
     _check2d(Y, "Y")
     st = lib().bi_nvfp4_gemm_ex(_ptr(A), _ptr(A_scales), a_fmt, lda, _ptr(W), _ptr(W_scales),
                                 float(alpha), _ptr(Y), Y.stride(0), M, N, K, _stream(stream),
-                                _opts(max_workgroups))
+                                _opts(max_workgroups, tile_variant))
     _raise(st, "bi_nvfp4_gemm")
     return Y
 

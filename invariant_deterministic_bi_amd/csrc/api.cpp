@@ -65,34 +65,37 @@ bi_status device_cus(int *out) {
 }
 
 // ---------------------------------------------------------------------------
-// Recipe table.  Variants index the compiled tile shapes in gemm.hip:
-//   0: 128 x 128, 1: 128 x 64, 2: 64 x 64.
+// Recipe table: (op, N, K) -> index into bi::kTileShapes.  Every output
+// element is computed the same way by every tile shape (16x16x32 bf16 MFMA,
+// K ascending in chunks of 32); the shape is chosen per (N, K) for speed
+// alone: at small M the number of tiles, N / bn, decides how many compute
+// units stream the weight, at large M the tile's bm * bn / (bm + bn) decides
+// the operand traffic per MFMA.
 // ---------------------------------------------------------------------------
-struct VariantShape {
-    int bm, bn;
-};
-constexpr VariantShape kVariants[] = {{128, 128}, {128, 64}, {64, 64}};
+constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offsets
 
 int gemm_variant(int op, int64_t N, int64_t K) {
     (void)K;
-    if (op == BI_OP_BMM) return 2;
-    if (N <= 1024) return 2;
-    if (N >= 8192) return 0;
-    return 1;
+    if (op == BI_OP_BMM) return 5;      // 64 x 64
+    if (N >= 16384) return 0;           // 256 x 128
+    if (N >= 2048) return 3;            // 256 x 64
+    if (N >= 512) return 4;             // 128 x 64
+    return 5;                           // 64 x 64
 }
 
-void fill_gemm_plan(int op, int variant, bi_plan *out) {
+void fill_tile_plan(int op, int variant, bi_plan *out) {
+    const bi::TileShape &t = bi::kTileShapes[variant];
     std::memset(out, 0, sizeof *out);
     out->op = op;
-    out->bm = kVariants[variant].bm;
-    out->bn = kVariants[variant].bn;
+    out->bm = t.bm;
+    out->bn = t.bn;
     out->bk = 64;
     out->mfma_m = 16;
     out->mfma_n = 16;
     out->mfma_k = 32;
-    out->waves = 4;
-    out->lds_stages = 2;
-    out->threads = 256;
+    out->waves = t.wgm * t.wgn;
+    out->lds_stages = t.stages;
+    out->threads = 64 * t.wgm * t.wgn;
     out->chunks_per_thread = 0;
 }
 
@@ -116,19 +119,27 @@ int default_grid(int tiles, int cus, const bi_launch_opts *opts, int per_cu) {
 
 bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *stream,
                    const bi_launch_opts *opts) {
-    const int variant = gemm_variant(op, in.N, in.K);
-    GemmRecipe r{kVariants[variant].bm, kVariants[variant].bn, variant};
+    int variant = gemm_variant(op, in.N, in.K);
+    if (opts && opts->tile_variant != 0) {
+        if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;
+        variant = opts->tile_variant - 1;
+    }
+    const bi::TileShape &t = bi::kTileShapes[variant];
+    if (op == BI_OP_BMM && (t.bn % 8 != 0)) return BI_ERR_UNSUPPORTED;
     GemmArgs a = in;
-    a.tiles_m = static_cast<int>((a.M + r.bm - 1) / r.bm);
-    a.tiles_n = static_cast<int>((a.N + r.bn - 1) / r.bn);
+    a.tiles_m = static_cast<int>((a.M + t.bm - 1) / t.bm);
+    a.tiles_n = static_cast<int>((a.N + t.bn - 1) / t.bn);
     const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n * a.batch;
     if (tiles > kI32Max) return BI_ERR_UNSUPPORTED;
     a.num_tiles = static_cast<int>(tiles);
     int cus = 0;
     bi_status st = device_cus(&cus);
     if (st != BI_OK) return st;
-    const int grid = default_grid(a.num_tiles, cus, opts, 2);
-    hipError_t e = bi::launch_gemm(a_mode, b_mode, r, a, grid, static_cast<hipStream_t>(stream));
+    int per_cu = bi::kLdsPerCu / bi::tile_lds_bytes(t);
+    if (per_cu < 1) per_cu = 1;
+    const int grid = default_grid(a.num_tiles, cus, opts, per_cu);
+    hipError_t e = bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
+                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
@@ -149,7 +160,14 @@ const char *bi_status_str(bi_status s) {
     return "unknown bi_status";
 }
 
-const char *bi_version(void) { return "bi 0.1.0 gfx950"; }
+const char *bi_version(void) { return "bi 0.2.0 gfx950"; }
+
+bi_status bi_tile_shape(int v, bi_plan *out) {
+    if (!out) return BI_ERR_NULL;
+    if (v < 0 || v >= bi::kNumTileShapes) return BI_ERR_SHAPE;
+    fill_tile_plan(-1, v, out);
+    return BI_OK;
+}
 
 bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
     if (!out) return BI_ERR_NULL;
@@ -161,7 +179,7 @@ bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
             if (op == BI_OP_NVFP4_GEMM ? (K % 32 != 0) : (K % 8 != 0)) return BI_ERR_SHAPE;
             if (op == BI_OP_BMM && N % 8 != 0) return BI_ERR_SHAPE;
             if (N > kI32Max || K > kI32Max) return BI_ERR_UNSUPPORTED;
-            fill_gemm_plan(op, gemm_variant(op, N, K), out);
+            fill_tile_plan(op, gemm_variant(op, N, K), out);
             return BI_OK;
         }
         case BI_OP_RMSNORM: {
@@ -182,7 +200,8 @@ bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, voi
                      int64_t M, int64_t N, int64_t K, void *stream, const bi_launch_opts *opts) {
     if (M < 0 || N <= 0 || K <= 0 || K % 8 != 0) return BI_ERR_SHAPE;
     if (lda < K || ldb < K || ldy < N) return BI_ERR_SHAPE;
-    if (M > kI32Max || N > kI32Max || K > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M > kI32Max || N > kI32Max || K > kI32Max || lda >= kMaxLd || ldb >= kMaxLd)
+        return BI_ERR_UNSUPPORTED;
     if (M == 0) return BI_OK;
     if (!A || !B || !Y) return BI_ERR_NULL;
     if (!aligned16(A) || !aligned16(B) || !aligned16(Y) || lda % 8 || ldb % 8) return BI_ERR_ALIGN;
@@ -210,7 +229,8 @@ bi_status bi_bmm_ex(const void *A, int64_t sA, int64_t lda, const void *B, int64
     if (batch > 1 && (sA < (M > 0 ? (M - 1) * lda + K : 0) || sB < (K - 1) * ldb + N ||
                       sY < (M > 0 ? (M - 1) * ldy + N : 0) || sA < 0 || sB < 0 || sY < 0))
         return BI_ERR_SHAPE;
-    if (M > kI32Max || N > kI32Max || K > kI32Max || batch > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M > kI32Max || N > kI32Max || K > kI32Max || batch > kI32Max || lda >= kMaxLd)
+        return BI_ERR_UNSUPPORTED;
     if (M == 0) return BI_OK;
     if (!A || !B || !Y) return BI_ERR_NULL;
     if (!aligned16(A) || !aligned16(B) || !aligned16(Y) || lda % 8 || ldb % 8 || sA % 8 || sB % 8 ||
@@ -243,7 +263,7 @@ bi_status bi_nvfp4_gemm_ex(const void *A, const void *A_scales, int a_fmt, int64
     if (a_fmt != BI_A_BF16 && a_fmt != BI_A_NVFP4) return BI_ERR_SHAPE;
     if (M < 0 || N <= 0 || K <= 0 || K % 32 != 0) return BI_ERR_SHAPE;
     if (lda < K || ldy < N) return BI_ERR_SHAPE;
-    if (M > kI32Max || N > kI32Max || K > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M > kI32Max || N > kI32Max || K > kI32Max || lda >= kMaxLd) return BI_ERR_UNSUPPORTED;
     if (M == 0) return BI_OK;
     if (!A || !W || !W_scales || !Y || (a_fmt == BI_A_NVFP4 && !A_scales)) return BI_ERR_NULL;
     if (!aligned16(A) || !aligned16(W) || !aligned16(W_scales) || !aligned16(Y)) return BI_ERR_ALIGN;

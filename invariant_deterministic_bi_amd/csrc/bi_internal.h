@@ -14,11 +14,38 @@ enum OperandMode : int {
     OPND_NVFP4_ROWS = 2  // e2m1 codes [rows, K/2] + e4m3 scales [rows, K/16]
 };
 
-// Tile recipe selected from (op, N, K).  `variant` indexes the compiled
-// kernel instantiation that implements (bm, bn).
+// Compiled tile shapes of the GEMM mainloop.  A tile is bm x bn outputs,
+// computed by wgm x wgn wavefronts (each owning a (bm/wgm) x (bn/wgn) block),
+// with `stages` LDS buffers of 64 K-columns.  The shape changes which lanes
+// and workgroups compute which outputs, never the arithmetic of one output.
+struct TileShape {
+    int bm, bn, wgm, wgn, stages;
+};
+
+constexpr TileShape kTileShapes[] = {
+    {256, 128, 2, 2, 3},  // 0
+    {256, 128, 4, 2, 3},  // 1
+    {128, 128, 2, 2, 3},  // 2
+    {256, 64, 4, 1, 3},   // 3
+    {128, 64, 2, 2, 3},   // 4
+    {64, 64, 2, 2, 3},    // 5
+    {256, 32, 4, 1, 3},   // 6
+    {128, 32, 4, 1, 3},   // 7
+};
+constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
+
+// LDS bytes of one workgroup: the pipeline buffers, or the padded bf16
+// output tile of the epilogue if that is larger.
+constexpr int tile_lds_bytes(const TileShape &t) {
+    const int pipe = t.stages * (t.bm + t.bn) * 64 * 2;
+    const int ctile = t.bm * (t.bn * 2 + 16);
+    return pipe > ctile ? pipe : ctile;
+}
+constexpr int kLdsPerCu = 160 * 1024;
+
+// Tile recipe selected from (op, N, K).
 struct GemmRecipe {
-    int bm, bn;
-    int variant;
+    int variant;  // index into kTileShapes
 };
 
 struct GemmArgs {

@@ -9,32 +9,64 @@
 //     32-wide K chunks in ascending order, starting from +0, followed by one
 //     bf16 round-to-nearest-even (and, for NVFP4, one fp32 multiply by alpha
 //     just before it);
-//   * rows beyond M are zero-filled in LDS and never read from memory; their
-//     MFMA blocks are skipped when a whole 16-row block is out of range.
-//     Neither touches a valid row's chain;
+//   * operand rows beyond M (or N) and K columns beyond K are zero-filled in
+//     LDS (out-of-range buffer loads return zero) and never read from memory;
+//     MFMA blocks whose 16 rows are all beyond M are skipped.  Neither touches
+//     a valid row's chain;
 //   * the tile shape comes from (N, K) only; M sets the tile count; the
-//     persistent grid size only decides which workgroup runs which tile.
+//     persistent grid size and the tile-to-workgroup order only decide which
+//     workgroup runs which tile.
+//
+// Data movement: bf16 operands stored [rows, K] go from HBM straight into LDS
+// (buffer_load ... lds, 16 bytes per lane) STAGES-1 K-steps ahead of the
+// MFMAs; operands that need a transform on the way (the [K, N] BMM operand,
+// NVFP4 codes) go through registers and are stored one step ahead.  The
+// output tile is staged through LDS so that every global store is a full
+// 16-byte chunk of a row.
 //
 // Prior art: the vLLM PR #39912 summary page (section "implementation
 // breakdown") pins a persistent tile scheduler and one default config for the
 // batch-invariant NVFP4 GEMM on NVIDIA parts; the same principle is kept, the
-// tiling is this file's own for 64-wide wavefronts and bf16 MFMA.
+// tiling here is this file's own for 64-wide wavefronts, LDS DMA and bf16
+// MFMA on gfx950.
 
 #include "bi_internal.h"
+
+typedef int bi_i32x4 __attribute__((ext_vector_type(4)));
+
+// LLVM intrinsic: per-lane buffer load of `size` bytes written to LDS at
+// M0-base + lane * size; an offset outside the buffer's range writes zeros.
+__device__ void bi_raw_buffer_load_lds(bi_i32x4 rsrc,
+                                       __attribute__((address_space(3))) uint32_t *lds, int size,
+                                       int voffset, int soffset, int offset,
+                                       int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 namespace bi {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef bi_i32x4 i32x4;
 
-constexpr int kThreads = 256;  // 4 wavefronts, arranged 2 x 2 over the tile
-constexpr int kBK = 64;        // K columns per LDS stage (two 32-wide MFMA steps)
+constexpr int kBK = 64;  // K columns per LDS stage (two 32-wide MFMA steps)
+constexpr int kRowBytes = kBK * 2;  // one staged operand row: eight 16-byte chunks
+
+// Buffer resource for a byte range starting at `base` (gfx9 data format word).
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+    r.z = __builtin_amdgcn_readfirstlane((int)num_bytes);
+    r.w = 0x00020000;
+    return r;
+}
 
 // LDS layout of a staged operand tile: row r (an M row of A or an N column
-// of B) holds kBK bf16 = eight 16-byte chunks; chunk c of row r lives in
-// slot r*8 + swz(r, c).  The XOR spreads the 16 rows that one MFMA fragment
-// read touches over distinct bank groups.
+// of B) holds kBK bf16 = eight 16-byte chunks; logical chunk c of row r lives
+// in physical slot r*8 + swz(r, c).  The XOR spreads the 16 rows that one
+// MFMA fragment read touches, and the 8 rows one LDS-DMA instruction fills,
+// over distinct bank groups.  swz(r, .) is an involution.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -82,55 +114,68 @@ __device__ __forceinline__ void decode32(const uint4 &codes, uint32_t sc, uint4 
 }
 
 // ---------------------------------------------------------------------------
-// Operand stagers: global -> registers (load), registers -> LDS (store).
-// ROWS is the tile extent along M (for A) or N (for B).
+// Direct (LDS-DMA) operand: bf16 [rows, K], K contiguous.  Wave w fills rows
+// [w*ROWS/NW, (w+1)*ROWS/NW) of the tile, eight rows per instruction.
 // ---------------------------------------------------------------------------
-template <int ROWS, int MODE>
-struct Stager;
+template <int ROWS, int NW>
+struct DirectOperand {
+    static constexpr int RPW = ROWS / NW;   // rows per wave
+    static constexpr int INSTR = RPW / 8;   // LDS-DMA instructions per wave per stage
+    static_assert(RPW % 8 == 0, "tile rows must give each wavefront a multiple of 8 rows");
 
-// bf16 [rows, K], K contiguous.
-template <int ROWS>
-struct Stager<ROWS, OPND_BF16_ROWS> {
-    static constexpr int TOTAL = ROWS * (kBK / 8);
-    static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
-    uint4 r[PER];
+    i32x4 rsrc;
+    int row_off[INSTR];  // byte offset of this lane's row within the tile (or -1)
 
-    __device__ __forceinline__ void load(const void *base, const void *, int64_t ld, int row0,
-                                         int nrows, int k0, int K, int tid) {
-        const uint16_t *p = static_cast<const uint16_t *>(base);
+    // base: the tile's first row; rows_valid rows exist; ld in elements.
+    __device__ __forceinline__ void setup(const uint16_t *base, int rows_valid, int64_t ld, int K,
+                                          int wave, int lane) {
+        const uint32_t bytes = rows_valid > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * ld + K) * 2) : 0u;
+        rsrc = make_rsrc(base, bytes);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int q = tid + i * kThreads;
-            if (TOTAL % kThreads == 0 || q < TOTAL) {
-                const int row = q >> 3, c = q & 7;
-                const int gr = row0 + row, gk = k0 + c * 8;
-                if (gr < nrows && gk < K)
-                    r[i] = *reinterpret_cast<const uint4 *>(p + (int64_t)gr * ld + gk);
-                else
-                    r[i] = make_uint4(0, 0, 0, 0);
-            }
+        for (int j = 0; j < INSTR; ++j) {
+            const int row = wave * RPW + j * 8 + (lane >> 3);
+            row_off[j] = row < rows_valid ? (int)(row * ld * 2) : -1;
         }
     }
-    __device__ __forceinline__ void store(uint4 *lds, int tid) const {
+
+    // Issue the loads of K-step `k0` into the LDS tile at `lds_tile`.
+    __device__ __forceinline__ void issue(char *lds_tile, int k0, int K, int wave, int lane) const {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int q = tid + i * kThreads;
-            if (TOTAL % kThreads == 0 || q < TOTAL) {
-                const int row = q >> 3, c = q & 7;
-                lds[row * 8 + swz(row, c)] = r[i];
-            }
+        for (int j = 0; j < INSTR; ++j) {
+            const int row = wave * RPW + j * 8 + (lane >> 3);
+            const int c = swz(row, lane & 7);           // logical chunk landing in slot lane&7
+            const int gk = k0 + c * 8;
+            const int voff = (row_off[j] >= 0 && gk < K) ? row_off[j] + gk * 2 : (int)0x80000000;
+            char *dst = lds_tile + (wave * RPW + j * 8) * kRowBytes;
+            bi_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t *)dst, 16, voff,
+                                0, 0, 0);
         }
     }
+};
+
+// ---------------------------------------------------------------------------
+// Register-staged operands: global -> registers (load), registers -> LDS
+// (store).  NT threads cooperate.
+// ---------------------------------------------------------------------------
+template <int ROWS, int MODE, int NT>
+struct Staged;
+
+// bf16 [rows, K] operands are loaded directly into LDS; nothing is staged.
+template <int ROWS, int NT>
+struct Staged<ROWS, OPND_BF16_ROWS, NT> {
+    __device__ __forceinline__ void load(const void *, const void *, int64_t, int, int, int, int,
+                                         int) {}
+    __device__ __forceinline__ void store(char *, int) const {}
 };
 
 // bf16 [K, cols], cols contiguous (the BMM right operand).  Each 16-byte
 // global chunk holds 8 consecutive columns at one k; it is transposed into the
 // row-per-column LDS layout with 2-byte stores.
-template <int ROWS>
-struct Stager<ROWS, OPND_BF16_KN> {
+template <int ROWS, int NT>
+struct Staged<ROWS, OPND_BF16_KN, NT> {
     static constexpr int CPR = ROWS / 8;  // chunks per k row of the tile
     static constexpr int TOTAL = kBK * CPR;
-    static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
+    static constexpr int PER = (TOTAL + NT - 1) / NT;
     uint4 r[PER];
 
     __device__ __forceinline__ void load(const void *base, const void *, int64_t ld, int col0,
@@ -138,8 +183,8 @@ struct Stager<ROWS, OPND_BF16_KN> {
         const uint16_t *p = static_cast<const uint16_t *>(base);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = tid + i * kThreads;
-            if (TOTAL % kThreads == 0 || q < TOTAL) {
+            const int q = tid + i * NT;
+            if (TOTAL % NT == 0 || q < TOTAL) {
                 const int kk = q / CPR, n8 = q % CPR;
                 const int gk = k0 + kk, gn = col0 + n8 * 8;
                 if (gk < K && gn < ncols)
@@ -149,12 +194,12 @@ struct Stager<ROWS, OPND_BF16_KN> {
             }
         }
     }
-    __device__ __forceinline__ void store(uint4 *lds, int tid) const {
-        uint16_t *l16 = reinterpret_cast<uint16_t *>(lds);
+    __device__ __forceinline__ void store(char *lds_tile, int tid) const {
+        uint16_t *l16 = reinterpret_cast<uint16_t *>(lds_tile);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = tid + i * kThreads;
-            if (TOTAL % kThreads == 0 || q < TOTAL) {
+            const int q = tid + i * NT;
+            if (TOTAL % NT == 0 || q < TOTAL) {
                 const int kk = q / CPR, n8 = q % CPR;
                 const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
 #pragma unroll
@@ -172,10 +217,10 @@ struct Stager<ROWS, OPND_BF16_KN> {
 // elements (codes stride ld/2 bytes, scales stride ld/16 bytes).  One unit is
 // 32 elements: 16 code bytes and 2 scale bytes, decoded to bf16 at LDS-store
 // time.
-template <int ROWS>
-struct Stager<ROWS, OPND_NVFP4_ROWS> {
+template <int ROWS, int NT>
+struct Staged<ROWS, OPND_NVFP4_ROWS, NT> {
     static constexpr int TOTAL = ROWS * (kBK / 32);
-    static constexpr int PER = (TOTAL + kThreads - 1) / kThreads;
+    static constexpr int PER = (TOTAL + NT - 1) / NT;
     uint4 r[PER];
     uint32_t s[PER];
 
@@ -185,8 +230,8 @@ struct Stager<ROWS, OPND_NVFP4_ROWS> {
         const uint8_t *ps = static_cast<const uint8_t *>(scales);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = tid + i * kThreads;
-            if (TOTAL % kThreads == 0 || q < TOTAL) {
+            const int q = tid + i * NT;
+            if (TOTAL % NT == 0 || q < TOTAL) {
                 const int row = q >> 1, h = q & 1;
                 const int gr = row0 + row, gk = k0 + h * 32;
                 if (gr < nrows && gk < K) {
@@ -199,11 +244,12 @@ struct Stager<ROWS, OPND_NVFP4_ROWS> {
             }
         }
     }
-    __device__ __forceinline__ void store(uint4 *lds, int tid) const {
+    __device__ __forceinline__ void store(char *lds_tile, int tid) const {
+        uint4 *lds = reinterpret_cast<uint4 *>(lds_tile);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = tid + i * kThreads;
-            if (TOTAL % kThreads == 0 || q < TOTAL) {
+            const int q = tid + i * NT;
+            if (TOTAL % NT == 0 || q < TOTAL) {
                 const int row = q >> 1, h = q & 1;
                 uint4 out[4];
                 decode32(r[i], s[i], out);
@@ -220,119 +266,277 @@ __device__ __forceinline__ int64_t elem_bytes_x2() {
     return MODE == OPND_NVFP4_ROWS ? 1 : 4;
 }
 
-// ---------------------------------------------------------------------------
-// The kernel.  Tile (bh, tm, tn) covers rows tm*BM.. of head bh and output
-// columns tn*BN..; tiles are enumerated with tn fastest.
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int AMODE, int BMODE>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs p) {
-    constexpr int WTM = BM / 2, WTN = BN / 2;  // per-wavefront sub-tile
-    constexpr int FM = WTM / 16, FN = WTN / 16;
-    __shared__ uint4 lds[2][(BM + BN) * 8];
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (they retire in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
+// ---------------------------------------------------------------------------
+// Tile order.  A workgroup's linear slot L (after spreading consecutive slots
+// over the 8 XCDs so each XCD gets a contiguous run) is mapped to (head, tm,
+// tn) in groups of GM tile-rows: consecutive slots walk down GM M-tiles, then
+// step to the next N-tile, so the workgroups resident on one XCD share both
+// A rows and B columns in its L2.
+// ---------------------------------------------------------------------------
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int &bh, int &tm,
+                                            int &tn) {
+    const int per_head = tiles_m * tiles_n;
+    bh = L / per_head;
+    const int l = L - bh * per_head;
+    const int in_group = kGroupM * tiles_n;
+    const int g = l / in_group;
+    const int first = g * kGroupM;
+    const int gsz = min(tiles_m - first, kGroupM);
+    const int r = l - g * in_group;
+    tm = first + r % gsz;
+    tn = r / gsz;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int STAGES, int AMODE, int BMODE>
+struct Cfg {
+    static constexpr int NW = WGM * WGN, NT = NW * 64;
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int C_STRIDE = BN * 2 + 16;  // padded bf16 output row in LDS
+    static constexpr int C_BYTES = BM * C_STRIDE;
+    static constexpr int PIPE_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int LDS_BYTES = PIPE_BYTES > C_BYTES ? PIPE_BYTES : C_BYTES;
+    static constexpr bool A_DIRECT = AMODE == OPND_BF16_ROWS;
+    static constexpr bool B_DIRECT = BMODE == OPND_BF16_ROWS;
+    static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 16x16 block");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of gfx950");
+};
+
+// LDS barrier for the mainloop: this wavefront's LDS reads and writes are
+// complete, then all wavefronts meet.  Unlike __syncthreads() it does not
+// drain outstanding global loads (the LDS-DMA prefetch of later stages keeps
+// flying); the vmcnt wait before it covers the stage about to be read.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One tile.  NL = number of leading 16-row MFMA blocks of this wavefront's
+// sub-tile that hold a valid row (FM for a full tile, fewer at the M edge, 0
+// for a wavefront whose rows all lie beyond M).  Blocks fm >= NL are neither
+// read nor multiplied; every block fm < NL runs the same chain of MFMAs in
+// the same order whatever NL is, so a row's bits do not depend on it.  All
+// wavefronts run the same sequence of loads and barriers.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int AMODE, int BMODE, int NL>
+__device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, int n0,
+                                         const char *Ab, const char *Bb, uint16_t *Yb) {
+    using C = Cfg<BM, BN, WGM, WGN, STAGES, AMODE, BMODE>;
+    constexpr int NT = C::NT, FN = C::FN, WTM = C::WTM, WTN = C::WTN;
+    constexpr int LD = (C::A_DIRECT ? DirectOperand<BM, C::NW>::INSTR : 0) +
+                       (C::B_DIRECT ? DirectOperand<BN, C::NW>::INSTR : 0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int nk = (p.K + kBK - 1) / kBK;
 
-    Stager<BM, AMODE> sa;
-    Stager<BN, BMODE> sb;
+    DirectOperand<BM, C::NW> da;
+    DirectOperand<BN, C::NW> db;
+    Staged<BM, AMODE, NT> sa;
+    Staged<BN, BMODE, NT> sb;
+    if constexpr (C::A_DIRECT)
+        da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(BM, p.M - m0),
+                 p.lda, p.K, wave, lane);
+    if constexpr (C::B_DIRECT)
+        db.setup(reinterpret_cast<const uint16_t *>(Bb) + (int64_t)n0 * p.ldb, min(BN, p.N - n0),
+                 p.ldb, p.K, wave, lane);
 
-    for (int t = blockIdx.x; t < p.num_tiles; t += gridDim.x) {
-        const int tn = t % p.tiles_n;
-        const int rest = t / p.tiles_n;
-        const int tm = rest % p.tiles_m;
-        const int bh = rest / p.tiles_m;
+    f32x4 acc[NL > 0 ? NL : 1][FN];
+#pragma unroll
+    for (int fm = 0; fm < NL; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto stage_ptr = [&](int s) -> char * { return lds + (s % STAGES) * C::STAGE_BYTES; };
+
+    // prologue: register-staged stage 0, direct stages 0..STAGES-2
+    if constexpr (!C::A_DIRECT) {
+        sa.load(Ab, p.A_scales, p.lda, m0, p.M, 0, p.K, tid);
+        sa.store(stage_ptr(0), tid);
+    }
+    if constexpr (!C::B_DIRECT) {
+        sb.load(Bb, p.B_scales, p.ldb, n0, p.N, 0, p.K, tid);
+        sb.store(stage_ptr(0) + C::A_BYTES, tid);
+    }
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+        if (s < nk) {
+            if constexpr (C::A_DIRECT) da.issue(stage_ptr(s), s * kBK, p.K, wave, lane);
+            if constexpr (C::B_DIRECT) db.issue(stage_ptr(s) + C::A_BYTES, s * kBK, p.K, wave, lane);
+        }
+    }
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt's LDS-DMA loads have landed once no more than the loads of
+        // the later stages already in flight are outstanding
+        if constexpr (LD > 0) {
+            if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * LD>();
+            else wait_vmcnt<0>();
+        }
+        lds_barrier();
+        // register-staged loads for kt+1 first, then the next direct stage, so
+        // that waiting on the former never waits on the latter
+        const bool more = kt + 1 < nk;
+        if constexpr (!C::A_DIRECT) if (more) sa.load(Ab, p.A_scales, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid);
+        if constexpr (!C::B_DIRECT) if (more) sb.load(Bb, p.B_scales, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
+        if (kt + STAGES - 1 < nk) {
+            const int s = kt + STAGES - 1;
+            if constexpr (C::A_DIRECT) da.issue(stage_ptr(s), s * kBK, p.K, wave, lane);
+            if constexpr (C::B_DIRECT) db.issue(stage_ptr(s) + C::A_BYTES, s * kBK, p.K, wave, lane);
+        }
+
+        if constexpr (NL > 0) {
+            const uint4 *la = reinterpret_cast<const uint4 *>(stage_ptr(kt));
+            const uint4 *lb = reinterpret_cast<const uint4 *>(stage_ptr(kt) + C::A_BYTES);
+            constexpr int KS = kBK / 32;
+            bf16x8 bfrag[KS][FN], afrag[KS][NL];
+            // all fragment reads of the stage first (they return in order), then
+            // the MFMAs, which wait only for the fragments they consume
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = ks * 4 + (lane >> 4);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int col = wn * WTN + fn * 16 + (lane & 15);
+                    bfrag[ks][fn] = __builtin_bit_cast(bf16x8, lb[col * 8 + swz(col, c)]);
+                }
+#pragma unroll
+                for (int fm = 0; fm < NL; ++fm) {
+                    const int row = wm * WTM + fm * 16 + (lane & 15);
+                    afrag[ks][fm] = __builtin_bit_cast(bf16x8, la[row * 8 + swz(row, c)]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int fm = 0; fm < NL; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            afrag[ks][fm], bfrag[ks][fn], acc[fm][fn], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more) {
+            if constexpr (!C::A_DIRECT) sa.store(stage_ptr(kt + 1), tid);
+            if constexpr (!C::B_DIRECT) sb.store(stage_ptr(kt + 1) + C::A_BYTES, tid);
+        }
+    }
+
+    // Epilogue: fp32 -> (alpha) -> bf16 RNE into a padded LDS tile, then
+    // full 16-byte row chunks to global memory.
+    __syncthreads();
+#pragma unroll
+    for (int fm = 0; fm < NL; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int col = wn * WTN + fn * 16 + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
+                float v = acc[fm][fn][i];
+                if constexpr (BMODE == OPND_NVFP4_ROWS) v = v * p.alpha;
+                *reinterpret_cast<uint16_t *>(lds + row * C::C_STRIDE + col * 2) =
+                    (uint16_t)f32_to_bf16_rne(v);
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int CPR = BN / 8;  // 16-byte chunks per output row
+    const int rows_valid = min(BM, p.M - m0);
+    for (int q = tid; q < rows_valid * CPR; q += NT) {
+        const int row = q / CPR, c8 = q % CPR;
+        const int col = n0 + c8 * 8;
+        const uint4 v = *reinterpret_cast<const uint4 *>(lds + row * C::C_STRIDE + c8 * 16);
+        uint16_t *dst = Yb + (int64_t)(m0 + row) * p.ldy + col;
+        if (col + 8 <= p.N && (((uintptr_t)dst) & 15) == 0) {
+            *reinterpret_cast<uint4 *>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (col + j < p.N) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+        }
+    }
+    __syncthreads();  // the LDS tile is reused by the next tile's prologue
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, int AMODE, int BMODE>
+__global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
+    using C = Cfg<BM, BN, WGM, WGN, STAGES, AMODE, BMODE>;
+    constexpr int FM = C::FM, WTM = C::WTM;
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WGN;
+    const int G = gridDim.x;
+    const bool spread = (G % 8) == 0;
+    const int slot = spread ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+
+    for (int base = 0; base < p.num_tiles; base += G) {
+        const int L = base + slot;
+        if (L >= p.num_tiles) break;
+        int bh, tm, tn;
+        tile_coords(L, p.tiles_m, p.tiles_n, bh, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
-
         const char *Ab = static_cast<const char *>(p.A) + bh * p.sA * elem_bytes_x2<AMODE>() / 2;
         const char *Bb = static_cast<const char *>(p.B) + bh * p.sB * elem_bytes_x2<BMODE>() / 2;
         uint16_t *Yb = static_cast<uint16_t *>(p.Y) + bh * p.sY;
 
-        // wave-uniform: does this wavefront's fm-th 16-row block hold a valid row?
-        bool live[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) live[fm] = (m0 + wm * WTM + fm * 16) < p.M;
-
-        f32x4 acc[FM][FN];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        sa.load(Ab, p.A_scales, p.lda, m0, p.M, 0, p.K, tid);
-        sb.load(Bb, p.B_scales, p.ldb, n0, p.N, 0, p.K, tid);
-        sa.store(lds[0], tid);
-        sb.store(lds[0] + BM * 8, tid);
-        __syncthreads();
-
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) {
-                sa.load(Ab, p.A_scales, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid);
-                sb.load(Bb, p.B_scales, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
-            }
-            const uint4 *la = lds[cur];
-            const uint4 *lb = lds[cur] + BM * 8;
-#pragma unroll
-            for (int ks = 0; ks < kBK / 32; ++ks) {
-                const int c = ks * 4 + (lane >> 4);
-                bf16x8 bfrag[FN];
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    const int col = wn * WTN + fn * 16 + (lane & 15);
-                    bfrag[fn] = __builtin_bit_cast(bf16x8, lb[col * 8 + swz(col, c)]);
-                }
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    if (!live[fm]) continue;
-                    const int row = wm * WTM + fm * 16 + (lane & 15);
-                    const bf16x8 afrag = __builtin_bit_cast(bf16x8, la[row * 8 + swz(row, c)]);
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[fn],
-                                                                              acc[fm][fn], 0, 0, 0);
-                }
-            }
-            if (kt + 1 < nk) {
-                sa.store(lds[cur ^ 1], tid);
-                sb.store(lds[cur ^ 1] + BM * 8, tid);
-            }
-            __syncthreads();
-        }
-
-        // Epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each block.
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            if (!live[fm]) continue;
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int col = n0 + wn * WTN + fn * 16 + (lane & 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = m0 + wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
-                    if (row < p.M && col < p.N) {
-                        float v = acc[fm][fn][i];
-                        if constexpr (BMODE == OPND_NVFP4_ROWS) v = v * p.alpha;
-                        Yb[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
-                    }
-                }
-            }
-        }
+        // live 16-row blocks of this wavefront's sub-tile, rounded up to the
+        // next instantiated count (wave-uniform)
+        const int rows_left = p.M - m0 - wm * WTM;
+        const int nlive = rows_left <= 0 ? 0 : min(FM, (rows_left + 15) / 16);
+        if (nlive == 0)
+            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, 0>(p, lds, m0, n0, Ab, Bb, Yb);
+        else if (nlive == 1 || FM == 1)
+            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, 1>(p, lds, m0, n0, Ab, Bb, Yb);
+        else if (nlive <= 2 || FM == 2)
+            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, (FM < 2 ? FM : 2)>(p, lds, m0, n0, Ab, Bb, Yb);
+        else if (nlive <= 4 || FM <= 4)
+            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, (FM < 4 ? FM : 4)>(p, lds, m0, n0, Ab, Bb, Yb);
+        else
+            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, FM>(p, lds, m0, n0, Ab, Bb, Yb);
     }
 }
 
-template <int BM, int BN, int AM, int BMD>
+template <int BM, int BN, int WGM, int WGN, int ST, int AM, int BMD>
 hipError_t launch_one(const GemmArgs &a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, AM, BMD>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, ST, AM, BMD>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, s, a);
     return hipGetLastError();
+}
+
+template <int AM, int BMD, int V>
+hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
+    constexpr TileShape t = kTileShapes[V];
+    return launch_one<t.bm, t.bn, t.wgm, t.wgn, t.stages, AM, BMD>(a, grid, s);
 }
 
 template <int AM, int BMD>
 hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s) {
+    static_assert(kNumTileShapes == 8, "one case per compiled tile shape");
     switch (r.variant) {
-        case 0: return launch_one<128, 128, AM, BMD>(a, grid, s);
-        case 1: return launch_one<128, 64, AM, BMD>(a, grid, s);
-        case 2: return launch_one<64, 64, AM, BMD>(a, grid, s);
+        case 0: return launch_variant<AM, BMD, 0>(a, grid, s);
+        case 1: return launch_variant<AM, BMD, 1>(a, grid, s);
+        case 2: return launch_variant<AM, BMD, 2>(a, grid, s);
+        case 3: return launch_variant<AM, BMD, 3>(a, grid, s);
+        case 4: return launch_variant<AM, BMD, 4>(a, grid, s);
+        case 5: return launch_variant<AM, BMD, 5>(a, grid, s);
+        case 6: return launch_variant<AM, BMD, 6>(a, grid, s);
+        case 7: return launch_variant<AM, BMD, 7>(a, grid, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -177,3 +177,23 @@ def test_rmsnorm_closed_forms_and_inplace():
     ref = host(B.bi_rmsnorm(Xd, dev(gam), 1e-6))
     B.bi_rmsnorm(Xd, dev(gam), 1e-6, Xd)      # in place
     assert np.array_equal(host(Xd), ref)
+
+
+def test_tile_shapes_bmm_and_nvfp4():
+    """Every compiled tile shape gives the plan's bits for BMM and NVFP4."""
+    nshapes = len(B.tile_shapes())
+    A = inputs.randn_bf16((16, 100, 128), tag=(140,))
+    W = inputs.randn_bf16((16, 128, 512), tag=(141,))
+    Ad, Wd = dev(A), dev(W)
+    y = host(B.bi_bmm(Ad, Wd))
+    for v in range(1, nshapes + 1):
+        note(f"bmm tile variant {v}")
+        assert np.array_equal(host(B.bi_bmm(Ad, Wd, tile_variant=v)), y), v
+    Wq, Ws, g = _nvfp4_weights(1000, 1024, (142,))
+    X = inputs.randn_bf16((130, 1024), tag=(143,))
+    Xd, Wqd, Wsd = dev(X), dev(Wq), dev(Ws)
+    alpha = float(np.float32(1.0) / g)
+    y = host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha))
+    for v in range(1, nshapes + 1):
+        note(f"nvfp4 tile variant {v}")
+        assert np.array_equal(host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha, tile_variant=v)), y), v

@@ -196,3 +196,21 @@ def test_empty_and_strided():
     yb = host(ybig)
     assert np.array_equal(yb[:, :136], y)
     assert not yb[:, 136:].any()
+
+
+def test_every_tile_shape_gives_the_same_bits():
+    """The tile shape only decides which lane and workgroup computes an
+    output: forcing each compiled shape must reproduce the plan's bits."""
+    shapes = B.tile_shapes()
+    assert len(shapes) >= 4
+    for (M, N, K) in [(300, 4096, 4096), (5, 6144, 4096), (77, 200, 544)]:
+        A = inputs.randn_bf16((M, K), tag=(70, M, N))
+        W = inputs.randn_bf16((N, K), 0.02, tag=(71, M, N))
+        Ad, Wd = dev(A), dev(W)
+        y = host(gemm(Ad, Wd))
+        for v in range(1, len(shapes) + 1):
+            note(f"gemm tile variant {v} M={M} N={N} K={K}")
+            yv = host(gemm(Ad, Wd, tile_variant=v))
+            assert np.array_equal(yv, y), f"tile variant {v} ({shapes[v - 1]}) differs"
+    with pytest.raises(B.BiError):
+        gemm(Ad, Wd, tile_variant=len(shapes) + 1)
