@@ -94,7 +94,7 @@ void fill_tile_plan(int op, int variant, bi_plan *out) {
     out->mfma_n = 16;
     out->mfma_k = 32;
     out->waves = t.wgm * t.wgn;
-    out->lds_stages = t.stages;
+    out->lds_stages = t.sb;
     out->threads = 64 * t.wgm * t.wgn;
     out->chunks_per_thread = 0;
 }

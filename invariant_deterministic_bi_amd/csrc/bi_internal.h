@@ -15,29 +15,32 @@ enum OperandMode : int {
 };
 
 // Compiled tile shapes of the GEMM mainloop.  A tile is bm x bn outputs,
-// computed by wgm x wgn wavefronts (each owning a (bm/wgm) x (bn/wgn) block),
-// with `stages` LDS buffers of 64 K-columns.  The shape changes which lanes
-// and workgroups compute which outputs, never the arithmetic of one output.
+// computed by wgm x wgn wavefronts (each owning a (bm/wgm) x (bn/wgn) block).
+// K is staged through LDS 64 columns at a time, in a ring of `sa` buffers for
+// A and `sb` buffers for B (sb >= sa >= 2): a deep B ring keeps enough of the
+// weight in flight per compute unit to stream it at small M.  The shape
+// changes which lanes and workgroups compute which outputs, never the
+// arithmetic of one output.
 struct TileShape {
-    int bm, bn, wgm, wgn, stages;
+    int bm, bn, wgm, wgn, sa, sb;
 };
 
 constexpr TileShape kTileShapes[] = {
-    {256, 128, 2, 2, 3},  // 0
-    {256, 128, 4, 2, 3},  // 1
-    {128, 128, 2, 2, 3},  // 2
-    {256, 64, 4, 1, 3},   // 3
-    {128, 64, 2, 2, 3},   // 4
-    {64, 64, 2, 2, 3},    // 5
-    {256, 32, 4, 1, 3},   // 6
-    {128, 32, 4, 1, 3},   // 7
+    {256, 128, 2, 2, 2, 4},  // 0
+    {256, 128, 4, 2, 2, 4},  // 1
+    {128, 128, 2, 2, 3, 4},  // 2
+    {256, 64, 4, 1, 2, 8},   // 3
+    {128, 64, 2, 2, 3, 8},   // 4
+    {64, 64, 2, 2, 4, 8},    // 5
+    {256, 32, 4, 1, 2, 16},  // 6
+    {128, 32, 4, 1, 3, 16},  // 7
 };
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 
-// LDS bytes of one workgroup: the pipeline buffers, or the padded bf16
-// output tile of the epilogue if that is larger.
+// LDS bytes of one workgroup: the two rings, or the padded bf16 output tile
+// of the epilogue if that is larger.
 constexpr int tile_lds_bytes(const TileShape &t) {
-    const int pipe = t.stages * (t.bm + t.bn) * 64 * 2;
+    const int pipe = (t.sa * t.bm + t.sb * t.bn) * 64 * 2;
     const int ctile = t.bm * (t.bn * 2 + 16);
     return pipe > ctile ? pipe : ctile;
 }

@@ -18,9 +18,10 @@
 //     workgroup runs which tile.
 //
 // Data movement: bf16 operands stored [rows, K] go from HBM straight into LDS
-// (buffer_load ... lds, 16 bytes per lane) STAGES-1 K-steps ahead of the
-// MFMAs; operands that need a transform on the way (the [K, N] BMM operand,
-// NVFP4 codes) go through registers and are stored one step ahead.  The
+// (buffer_load ... lds, 16 bytes per lane) into rings of SA (A) and SB (B)
+// buffers, SA-1 and SB-1 K-steps ahead of the MFMAs; operands that need a
+// transform on the way (the [K, N] BMM operand, NVFP4 codes) go through
+// registers and are stored one step ahead.  The
 // output tile is staged through LDS so that every global store is a full
 // 16-byte chunk of a row.
 //
@@ -300,21 +301,34 @@ __device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN, int STAGES, int AMODE, int BMODE>
+template <int BM, int BN, int WGM, int WGN, int SA, int SB, int AMODE, int BMODE>
 struct Cfg {
     static constexpr int NW = WGM * WGN, NT = NW * 64;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
     static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int B_RING = SA * A_BYTES;  // B ring follows the A ring
     static constexpr int C_STRIDE = BN * 2 + 16;  // padded bf16 output row in LDS
     static constexpr int C_BYTES = BM * C_STRIDE;
-    static constexpr int PIPE_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int PIPE_BYTES = SA * A_BYTES + SB * B_BYTES;
     static constexpr int LDS_BYTES = PIPE_BYTES > C_BYTES ? PIPE_BYTES : C_BYTES;
     static constexpr bool A_DIRECT = AMODE == OPND_BF16_ROWS;
     static constexpr bool B_DIRECT = BMODE == OPND_BF16_ROWS;
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 16x16 block");
+    static_assert(SA >= 2 && SB >= SA, "ring depths");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of gfx950");
+
+    // LDS-DMA instructions per wavefront per stage.
+    static constexpr int LA = A_DIRECT ? BM / NW / 8 : 0;
+    static constexpr int LB = B_DIRECT ? BN / NW / 8 : 0;
+    // Loads are issued in virtual iterations j (j < 0 is the prologue):
+    // iteration j issues A(j+SA-1) then B(j+SB-1) when those stages exist.
+    // Before computing stage kt, the later-issued of A(kt), B(kt) must have
+    // landed; WAIT = how many direct loads were issued after it, valid while
+    // every one of them exists (kt + LAST - 2 < nk); otherwise wait for all.
+    static constexpr int LAST = B_DIRECT ? SB : SA;
+    static constexpr int WAIT = (B_DIRECT && SB > SA) ? LB + (SA - 2) * (LA + LB)
+                                                      : (SA - 2) * (LA + LB);
 };
 
 // LDS barrier for the mainloop: this wavefront's LDS reads and writes are
@@ -331,13 +345,11 @@ __device__ __forceinline__ void lds_barrier() {
 // read nor multiplied; every block fm < NL runs the same chain of MFMAs in
 // the same order whatever NL is, so a row's bits do not depend on it.  All
 // wavefronts run the same sequence of loads and barriers.
-template <int BM, int BN, int WGM, int WGN, int STAGES, int AMODE, int BMODE, int NL>
+template <int BM, int BN, int WGM, int WGN, int SA, int SB, int AMODE, int BMODE, int NL>
 __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, int n0,
                                          const char *Ab, const char *Bb, uint16_t *Yb) {
-    using C = Cfg<BM, BN, WGM, WGN, STAGES, AMODE, BMODE>;
+    using C = Cfg<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE>;
     constexpr int NT = C::NT, FN = C::FN, WTM = C::WTM, WTN = C::WTN;
-    constexpr int LD = (C::A_DIRECT ? DirectOperand<BM, C::NW>::INSTR : 0) +
-                       (C::B_DIRECT ? DirectOperand<BN, C::NW>::INSTR : 0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int nk = (p.K + kBK - 1) / kBK;
@@ -359,47 +371,47 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto stage_ptr = [&](int s) -> char * { return lds + (s % STAGES) * C::STAGE_BYTES; };
+    auto a_buf = [&](int s) -> char * { return lds + (s % SA) * C::A_BYTES; };
+    auto b_buf = [&](int s) -> char * { return lds + C::B_RING + (s % SB) * C::B_BYTES; };
+    // virtual iteration j of the issue schedule (see Cfg::WAIT)
+    auto issue = [&](int j) {
+        if constexpr (C::A_DIRECT) {
+            const int s = j + SA - 1;
+            if (s >= 0 && s < nk) da.issue(a_buf(s), s * kBK, p.K, wave, lane);
+        }
+        if constexpr (C::B_DIRECT) {
+            const int s = j + SB - 1;
+            if (s >= 0 && s < nk) db.issue(b_buf(s), s * kBK, p.K, wave, lane);
+        }
+    };
 
-    // prologue: register-staged stage 0, direct stages 0..STAGES-2
+    // prologue: register-staged stage 0, then virtual iterations -(SB-1)..-1
     if constexpr (!C::A_DIRECT) {
         sa.load(Ab, p.A_scales, p.lda, m0, p.M, 0, p.K, tid);
-        sa.store(stage_ptr(0), tid);
+        sa.store(a_buf(0), tid);
     }
     if constexpr (!C::B_DIRECT) {
         sb.load(Bb, p.B_scales, p.ldb, n0, p.N, 0, p.K, tid);
-        sb.store(stage_ptr(0) + C::A_BYTES, tid);
+        sb.store(b_buf(0), tid);
     }
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-        if (s < nk) {
-            if constexpr (C::A_DIRECT) da.issue(stage_ptr(s), s * kBK, p.K, wave, lane);
-            if constexpr (C::B_DIRECT) db.issue(stage_ptr(s) + C::A_BYTES, s * kBK, p.K, wave, lane);
-        }
-    }
+    for (int j = -(C::LAST - 1); j < 0; ++j) issue(j);
 
     for (int kt = 0; kt < nk; ++kt) {
-        // stage kt's LDS-DMA loads have landed once no more than the loads of
-        // the later stages already in flight are outstanding
-        if constexpr (LD > 0) {
-            if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * LD>();
+        if constexpr (C::LA + C::LB > 0) {
+            if (kt + C::LAST - 2 < nk) wait_vmcnt<C::WAIT>();
             else wait_vmcnt<0>();
         }
         lds_barrier();
-        // register-staged loads for kt+1 first, then the next direct stage, so
-        // that waiting on the former never waits on the latter
+        // register-staged loads for kt+1 first, then this iteration's direct
+        // loads, so that waiting on the former never waits on the latter
         const bool more = kt + 1 < nk;
         if constexpr (!C::A_DIRECT) if (more) sa.load(Ab, p.A_scales, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid);
         if constexpr (!C::B_DIRECT) if (more) sb.load(Bb, p.B_scales, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
-        if (kt + STAGES - 1 < nk) {
-            const int s = kt + STAGES - 1;
-            if constexpr (C::A_DIRECT) da.issue(stage_ptr(s), s * kBK, p.K, wave, lane);
-            if constexpr (C::B_DIRECT) db.issue(stage_ptr(s) + C::A_BYTES, s * kBK, p.K, wave, lane);
-        }
+        issue(kt);
 
         if constexpr (NL > 0) {
-            const uint4 *la = reinterpret_cast<const uint4 *>(stage_ptr(kt));
-            const uint4 *lb = reinterpret_cast<const uint4 *>(stage_ptr(kt) + C::A_BYTES);
+            const uint4 *la = reinterpret_cast<const uint4 *>(a_buf(kt));
+            const uint4 *lb = reinterpret_cast<const uint4 *>(b_buf(kt));
             constexpr int KS = kBK / 32;
             bf16x8 bfrag[KS][FN], afrag[KS][NL];
             // all fragment reads of the stage first (they return in order), then
@@ -430,8 +442,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
             __builtin_amdgcn_sched_barrier(0);
         }
         if (more) {
-            if constexpr (!C::A_DIRECT) sa.store(stage_ptr(kt + 1), tid);
-            if constexpr (!C::B_DIRECT) sb.store(stage_ptr(kt + 1) + C::A_BYTES, tid);
+            if constexpr (!C::A_DIRECT) sa.store(a_buf(kt + 1), tid);
+            if constexpr (!C::B_DIRECT) sb.store(b_buf(kt + 1), tid);
         }
     }
 
@@ -473,9 +485,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     __syncthreads();  // the LDS tile is reused by the next tile's prologue
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int AMODE, int BMODE>
+template <int BM, int BN, int WGM, int WGN, int SA, int SB, int AMODE, int BMODE>
 __global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
-    using C = Cfg<BM, BN, WGM, WGN, STAGES, AMODE, BMODE>;
+    using C = Cfg<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE>;
     constexpr int FM = C::FM, WTM = C::WTM;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
 
@@ -500,21 +512,21 @@ __global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
         const int rows_left = p.M - m0 - wm * WTM;
         const int nlive = rows_left <= 0 ? 0 : min(FM, (rows_left + 15) / 16);
         if (nlive == 0)
-            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, 0>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0>(p, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive == 1 || FM == 1)
-            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, 1>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1>(p, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive <= 2 || FM == 2)
-            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, (FM < 2 ? FM : 2)>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 2 ? FM : 2)>(p, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive <= 4 || FM <= 4)
-            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, (FM < 4 ? FM : 4)>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 4 ? FM : 4)>(p, lds, m0, n0, Ab, Bb, Yb);
         else
-            run_tile<BM, BN, WGM, WGN, STAGES, AMODE, BMODE, FM>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, FM>(p, lds, m0, n0, Ab, Bb, Yb);
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int ST, int AM, int BMD>
+template <int BM, int BN, int WGM, int WGN, int SA, int SB, int AM, int BMD>
 hipError_t launch_one(const GemmArgs &a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, ST, AM, BMD>), dim3(grid),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, SA, SB, AM, BMD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, s, a);
     return hipGetLastError();
 }
@@ -522,7 +534,10 @@ hipError_t launch_one(const GemmArgs &a, int grid, hipStream_t s) {
 template <int AM, int BMD, int V>
 hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
     constexpr TileShape t = kTileShapes[V];
-    return launch_one<t.bm, t.bn, t.wgm, t.wgn, t.stages, AM, BMD>(a, grid, s);
+    // register-staged B (NVFP4 codes, the [K, N] BMM operand) is stored one
+    // step ahead, so its ring needs only as many buffers as A's
+    constexpr int sb = BMD == OPND_BF16_ROWS ? t.sb : t.sa;
+    return launch_one<t.bm, t.bn, t.wgm, t.wgn, t.sa, sb, AM, BMD>(a, grid, s);
 }
 
 template <int AM, int BMD>
