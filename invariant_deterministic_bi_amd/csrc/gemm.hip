@@ -115,41 +115,42 @@ __device__ __forceinline__ void decode32(const uint4 &codes, uint32_t sc, uint4 
 }
 
 // ---------------------------------------------------------------------------
-// Direct (LDS-DMA) operand: bf16 [rows, K], K contiguous.  Wave w fills rows
-// [w*ROWS/NW, (w+1)*ROWS/NW) of the tile, eight rows per instruction.
+// Direct (LDS-DMA) operand: bf16 [rows, K], K contiguous.  NWI wavefronts
+// issue its loads; issuing wavefront w fills rows [w*ROWS/NWI, (w+1)*ROWS/NWI)
+// of the tile, eight rows per instruction.
 // ---------------------------------------------------------------------------
-template <int ROWS, int NW>
+template <int ROWS, int NWI>
 struct DirectOperand {
-    static constexpr int RPW = ROWS / NW;   // rows per wave
-    static constexpr int INSTR = RPW / 8;   // LDS-DMA instructions per wave per stage
-    static_assert(RPW % 8 == 0, "tile rows must give each wavefront a multiple of 8 rows");
+    static constexpr int RPW = ROWS / NWI;  // rows per issuing wavefront
+    static constexpr int INSTR = RPW / 8;   // LDS-DMA instructions per wavefront per stage
+    static_assert(RPW % 8 == 0, "each issuing wavefront must own a multiple of 8 rows");
 
     i32x4 rsrc;
     int row_off[INSTR];  // byte offset of this lane's row within the tile (or -1)
 
     // base: the tile's first row; rows_valid rows exist; ld in elements.
     __device__ __forceinline__ void setup(const uint16_t *base, int rows_valid, int64_t ld, int K,
-                                          int wave, int lane) {
+                                          int w, int lane) {
         const uint32_t bytes = rows_valid > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * ld + K) * 2) : 0u;
         rsrc = make_rsrc(base, bytes);
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
-            const int row = wave * RPW + j * 8 + (lane >> 3);
+            const int row = w * RPW + j * 8 + (lane >> 3);
             row_off[j] = row < rows_valid ? (int)(row * ld * 2) : -1;
         }
     }
 
     // Issue the loads of K-step `k0` into the LDS tile at `lds_tile`.
-    __device__ __forceinline__ void issue(char *lds_tile, int k0, int K, int wave, int lane) const {
+    __device__ __forceinline__ void issue(char *lds_tile, int k0, int K, int w, int lane) const {
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
-            const int row = wave * RPW + j * 8 + (lane >> 3);
+            const int row = w * RPW + j * 8 + (lane >> 3);
             const int c = swz(row, lane & 7);           // logical chunk landing in slot lane&7
             const int gk = k0 + c * 8;
             const int voff = (row_off[j] >= 0 && gk < K) ? row_off[j] + gk * 2 : (int)0x80000000;
-            char *dst = lds_tile + (wave * RPW + j * 8) * kRowBytes;
+            char *dst = lds_tile + (w * RPW + j * 8) * kRowBytes;
             bi_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t *)dst, 16, voff,
-                                0, 0, 0);
+                                   0, 0, 0);
         }
     }
 };
@@ -318,17 +319,23 @@ struct Cfg {
     static_assert(SA >= 2 && SB >= SA, "ring depths");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of gfx950");
 
-    // LDS-DMA instructions per wavefront per stage.
-    static constexpr int LA = A_DIRECT ? BM / NW / 8 : 0;
-    static constexpr int LB = B_DIRECT ? BN / NW / 8 : 0;
-    // Loads are issued in virtual iterations j (j < 0 is the prologue):
-    // iteration j issues A(j+SA-1) then B(j+SB-1) when those stages exist.
-    // Before computing stage kt, the later-issued of A(kt), B(kt) must have
-    // landed; WAIT = how many direct loads were issued after it, valid while
-    // every one of them exists (kt + LAST - 2 < nk); otherwise wait for all.
-    static constexpr int LAST = B_DIRECT ? SB : SA;
-    static constexpr int WAIT = (B_DIRECT && SB > SA) ? LB + (SA - 2) * (LA + LB)
-                                                      : (SA - 2) * (LA + LB);
+    // When both operands are loaded by LDS DMA, the first half of the
+    // wavefronts issues all A loads and the second half all B loads.  A
+    // wavefront's vmcnt then counts only its own operand's loads, which
+    // retire in issue order, so waiting for A(kt) never waits for the deeper
+    // B prefetch.  Otherwise every wavefront issues its share of A.
+    static constexpr bool SPLIT = A_DIRECT && B_DIRECT;
+    static constexpr int NWA = SPLIT ? NW / 2 : NW;
+    static constexpr int NWB = SPLIT ? NW - NW / 2 : NW;
+    static constexpr int LA = A_DIRECT ? BM / NWA / 8 : 0;  // instructions per A wavefront per stage
+    static constexpr int LB = B_DIRECT ? BN / NWB / 8 : 0;  // per B wavefront per stage
+    // Iteration kt issues A(kt+SA-1) (A wavefronts) and B(kt+SB-1) (B
+    // wavefronts).  Before stage kt is read, an A wavefront has issued
+    // (SA-2)*LA loads after A(kt) while all of them exist (kt + SA - 2 < nk),
+    // a B wavefront (SB-2)*LB after B(kt) while kt + SB - 2 < nk; otherwise
+    // it waits for all of its loads.
+    static constexpr int WAIT_A = (SA - 2) * LA;
+    static constexpr int WAIT_B = (SB - 2) * LB;
 };
 
 // LDS barrier for the mainloop: this wavefront's LDS reads and writes are
@@ -354,16 +361,22 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     const int wm = wave / WGN, wn = wave % WGN;
     const int nk = (p.K + kBK - 1) / kBK;
 
-    DirectOperand<BM, C::NW> da;
-    DirectOperand<BN, C::NW> db;
+    DirectOperand<BM, C::NWA> da;
+    DirectOperand<BN, C::NWB> db;
     Staged<BM, AMODE, NT> sa;
     Staged<BN, BMODE, NT> sb;
+    // wave-uniform roles
+    const bool a_wave = C::A_DIRECT && (!C::SPLIT || wave < C::NWA);
+    const bool b_wave = C::B_DIRECT && (!C::SPLIT || wave >= C::NWA);
+    const int bw = C::SPLIT ? wave - C::NWA : wave;
     if constexpr (C::A_DIRECT)
-        da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(BM, p.M - m0),
-                 p.lda, p.K, wave, lane);
+        if (a_wave)
+            da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(BM, p.M - m0),
+                     p.lda, p.K, wave, lane);
     if constexpr (C::B_DIRECT)
-        db.setup(reinterpret_cast<const uint16_t *>(Bb) + (int64_t)n0 * p.ldb, min(BN, p.N - n0),
-                 p.ldb, p.K, wave, lane);
+        if (b_wave)
+            db.setup(reinterpret_cast<const uint16_t *>(Bb) + (int64_t)n0 * p.ldb, min(BN, p.N - n0),
+                     p.ldb, p.K, bw, lane);
 
     f32x4 acc[NL > 0 ? NL : 1][FN];
 #pragma unroll
@@ -373,19 +386,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
 
     auto a_buf = [&](int s) -> char * { return lds + (s % SA) * C::A_BYTES; };
     auto b_buf = [&](int s) -> char * { return lds + C::B_RING + (s % SB) * C::B_BYTES; };
-    // virtual iteration j of the issue schedule (see Cfg::WAIT)
+    // iteration j of the issue schedule (j < 0: prologue; see Cfg::WAIT_A)
     auto issue = [&](int j) {
         if constexpr (C::A_DIRECT) {
             const int s = j + SA - 1;
-            if (s >= 0 && s < nk) da.issue(a_buf(s), s * kBK, p.K, wave, lane);
+            if (a_wave && s >= 0 && s < nk) da.issue(a_buf(s), s * kBK, p.K, wave, lane);
         }
         if constexpr (C::B_DIRECT) {
             const int s = j + SB - 1;
-            if (s >= 0 && s < nk) db.issue(b_buf(s), s * kBK, p.K, wave, lane);
+            if (b_wave && s >= 0 && s < nk) db.issue(b_buf(s), s * kBK, p.K, bw, lane);
         }
     };
 
-    // prologue: register-staged stage 0, then virtual iterations -(SB-1)..-1
+    // prologue: register-staged stage 0, then schedule iterations -(SB-1)..-1
     if constexpr (!C::A_DIRECT) {
         sa.load(Ab, p.A_scales, p.lda, m0, p.M, 0, p.K, tid);
         sa.store(a_buf(0), tid);
@@ -394,12 +407,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         sb.load(Bb, p.B_scales, p.ldb, n0, p.N, 0, p.K, tid);
         sb.store(b_buf(0), tid);
     }
-    for (int j = -(C::LAST - 1); j < 0; ++j) issue(j);
+    for (int j = -(SB - 1); j < 0; ++j) issue(j);
 
     for (int kt = 0; kt < nk; ++kt) {
-        if constexpr (C::LA + C::LB > 0) {
-            if (kt + C::LAST - 2 < nk) wait_vmcnt<C::WAIT>();
-            else wait_vmcnt<0>();
+        if constexpr (C::A_DIRECT) {
+            if (a_wave) {
+                if (kt + SA - 2 < nk) wait_vmcnt<C::WAIT_A>();
+                else wait_vmcnt<0>();
+            }
+        }
+        if constexpr (C::B_DIRECT) {
+            if (b_wave && !a_wave) {
+                if (kt + SB - 2 < nk) wait_vmcnt<C::WAIT_B>();
+                else wait_vmcnt<0>();
+            }
         }
         lds_barrier();
         // register-staged loads for kt+1 first, then this iteration's direct
