@@ -76,11 +76,11 @@ constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offse
 
 int gemm_variant(int op, int64_t N, int64_t K) {
     (void)K;
-    if (op == BI_OP_BMM) return 5;      // 64 x 64
-    if (N >= 16384) return 0;           // 256 x 128
-    if (N >= 2048) return 3;            // 256 x 64
-    if (N >= 512) return 4;             // 128 x 64
-    return 5;                           // 64 x 64
+    if (op == BI_OP_BMM) return 6;      // 64 x 64
+    if (N >= 16384) return 1;           // 256 x 128
+    if (N >= 2048) return 4;            // 256 x 64
+    if (N >= 512) return 5;             // 128 x 64
+    return 6;                           // 64 x 64
 }
 
 void fill_tile_plan(int op, int variant, bi_plan *out) {

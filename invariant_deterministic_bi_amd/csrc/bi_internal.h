@@ -26,14 +26,15 @@ struct TileShape {
 };
 
 constexpr TileShape kTileShapes[] = {
-    {256, 128, 2, 2, 2, 4},  // 0
-    {256, 128, 4, 2, 2, 4},  // 1
-    {128, 128, 2, 2, 3, 4},  // 2
-    {256, 64, 4, 1, 2, 8},   // 3
-    {128, 64, 2, 2, 3, 8},   // 4
-    {64, 64, 2, 2, 4, 8},    // 5
-    {256, 32, 4, 1, 2, 16},  // 6
-    {128, 32, 4, 1, 3, 16},  // 7
+    {256, 256, 2, 2, 2, 2},   // 0
+    {256, 128, 2, 2, 2, 4},   // 1
+    {256, 128, 4, 2, 2, 4},   // 2
+    {128, 128, 2, 2, 3, 4},   // 3
+    {256, 64, 4, 1, 2, 8},    // 4
+    {128, 64, 2, 2, 3, 8},    // 5
+    {64, 64, 2, 2, 4, 8},     // 6
+    {256, 32, 4, 1, 2, 16},   // 7
+    {128, 32, 4, 1, 3, 16},   // 8
 };
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 

@@ -1,4 +1,5 @@
-// Batch-invariant GEMM mainloop for gfx950: dense bf16 GEMM, BMM and the
+// Batch-invariant GEMM mainloop for gfx950 (kernel template; instantiated
+// once per operand mode in gemm_<mode>.hip): dense bf16 GEMM, BMM and the
 // NVFP4 weight GEMM share one kernel template.
 //
 // Invariance argument (what makes output row i independent of M and of the
@@ -31,6 +32,8 @@
 // tiling here is this file's own for 64-wide wavefronts, LDS DMA and bf16
 // MFMA on gfx950.
 
+#pragma once
+
 #include "bi_internal.h"
 
 typedef int bi_i32x4 __attribute__((ext_vector_type(4)));
@@ -43,7 +46,7 @@ __device__ void bi_raw_buffer_load_lds(bi_i32x4 rsrc,
                                        int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 namespace bi {
-namespace {
+namespace gemm_detail {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -65,10 +68,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes)
 
 // LDS layout of a staged operand tile: row r (an M row of A or an N column
 // of B) holds kBK bf16 = eight 16-byte chunks; logical chunk c of row r lives
-// in physical slot r*8 + swz(r, c).  The XOR spreads the 16 rows that one
-// MFMA fragment read touches, and the 8 rows one LDS-DMA instruction fills,
-// over distinct bank groups.  swz(r, .) is an involution.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// in physical slot r*8 + swz(r, c).  The XOR depends on r's low four bits
+// only, so the 16 rows one MFMA fragment read touches land in 16 distinct
+// bank groups, and fragment blocks 16 rows apart differ by a constant byte
+// offset (an instruction immediate).  swz(r, .) is an involution.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -140,14 +144,17 @@ struct DirectOperand {
         }
     }
 
-    // Issue the loads of K-step `k0` into the LDS tile at `lds_tile`.
-    __device__ __forceinline__ void issue(char *lds_tile, int k0, int K, int w, int lane) const {
+    // Issue the loads of K-step `k0` into the LDS tile at `lds_tile`.  A
+    // step with live == false issues the same instructions with every lane
+    // out of range: they write zeros and keep the vmcnt bookkeeping exact.
+    __device__ __forceinline__ void issue(char *lds_tile, int k0, int K, int w, int lane,
+                                          bool live) const {
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
             const int row = w * RPW + j * 8 + (lane >> 3);
             const int c = swz(row, lane & 7);           // logical chunk landing in slot lane&7
             const int gk = k0 + c * 8;
-            const int voff = (row_off[j] >= 0 && gk < K) ? row_off[j] + gk * 2 : (int)0x80000000;
+            const int voff = (live && row_off[j] >= 0 && gk < K) ? row_off[j] + gk * 2 : (int)0x80000000;
             char *dst = lds_tile + (w * RPW + j * 8) * kRowBytes;
             bi_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t *)dst, 16, voff,
                                    0, 0, 0);
@@ -330,10 +337,9 @@ struct Cfg {
     static constexpr int LA = A_DIRECT ? BM / NWA / 8 : 0;  // instructions per A wavefront per stage
     static constexpr int LB = B_DIRECT ? BN / NWB / 8 : 0;  // per B wavefront per stage
     // Iteration kt issues A(kt+SA-1) (A wavefronts) and B(kt+SB-1) (B
-    // wavefronts).  Before stage kt is read, an A wavefront has issued
-    // (SA-2)*LA loads after A(kt) while all of them exist (kt + SA - 2 < nk),
-    // a B wavefront (SB-2)*LB after B(kt) while kt + SB - 2 < nk; otherwise
-    // it waits for all of its loads.
+    // wavefronts), out-of-range steps included (as zero-filling no-ops), so
+    // before stage kt is read an A wavefront has issued exactly (SA-2)*LA
+    // loads after A(kt) and a B wavefront (SB-2)*LB after B(kt).
     static constexpr int WAIT_A = (SA - 2) * LA;
     static constexpr int WAIT_B = (SB - 2) * LB;
 };
@@ -357,7 +363,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
                                          const char *Ab, const char *Bb, uint16_t *Yb) {
     using C = Cfg<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE>;
     constexpr int NT = C::NT, FN = C::FN, WTM = C::WTM, WTN = C::WTN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int wm = wave / WGN, wn = wave % WGN;
     const int nk = (p.K + kBK - 1) / kBK;
 
@@ -390,11 +397,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     auto issue = [&](int j) {
         if constexpr (C::A_DIRECT) {
             const int s = j + SA - 1;
-            if (a_wave && s >= 0 && s < nk) da.issue(a_buf(s), s * kBK, p.K, wave, lane);
+            if (a_wave && s >= 0) da.issue(a_buf(s), s * kBK, p.K, wave, lane, s < nk);
         }
         if constexpr (C::B_DIRECT) {
             const int s = j + SB - 1;
-            if (b_wave && s >= 0 && s < nk) db.issue(b_buf(s), s * kBK, p.K, bw, lane);
+            if (b_wave && s >= 0) db.issue(b_buf(s), s * kBK, p.K, bw, lane, s < nk);
         }
     };
 
@@ -410,18 +417,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     for (int j = -(SB - 1); j < 0; ++j) issue(j);
 
     for (int kt = 0; kt < nk; ++kt) {
-        if constexpr (C::A_DIRECT) {
-            if (a_wave) {
-                if (kt + SA - 2 < nk) wait_vmcnt<C::WAIT_A>();
-                else wait_vmcnt<0>();
-            }
-        }
-        if constexpr (C::B_DIRECT) {
-            if (b_wave && !a_wave) {
-                if (kt + SB - 2 < nk) wait_vmcnt<C::WAIT_B>();
-                else wait_vmcnt<0>();
-            }
-        }
+        if constexpr (C::A_DIRECT)
+            if (a_wave) wait_vmcnt<C::WAIT_A>();
+        if constexpr (C::B_DIRECT)
+            if (b_wave && !a_wave) wait_vmcnt<C::WAIT_B>();
         lds_barrier();
         // register-staged loads for kt+1 first, then this iteration's direct
         // loads, so that waiting on the former never waits on the latter
@@ -434,33 +433,50 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
             const uint4 *la = reinterpret_cast<const uint4 *>(a_buf(kt));
             const uint4 *lb = reinterpret_cast<const uint4 *>(b_buf(kt));
             constexpr int KS = kBK / 32;
-            bf16x8 bfrag[KS][FN], afrag[KS][NL];
-            // all fragment reads of the stage first (they return in order), then
-            // the MFMAs, which wait only for the fragments they consume
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            // Small wave tiles read every fragment of the stage first (they
+            // return in order) and then run the MFMAs, which wait only for
+            // the fragments they consume.  A 128x128 wave tile would need 128
+            // fragment registers for that, so it reads one 32-wide K step at a
+            // time.  Either way each accumulator sees the same MFMA sequence.
+            constexpr bool ALL_FIRST = NL * FN < 64;
+            bf16x8 bfrag[ALL_FIRST ? KS : 1][FN], afrag[ALL_FIRST ? KS : 1][NL > 0 ? NL : 1];
+            auto read_frags = [&](int ks, int slot) {
                 const int c = ks * 4 + (lane >> 4);
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
                     const int col = wn * WTN + fn * 16 + (lane & 15);
-                    bfrag[ks][fn] = __builtin_bit_cast(bf16x8, lb[col * 8 + swz(col, c)]);
+                    bfrag[slot][fn] = __builtin_bit_cast(bf16x8, lb[col * 8 + swz(col, c)]);
                 }
 #pragma unroll
                 for (int fm = 0; fm < NL; ++fm) {
                     const int row = wm * WTM + fm * 16 + (lane & 15);
-                    afrag[ks][fm] = __builtin_bit_cast(bf16x8, la[row * 8 + swz(row, c)]);
+                    afrag[slot][fm] = __builtin_bit_cast(bf16x8, la[row * 8 + swz(row, c)]);
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            };
+            auto mfmas = [&](int slot) {
 #pragma unroll
                 for (int fm = 0; fm < NL; ++fm)
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
                         acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            afrag[ks][fm], bfrag[ks][fn], acc[fm][fn], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                            afrag[slot][fm], bfrag[slot][fn], acc[fm][fn], 0, 0, 0);
+            };
+            if constexpr (ALL_FIRST) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) read_frags(ks, ks);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) mfmas(ks);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    read_frags(ks, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfmas(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
         if (more) {
             if constexpr (!C::A_DIRECT) sa.store(a_buf(kt + 1), tid);
@@ -512,7 +528,7 @@ __global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
     constexpr int FM = C::FM, WTM = C::WTM;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WGN;
     const int G = gridDim.x;
     const bool spread = (G % 8) == 0;
@@ -563,7 +579,7 @@ hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
 
 template <int AM, int BMD>
 hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s) {
-    static_assert(kNumTileShapes == 8, "one case per compiled tile shape");
+    static_assert(kNumTileShapes == 9, "one case per compiled tile shape");
     switch (r.variant) {
         case 0: return launch_variant<AM, BMD, 0>(a, grid, s);
         case 1: return launch_variant<AM, BMD, 1>(a, grid, s);
@@ -573,23 +589,10 @@ hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStr
         case 5: return launch_variant<AM, BMD, 5>(a, grid, s);
         case 6: return launch_variant<AM, BMD, 6>(a, grid, s);
         case 7: return launch_variant<AM, BMD, 7>(a, grid, s);
+        case 8: return launch_variant<AM, BMD, 8>(a, grid, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmArgs &args,
-                       int grid, hipStream_t stream) {
-    if (a_mode == OPND_BF16_ROWS && b_mode == OPND_BF16_ROWS)
-        return launch_modes<OPND_BF16_ROWS, OPND_BF16_ROWS>(r, args, grid, stream);
-    if (a_mode == OPND_BF16_ROWS && b_mode == OPND_BF16_KN)
-        return launch_modes<OPND_BF16_ROWS, OPND_BF16_KN>(r, args, grid, stream);
-    if (a_mode == OPND_BF16_ROWS && b_mode == OPND_NVFP4_ROWS)
-        return launch_modes<OPND_BF16_ROWS, OPND_NVFP4_ROWS>(r, args, grid, stream);
-    if (a_mode == OPND_NVFP4_ROWS && b_mode == OPND_NVFP4_ROWS)
-        return launch_modes<OPND_NVFP4_ROWS, OPND_NVFP4_ROWS>(r, args, grid, stream);
-    return hipErrorInvalidValue;
-}
-
+}  // namespace gemm_detail
 }  // namespace bi
