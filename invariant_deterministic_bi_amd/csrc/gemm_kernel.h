@@ -156,7 +156,12 @@ struct DirectOperand {
             const int gk = k0 + c * 8;
             const int voff = (live && row_off[j] >= 0 && gk < K) ? row_off[j] + gk * 2 : (int)0x80000000;
             char *dst = lds_tile + (w * RPW + j * 8) * kRowBytes;
-            bi_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t *)dst, 16, voff,
+            i32x4 r;  // the descriptor must be scalar: restate its uniformity here
+            r.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+            r.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+            r.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+            r.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+            bi_raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t *)dst, 16, voff,
                                    0, 0, 0);
         }
     }
@@ -376,14 +381,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     const bool a_wave = C::A_DIRECT && (!C::SPLIT || wave < C::NWA);
     const bool b_wave = C::B_DIRECT && (!C::SPLIT || wave >= C::NWA);
     const int bw = C::SPLIT ? wave - C::NWA : wave;
+    // set up both descriptors on every wavefront (unconditionally, so the
+    // compiler keeps them uniform); each wavefront issues only its role's loads
     if constexpr (C::A_DIRECT)
-        if (a_wave)
-            da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(BM, p.M - m0),
-                     p.lda, p.K, wave, lane);
+        da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(BM, p.M - m0),
+                 p.lda, p.K, C::SPLIT ? wave % C::NWA : wave, lane);
     if constexpr (C::B_DIRECT)
-        if (b_wave)
-            db.setup(reinterpret_cast<const uint16_t *>(Bb) + (int64_t)n0 * p.ldb, min(BN, p.N - n0),
-                     p.ldb, p.K, bw, lane);
+        db.setup(reinterpret_cast<const uint16_t *>(Bb) + (int64_t)n0 * p.ldb, min(BN, p.N - n0),
+                 p.ldb, p.K, C::SPLIT ? bw % C::NWB : bw, lane);
 
     f32x4 acc[NL > 0 ? NL : 1][FN];
 #pragma unroll
