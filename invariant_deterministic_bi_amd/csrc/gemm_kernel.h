@@ -363,7 +363,7 @@ __device__ __forceinline__ void lds_barrier() {
 // read nor multiplied; every block fm < NL runs the same chain of MFMAs in
 // the same order whatever NL is, so a row's bits do not depend on it.  All
 // wavefronts run the same sequence of loads and barriers.
-template <int BM, int BN, int WGM, int WGN, int SA, int SB, int AMODE, int BMODE, int NL>
+template <int BM, int BN, int WGM, int WGN, int SA, int SB, int AMODE, int BMODE, int NL, bool COMPACT>
 __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, int n0,
                                          const char *Ab, const char *Bb, uint16_t *Yb) {
     using C = Cfg<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE>;
@@ -373,19 +373,29 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     const int wm = wave / WGN, wn = wave % WGN;
     const int nk = (p.K + kBK - 1) / kBK;
 
-    DirectOperand<BM, C::NWA> da;
+    // COMPACT (a tile whose valid rows all lie in its first 16): rows beyond
+    // M are neither loaded nor multiplied, so the A ring is re-laid out as
+    // SB stages of 16 rows, all issued by wavefront 0.  A is then prefetched
+    // as deep as B; the K order and every MFMA of the valid rows are unchanged.
+    constexpr bool CA = COMPACT && C::A_DIRECT;
+    constexpr int SAX = CA ? SB : SA;              // A ring depth
+    constexpr int A_ROWS = CA ? 16 : BM;           // rows per A stage
+    static_assert(!CA || SB * 16 <= SA * BM, "compact A ring must fit the A region");
+    DirectOperand<A_ROWS, CA ? 1 : C::NWA> da;
     DirectOperand<BN, C::NWB> db;
     Staged<BM, AMODE, NT> sa;
     Staged<BN, BMODE, NT> sb;
     // wave-uniform roles
-    const bool a_wave = C::A_DIRECT && (!C::SPLIT || wave < C::NWA);
+    const bool a_wave = C::A_DIRECT && (CA ? wave == 0 : (!C::SPLIT || wave < C::NWA));
     const bool b_wave = C::B_DIRECT && (!C::SPLIT || wave >= C::NWA);
     const int bw = C::SPLIT ? wave - C::NWA : wave;
+    constexpr int LAX = CA ? 2 : C::LA;            // A instructions per A wavefront per stage
+    constexpr int WAIT_AX = (SAX - 2) * LAX;
     // set up both descriptors on every wavefront (unconditionally, so the
     // compiler keeps them uniform); each wavefront issues only its role's loads
     if constexpr (C::A_DIRECT)
-        da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(BM, p.M - m0),
-                 p.lda, p.K, C::SPLIT ? wave % C::NWA : wave, lane);
+        da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(A_ROWS, p.M - m0),
+                 p.lda, p.K, CA ? 0 : (C::SPLIT ? wave % C::NWA : wave), lane);
     if constexpr (C::B_DIRECT)
         db.setup(reinterpret_cast<const uint16_t *>(Bb) + (int64_t)n0 * p.ldb, min(BN, p.N - n0),
                  p.ldb, p.K, C::SPLIT ? bw % C::NWB : bw, lane);
@@ -396,13 +406,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto a_buf = [&](int s) -> char * { return lds + (s % SA) * C::A_BYTES; };
+    auto a_buf = [&](int s) -> char * { return lds + (s % SAX) * (A_ROWS * kRowBytes); };
     auto b_buf = [&](int s) -> char * { return lds + C::B_RING + (s % SB) * C::B_BYTES; };
     // iteration j of the issue schedule (j < 0: prologue; see Cfg::WAIT_A)
     auto issue = [&](int j) {
         if constexpr (C::A_DIRECT) {
-            const int s = j + SA - 1;
-            if (a_wave && s >= 0) da.issue(a_buf(s), s * kBK, p.K, wave, lane, s < nk);
+            const int s = j + SAX - 1;
+            if (a_wave && s >= 0) da.issue(a_buf(s), s * kBK, p.K, CA ? 0 : wave, lane, s < nk);
         }
         if constexpr (C::B_DIRECT) {
             const int s = j + SB - 1;
@@ -419,11 +429,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         sb.load(Bb, p.B_scales, p.ldb, n0, p.N, 0, p.K, tid);
         sb.store(b_buf(0), tid);
     }
-    for (int j = -(SB - 1); j < 0; ++j) issue(j);
+    for (int j = -(SB > SAX ? SB - 1 : SAX - 1); j < 0; ++j) issue(j);
 
     for (int kt = 0; kt < nk; ++kt) {
         if constexpr (C::A_DIRECT)
-            if (a_wave) wait_vmcnt<C::WAIT_A>();
+            if (a_wave) wait_vmcnt<WAIT_AX>();
         if constexpr (C::B_DIRECT)
             if (b_wave && !a_wave) wait_vmcnt<C::WAIT_B>();
         lds_barrier();
@@ -553,16 +563,22 @@ __global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
         // next instantiated count (wave-uniform)
         const int rows_left = p.M - m0 - wm * WTM;
         const int nlive = rows_left <= 0 ? 0 : min(FM, (rows_left + 15) / 16);
-        if (nlive == 0)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0>(p, lds, m0, n0, Ab, Bb, Yb);
+        if (p.M - m0 <= 16) {
+            // every valid row of the tile is in wavefront row 0's first block
+            if (wm == 0)
+                run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1, true>(p, lds, m0, n0, Ab, Bb, Yb);
+            else
+                run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0, true>(p, lds, m0, n0, Ab, Bb, Yb);
+        } else if (nlive == 0)
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0, false>(p, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive == 1 || FM == 1)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1, false>(p, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive <= 2 || FM == 2)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 2 ? FM : 2)>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 2 ? FM : 2), false>(p, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive <= 4 || FM <= 4)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 4 ? FM : 4)>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 4 ? FM : 4), false>(p, lds, m0, n0, Ab, Bb, Yb);
         else
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, FM>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, FM, false>(p, lds, m0, n0, Ab, Bb, Yb);
     }
 }
 
