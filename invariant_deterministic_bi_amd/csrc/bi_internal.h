@@ -26,7 +26,7 @@ struct TileShape {
 };
 
 constexpr TileShape kTileShapes[] = {
-    {256, 256, 2, 2, 2, 2},   // 0
+    {256, 256, 4, 2, 2, 2},   // 0
     {256, 128, 2, 2, 2, 4},   // 1
     {256, 128, 4, 2, 2, 4},   // 2
     {128, 128, 2, 2, 3, 4},   // 3

@@ -130,18 +130,19 @@ struct DirectOperand {
     static_assert(RPW % 8 == 0, "each issuing wavefront must own a multiple of 8 rows");
 
     i32x4 rsrc;
-    int row_off[INSTR];  // byte offset of this lane's row within the tile (or -1)
+    int row0_off;   // byte offset of this lane's row for instruction 0
+    int rows_left;  // valid rows from this lane's row for instruction 0 on
+    int step_off;   // byte offset between consecutive instructions (8 rows)
 
     // base: the tile's first row; rows_valid rows exist; ld in elements.
     __device__ __forceinline__ void setup(const uint16_t *base, int rows_valid, int64_t ld, int K,
                                           int w, int lane) {
         const uint32_t bytes = rows_valid > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * ld + K) * 2) : 0u;
         rsrc = make_rsrc(base, bytes);
-#pragma unroll
-        for (int j = 0; j < INSTR; ++j) {
-            const int row = w * RPW + j * 8 + (lane >> 3);
-            row_off[j] = row < rows_valid ? (int)(row * ld * 2) : -1;
-        }
+        const int row = w * RPW + (lane >> 3);
+        row0_off = (int)(row * ld * 2);
+        rows_left = rows_valid - row;
+        step_off = (int)(8 * ld * 2);
     }
 
     // Issue the loads of K-step `k0` into the LDS tile at `lds_tile`.  A
@@ -154,7 +155,8 @@ struct DirectOperand {
             const int row = w * RPW + j * 8 + (lane >> 3);
             const int c = swz(row, lane & 7);           // logical chunk landing in slot lane&7
             const int gk = k0 + c * 8;
-            const int voff = (live && row_off[j] >= 0 && gk < K) ? row_off[j] + gk * 2 : (int)0x80000000;
+            const bool ok = live && j * 8 < rows_left && gk < K;
+            const int voff = ok ? row0_off + j * step_off + gk * 2 : (int)0x80000000;
             char *dst = lds_tile + (w * RPW + j * 8) * kRowBytes;
             i32x4 r;  // the descriptor must be scalar: restate its uniformity here
             r.x = __builtin_amdgcn_readfirstlane(rsrc.x);
@@ -448,12 +450,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
             const uint4 *la = reinterpret_cast<const uint4 *>(a_buf(kt));
             const uint4 *lb = reinterpret_cast<const uint4 *>(b_buf(kt));
             constexpr int KS = kBK / 32;
-            // Small wave tiles read every fragment of the stage first (they
-            // return in order) and then run the MFMAs, which wait only for
-            // the fragments they consume.  A 128x128 wave tile would need 128
-            // fragment registers for that, so it reads one 32-wide K step at a
-            // time.  Either way each accumulator sees the same MFMA sequence.
-            constexpr bool ALL_FIRST = NL * FN < 64;
+            // With four wavefronts (one per SIMD), small wave tiles read every
+            // fragment of the stage first (they return in order) and then run
+            // the MFMAs, which wait only for the fragments they consume.  With
+            // eight wavefronts the SIMD's second wavefront hides the read
+            // latency, and a 128x128 wave tile would need 128 fragment
+            // registers, so those read one 32-wide K step at a time.  Either
+            // way each accumulator sees the same MFMA sequence.
+            constexpr bool ALL_FIRST = NL * FN < 64 && C::NW < 8;
             bf16x8 bfrag[ALL_FIRST ? KS : 1][FN], afrag[ALL_FIRST ? KS : 1][NL > 0 ? NL : 1];
             auto read_frags = [&](int ks, int slot) {
                 const int c = ks * 4 + (lane >> 4);
