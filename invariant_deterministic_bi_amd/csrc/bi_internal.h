@@ -35,6 +35,9 @@ constexpr TileShape kTileShapes[] = {
     {64, 64, 2, 2, 4, 8},     // 6
     {256, 32, 4, 1, 2, 16},   // 7
     {128, 32, 4, 1, 3, 16},   // 8
+    {256, 128, 4, 2, 3, 4},   // 9
+    {128, 128, 2, 2, 4, 4},   // 10
+    {128, 128, 4, 2, 4, 4},   // 11
 };
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 

@@ -604,7 +604,7 @@ hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
 
 template <int AM, int BMD>
 hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s) {
-    static_assert(kNumTileShapes == 9, "one case per compiled tile shape");
+    static_assert(kNumTileShapes == 12, "one case per compiled tile shape");
     switch (r.variant) {
         case 0: return launch_variant<AM, BMD, 0>(a, grid, s);
         case 1: return launch_variant<AM, BMD, 1>(a, grid, s);
@@ -615,6 +615,9 @@ hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStr
         case 6: return launch_variant<AM, BMD, 6>(a, grid, s);
         case 7: return launch_variant<AM, BMD, 7>(a, grid, s);
         case 8: return launch_variant<AM, BMD, 8>(a, grid, s);
+        case 9: return launch_variant<AM, BMD, 9>(a, grid, s);
+        case 10: return launch_variant<AM, BMD, 10>(a, grid, s);
+        case 11: return launch_variant<AM, BMD, 11>(a, grid, s);
         default: return hipErrorInvalidValue;
     }
 }
