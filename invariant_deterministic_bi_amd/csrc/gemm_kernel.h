@@ -376,13 +376,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     const int nk = (p.K + kBK - 1) / kBK;
 
     // COMPACT (a tile whose valid rows all lie in its first 16): rows beyond
-    // M are neither loaded nor multiplied, so the A ring is re-laid out as
-    // SB stages of 16 rows, all issued by wavefront 0.  A is then prefetched
-    // as deep as B; the K order and every MFMA of the valid rows are unchanged.
+    // M are neither loaded nor multiplied, so the LDS is re-laid out as rings
+    // of SBX stages: 16 A rows and (for a bf16 B) a full B stage each, as many
+    // as the workgroup's LDS holds (at most 16).  A is issued by wavefront 0.
+    // A and B are then prefetched deep enough to stream the weight at the
+    // per-CU rate; the K order and every MFMA of the valid rows are unchanged.
     constexpr bool CA = COMPACT && C::A_DIRECT;
-    constexpr int SAX = CA ? SB : SA;              // A ring depth
-    constexpr int A_ROWS = CA ? 16 : BM;           // rows per A stage
-    static_assert(!CA || SB * 16 <= SA * BM, "compact A ring must fit the A region");
+    constexpr int A16 = 16 * kRowBytes;
+    constexpr int SBC_RAW = C::B_DIRECT ? C::LDS_BYTES / (A16 + C::B_BYTES) : SB;
+    constexpr int SBC = SBC_RAW > 16 ? 16 : (SBC_RAW < SB ? SB : SBC_RAW);
+    constexpr int SBX = (CA && C::B_DIRECT) ? SBC : SB;   // B ring depth
+    constexpr int SAX = CA ? SBX : SA;                      // A ring depth
+    constexpr int A_ROWS = CA ? 16 : BM;                    // rows per A stage
+    constexpr int B_RING_X = CA ? SAX * A16 : C::B_RING;    // B ring offset
+    static_assert(!CA || SAX * A16 + SBX * C::B_BYTES <= C::LDS_BYTES, "compact rings must fit");
     DirectOperand<A_ROWS, CA ? 1 : C::NWA> da;
     DirectOperand<BN, C::NWB> db;
     Staged<BM, AMODE, NT> sa;
@@ -409,7 +416,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto a_buf = [&](int s) -> char * { return lds + (s % SAX) * (A_ROWS * kRowBytes); };
-    auto b_buf = [&](int s) -> char * { return lds + C::B_RING + (s % SB) * C::B_BYTES; };
+    auto b_buf = [&](int s) -> char * { return lds + B_RING_X + (s % SBX) * C::B_BYTES; };
     // iteration j of the issue schedule (j < 0: prologue; see Cfg::WAIT_A)
     auto issue = [&](int j) {
         if constexpr (C::A_DIRECT) {
@@ -417,7 +424,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
             if (a_wave && s >= 0) da.issue(a_buf(s), s * kBK, p.K, CA ? 0 : wave, lane, s < nk);
         }
         if constexpr (C::B_DIRECT) {
-            const int s = j + SB - 1;
+            const int s = j + SBX - 1;
             if (b_wave && s >= 0) db.issue(b_buf(s), s * kBK, p.K, bw, lane, s < nk);
         }
     };
@@ -431,13 +438,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         sb.load(Bb, p.B_scales, p.ldb, n0, p.N, 0, p.K, tid);
         sb.store(b_buf(0), tid);
     }
-    for (int j = -(SB > SAX ? SB - 1 : SAX - 1); j < 0; ++j) issue(j);
+    for (int j = -(SBX > SAX ? SBX - 1 : SAX - 1); j < 0; ++j) issue(j);
 
     for (int kt = 0; kt < nk; ++kt) {
         if constexpr (C::A_DIRECT)
             if (a_wave) wait_vmcnt<WAIT_AX>();
         if constexpr (C::B_DIRECT)
-            if (b_wave && !a_wave) wait_vmcnt<C::WAIT_B>();
+            if (b_wave && !a_wave) wait_vmcnt<(SBX - 2) * C::LB>();
         lds_barrier();
         // register-staged loads for kt+1 first, then this iteration's direct
         // loads, so that waiting on the former never waits on the latter
