@@ -74,11 +74,17 @@ bi_status device_cus(int *out) {
 // ---------------------------------------------------------------------------
 constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offsets
 
+// The choices below come from sweeping every compiled shape on MI355X at
+// M = 1, 16 and 2048 for each Qwen3-8B-shaped (N, K): at M <= 16 the number
+// of tiles N / bn bounds how many compute units stream the weight (about
+// 50 GB/s each), at M = 2048 a wide tile cuts operand traffic per MFMA.  The
+// shape is the one with the best balance of the two for that N.
 int gemm_variant(int op, int64_t N, int64_t K) {
     (void)K;
     if (op == BI_OP_BMM) return 6;      // 64 x 64
-    if (N >= 16384) return 1;           // 256 x 128
-    if (N >= 2048) return 4;            // 256 x 64
+    if (N >= 16384) return 0;           // 256 x 256, 8 wavefronts
+    if (N >= 5120) return 11;           // 128 x 128, 8 wavefronts
+    if (N >= 2048) return 9;            // 256 x 128, 8 wavefronts, 3-deep A ring
     if (N >= 512) return 5;             // 128 x 64
     return 6;                           // 64 x 64
 }
