@@ -2,7 +2,7 @@
 
 One step = one pass of every operation of the path over one batch of
 synthetic, seeded inputs already resident in HBM, shaped like a Qwen3-8B
-decoder layer's linear layers at M tokens (default M = 2048):
+decoder layer at M tokens (default M = 2048):
     RMSNorm(H=4096) -> qkv GEMM (N=6144, K=4096) -> MLA-absorbed BMM
     (128 heads, [M_b,128] . [128,512], M_b = min(M, 1024)) -> o_proj GEMM
     (4096, 4096) -> RMSNorm -> gate_up GEMM (24576, 4096) -> down GEMM
@@ -10,16 +10,26 @@ decoder layer's linear layers at M tokens (default M = 2048):
 Activations ~ N(0,1), weights ~ N(0,0.02), rounded to bf16; the NVFP4
 weight is the host quantisation of N(0,0.02) values; gamma ~ U(0.5,1.5).
 
-Prints one JSON line.  `value` is the step's GEMM-family TFLOP/s (all
-flops of the step over the measured step time).  `roofline` is for the
-dominant kernel (the bf16 gate_up GEMM), its duration measured with HIP
-events on the stream it is launched on.  `sweep` adds per-op figures at
-M = 1 and 16 (HBM GB/s, with >= 1 GiB of rotating weight copies so the
-256 MB last-level cache cannot serve them) and at the step's M.
-`invariance` counts bitwise checks of small-M rows against the step's rows.
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same step.
+Prints one JSON line.  `value` is the step's GEMM-family TFLOP/s (all flops
+of the step over the measured step time).  `roofline` is for the dominant
+kernel, the bf16 gate_up GEMM; its duration is measured with HIP events on
+the stream it is launched on, and `traffic` comes from the committed
+counter summary in profiles/ when that was taken with the current kernel
+sources.  `sweep` adds per-op figures at M = 1 and 16 (HBM GB/s with >= 1
+GiB of rotating weight copies, so the 256 MB last-level cache cannot serve
+them) and at the step's M.  `invariance` counts bitwise checks of small-M
+rows against the step's rows and of repeated steps.  `cpu_baseline` times
+the fp64 oracle on a bounded sample of the same step.
+
+Profiler passes (run under rocprofv3; see profiles/):
+    python bench.py --only-step --calib-copy --steps 5 --warmup 2
+and their summary:
+    python bench.py --summarize <rocprofv3 output dir> --out <file>
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +41,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CALIB_BYTES = 512 << 20     # bytes read (and written) by one calibration copy
+GATE_UP_KERNEL = "gemm_kernelILi256ELi256ELi4ELi2ELi2ELi2ELi0ELi0E"   # bf16 256x256 tile
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_M2048_counters.txt")
 
 
 def parse():
@@ -43,7 +56,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     p.add_argument("--only-step", action="store_true",
-                   help="run the timed steps only (for profiler runs)")
+                   help="run the timed steps only (for profiler passes)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="after the steps, copy 512 MiB three times (counter calibration)")
+    p.add_argument("--summarize", metavar="DIR", help="summarise rocprofv3 CSV output in DIR")
+    p.add_argument("--out", metavar="FILE", help="where --summarize writes its summary")
+    p.add_argument("--command", default="", help="command line recorded by --summarize")
     return p.parse_args()
 
 
@@ -51,8 +69,75 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_source_sha() -> str:
+    """Hash of the HIP/C++ sources: a counter summary is valid only for them."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "invariant_deterministic_bi_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".h", ".hip", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters_summary():
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ summaries
+
+def summarize(d, out, command):
+    """Condense rocprofv3 CSV output (kernel stats or counters) into text."""
+    lines = [f"# rocprofv3 summary written by: python bench.py --summarize {d}",
+             f"# profiled command: {command}" if command else "#",
+             f"kernel_source_sha: {kernel_source_sha()}"]
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    for path in stats:
+        rows = list(csv.DictReader(open(path)))
+        lines.append(f"# kernel stats ({os.path.basename(path)}): name | calls | avg ns | total ns | %")
+        for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
+            lines.append(f"{r['Name'][:150]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                         f"{float(r['TotalDurationNs']):.0f} | {float(r.get('Percentage', 0) or 0):.2f}")
+    ctr = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    for path in ctr:
+        rows = list(csv.DictReader(open(path)))
+        acc = {}
+        for r in rows:
+            name = r["Kernel_Name"]
+            kind = "gate_up" if GATE_UP_KERNEL in name else ("copy" if "copy" in name.lower() else None)
+            if kind is None:
+                continue
+            acc.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        lines.append(f"# counters ({os.path.basename(path)}), mean per dispatch")
+        for (kind, cn), v in sorted(acc.items()):
+            lines.append(f"{kind}_{cn}_per_dispatch: {sum(v) / len(v):.1f}")
+            lines.append(f"{kind}_{cn}_dispatches: {len(v)}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ------------------------------------------------------------------ main
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.out or os.path.join(args.summarize, "summary.txt"), args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the batch-invariant path here is single-GPU "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
@@ -149,11 +234,19 @@ def main():
     gu_tflops = flops["gate_up"] / (gu_ms * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; gate_up {gu_ms * 1e3:.1f} us "
         f"{gu_tflops:.1f} TFLOP/s")
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copies of {CALIB_BYTES} bytes done")
     if args.only_step:
         print(json.dumps({"metric": "step", "ms_per_step": ms_per_step, "value": value,
                           "gate_up_us": gu_ms * 1e3}), flush=True)
         return
 
+    traffic = read_counters_summary()
     result = {
         "metric": "batch-invariant GEMM TFLOP/s & GB/s vs M, % roofline; bitwise-invariance pass %",
         "value": round(value, 2),
@@ -171,9 +264,10 @@ def main():
                                f"qkv 6144x4096, MLA BMM 128x[{Mb},128]x[128,512], o_proj 4096x4096, "
                                f"rmsnorm, gate_up 24576x4096, down 4096x12288, NVFP4 gate_up 24576x4096",
                    "M": M, "global_batch": M, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "bi_gemm gate_up N=24576 K=4096",
+        "roofline": {"bound": "mfma", "kernel": "bi_gemm gate_up N=24576 K=4096 (256x256 tile)",
                      "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
                      "per_launch_flops": flops["gate_up"], "avg_launch_us": round(gu_ms * 1e3, 2)},
     }
 
@@ -181,6 +275,18 @@ def main():
     if not args.no_sweep:
         sweep = []
         inv_checked = inv_passed = 0
+
+        def timed(fn, reps):
+            fn(0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(reps):
+                fn(r)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
         specs = [("qkv", t["Wqkv"], out["Xn"], out["Yqkv"], H),
                  ("o_proj", t["Wo"], t["Ao"], out["Yo"], H),
                  ("gate_up", t["Wgu"], out["Xn2"], out["Ygu"], H),
@@ -193,17 +299,7 @@ def main():
             for m in (1, 16):
                 A = Afull[:m]
                 Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
-                for c in copies:
-                    B.bi_gemm(A, c, Y)
-                torch.cuda.synchronize()
-                reps = 20 * ncopy
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for r in range(reps):
-                    B.bi_gemm(A, copies[r % ncopy], Y)
-                e1.record()
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / reps
+                us = timed(lambda r: B.bi_gemm(A, copies[r % ncopy], Y), 20 * ncopy)
                 byt = 2.0 * (m * K + N * K + m * N)
                 gbs = byt / (us * 1e-6) / 1e9
                 sweep.append({"op": name, "N": N, "K": K, "M": m, "us": round(us, 2),
@@ -213,29 +309,40 @@ def main():
                 inv_passed += int(torch.equal(Y, ref16[:m]))
             del copies
             torch.cuda.empty_cache()
-        # per-op figures at the step's M (one launch each, weights cold in the
-        # cache only as far as the step's own rotation makes them)
+        # NVFP4 gate_up at M = 1, 16 (rotating weight copies)
+        ncopy = 8
+        w4c = [t["W4"]] + [t["W4"].clone() for _ in range(ncopy - 1)]
+        s4c = [t["W4s"]] + [t["W4s"].clone() for _ in range(ncopy - 1)]
+        ref16 = out["Y4"][:16].clone()
+        for m in (1, 16):
+            A = out["Xn2"][:m]
+            Y = torch.empty((m, Ngu), dtype=torch.bfloat16, device=dev)
+            us = timed(lambda r: B.bi_nvfp4_gemm(A, w4c[r % ncopy], s4c[r % ncopy], alpha4, Y), 24)
+            byt = 2.0 * m * H + Ngu * H / 2 + Ngu * H / 16 + 2.0 * m * Ngu
+            gbs = byt / (us * 1e-6) / 1e9
+            sweep.append({"op": "nvfp4_gate_up", "N": Ngu, "K": H, "M": m, "us": round(us, 2),
+                          "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+            inv_checked += 1
+            inv_passed += int(torch.equal(Y, ref16[:m]))
+        del w4c, s4c
+        # per-op figures at the step's M
         for name, fn, fl in [
-            ("qkv", lambda: B.bi_gemm(out["Xn"], t["Wqkv"], out["Yqkv"]), flops["qkv"]),
-            ("o_proj", lambda: B.bi_gemm(t["Ao"], t["Wo"], out["Yo"]), flops["o_proj"]),
-            ("gate_up", lambda: B.bi_gemm(out["Xn2"], t["Wgu"], out["Ygu"]), flops["gate_up"]),
-            ("down", lambda: B.bi_gemm(t["Adn"], t["Wdn"], out["Ydn"]), flops["down"]),
-            ("nvfp4_gate_up", lambda: B.bi_nvfp4_gemm(out["Xn2"], t["W4"], t["W4s"], alpha4, out["Y4"]),
+            ("qkv", lambda r: B.bi_gemm(out["Xn"], t["Wqkv"], out["Yqkv"]), flops["qkv"]),
+            ("o_proj", lambda r: B.bi_gemm(t["Ao"], t["Wo"], out["Yo"]), flops["o_proj"]),
+            ("gate_up", lambda r: B.bi_gemm(out["Xn2"], t["Wgu"], out["Ygu"]), flops["gate_up"]),
+            ("down", lambda r: B.bi_gemm(t["Adn"], t["Wdn"], out["Ydn"]), flops["down"]),
+            ("nvfp4_gate_up", lambda r: B.bi_nvfp4_gemm(out["Xn2"], t["W4"], t["W4s"], alpha4, out["Y4"]),
              flops["nvfp4_gate_up"]),
-            ("bmm", lambda: B.bi_bmm(t["Amla"], t["Bmla"], out["Ymla"]), flops["bmm"]),
+            ("bmm", lambda r: B.bi_bmm(t["Amla"], t["Bmla"], out["Ymla"]), flops["bmm"]),
         ]:
-            fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(10):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / 10
+            us = timed(fn, 10)
             tf = fl / (us * 1e-6) / 1e12
             sweep.append({"op": name, "M": M if name != "bmm" else Mb, "us": round(us, 2),
                           "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        us = timed(lambda r: B.bi_rmsnorm(t["X"], t["g1"], eps, out["Xn"]), 20)
+        gbs = (4.0 * M * H + 2.0 * H) / (us * 1e-6) / 1e9
+        sweep.append({"op": "rmsnorm", "M": M, "H": H, "us": round(us, 2), "GB/s": round(gbs, 1),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
         # run-to-run: the step's outputs are identical over repeats
         snap = {k: v.clone() for k, v in out.items()}
         for _ in range(3):
@@ -267,7 +374,7 @@ def main():
             return done
 
         tc = time.perf_counter()
-        f1 = oracle_rows(1)
+        oracle_rows(1)
         dt1 = time.perf_counter() - tc
         r = int(max(1, min(M, args.cpu_seconds / max(dt1, 1e-3))))
         log(f"oracle: 1 row {dt1:.2f}s; timing {r} rows")
