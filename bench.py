@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 CALIB_BYTES = 512 << 20     # bytes read (and written) by one calibration copy
-GATE_UP_KERNEL = "gemm_kernelILi256ELi256ELi4ELi2ELi2ELi2ELi0ELi0E"   # bf16 256x256 tile
+GATE_UP_KERNEL = "gemm_kernel<256, 256, 4, 2, 2, 2, 0, 0>"   # bf16 GEMM, 256x256 tile
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_M2048_counters.txt")
 
 
@@ -59,7 +59,8 @@ def parse():
                    help="run the timed steps only (for profiler passes)")
     p.add_argument("--calib-copy", action="store_true",
                    help="after the steps, copy 512 MiB three times (counter calibration)")
-    p.add_argument("--summarize", metavar="DIR", help="summarise rocprofv3 CSV output in DIR")
+    p.add_argument("--summarize", metavar="DIR", nargs="+",
+                   help="summarise rocprofv3 CSV output in DIR(s)")
     p.add_argument("--out", metavar="FILE", help="where --summarize writes its summary")
     p.add_argument("--command", default="", help="command line recorded by --summarize")
     return p.parse_args()
@@ -100,32 +101,49 @@ def read_counters_summary():
 
 # ------------------------------------------------------------------ summaries
 
-def summarize(d, out, command):
-    """Condense rocprofv3 CSV output (kernel stats or counters) into text."""
-    lines = [f"# rocprofv3 summary written by: python bench.py --summarize {d}",
-             f"# profiled command: {command}" if command else "#",
+def summarize(dirs, out, command):
+    """Condense rocprofv3 CSV output (kernel stats, counters) into text.
+
+    Counters are averaged per dispatch for the bf16 gate_up GEMM and for the
+    calibration copy; each counter of the GEMM is scaled by (true bytes of the
+    copy / what the same counter reads for it).  traffic_bytes_per_launch is
+    the scaled FETCH_SIZE plus the scaled WRITE_SIZE.
+    """
+    lines = [f"# rocprofv3 summary written by: python bench.py --summarize {' '.join(dirs)}",
+             f"# profiled command(s): {command}" if command else "#",
              f"kernel_source_sha: {kernel_source_sha()}"]
-    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    for path in stats:
-        rows = list(csv.DictReader(open(path)))
-        lines.append(f"# kernel stats ({os.path.basename(path)}): name | calls | avg ns | total ns | %")
-        for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
-            lines.append(f"{r['Name'][:150]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
-                         f"{float(r['TotalDurationNs']):.0f} | {float(r.get('Percentage', 0) or 0):.2f}")
-    ctr = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-    for path in ctr:
-        rows = list(csv.DictReader(open(path)))
-        acc = {}
-        for r in rows:
-            name = r["Kernel_Name"]
-            kind = "gate_up" if GATE_UP_KERNEL in name else ("copy" if "copy" in name.lower() else None)
-            if kind is None:
-                continue
-            acc.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
-        lines.append(f"# counters ({os.path.basename(path)}), mean per dispatch")
+    acc = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            rows = list(csv.DictReader(open(path)))
+            lines.append(f"# kernel stats ({os.path.basename(path)}): name | calls | avg ns | total ns | %")
+            for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
+                lines.append(f"{r['Name'][:150]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                             f"{float(r['TotalDurationNs']):.0f} | {float(r.get('Percentage', 0) or 0):.2f}")
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                name = r["Kernel_Name"]
+                kind = ("gate_up" if GATE_UP_KERNEL in name else
+                        "copy" if "direct_copy" in name else None)
+                if kind is not None:
+                    acc.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    if acc:
+        lines.append("# counters, mean per dispatch (KiB)")
         for (kind, cn), v in sorted(acc.items()):
             lines.append(f"{kind}_{cn}_per_dispatch: {sum(v) / len(v):.1f}")
             lines.append(f"{kind}_{cn}_dispatches: {len(v)}")
+        total, parts = 0.0, 0
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            g, c = acc.get(("gate_up", cn)), acc.get(("copy", cn))
+            if g and c:
+                factor = CALIB_BYTES / (sum(c) / len(c) * 1024.0)
+                scaled = sum(g) / len(g) * 1024.0 * factor
+                lines.append(f"copy_{cn}_scale: {factor:.4f}")
+                lines.append(f"gate_up_{cn}_bytes_scaled: {scaled:.0f}")
+                total += scaled
+                parts += 1
+        if parts == 2:
+            lines.append(f"traffic_bytes_per_launch: {total:.0f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -136,7 +154,8 @@ def summarize(d, out, command):
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize, args.out or os.path.join(args.summarize, "summary.txt"), args.command)
+        summarize(args.summarize, args.out or os.path.join(args.summarize[0], "summary.txt"),
+                  args.command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the batch-invariant path here is single-GPU "
@@ -235,8 +254,10 @@ def main():
     log(f"step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; gate_up {gu_ms * 1e3:.1f} us "
         f"{gu_tflops:.1f} TFLOP/s")
     if args.calib_copy:
+        # a plain elementwise copy (bf16 -> fp16 conversion): reads and writes
+        # exactly CALIB_BYTES each, with a kernel of its own name
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
+        dst = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
