@@ -291,7 +291,10 @@ bi_status bi_nvfp4_gemm_ex(const void *A, const void *A_scales, int a_fmt, int64
     a.alpha = alpha;
     a.use_alpha = 1;
     const int am = a_fmt == BI_A_BF16 ? bi::OPND_BF16_ROWS : bi::OPND_NVFP4_ROWS;
-    return run_gemm(am, bi::OPND_NVFP4_ROWS, BI_OP_NVFP4_GEMM, a, stream, opts);
+    // weight bytes by LDS DMA into a raw ring when the scale rows are
+    // dword-aligned (K % 64 == 0); otherwise through registers (same bits)
+    const int bm = (am == bi::OPND_BF16_ROWS && K % 64 == 0) ? bi::OPND_NVFP4_RAW : bi::OPND_NVFP4_ROWS;
+    return run_gemm(am, bm, BI_OP_NVFP4_GEMM, a, stream, opts);
 }
 
 bi_status bi_nvfp4_gemm(const void *A, const void *A_scales, int a_fmt, int64_t lda, const void *W,

@@ -11,7 +11,8 @@ namespace bi {
 enum OperandMode : int {
     OPND_BF16_ROWS = 0,  // bf16 [rows, K], K contiguous (GEMM A and B, BMM A)
     OPND_BF16_KN = 1,    // bf16 [K, cols], cols contiguous (BMM B)
-    OPND_NVFP4_ROWS = 2  // e2m1 codes [rows, K/2] + e4m3 scales [rows, K/16]
+    OPND_NVFP4_ROWS = 2, // e2m1 codes [rows, K/2] + e4m3 scales [rows, K/16], via registers
+    OPND_NVFP4_RAW = 3   // the same bytes, LDS-DMA into a raw ring, decoded in LDS (K % 64 == 0)
 };
 
 // Compiled tile shapes of the GEMM mainloop.  A tile is bm x bn outputs,

@@ -6,6 +6,7 @@ namespace bi {
 hipError_t launch_gemm_bf16(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s);
 hipError_t launch_gemm_kn(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s);
 hipError_t launch_gemm_nvfp4(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s);
+hipError_t launch_gemm_nvfp4raw(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s);
 hipError_t launch_gemm_nvfp4a(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s);
 
 hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmArgs &args,
@@ -16,6 +17,8 @@ hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmAr
         return launch_gemm_kn(r, args, grid, stream);
     if (a_mode == OPND_BF16_ROWS && b_mode == OPND_NVFP4_ROWS)
         return launch_gemm_nvfp4(r, args, grid, stream);
+    if (a_mode == OPND_BF16_ROWS && b_mode == OPND_NVFP4_RAW)
+        return launch_gemm_nvfp4raw(r, args, grid, stream);
     if (a_mode == OPND_NVFP4_ROWS && b_mode == OPND_NVFP4_ROWS)
         return launch_gemm_nvfp4a(r, args, grid, stream);
     return hipErrorInvalidValue;

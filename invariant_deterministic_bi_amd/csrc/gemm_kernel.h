@@ -36,6 +36,8 @@
 
 #include "bi_internal.h"
 
+#include <type_traits>
+
 typedef int bi_i32x4 __attribute__((ext_vector_type(4)));
 
 // LLVM intrinsic: per-lane buffer load of `size` bytes written to LDS at
@@ -118,6 +120,37 @@ __device__ __forceinline__ void decode32(const uint4 &codes, uint32_t sc, uint4 
     }
 }
 
+// The same 32 elements, decoded with a byte-permute table: v_perm_b32 maps
+// each 3-bit magnitude code m to the integer 2*|e2m1(m)| in {0,1,2,3,4,6,8,12};
+// that integer converted to fp32 times scale/2 is the exact magnitude of
+// e2m1(m) * e4m3(s) (scale/2 is exact: the smallest e4m3 is 2^-9), and the
+// code's sign bit is XORed into the fp32 sign.  Bit-identical to decode32 for
+// every code nibble and every finite scale; about five VALU ops per element.
+constexpr uint32_t kE2m1LutLo = 0x03020100u;  // 2*|value| for codes 0..3
+constexpr uint32_t kE2m1LutHi = 0x0C080604u;  // 2*|value| for codes 4..7
+
+__device__ __forceinline__ void decode32_fast(const uint4 &codes, uint32_t sc, uint4 out[4]) {
+    const float h0 = e4m3_value(sc & 0xFFu) * 0.5f, h1 = e4m3_value((sc >> 8) & 0xFFu) * 0.5f;
+    const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float h = j < 2 ? h0 : h1;
+        const uint32_t tl = __builtin_amdgcn_perm(kE2m1LutHi, kE2m1LutLo, cw[j] & 0x07070707u);
+        const uint32_t th = __builtin_amdgcn_perm(kE2m1LutHi, kE2m1LutLo, (cw[j] >> 4) & 0x07070707u);
+        uint32_t o[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            // element 2b: low nibble of byte b (sign bit 8b+3); 2b+1: high nibble (8b+7)
+            const uint32_t ul = __float_as_uint((float)((tl >> (8 * b)) & 0xFFu) * h) ^
+                                ((cw[j] << (28 - 8 * b)) & 0x80000000u);
+            const uint32_t uh = __float_as_uint((float)((th >> (8 * b)) & 0xFFu) * h) ^
+                                ((cw[j] << (24 - 8 * b)) & 0x80000000u);
+            o[b] = __builtin_amdgcn_perm(uh, ul, 0x07060302u);  // {bf16(ul), bf16(uh)}
+        }
+        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Direct (LDS-DMA) operand: bf16 [rows, K], K contiguous.  NWI wavefronts
 // issue its loads; issuing wavefront w fills rows [w*ROWS/NWI, (w+1)*ROWS/NWI)
@@ -170,19 +203,112 @@ struct DirectOperand {
 };
 
 // ---------------------------------------------------------------------------
+// NVFP4 operand through a raw LDS ring: the code bytes ([rows, K/2]) and the
+// scale bytes ([rows, K/16]) of a 64-column K step go from HBM into LDS by
+// DMA -- codes as 16-byte chunks (32 rows per instruction), scales as dwords
+// (64 rows per instruction, issued by the first issuing wavefront only) --
+// and are decoded into the bf16 tile layout by all threads one step before
+// the MFMAs read them.  Needs K % 64 == 0 (dword-aligned scale rows).
+// ---------------------------------------------------------------------------
+template <int ROWS, int NWI>
+struct RawNvfp4Operand {
+    static constexpr int RPW = ROWS / NWI;            // rows per issuing wavefront
+    static constexpr int CODE_INSTR = RPW / 32;       // code instructions per wavefront per stage
+    static constexpr int SCALE_INSTR = ROWS / 64;     // scale instructions (wavefront 0 only)
+    static constexpr int CODES = ROWS * 32;           // code bytes per stage
+    static constexpr int STAGE = ROWS * 36;           // + scale bytes
+    static_assert(RPW % 32 == 0 && ROWS % 64 == 0, "raw NVFP4 ring needs 32 rows per wavefront");
+
+    i32x4 rc, rs;          // code and scale descriptors for the tile's rows
+    int code_off;          // byte offset of this lane's code chunk for instruction 0
+    int scale_off;         // byte offset of this lane's scale dword for instruction 0
+    int rows_left_c, rows_left_s;
+    int code_row_step;     // bytes between code rows 32 apart
+    int scale_row_step;    // bytes between scale rows 64 apart
+
+    __device__ __forceinline__ void setup(const uint8_t *codes, const uint8_t *scales, int rows_valid,
+                                          int K, int w, int lane) {
+        const int cpr = K >> 1, spr = K >> 4;  // code / scale bytes per row
+        rc = make_rsrc(codes, rows_valid > 0 ? (uint32_t)(rows_valid * cpr) : 0u);
+        rs = make_rsrc(scales, rows_valid > 0 ? (uint32_t)(rows_valid * spr) : 0u);
+        const int crow = w * RPW + (lane >> 1);
+        code_off = crow * cpr + (lane & 1) * 16;
+        rows_left_c = rows_valid - crow;
+        scale_off = lane * spr;
+        rows_left_s = rows_valid - lane;
+        code_row_step = 32 * cpr;
+        scale_row_step = 64 * spr;
+    }
+
+    // Loads of K step k0 into the raw stage at `raw`; live == false issues the
+    // same instructions with every lane out of range (zero-filling no-ops).
+    __device__ __forceinline__ void issue(char *raw, int k0, int w, int lane, bool live) const {
+        i32x4 r;
+        r.x = __builtin_amdgcn_readfirstlane(rc.x);
+        r.y = __builtin_amdgcn_readfirstlane(rc.y);
+        r.z = __builtin_amdgcn_readfirstlane(rc.z);
+        r.w = __builtin_amdgcn_readfirstlane(rc.w);
+#pragma unroll
+        for (int j = 0; j < CODE_INSTR; ++j) {
+            const bool ok = live && j * 32 < rows_left_c;
+            const int voff = ok ? code_off + j * code_row_step + (k0 >> 1) : (int)0x80000000;
+            char *dst = raw + (w * RPW + j * 32) * 32;
+            bi_raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t *)dst, 16, voff, 0, 0, 0);
+        }
+        if (w == 0) {
+            i32x4 q;
+            q.x = __builtin_amdgcn_readfirstlane(rs.x);
+            q.y = __builtin_amdgcn_readfirstlane(rs.y);
+            q.z = __builtin_amdgcn_readfirstlane(rs.z);
+            q.w = __builtin_amdgcn_readfirstlane(rs.w);
+#pragma unroll
+            for (int j = 0; j < SCALE_INSTR; ++j) {
+                const bool ok = live && j * 64 < rows_left_s;
+                const int voff = ok ? scale_off + j * scale_row_step + (k0 >> 4) : (int)0x80000000;
+                char *dst = raw + CODES + j * 64 * 4;
+                bi_raw_buffer_load_lds(q, (__attribute__((address_space(3))) uint32_t *)dst, 4, voff, 0, 0, 0);
+            }
+        }
+    }
+
+    // Decode the raw stage into the bf16 tile (all NT threads).
+    template <int NT>
+    __device__ __forceinline__ static void decode(const char *raw, char *tile, int tid) {
+        constexpr int UNITS = ROWS * 2;  // 32 elements each
+        uint4 *dst = reinterpret_cast<uint4 *>(tile);
+#pragma unroll
+        for (int i = 0; i < (UNITS + NT - 1) / NT; ++i) {
+            const int u = tid + i * NT;
+            if (UNITS % NT == 0 || u < UNITS) {
+                const int row = u >> 1, h = u & 1;
+                const uint4 c = *reinterpret_cast<const uint4 *>(raw + row * 32 + h * 16);
+                const uint32_t sc = *reinterpret_cast<const uint16_t *>(raw + CODES + row * 4 + h * 2);
+                uint4 out[4];
+                decode32_fast(c, sc, out);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[row * 8 + swz(row, h * 4 + j)] = out[j];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // Register-staged operands: global -> registers (load), registers -> LDS
 // (store).  NT threads cooperate.
 // ---------------------------------------------------------------------------
 template <int ROWS, int MODE, int NT>
 struct Staged;
 
-// bf16 [rows, K] operands are loaded directly into LDS; nothing is staged.
+// bf16 [rows, K] and raw-ring NVFP4 operands go to LDS by DMA; nothing is
+// staged in registers.
 template <int ROWS, int NT>
 struct Staged<ROWS, OPND_BF16_ROWS, NT> {
     __device__ __forceinline__ void load(const void *, const void *, int64_t, int, int, int, int,
                                          int) {}
     __device__ __forceinline__ void store(char *, int) const {}
 };
+template <int ROWS, int NT>
+struct Staged<ROWS, OPND_NVFP4_RAW, NT> : Staged<ROWS, OPND_BF16_ROWS, NT> {};
 
 // bf16 [K, cols], cols contiguous (the BMM right operand).  Each 16-byte
 // global chunk holds 8 consecutive columns at one k; it is transposed into the
@@ -279,7 +405,7 @@ struct Staged<ROWS, OPND_NVFP4_ROWS, NT> {
 template <int MODE>
 __device__ __forceinline__ int64_t elem_bytes_x2() {
     // twice the bytes per element, so NVFP4 (half a byte) stays integral
-    return MODE == OPND_NVFP4_ROWS ? 1 : 4;
+    return (MODE == OPND_NVFP4_ROWS || MODE == OPND_NVFP4_RAW) ? 1 : 4;
 }
 
 // Wait until at most N vector-memory operations of this wavefront are
@@ -325,10 +451,14 @@ struct Cfg {
     static constexpr int B_RING = SA * A_BYTES;  // B ring follows the A ring
     static constexpr int C_STRIDE = BN * 2 + 16;  // padded bf16 output row in LDS
     static constexpr int C_BYTES = BM * C_STRIDE;
-    static constexpr int PIPE_BYTES = SA * A_BYTES + SB * B_BYTES;
-    static constexpr int LDS_BYTES = PIPE_BYTES > C_BYTES ? PIPE_BYTES : C_BYTES;
     static constexpr bool A_DIRECT = AMODE == OPND_BF16_ROWS;
     static constexpr bool B_DIRECT = BMODE == OPND_BF16_ROWS;
+    static constexpr bool B_RAW = BMODE == OPND_NVFP4_RAW;
+    // B_RAW: a bf16 B double buffer plus a raw ring of SB stages
+    static constexpr int RAW_STAGE = BN * 36;
+    static constexpr int PIPE_BYTES =
+        SA * A_BYTES + (B_RAW ? 2 * B_BYTES + SB * RAW_STAGE : SB * B_BYTES);
+    static constexpr int LDS_BYTES = PIPE_BYTES > C_BYTES ? PIPE_BYTES : C_BYTES;
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 16x16 block");
     static_assert(SA >= 2 && SB >= SA, "ring depths");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of gfx950");
@@ -338,11 +468,13 @@ struct Cfg {
     // wavefront's vmcnt then counts only its own operand's loads, which
     // retire in issue order, so waiting for A(kt) never waits for the deeper
     // B prefetch.  Otherwise every wavefront issues its share of A.
-    static constexpr bool SPLIT = A_DIRECT && B_DIRECT;
+    static constexpr bool SPLIT = A_DIRECT && (B_DIRECT || B_RAW);
     static constexpr int NWA = SPLIT ? NW / 2 : NW;
     static constexpr int NWB = SPLIT ? NW - NW / 2 : NW;
     static constexpr int LA = A_DIRECT ? BM / NWA / 8 : 0;  // instructions per A wavefront per stage
     static constexpr int LB = B_DIRECT ? BN / NWB / 8 : 0;  // per B wavefront per stage
+    static constexpr int LR = B_RAW ? BN / NWB / 32 : 0;    // raw code instructions per B wavefront
+    static constexpr int LR0 = B_RAW ? BN / 64 : 0;         // + raw scale instructions (B wavefront 0)
     // Iteration kt issues A(kt+SA-1) (A wavefronts) and B(kt+SB-1) (B
     // wavefronts), out-of-range steps included (as zero-filling no-ops), so
     // before stage kt is read an A wavefront has issued exactly (SA-2)*LA
@@ -382,25 +514,33 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     // A and B are then prefetched deep enough to stream the weight at the
     // per-CU rate; the K order and every MFMA of the valid rows are unchanged.
     constexpr bool CA = COMPACT && C::A_DIRECT;
+    constexpr bool BDMA = C::B_DIRECT || C::B_RAW;        // B arrives by LDS DMA
     constexpr int A16 = 16 * kRowBytes;
-    constexpr int SBC_RAW = C::B_DIRECT ? C::LDS_BYTES / (A16 + C::B_BYTES) : SB;
-    constexpr int SBC = SBC_RAW > 16 ? 16 : (SBC_RAW < SB ? SB : SBC_RAW);
-    constexpr int SBX = (CA && C::B_DIRECT) ? SBC : SB;   // B ring depth
+    constexpr int FREE = C::B_RAW ? C::LDS_BYTES - 2 * C::B_BYTES : C::LDS_BYTES;
+    constexpr int PER_STAGE = A16 + (C::B_RAW ? C::RAW_STAGE : C::B_BYTES);
+    constexpr int DC_RAW = BDMA ? FREE / PER_STAGE : SB;
+    constexpr int DC = DC_RAW > 16 ? 16 : (DC_RAW < SB ? SB : DC_RAW);
+    constexpr int SBX = (CA && BDMA) ? DC : SB;             // B ring depth (raw ring for B_RAW)
     constexpr int SAX = CA ? SBX : SA;                      // A ring depth
     constexpr int A_ROWS = CA ? 16 : BM;                    // rows per A stage
-    constexpr int B_RING_X = CA ? SAX * A16 : C::B_RING;    // B ring offset
-    static_assert(!CA || SAX * A16 + SBX * C::B_BYTES <= C::LDS_BYTES, "compact rings must fit");
+    // LDS: [A ring][B ring: SBX bf16 stages, or 2 for B_RAW][raw ring: SBX stages]
+    constexpr int B_RING_X = SAX * A_ROWS * kRowBytes;
+    constexpr int RAW_RING_X = B_RING_X + 2 * C::B_BYTES;
+    static_assert(!C::B_RAW || RAW_RING_X + SBX * C::RAW_STAGE <= C::LDS_BYTES, "raw ring must fit");
+    static_assert(!CA || C::B_RAW || B_RING_X + SBX * C::B_BYTES <= C::LDS_BYTES, "compact rings must fit");
+    using RawOp = RawNvfp4Operand<(C::B_RAW ? BN : 64), (C::B_RAW ? C::NWB : 2)>;
     DirectOperand<A_ROWS, CA ? 1 : C::NWA> da;
     DirectOperand<BN, C::NWB> db;
+    RawOp dr;
     Staged<BM, AMODE, NT> sa;
     Staged<BN, BMODE, NT> sb;
     // wave-uniform roles
     const bool a_wave = C::A_DIRECT && (CA ? wave == 0 : (!C::SPLIT || wave < C::NWA));
-    const bool b_wave = C::B_DIRECT && (!C::SPLIT || wave >= C::NWA);
+    const bool b_wave = BDMA && (!C::SPLIT || wave >= C::NWA);
     const int bw = C::SPLIT ? wave - C::NWA : wave;
     constexpr int LAX = CA ? 2 : C::LA;            // A instructions per A wavefront per stage
     constexpr int WAIT_AX = (SAX - 2) * LAX;
-    // set up both descriptors on every wavefront (unconditionally, so the
+    // set up the descriptors on every wavefront (unconditionally, so the
     // compiler keeps them uniform); each wavefront issues only its role's loads
     if constexpr (C::A_DIRECT)
         da.setup(reinterpret_cast<const uint16_t *>(Ab) + (int64_t)m0 * p.lda, min(A_ROWS, p.M - m0),
@@ -408,6 +548,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     if constexpr (C::B_DIRECT)
         db.setup(reinterpret_cast<const uint16_t *>(Bb) + (int64_t)n0 * p.ldb, min(BN, p.N - n0),
                  p.ldb, p.K, C::SPLIT ? bw % C::NWB : bw, lane);
+    if constexpr (C::B_RAW)
+        dr.setup(reinterpret_cast<const uint8_t *>(Bb) + (int64_t)n0 * (p.K >> 1),
+                 static_cast<const uint8_t *>(p.B_scales) + (int64_t)n0 * (p.K >> 4), min(BN, p.N - n0),
+                 p.K, C::SPLIT ? bw % C::NWB : bw, lane);
 
     f32x4 acc[NL > 0 ? NL : 1][FN];
 #pragma unroll
@@ -416,8 +560,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto a_buf = [&](int s) -> char * { return lds + (s % SAX) * (A_ROWS * kRowBytes); };
-    auto b_buf = [&](int s) -> char * { return lds + B_RING_X + (s % SBX) * C::B_BYTES; };
-    // iteration j of the issue schedule (j < 0: prologue; see Cfg::WAIT_A)
+    auto b_buf = [&](int s) -> char * {
+        return lds + B_RING_X + (C::B_RAW ? (s & 1) : (s % SBX)) * C::B_BYTES;
+    };
+    auto raw_buf = [&](int s) -> char * { return lds + RAW_RING_X + (s % SBX) * C::RAW_STAGE; };
+    // iteration j of the issue schedule (j < 0: prologue): A(j+SAX-1),
+    // B(j+SBX-1), raw(j+SBX) -- a raw stage is decoded one iteration before
+    // its MFMAs, so it is fetched one iteration earlier.
     auto issue = [&](int j) {
         if constexpr (C::A_DIRECT) {
             const int s = j + SAX - 1;
@@ -427,31 +576,55 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
             const int s = j + SBX - 1;
             if (b_wave && s >= 0) db.issue(b_buf(s), s * kBK, p.K, bw, lane, s < nk);
         }
+        if constexpr (C::B_RAW) {
+            const int s = j + SBX;
+            if (b_wave && s >= 0) dr.issue(raw_buf(s), s * kBK, bw, lane, s < nk);
+        }
+    };
+    // raw-ring wait of a B wavefront: its loads after raw(s) number exactly
+    // `after` schedule iterations' worth
+    auto wait_raw = [&](auto after_tag) {
+        constexpr int AFTER = decltype(after_tag)::value;
+        if (bw == 0) wait_vmcnt<AFTER * (C::LR + C::LR0)>();
+        else wait_vmcnt<AFTER * C::LR>();
     };
 
-    // prologue: register-staged stage 0, then schedule iterations -(SB-1)..-1
+    // prologue: register-staged stage 0, then schedule iterations up to -1
     if constexpr (!C::A_DIRECT) {
         sa.load(Ab, p.A_scales, p.lda, m0, p.M, 0, p.K, tid);
         sa.store(a_buf(0), tid);
     }
-    if constexpr (!C::B_DIRECT) {
+    if constexpr (!C::B_DIRECT && !C::B_RAW) {
         sb.load(Bb, p.B_scales, p.ldb, n0, p.N, 0, p.K, tid);
         sb.store(b_buf(0), tid);
     }
-    for (int j = -(SBX > SAX ? SBX - 1 : SAX - 1); j < 0; ++j) issue(j);
+    constexpr int LEAD = C::B_RAW ? (SBX > SAX - 1 ? SBX : SAX - 1) : (SBX > SAX ? SBX - 1 : SAX - 1);
+    for (int j = -LEAD; j < 0; ++j) issue(j);
+    if constexpr (C::B_RAW) {
+        // raw(0) was issued in iteration -SBX: SBX-1 iterations follow it
+        if (b_wave) wait_raw(std::integral_constant<int, SBX - 1>{});
+        lds_barrier();
+        RawOp::template decode<NT>(raw_buf(0), b_buf(0), tid);
+    }
 
     for (int kt = 0; kt < nk; ++kt) {
         if constexpr (C::A_DIRECT)
             if (a_wave) wait_vmcnt<WAIT_AX>();
         if constexpr (C::B_DIRECT)
             if (b_wave && !a_wave) wait_vmcnt<(SBX - 2) * C::LB>();
+        if constexpr (C::B_RAW)
+            // raw(kt+1), decoded in this iteration, was issued SBX-2 iterations
+            // before the last one
+            if (b_wave && !a_wave) wait_raw(std::integral_constant<int, SBX - 2>{});
         lds_barrier();
         // register-staged loads for kt+1 first, then this iteration's direct
         // loads, so that waiting on the former never waits on the latter
         const bool more = kt + 1 < nk;
         if constexpr (!C::A_DIRECT) if (more) sa.load(Ab, p.A_scales, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid);
-        if constexpr (!C::B_DIRECT) if (more) sb.load(Bb, p.B_scales, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
+        if constexpr (!C::B_DIRECT && !C::B_RAW) if (more) sb.load(Bb, p.B_scales, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
         issue(kt);
+        if constexpr (C::B_RAW)
+            if (more) RawOp::template decode<NT>(raw_buf(kt + 1), b_buf(kt + 1), tid);
 
         if constexpr (NL > 0) {
             const uint4 *la = reinterpret_cast<const uint4 *>(a_buf(kt));
@@ -506,7 +679,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         }
         if (more) {
             if constexpr (!C::A_DIRECT) sa.store(a_buf(kt + 1), tid);
-            if constexpr (!C::B_DIRECT) sb.store(b_buf(kt + 1), tid);
+            if constexpr (!C::B_DIRECT && !C::B_RAW) sb.store(b_buf(kt + 1), tid);
         }
     }
 
@@ -522,7 +695,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
             for (int i = 0; i < 4; ++i) {
                 const int row = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
                 float v = acc[fm][fn][i];
-                if constexpr (BMODE == OPND_NVFP4_ROWS) v = v * p.alpha;
+                if constexpr (BMODE == OPND_NVFP4_ROWS || BMODE == OPND_NVFP4_RAW) v = v * p.alpha;
                 *reinterpret_cast<uint16_t *>(lds + row * C::C_STRIDE + col * 2) =
                     (uint16_t)f32_to_bf16_rne(v);
             }
@@ -604,9 +777,14 @@ template <int AM, int BMD, int V>
 hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
     constexpr TileShape t = kTileShapes[V];
     // register-staged B (NVFP4 codes, the [K, N] BMM operand) is stored one
-    // step ahead, so its ring needs only as many buffers as A's
-    constexpr int sb = BMD == OPND_BF16_ROWS ? t.sb : t.sa;
-    return launch_one<t.bm, t.bn, t.wgm, t.wgn, t.sa, sb, AM, BMD>(a, grid, s);
+    // step ahead, so its ring needs only as many buffers as A's.  A raw NVFP4
+    // ring needs 32 rows per B wavefront; other shapes take the staged path
+    // (same bits).
+    constexpr int nwb = (AM == OPND_BF16_ROWS) ? t.wgm * t.wgn - t.wgm * t.wgn / 2 : t.wgm * t.wgn;
+    constexpr bool raw_ok = (t.bn / nwb) % 32 == 0 && t.bn % 64 == 0;
+    constexpr int bmd = (BMD == OPND_NVFP4_RAW && !raw_ok) ? OPND_NVFP4_ROWS : BMD;
+    constexpr int sb = (bmd == OPND_BF16_ROWS || bmd == OPND_NVFP4_RAW) ? t.sb : t.sa;
+    return launch_one<t.bm, t.bn, t.wgm, t.wgn, t.sa, sb, AM, bmd>(a, grid, s);
 }
 
 template <int AM, int BMD>
