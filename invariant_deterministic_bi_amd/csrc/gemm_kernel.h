@@ -52,6 +52,7 @@ namespace gemm_detail {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef bi_i32x4 i32x4;
 
 constexpr int kBK = 64;  // K columns per LDS stage (two 32-wide MFMA steps)
@@ -76,18 +77,41 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes)
 // offset (an instruction immediate).  swz(r, .) is an involution.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
+// LDS accesses that overlap in-flight LDS-DMA prefetch.  The compiler cannot
+// tell which LDS bytes an LDS DMA writes, so before any LDS access it can see
+// it waits for every outstanding one (vmcnt(0)), which would drain the whole
+// prefetch ring each K step.  These accesses are written as inline asm, which
+// it does not track; every buffer they touch is ordered by the explicit vmcnt
+// waits and barriers of the mainloop instead, and each read waits for its own
+// result (lgkmcnt) before returning.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p;
+}
+__device__ __forceinline__ uint2 lds_read_b64_u8(const void *p8, const void *pb, uint32_t &byte) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v;
+    asm volatile("ds_read_u8 %1, %3\n\tds_read_b64 %0, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v), "=v"(byte)
+                 : "v"(lds_addr(p8)), "v"(lds_addr(pb))
+                 : "memory");
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void lds_write_b16(void *p, uint32_t v) {  // low half of v
+    asm volatile("ds_write_b16 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write_b16_hi(void *p, uint32_t v) {  // high half of v
+    asm volatile("ds_write_b16_d16_hi %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write_b128(void *p, const uint4 &v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(w) : "memory");
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
-}
-
-// FP4 E2M1 code (sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0)
-// as an fp32 bit pattern.
-__device__ __forceinline__ uint32_t e2m1_bits(uint32_t c) {
-    const uint32_t mag = c & 7u, e = mag >> 1, m = mag & 1u;
-    const uint32_t b = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
-    return b | ((c & 8u) << 28);
 }
 
 // FP8 E4M3 (fn) byte (sign bit 7, exponent bits 6..3 with bias 7, mantissa
@@ -98,57 +122,23 @@ __device__ __forceinline__ float e4m3_value(uint32_t s) {
     return (s & 0x80u) ? -v : v;
 }
 
-// 32 NVFP4 elements (16 code bytes, low nibble first) with their two scales
-// -> four 16-byte chunks of bf16.  e2m1 * e4m3 has at most 6 significant bits
-// and lies in [2^-10, 2688], so the fp32 product is exact and its top half is
-// the exact bf16.
-__device__ __forceinline__ void decode32(const uint4 &codes, uint32_t sc, uint4 out[4]) {
-    const float s0 = e4m3_value(sc & 0xFFu), s1 = e4m3_value((sc >> 8) & 0xFFu);
-    const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float s = j < 2 ? s0 : s1;
-        uint32_t o[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t byte = (cw[j] >> (8 * b)) & 0xFFu;
-            const uint32_t lo = __float_as_uint(__uint_as_float(e2m1_bits(byte & 15u)) * s) >> 16;
-            const uint32_t hi = __float_as_uint(__uint_as_float(e2m1_bits(byte >> 4)) * s) >> 16;
-            o[b] = lo | (hi << 16);
-        }
-        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+// Eight NVFP4 elements (one code dword, element 2j in the low nibble of byte
+// j) sharing one E4M3 scale -> one 16-byte chunk of bf16, using gfx950's
+// FP4 -> fp32 pair convert.  That instruction applies only the power-of-two
+// part of its scale operand, so it is given 1.0 and yields the exact e2m1
+// values; one fp32 multiply by the scale is then exact (e2m1 * e4m3 has at
+// most 6 significant bits and lies in [2^-10, 2688], normal in fp32 and
+// bf16), and the top halves of the products are the exact bf16s -- for every
+// code and every finite scale byte, in two VALU ops per element.
+template <int BYTE>
+__device__ __forceinline__ uint32_t decode_pair(uint32_t cw, float s) {
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, BYTE);
+    return __builtin_amdgcn_perm(__float_as_uint(v.y * s), __float_as_uint(v.x * s), 0x07060302u);
 }
 
-// The same 32 elements, decoded with a byte-permute table: v_perm_b32 maps
-// each 3-bit magnitude code m to the integer 2*|e2m1(m)| in {0,1,2,3,4,6,8,12};
-// that integer converted to fp32 times scale/2 is the exact magnitude of
-// e2m1(m) * e4m3(s) (scale/2 is exact: the smallest e4m3 is 2^-9), and the
-// code's sign bit is XORed into the fp32 sign.  Bit-identical to decode32 for
-// every code nibble and every finite scale; about five VALU ops per element.
-constexpr uint32_t kE2m1LutLo = 0x03020100u;  // 2*|value| for codes 0..3
-constexpr uint32_t kE2m1LutHi = 0x0C080604u;  // 2*|value| for codes 4..7
-
-__device__ __forceinline__ void decode32_fast(const uint4 &codes, uint32_t sc, uint4 out[4]) {
-    const float h0 = e4m3_value(sc & 0xFFu) * 0.5f, h1 = e4m3_value((sc >> 8) & 0xFFu) * 0.5f;
-    const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float h = j < 2 ? h0 : h1;
-        const uint32_t tl = __builtin_amdgcn_perm(kE2m1LutHi, kE2m1LutLo, cw[j] & 0x07070707u);
-        const uint32_t th = __builtin_amdgcn_perm(kE2m1LutHi, kE2m1LutLo, (cw[j] >> 4) & 0x07070707u);
-        uint32_t o[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            // element 2b: low nibble of byte b (sign bit 8b+3); 2b+1: high nibble (8b+7)
-            const uint32_t ul = __float_as_uint((float)((tl >> (8 * b)) & 0xFFu) * h) ^
-                                ((cw[j] << (28 - 8 * b)) & 0x80000000u);
-            const uint32_t uh = __float_as_uint((float)((th >> (8 * b)) & 0xFFu) * h) ^
-                                ((cw[j] << (24 - 8 * b)) & 0x80000000u);
-            o[b] = __builtin_amdgcn_perm(uh, ul, 0x07060302u);  // {bf16(ul), bf16(uh)}
-        }
-        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+__device__ __forceinline__ uint4 decode8(uint32_t cw, float s) {
+    return make_uint4(decode_pair<0>(cw, s), decode_pair<1>(cw, s), decode_pair<2>(cw, s),
+                      decode_pair<3>(cw, s));
 }
 
 // ---------------------------------------------------------------------------
@@ -271,22 +261,22 @@ struct RawNvfp4Operand {
         }
     }
 
-    // Decode the raw stage into the bf16 tile (all NT threads).
+    // Decode the raw stage into the bf16 tile (all NT threads, one 16-element
+    // scale block per thread and pass).
     template <int NT>
     __device__ __forceinline__ static void decode(const char *raw, char *tile, int tid) {
-        constexpr int UNITS = ROWS * 2;  // 32 elements each
+        constexpr int UNITS = ROWS * 4;  // 16 elements each
         uint4 *dst = reinterpret_cast<uint4 *>(tile);
 #pragma unroll
         for (int i = 0; i < (UNITS + NT - 1) / NT; ++i) {
             const int u = tid + i * NT;
             if (UNITS % NT == 0 || u < UNITS) {
-                const int row = u >> 1, h = u & 1;
-                const uint4 c = *reinterpret_cast<const uint4 *>(raw + row * 32 + h * 16);
-                const uint32_t sc = *reinterpret_cast<const uint16_t *>(raw + CODES + row * 4 + h * 2);
-                uint4 out[4];
-                decode32_fast(c, sc, out);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dst[row * 8 + swz(row, h * 4 + j)] = out[j];
+                const int row = u >> 2, q = u & 3;
+                uint32_t sbyte;
+                const uint2 c = lds_read_b64_u8(raw + row * 32 + q * 8, raw + CODES + row * 4 + q, sbyte);
+                const float s = e4m3_value(sbyte);
+                lds_write_b128(dst + row * 8 + swz(row, q * 2), decode8(c.x, s));
+                lds_write_b128(dst + row * 8 + swz(row, q * 2 + 1), decode8(c.y, s));
             }
         }
     }
@@ -347,8 +337,9 @@ struct Staged<ROWS, OPND_BF16_KN, NT> {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int n = n8 * 8 + j;
-                    const uint16_t v = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
-                    l16[(n * 8 + swz(n, kk >> 3)) * 8 + (kk & 7)] = v;
+                    uint16_t *dst = l16 + (n * 8 + swz(n, kk >> 3)) * 8 + (kk & 7);
+                    if (j & 1) lds_write_b16_hi(dst, w[j >> 1]);
+                    else lds_write_b16(dst, w[j >> 1]);
                 }
             }
         }
@@ -393,10 +384,11 @@ struct Staged<ROWS, OPND_NVFP4_ROWS, NT> {
             const int q = tid + i * NT;
             if (TOTAL % NT == 0 || q < TOTAL) {
                 const int row = q >> 1, h = q & 1;
-                uint4 out[4];
-                decode32(r[i], s[i], out);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) lds[row * 8 + swz(row, h * 4 + j)] = out[j];
+                const float s0 = e4m3_value(s[i] & 0xFFu), s1 = e4m3_value((s[i] >> 8) & 0xFFu);
+                lds_write_b128(lds + row * 8 + swz(row, h * 4 + 0), decode8(r[i].x, s0));
+                lds_write_b128(lds + row * 8 + swz(row, h * 4 + 1), decode8(r[i].y, s0));
+                lds_write_b128(lds + row * 8 + swz(row, h * 4 + 2), decode8(r[i].z, s1));
+                lds_write_b128(lds + row * 8 + swz(row, h * 4 + 3), decode8(r[i].w, s1));
             }
         }
     }

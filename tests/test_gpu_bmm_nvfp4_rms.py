@@ -80,14 +80,54 @@ def test_nvfp4_integer_exact_pow2():
     assert np.array_equal(y, rne_bf16_of_exact(ref))
 
 
+def _e2m1_e4m3_table():
+    lut = np.array([oracle.e2m1_value(c) for c in range(16)])
+    sv = np.array([oracle.e4m3_value(c) for c in range(256)])
+    return lut, sv
+
+
+@pytest.mark.parametrize("K,a_nvfp4", [(512, False), (480, False), (512, True)])
+def test_nvfp4_decode_every_code_and_scale(K, a_nvfp4):
+    """An identity A picks out single decoded weights: Y[k, n] = w(n, k)
+    exactly (one nonzero product, exact in bf16).  Every one of the 16 codes
+    appears under each of the 254 finite E4M3 scale bytes (0x7F and 0xFF are
+    NaN).  K = 512 takes the raw-ring weight path, K = 480 (not a multiple of
+    64) the register-staged one; with a_nvfp4 the identity is itself NVFP4
+    (code 2 = 1.0 under scale 0x38 = 1.0), which decodes A as well."""
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    bpr = K // 16
+    N = -(-finite.size // bpr)
+    Ws = np.full(N * bpr, 0x38, np.uint8)
+    Ws[:finite.size] = finite
+    Ws = Ws.reshape(N, bpr)
+    block = np.array([((2 * j + 1) << 4) | (2 * j) for j in range(8)], np.uint8)  # codes 0..15
+    W = np.tile(block, N * bpr).reshape(N, K // 2)
+    lut, sv = _e2m1_e4m3_table()
+    # [K, N]; a zero weight sums to +0 (the fp32 accumulator starts at +0)
+    want = lut[np.arange(K) % 16][:, None] * sv[Ws[:, np.arange(K) // 16]].T + 0.0
+    want_bits = inputs.to_bf16_bits(want)
+    assert np.array_equal(bf16_to_f64(want_bits), want)                          # exact in bf16
+    if a_nvfp4:
+        codes = np.zeros((K, K), np.uint8)
+        codes[np.arange(K), np.arange(K)] = 2
+        Aq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+        As = np.full((K, K // 16), 0x38, np.uint8)
+        note(f"nvfp4 decode table K={K} (NVFP4 identity)")
+        y = host(B.bi_nvfp4_gemm(dev(Aq), dev(W), dev(Ws), 1.0, A_scales=dev(As)))
+    else:
+        A = inputs.to_bf16_bits(np.eye(K))
+        note(f"nvfp4 decode table K={K}")
+        y = host(B.bi_nvfp4_gemm(dev(A), dev(W), dev(Ws), 1.0))
+    assert np.array_equal(y, want_bits)
+
+
 def test_nvfp4_equals_bf16_gemm_on_decoded_weights():
     """alpha == 1: bitwise the bf16 GEMM of the exactly decoded weights."""
     M, N, K = 96, 4096, 4096
     W, Ws, g = _nvfp4_weights(N, K, (123,))
     A = inputs.randn_bf16((M, K), tag=(124,))
     # decode with the oracle's decoders (test side), round (exactly) to bf16
-    lut = np.array([oracle.e2m1_value(c) for c in range(16)])
-    sv = np.array([oracle.e4m3_value(c) if c not in (0x7F, 0xFF) else 0.0 for c in range(256)])
+    lut, sv = _e2m1_e4m3_table()
     q = np.empty((N, K), np.int64)
     q[:, 0::2] = W & 15
     q[:, 1::2] = W >> 4
