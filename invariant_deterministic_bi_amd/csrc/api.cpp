@@ -128,6 +128,26 @@ int default_grid(int tiles, int cus, const bi_launch_opts *opts, int per_cu) {
 
 bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *stream,
                    const bi_launch_opts *opts) {
+    // M <= 16: every valid row fits one 16-row MFMA block; the skinny kernel
+    // streams 16-column blocks of the weight with no barrier.  It runs the
+    // same per-element MFMA chain as the tiled kernel (bits are identical);
+    // a forced tile_variant keeps the tiled kernel so the two can be compared.
+    if (op != BI_OP_BMM && in.M <= 16 && a_mode == bi::OPND_BF16_ROWS &&
+        (b_mode == bi::OPND_BF16_ROWS || b_mode == bi::OPND_NVFP4_RAW) &&
+        !(opts && opts->tile_variant != 0)) {
+        int cus = 0;
+        bi_status st = device_cus(&cus);
+        if (st != BI_OK) return st;
+        // 16-column items unless that leaves fewer than two per compute unit
+        const int nb = (in.N + 15) / 16 >= 2 * static_cast<int64_t>(cus) ? 16 : 8;
+        const int items = static_cast<int>((in.N + nb - 1) / nb);
+        int per_cu = bi::kLdsPerCu / bi::skinny_lds_bytes(b_mode, static_cast<int>(in.M), nb);
+        if (per_cu > 8) per_cu = 8;
+        if (per_cu < 1) per_cu = 1;
+        const int grid = default_grid(items, cus, opts, per_cu);
+        hipError_t e = bi::launch_skinny(b_mode, nb, in, grid, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+    }
     int variant = gemm_variant(op, in.N, in.K);
     if (opts && opts->tile_variant != 0) {
         if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;

@@ -75,6 +75,11 @@ struct GemmArgs {
 // Launchers; they return hipSuccess or the launch error.
 hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmArgs &args,
                        int grid, hipStream_t stream);
+// Skinny path for 1 <= M <= 16, bf16 A, weight OPND_BF16_ROWS or
+// OPND_NVFP4_RAW, batch 1; one 64-thread workgroup per nb-column block
+// (nb = 8 or 16).
+hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &args, int grid, hipStream_t stream);
+int skinny_lds_bytes(int b_mode, int M, int nb);
 
 struct RmsArgs {
     const void *X;

@@ -1,0 +1,284 @@
+// Skinny GEMM path for M <= 16 (bf16 A; bf16 or raw NVFP4 weight): every
+// valid output row fits one 16-row MFMA block, so the weight is the whole
+// traffic.  Each work item is one MFMA block of the output, NB = 16 or 8
+// columns wide (8 when N/16 would leave fewer than two items per compute
+// unit).  One 64-thread workgroup streams the item's weight rows and the A
+// rows through its own small LDS ring (runs of 256 bytes per row per slot,
+// consecutive slots continuing the row) and runs the block's MFMA chain.
+// Workgroups share nothing, so there is no barrier, and about eight fit on a
+// compute unit, which overlaps their LDS, decode and MFMA latencies.
+//
+// Bits: an output element is acc <- MFMA_16x16x32_bf16(a, b, acc) over the
+// 32-wide K chunks in ascending order from +0 -- the same instruction, chunk
+// count (2 * ceil(K / 64), as in the tiled kernel) and operand values as the
+// tiled mainloop -- then (x alpha for NVFP4) one bf16 RNE.  Which wavefront
+// and lane hold the element does not enter, so rows agree bit for bit with
+// the tiled kernel at any M; the invariance tests compare the two.
+
+#include "gemm_kernel.h"
+
+namespace bi {
+namespace skinny {
+
+using namespace gemm_detail;
+
+constexpr int kKC = 128;          // K columns per ring slot (four MFMA chunks)
+constexpr int kRowB = kKC * 2;    // bf16 bytes of one row per slot
+constexpr int kTrash = 1024;      // landing area of out-of-range slot loads
+constexpr int kLdsBudget = 20 * 1024;  // per workgroup: about eight per compute unit
+
+// 256-byte rows (16 chunks): chunk c of row r sits at c ^ f(r), f from row
+// bits 0..3 into chunk bits 2,3 / 0 / 1.  A fragment read (rows 0..15, chunks
+// 4c..4c+3 by lane group) then touches 16 distinct 16-byte bank groups in
+// every 16-lane LDS service set (lanes 8j..8j+7 with 8j+32..8j+39, or 16
+// consecutive lanes).
+__device__ __forceinline__ int swr(int r, int c) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1));
+}
+// 64-byte NVFP4 code rows (4 chunks): 32-bit reads of 16 rows x 4 dwords hit
+// 64 distinct banks.
+__device__ __forceinline__ int swc(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// MA: A rows loaded (4, 8 or 16 >= M); NB: weight rows (output columns) per
+// work item (8 or 16).
+template <int MA, int BMODE, int NB>
+struct SCfg {
+    static constexpr bool RAW = BMODE == OPND_NVFP4_RAW;
+    static constexpr int A_BYTES = MA * kRowB;
+    static constexpr int CODE_BYTES = 16 * (kKC / 2);           // 16 rows reserved
+    static constexpr int SCALE_BYTES = 256;                     // 16 rows x 8 B + landing pad
+    static constexpr int B_BYTES = RAW ? CODE_BYTES + SCALE_BYTES : NB * kRowB;
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int IA = MA / 4;                   // A loads per slot (four rows each)
+    static constexpr int IB = RAW ? 2 : NB / 4;         // B loads per slot
+    static constexpr int T = IA + IB;
+    static constexpr int S_VM = 62 / T + 2;
+    static constexpr int S_LDS = (kLdsBudget - kTrash) / SLOT;
+    static constexpr int S1 = S_VM < S_LDS ? S_VM : S_LDS;
+    static constexpr int S2 = S1 > 16 ? 16 : S1;
+    static constexpr int S = S2 < 3 ? 3 : S2;
+    static constexpr int LDS = S * SLOT + kTrash;
+    static_assert((S - 2) * T < 64, "vmcnt range");
+};
+
+__device__ __forceinline__ i32x4 uniform(const i32x4 &x) {
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(x.x);
+    r.y = __builtin_amdgcn_readfirstlane(x.y);
+    r.z = __builtin_amdgcn_readfirstlane(x.z);
+    r.w = __builtin_amdgcn_readfirstlane(x.w);
+    return r;
+}
+
+__device__ __forceinline__ void dma16(const i32x4 &rs, char *dst, int voff) {
+    bi_raw_buffer_load_lds(uniform(rs), (__attribute__((address_space(3))) uint32_t *)dst, 16, voff,
+                           0, 0, 0);
+}
+__device__ __forceinline__ void dma4(const i32x4 &rs, char *dst, int voff) {
+    bi_raw_buffer_load_lds(uniform(rs), (__attribute__((address_space(3))) uint32_t *)dst, 4, voff,
+                           0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 rd128(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t rd32(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t rd8(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+template <int MA, int BMODE, int NB>
+__global__ __launch_bounds__(64) void skinny_kernel(GemmArgs p) {
+    using C = SCfg<MA, BMODE, NB>;
+    constexpr int S = C::S, T = C::T, SLOT = C::SLOT;
+    constexpr bool RAW = C::RAW;
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+    char *trash = lds + S * SLOT;
+    const int lane = threadIdx.x;
+    const int nk = 2 * ((p.K + kBK - 1) / kBK);  // 32-wide chunks, as in the tiled kernel
+    const int nslots = (nk + 3) / 4;
+    const int items = (p.N + NB - 1) / NB;
+
+    // A rows 0..M-1 (M <= MA), shared by every work item
+    const i32x4 ra = make_rsrc(p.A, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
+    const int q_row = lane >> 4;   // + 4j for load j of a 256-byte-row operand
+    const int q_chunk = lane & 15; // physical chunk this lane fills
+
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int n0 = item * NB;
+        const int rows_b = min(NB, p.N - n0);
+        i32x4 rb, rsc;
+        if constexpr (RAW) {
+            rb = make_rsrc(static_cast<const uint8_t *>(p.B) + (int64_t)n0 * (p.K >> 1),
+                           (uint32_t)(rows_b * (p.K >> 1)));
+            rsc = make_rsrc(static_cast<const uint8_t *>(p.B_scales) + (int64_t)n0 * (p.K >> 4),
+                            (uint32_t)(rows_b * (p.K >> 4)));
+        } else {
+            rb = make_rsrc(static_cast<const uint16_t *>(p.B) + (int64_t)n0 * p.ldb,
+                           (uint32_t)(((int64_t)(rows_b - 1) * p.ldb + p.K) * 2));
+            rsc = rb;
+        }
+
+        // all loads of slot s (out-of-range slots land in the trash area and
+        // keep the per-slot load count exact)
+        auto issue = [&](int s) {
+            const bool live = s < nslots;
+            char *base = lds + (s % S) * SLOT;
+            const int k0 = s * kKC;
+#pragma unroll
+            for (int j = 0; j < C::IA; ++j) {
+                const int r = 4 * j + q_row;
+                const int k = k0 + swr(r, q_chunk) * 8;
+                const bool ok = live && r < p.M && k < p.K;
+                dma16(ra, live ? base + j * 1024 : trash,
+                      ok ? (int)((int64_t)r * p.lda * 2 + k * 2) : (int)0x80000000);
+            }
+            char *bb = base + C::A_BYTES;
+            if constexpr (RAW) {
+                {   // codes: lane -> row lane >> 2, 16-byte chunk lane & 3
+                    const int r = lane >> 2;
+                    const int byte = (k0 >> 1) + swc(r, lane & 3) * 16;
+                    const bool ok = live && r < rows_b && byte < (p.K >> 1);
+                    dma16(rb, live ? bb : trash, ok ? r * (p.K >> 1) + byte : (int)0x80000000);
+                }
+                {   // scales: lanes 0..31 -> row lane >> 1, dword lane & 1
+                    const int r = lane >> 1;
+                    const int sbyte = (k0 >> 4) + (lane & 1) * 4;
+                    const bool ok = live && lane < 32 && r < rows_b && sbyte < (p.K >> 4);
+                    dma4(rsc, live ? bb + C::CODE_BYTES : trash,
+                         ok ? r * (p.K >> 4) + sbyte : (int)0x80000000);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < C::IB; ++j) {
+                    const int r = 4 * j + q_row;
+                    const int k = k0 + swr(r, q_chunk) * 8;
+                    const bool ok = live && r < rows_b && k < p.K;
+                    dma16(rb, live ? bb + j * 1024 : trash,
+                          ok ? (int)((int64_t)r * p.ldb * 2 + k * 2) : (int)0x80000000);
+                }
+            }
+        };
+
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s) issue(s);
+
+        const int r = lane & 15, sub = lane >> 4;
+        const int ar = r < MA ? r : 0;        // A rows past MA are never loaded: reuse row 0
+        const int br = RAW ? r : (r < NB ? r : r - NB);  // weight rows past NB: reuse a loaded row
+        for (int kt = 0; kt < nslots; ++kt) {
+            wait_vmcnt<(S - 2) * T>();
+            const uint32_t sa = lds_addr(lds + (kt % S) * SLOT);
+            const uint32_t sb = sa + C::A_BYTES;
+            u32x4 af[4], bfr[4];
+            uint32_t cw[4], sc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                af[c] = rd128(sa + ar * kRowB + swr(ar, 4 * c + sub) * 16);
+                if constexpr (RAW) {
+                    cw[c] = rd32(sb + r * (kKC / 2) + swc(r, c) * 16 + 4 * sub);
+                    sc[c] = rd8(sb + C::CODE_BYTES + r * (kKC / 16) + 2 * c + (sub >> 1));
+                } else {
+                    bfr[c] = rd128(sb + br * kRowB + swr(br, 4 * c + sub) * 16);
+                }
+            }
+            // the reads are complete before their registers are used and
+            // before this slot's ring position is refilled
+            if constexpr (RAW)
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(cw[0]),
+                               "+v"(cw[1]), "+v"(cw[2]), "+v"(cw[3]), "+v"(sc[0]), "+v"(sc[1]),
+                               "+v"(sc[2]), "+v"(sc[3])::"memory");
+            else
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bfr[0]),
+                               "+v"(bfr[1]), "+v"(bfr[2]), "+v"(bfr[3])::"memory");
+            issue(kt + S - 1);
+            if constexpr (RAW) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint4 d = decode8(cw[c], e4m3_value(sc[c]));
+                    bfr[c] = u32x4{d.x, d.y, d.z, d.w};
+                }
+            }
+            if (kt * 4 + 4 <= nk) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[c]),
+                                                                  __builtin_bit_cast(bf16x8, bfr[c]),
+                                                                  acc, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (kt * 4 + c < nk)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, af[c]), __builtin_bit_cast(bf16x8, bfr[c]),
+                            acc, 0, 0, 0);
+            }
+        }
+
+        // lane holds rows 4*sub .. 4*sub+3 of column n0 + (lane & 15)
+        const int col = n0 + r;
+        if (r < NB && col < p.N) {
+            uint16_t *Y = static_cast<uint16_t *>(p.Y);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * sub + i;
+                float v = acc[i];
+                if constexpr (RAW) v = v * p.alpha;
+                if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+            }
+        }
+    }
+    wait_vmcnt<0>();  // trailing out-of-range loads land before the workgroup ends
+}
+
+template <int MA, int BMODE, int NB>
+hipError_t launch_ma(const GemmArgs &a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((skinny_kernel<MA, BMODE, NB>), dim3(grid), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BMODE, int NB>
+hipError_t launch_mode(const GemmArgs &a, int grid, hipStream_t s) {
+    if (a.M <= 4) return launch_ma<4, BMODE, NB>(a, grid, s);
+    if (a.M <= 8) return launch_ma<8, BMODE, NB>(a, grid, s);
+    return launch_ma<16, BMODE, NB>(a, grid, s);
+}
+
+template <int BMODE, int NB>
+int lds_of(int M) {
+    return M <= 4 ? SCfg<4, BMODE, NB>::LDS : M <= 8 ? SCfg<8, BMODE, NB>::LDS : SCfg<16, BMODE, NB>::LDS;
+}
+
+}  // namespace skinny
+
+int skinny_lds_bytes(int b_mode, int M, int nb) {
+    const bool raw = b_mode == OPND_NVFP4_RAW;
+    if (nb == 8) return raw ? skinny::lds_of<OPND_NVFP4_RAW, 8>(M) : skinny::lds_of<OPND_BF16_ROWS, 8>(M);
+    return raw ? skinny::lds_of<OPND_NVFP4_RAW, 16>(M) : skinny::lds_of<OPND_BF16_ROWS, 16>(M);
+}
+
+hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &a, int grid, hipStream_t s) {
+    if (a.M < 1 || a.M > 16 || (nb != 8 && nb != 16)) return hipErrorInvalidValue;
+    if (b_mode == OPND_BF16_ROWS)
+        return nb == 8 ? skinny::launch_mode<OPND_BF16_ROWS, 8>(a, grid, s)
+                       : skinny::launch_mode<OPND_BF16_ROWS, 16>(a, grid, s);
+    if (b_mode == OPND_NVFP4_RAW)
+        return nb == 8 ? skinny::launch_mode<OPND_NVFP4_RAW, 8>(a, grid, s)
+                       : skinny::launch_mode<OPND_NVFP4_RAW, 16>(a, grid, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bi
