@@ -746,7 +746,12 @@ __global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
         // next instantiated count (wave-uniform)
         const int rows_left = p.M - m0 - wm * WTM;
         const int nlive = rows_left <= 0 ? 0 : min(FM, (rows_left + 15) / 16);
-        if (p.M - m0 <= 16) {
+        // Compact tiles (valid rows all in the first 16) re-lay the LDS for
+        // deep weight prefetch.  The raw-NVFP4 256-column instance skips it:
+        // its deep raw ring does not fit the register file beside the full
+        // path, and M <= 16 calls take the skinny kernel anyway.  Such tiles
+        // run the full path with one live block (same bits).
+        if (p.M - m0 <= 16 && !(BMODE == OPND_NVFP4_RAW && BN >= 256)) {
             // every valid row of the tile is in wavefront row 0's first block
             if (wm == 0)
                 run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1, true>(p, lds, m0, n0, Ab, Bb, Yb);
