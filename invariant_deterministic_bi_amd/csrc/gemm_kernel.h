@@ -622,8 +622,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         if constexpr (!C::A_DIRECT) if (more) sa.load(Ab, p.A_scales, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid);
         if constexpr (!C::B_DIRECT && !C::B_RAW) if (more) sb.load(Bb, p.B_scales, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
         issue(kt);
+        // The next stage's decode: with eight wavefronts the two sharing a
+        // SIMD (w and w+4) take opposite orders -- w decodes before its MFMAs,
+        // w+4 after them -- so one's decode arithmetic runs beside the other's
+        // MFMAs and never holds registers while fragments are live.
+        const bool decode_first = C::NW < 8 || wave < C::NW / 2;
         if constexpr (C::B_RAW)
-            if (more) RawOp::template decode<NT>(raw_buf(kt + 1), b_buf(kt + 1), tid);
+            if (more && decode_first) RawOp::template decode<NT>(raw_buf(kt + 1), b_buf(kt + 1), tid);
 
         if constexpr (NL > 0) {
             const uint4 *la = reinterpret_cast<const uint4 *>(a_buf(kt));
@@ -676,6 +681,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
                 }
             }
         }
+        if constexpr (C::B_RAW)
+            if (more && !decode_first) RawOp::template decode<NT>(raw_buf(kt + 1), b_buf(kt + 1), tid);
         if (more) {
             if constexpr (!C::A_DIRECT) sa.store(a_buf(kt + 1), tid);
             if constexpr (!C::B_DIRECT && !C::B_RAW) sb.store(b_buf(kt + 1), tid);
