@@ -97,8 +97,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ uint2 lds_read_b64_u8(const void *p8, const void *pb, uint32_t &byte) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     u32x2 v;
+    // early-clobber outputs: the first read's result must not share a
+    // register with the second read's address
     asm volatile("ds_read_u8 %1, %3\n\tds_read_b64 %0, %2\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v), "=v"(byte)
+                 : "=&v"(v), "=&v"(byte)
                  : "v"(lds_addr(p8)), "v"(lds_addr(pb))
                  : "memory");
     return make_uint2(v.x, v.y);

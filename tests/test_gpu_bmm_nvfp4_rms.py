@@ -236,4 +236,5 @@ def test_tile_shapes_bmm_and_nvfp4():
     y = host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha))
     for v in range(1, nshapes + 1):
         note(f"nvfp4 tile variant {v}")
-        assert np.array_equal(host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha, tile_variant=v)), y), v
+        for rep in range(3):   # repeated: a timing-dependent LDS race shows as a rare mismatch
+            assert np.array_equal(host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha, tile_variant=v)), y), (v, rep)
