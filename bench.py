@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 CALIB_BYTES = 512 << 20     # bytes read (and written) by one calibration copy
-GATE_UP_KERNEL = "gemm_kernel<256, 256, 4, 2, 2, 2, 0, 0>"   # bf16 GEMM, 256x256 tile
+GATE_UP_KERNEL = "gemm_kernel<256, 256, 4, 2, 2, 3, 0, 0>"   # bf16 GEMM, 256x256 tile
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_M2048_counters.txt")
 
 

@@ -82,8 +82,7 @@ constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offse
 int gemm_variant(int op, int64_t N, int64_t K) {
     (void)K;
     if (op == BI_OP_BMM) return 2;      // 256 x 128, 8 wavefronts
-    if (N >= 16384) return 0;           // 256 x 256, 8 wavefronts
-    if (N >= 5120) return 11;           // 128 x 128, 8 wavefronts
+    if (N >= 5120) return 12;           // 256 x 256, 8 wavefronts, 3-deep B ring
     if (N >= 2048) return 9;            // 256 x 128, 8 wavefronts, 3-deep A ring
     if (N >= 512) return 5;             // 128 x 64
     return 6;                           // 64 x 64

@@ -39,6 +39,7 @@ constexpr TileShape kTileShapes[] = {
     {256, 128, 4, 2, 3, 4},   // 9
     {128, 128, 2, 2, 4, 4},   // 10
     {128, 128, 4, 2, 4, 4},   // 11
+    {256, 256, 4, 2, 2, 3},   // 12
 };
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 

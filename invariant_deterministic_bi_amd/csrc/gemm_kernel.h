@@ -568,15 +568,24 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
     // iteration j of the issue schedule (j < 0: prologue): A(j+SAX-1),
     // B(j+SBX-1), raw(j+SBX) -- a raw stage is decoded one iteration before
     // its MFMAs, so it is fetched one iteration earlier.
-    auto issue = [&](int j) {
-        if constexpr (C::A_DIRECT) {
-            const int s = j + SAX - 1;
-            if (a_wave && s >= 0) da.issue(a_buf(s), s * kBK, p.K, CA ? 0 : wave, lane, s < nk);
-        }
+    // When B wavefronts have a deeper ring than A (full tiles, split
+    // issue), they issue their B loads after their first K step's MFMAs:
+    // the A wavefronts' loads then go to the vector memory unit alone at the
+    // top of the step while the B wavefronts run MFMAs, and the other way
+    // round half a step later, so each SIMD always has one wavefront on MFMAs.
+    constexpr bool LATE_B = !COMPACT && C::SPLIT && C::B_DIRECT && SBX > SAX;
+    auto issue_b = [&](int j) {
         if constexpr (C::B_DIRECT) {
             const int s = j + SBX - 1;
             if (b_wave && s >= 0) db.issue(b_buf(s), s * kBK, p.K, bw, lane, s < nk);
         }
+    };
+    auto issue = [&](int j, bool with_b = true) {
+        if constexpr (C::A_DIRECT) {
+            const int s = j + SAX - 1;
+            if (a_wave && s >= 0) da.issue(a_buf(s), s * kBK, p.K, CA ? 0 : wave, lane, s < nk);
+        }
+        if (with_b) issue_b(j);
         if constexpr (C::B_RAW) {
             const int s = j + SBX;
             if (b_wave && s >= 0) dr.issue(raw_buf(s), s * kBK, bw, lane, s < nk);
@@ -623,7 +632,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
         const bool more = kt + 1 < nk;
         if constexpr (!C::A_DIRECT) if (more) sa.load(Ab, p.A_scales, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid);
         if constexpr (!C::B_DIRECT && !C::B_RAW) if (more) sb.load(Bb, p.B_scales, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
-        issue(kt);
+        issue(kt, !LATE_B);
+        bool b_issued = !LATE_B;
         // The next stage's decode: with eight wavefronts the two sharing a
         // SIMD (w and w+4) take opposite orders -- w decodes before its MFMAs,
         // w+4 after them -- so one's decode arithmetic runs beside the other's
@@ -680,9 +690,17 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
                     __builtin_amdgcn_sched_barrier(0);
                     mfmas(0);
                     __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (LATE_B)
+                        if (ks == 0) {
+                            issue_b(kt);
+                            b_issued = true;
+                        }
                 }
             }
         }
+        // every B wavefront issues exactly one B stage per iteration
+        if constexpr (LATE_B)
+            if (!b_issued) issue_b(kt);
         if constexpr (C::B_RAW)
             if (more && !decode_first) RawOp::template decode<NT>(raw_buf(kt + 1), b_buf(kt + 1), tid);
         if (more) {
@@ -802,7 +820,7 @@ hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
 
 template <int AM, int BMD>
 hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s) {
-    static_assert(kNumTileShapes == 12, "one case per compiled tile shape");
+    static_assert(kNumTileShapes == 13, "one case per compiled tile shape");
     switch (r.variant) {
         case 0: return launch_variant<AM, BMD, 0>(a, grid, s);
         case 1: return launch_variant<AM, BMD, 1>(a, grid, s);
@@ -816,6 +834,7 @@ hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStr
         case 9: return launch_variant<AM, BMD, 9>(a, grid, s);
         case 10: return launch_variant<AM, BMD, 10>(a, grid, s);
         case 11: return launch_variant<AM, BMD, 11>(a, grid, s);
+        case 12: return launch_variant<AM, BMD, 12>(a, grid, s);
         default: return hipErrorInvalidValue;
     }
 }
