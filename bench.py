@@ -104,10 +104,14 @@ def read_counters_summary():
 def summarize(dirs, out, command):
     """Condense rocprofv3 CSV output (kernel stats, counters) into text.
 
-    Counters are averaged per dispatch for the bf16 gate_up GEMM and for the
-    calibration copy; each counter of the GEMM is scaled by (true bytes of the
-    copy / what the same counter reads for it).  traffic_bytes_per_launch is
-    the scaled FETCH_SIZE plus the scaled WRITE_SIZE.
+    The gate_up GEMM shares its kernel instance with other GEMMs of the step
+    (same tile shape), so its dispatches are told apart by grid size: per
+    grid size the kernel trace gives the mean duration and the counters the
+    mean per dispatch, and the gate_up group is the one with the largest
+    FETCH_SIZE (the largest weight).  Each counter of that group is scaled by
+    (true bytes of the calibration copy / what the same counter reads for
+    it); traffic_bytes_per_launch is the scaled FETCH_SIZE plus the scaled
+    WRITE_SIZE.
     """
     lines = [f"# rocprofv3 summary written by: python bench.py --summarize {' '.join(dirs)}",
              f"# profiled command(s): {command}" if command else "#",
@@ -120,24 +124,43 @@ def summarize(dirs, out, command):
             for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
                 lines.append(f"{r['Name'][:150]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                              f"{float(r['TotalDurationNs']):.0f} | {float(r.get('Percentage', 0) or 0):.2f}")
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            groups = {}
+            for r in csv.DictReader(open(path)):
+                if GATE_UP_KERNEL in r["Kernel_Name"]:
+                    g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                    groups.setdefault(g, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            if groups:
+                lines.append(f"# {GATE_UP_KERNEL} by grid size (threads): calls | avg ns")
+                for g, v in sorted(groups.items()):
+                    lines.append(f"grid_{g}_calls_avg_ns: {len(v)} | {sum(v) / len(v):.0f}")
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(path)):
                 name = r["Kernel_Name"]
-                kind = ("gate_up" if GATE_UP_KERNEL in name else
-                        "copy" if "direct_copy" in name else None)
-                if kind is not None:
-                    acc.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                if GATE_UP_KERNEL in name:
+                    key = ("gemm", r["Counter_Name"], int(r["Grid_Size"]))
+                elif "direct_copy" in name:
+                    key = ("copy", r["Counter_Name"], 0)
+                else:
+                    continue
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
     if acc:
+        mean = {k: sum(v) / len(v) for k, v in acc.items()}
+        fetch = {g: m for (kind, cn, g), m in mean.items() if kind == "gemm" and cn == "FETCH_SIZE"}
+        gate_grid = max(fetch, key=fetch.get) if fetch else None
         lines.append("# counters, mean per dispatch (KiB)")
-        for (kind, cn), v in sorted(acc.items()):
-            lines.append(f"{kind}_{cn}_per_dispatch: {sum(v) / len(v):.1f}")
-            lines.append(f"{kind}_{cn}_dispatches: {len(v)}")
+        for (kind, cn, g), m in sorted(mean.items()):
+            tag = f"{kind}_grid{g}" if kind == "gemm" else kind
+            lines.append(f"{tag}_{cn}_per_dispatch: {m:.1f}")
+            lines.append(f"{tag}_{cn}_dispatches: {len(acc[(kind, cn, g)])}")
+        if gate_grid is not None:
+            lines.append(f"gate_up_grid_threads: {gate_grid}")
         total, parts = 0.0, 0
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-            g, c = acc.get(("gate_up", cn)), acc.get(("copy", cn))
-            if g and c:
-                factor = CALIB_BYTES / (sum(c) / len(c) * 1024.0)
-                scaled = sum(g) / len(g) * 1024.0 * factor
+            gm, cm = mean.get(("gemm", cn, gate_grid)), mean.get(("copy", cn, 0))
+            if gm is not None and cm:
+                factor = CALIB_BYTES / (cm * 1024.0)
+                scaled = gm * 1024.0 * factor
                 lines.append(f"copy_{cn}_scale: {factor:.4f}")
                 lines.append(f"gate_up_{cn}_bytes_scaled: {scaled:.0f}")
                 total += scaled
