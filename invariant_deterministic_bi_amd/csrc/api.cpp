@@ -134,6 +134,13 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         int cus = 0;
         bi_status st = device_cus(&cus);
         if (st != BI_OK) return st;
+        if (b_mode == bi::OPND_BF16_ROWS) {
+            // one wavefront per 16-column item, up to 16 per compute unit
+            const int items = static_cast<int>((in.N + 15) / 16);
+            const int grid = default_grid(items, cus, opts, 16);
+            hipError_t e = bi::launch_direct(in, grid, static_cast<hipStream_t>(stream));
+            return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+        }
         // 16-column items unless that leaves fewer than two per compute unit
         const int nb = (in.N + 15) / 16 >= 2 * static_cast<int64_t>(cus) ? 16 : 8;
         const int items = static_cast<int>((in.N + nb - 1) / nb);

@@ -81,6 +81,9 @@ hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmAr
 // (nb = 8 or 16).
 hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &args, int grid, hipStream_t stream);
 int skinny_lds_bytes(int b_mode, int M, int nb);
+// Direct path for 1 <= M <= 16, bf16 A and bf16 weight [N, K], batch 1: one
+// 64-thread workgroup per 16-column item, fragments loaded into registers.
+hipError_t launch_direct(const GemmArgs &args, int grid, hipStream_t stream);
 
 struct RmsArgs {
     const void *X;

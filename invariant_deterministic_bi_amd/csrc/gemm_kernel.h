@@ -46,6 +46,10 @@ __device__ void bi_raw_buffer_load_lds(bi_i32x4 rsrc,
                                        __attribute__((address_space(3))) uint32_t *lds, int size,
                                        int voffset, int soffset, int offset,
                                        int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// LLVM intrinsic: per-lane buffer load of 16 bytes into registers; an offset
+// outside the buffer's range reads zeros.
+__device__ bi_i32x4 bi_raw_buffer_load_b128(bi_i32x4 rsrc, int voffset, int soffset,
+                                            int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 
 namespace bi {
 namespace gemm_detail {

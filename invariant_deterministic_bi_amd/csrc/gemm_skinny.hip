@@ -281,4 +281,155 @@ hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &a, int grid, hipStr
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Direct path for a bf16 weight at M <= 16.  At this size the weight is the
+// whole HBM traffic and each weight byte is used once, so it skips LDS: every
+// lane loads its MFMA fragments straight into registers (16 bytes per lane,
+// one 1 KB instruction per 32-wide K chunk of a 16-column item) through a
+// rolling window of D chunk pairs in flight per wavefront.  One 64-thread
+// workgroup streams items b, b + grid, ...; the window runs on across item
+// boundaries.  A rows are loaded the same way.  For M <= 8 one A instruction
+// covers two chunks (rows 0..7 of chunk c in lanes 0..7 of each 16-lane row,
+// rows 0..7 of chunk c + 1 in lanes 8..15), and a DPP rotation by eight lanes
+// brings the second chunk into place; lanes 8..15 then carry A rows 8..15,
+// which only feed output rows beyond M.
+//
+// The hardware orders nothing here but the loads themselves: they are
+// compiler-visible, so the compiler places each vmcnt wait before the first
+// use of a loaded register.
+//
+// Bits: an output element's chain is the tiled kernel's (same MFMA, 32-K
+// chunks in ascending order from +0, 2 * ceil(K / 64) of them with a zero
+// trailing chunk when K % 64 == 32, one bf16 RNE), so rows are bitwise those
+// of the tiled kernel at any M.
+// ---------------------------------------------------------------------------
+namespace direct {
+
+using namespace gemm_detail;
+
+constexpr int kMark = (int)0x80000000;  // buffer offset that reads zero
+
+__device__ __forceinline__ i32x4 ror8(const i32x4 &v) {  // lane i <- lane i ^ 8 within 16
+    i32x4 o;
+    o.x = __builtin_amdgcn_mov_dpp(v.x, 0x128, 0xF, 0xF, false);
+    o.y = __builtin_amdgcn_mov_dpp(v.y, 0x128, 0xF, 0xF, false);
+    o.z = __builtin_amdgcn_mov_dpp(v.z, 0x128, 0xF, 0xF, false);
+    o.w = __builtin_amdgcn_mov_dpp(v.w, 0x128, 0xF, 0xF, false);
+    return o;
+}
+
+// AP: A packed two chunks per instruction (M <= 8).  D: chunk pairs in flight
+// (a divisor of the pair count ceil(K / 64), chosen by the host).
+template <int AP, int D>
+__global__ __launch_bounds__(64) void direct_kernel(GemmArgs p) {
+    constexpr int AL = AP ? 1 : 2;  // A loads per pair; the weight takes two
+    const int lane = threadIdx.x;
+    const int r = lane & 15, sub = lane >> 4;
+    const int items = (p.N + 15) >> 4;
+    const int np = (p.K + 63) >> 6;  // chunk pairs: 2 * ceil(K / 64) chunks
+    const int my_items = (items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const i32x4 ra = make_rsrc(p.A, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
+    // byte offset of a lane's 16 bytes within pair 0, and its first K column
+    int a_lane[AL], a_kl[AL];
+#pragma unroll
+    for (int j = 0; j < AL; ++j) {
+        const int row = AP ? (r & 7) : r, ch = AP ? (r >> 3) : j;
+        a_lane[j] = row < p.M ? (int)(row * p.lda * 2) + 64 * ch + 16 * sub : kMark;
+        a_kl[j] = 32 * ch + 8 * sub;
+    }
+    const int kfull = p.K >> 6;  // pairs whose 64 columns all lie below K
+
+    int is_item = 0, is_p = 0;   // next pair to load
+    i32x4 rb;
+    int w_lane[2];
+    auto set_item = [&]() {
+        const int n0 = ((int)blockIdx.x + is_item * (int)gridDim.x) * 16;
+        const int rows_b = is_item < my_items ? min(16, p.N - n0) : 0;
+        rb = make_rsrc(static_cast<const uint16_t *>(p.B) + (int64_t)(rows_b > 0 ? n0 : 0) * p.ldb,
+                       rows_b > 0 ? (uint32_t)(((int64_t)(rows_b - 1) * p.ldb + p.K) * 2) : 0u);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            w_lane[j] = r < rows_b ? (int)(r * p.ldb * 2) + 64 * j + 16 * sub : kMark;
+    };
+    set_item();
+    // loads of the next pair (past the last item: zero-reading offsets, no traffic)
+    auto issue = [&](i32x4 *av, i32x4 *wv) {
+        const int koff = is_p * 128;
+        const bool tail = is_p >= kfull;
+#pragma unroll
+        for (int j = 0; j < AL; ++j) {
+            int o = a_lane[j] + koff;
+            if (tail && 64 * is_p + a_kl[j] >= p.K) o = kMark;
+            av[j] = bi_raw_buffer_load_b128(ra, o, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int o = w_lane[j] + koff;
+            if (tail && 64 * is_p + 32 * j + 8 * sub >= p.K) o = kMark;
+            wv[j] = bi_raw_buffer_load_b128(rb, o, 0, 0);
+        }
+        if (++is_p == np) {
+            is_p = 0;
+            ++is_item;
+            set_item();
+        }
+    };
+
+    i32x4 as[D][AL], ws[D][2];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(as[d], ws[d]);
+    uint16_t *Y = static_cast<uint16_t *>(p.Y);
+    for (int t = 0; t < my_items; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int pb = 0; pb < np; pb += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const i32x4 a1 = AP ? ror8(as[d][0]) : as[d][AL - 1];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as[d][0]),
+                                                              __builtin_bit_cast(bf16x8, ws[d][0]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                              __builtin_bit_cast(bf16x8, ws[d][1]), acc, 0, 0, 0);
+                issue(as[d], ws[d]);
+            }
+        }
+        // lane holds rows 4*sub .. 4*sub+3 of column n0 + r
+        const int col = ((int)blockIdx.x + t * (int)gridDim.x) * 16 + r;
+        if (col < p.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * sub + i;
+                if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[i]);
+            }
+        }
+    }
+}
+
+template <int AP>
+hipError_t launch_ap(const GemmArgs &a, int d, int grid, hipStream_t s) {
+    switch (d) {
+        case 16: hipLaunchKernelGGL((direct_kernel<AP, 16>), dim3(grid), dim3(64), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((direct_kernel<AP, 8>), dim3(grid), dim3(64), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((direct_kernel<AP, 4>), dim3(grid), dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((direct_kernel<AP, 2>), dim3(grid), dim3(64), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((direct_kernel<AP, 1>), dim3(grid), dim3(64), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace direct
+
+int direct_depth(int K) {
+    const int np = (K + 63) / 64;
+    int d = K >= 8192 ? 16 : 8;
+    while (np % d) d >>= 1;
+    return d;
+}
+
+hipError_t launch_direct(const GemmArgs &a, int grid, hipStream_t s) {
+    if (a.M < 1 || a.M > 16 || grid < 1) return hipErrorInvalidValue;
+    const int d = direct_depth(a.K);
+    return a.M <= 8 ? direct::launch_ap<1>(a, d, grid, s) : direct::launch_ap<0>(a, d, grid, s);
+}
+
 }  // namespace bi
