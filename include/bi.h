@@ -106,15 +106,21 @@ typedef struct bi_plan {
  * the grid- and tile-override invariance tests check.  They exist for those
  * tests and for tuning sweeps; production calls pass NULL.
  *   max_workgroups: cap on the persistent grid (0 = the library's default,
- *     the device's compute-unit count times the tiles one unit holds).
+ *     the device's compute-unit count times the tiles one unit holds); for
+ *     the GEMMs at M <= 16 (no tile_variant), a cap on the streaming
+ *     wavefronts.
  *   tile_variant: GEMM family only; 0 = the plan's tile shape, v > 0 = the
  *     compiled tile shape v-1 (see bi_tile_shape).  BI_ERR_SHAPE if out of
  *     range.
+ *   pipeline_depth: GEMMs at M <= 16 only; weight load units in flight per
+ *     wavefront (0 = the library's choice; otherwise rounded down to a
+ *     supported power of two that divides the unit count).
  */
 typedef struct bi_launch_opts {
     int32_t max_workgroups;
     int32_t tile_variant;
-    int32_t reserved[6];
+    int32_t pipeline_depth;
+    int32_t reserved[5];
 } bi_launch_opts;
 
 /*

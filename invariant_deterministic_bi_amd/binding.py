@@ -39,7 +39,8 @@ class BiPlan(ctypes.Structure):
 
 
 class BiLaunchOpts(ctypes.Structure):
-    _fields_ = [("max_workgroups", _i32), ("tile_variant", _i32), ("reserved", _i32 * 6)]
+    _fields_ = [("max_workgroups", _i32), ("tile_variant", _i32), ("pipeline_depth", _i32),
+                ("reserved", _i32 * 5)]
 
 
 class BiError(RuntimeError):
@@ -124,12 +125,13 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _opts(max_workgroups=0, tile_variant=0):
-    if not max_workgroups and not tile_variant:
+def _opts(max_workgroups=0, tile_variant=0, pipeline_depth=0):
+    if not max_workgroups and not tile_variant and not pipeline_depth:
         return None
     o = BiLaunchOpts()
     o.max_workgroups = int(max_workgroups)
     o.tile_variant = int(tile_variant)
+    o.pipeline_depth = int(pipeline_depth)
     return ctypes.byref(o)
 
 
@@ -149,7 +151,7 @@ def _raise(st, what):
         raise BiError(st, what)
 
 
-def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
+def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0, pipeline_depth=0):
     """Y[M,N] = A[M,K] . B[N,K]^T (bf16); allocates Y with torch if not given."""
     _check2d(A, "A")
     _check2d(B, "B")
@@ -163,7 +165,7 @@ def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y must be [M, N]")
     st = lib().bi_gemm_ex(_ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(Y), Y.stride(0),
-                          M, N, K, _stream(stream), _opts(max_workgroups, tile_variant))
+                          M, N, K, _stream(stream), _opts(max_workgroups, tile_variant, pipeline_depth))
     _raise(st, "bi_gemm")
     return Y
 
@@ -188,7 +190,7 @@ def bi_bmm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
 
 
 def bi_nvfp4_gemm(A, W, W_scales, alpha, Y=None, *, A_scales=None, K=None, stream=None,
-                  max_workgroups=0, tile_variant=0):
+                  max_workgroups=0, tile_variant=0, pipeline_depth=0):
     """Y[M,N] = alpha * A . W^T with NVFP4 W (codes [N,K/2] uint8, scales [N,K/16] uint8).
 
     A is bf16 [M,K] when A_scales is None, else NVFP4 codes [M,K/2] with
@@ -220,7 +222,7 @@ def bi_nvfp4_gemm(A, W, W_scales, alpha, Y=None, *, A_scales=None, K=None, strea
     _check2d(Y, "Y")
     st = lib().bi_nvfp4_gemm_ex(_ptr(A), _ptr(A_scales), a_fmt, lda, _ptr(W), _ptr(W_scales),
                                 float(alpha), _ptr(Y), Y.stride(0), M, N, K, _stream(stream),
-                                _opts(max_workgroups, tile_variant))
+                                _opts(max_workgroups, tile_variant, pipeline_depth))
     _raise(st, "bi_nvfp4_gemm")
     return Y
 

@@ -134,11 +134,36 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         int cus = 0;
         bi_status st = device_cus(&cus);
         if (st != BI_OK) return st;
+        const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
+        // A in LDS when its copy into every compute unit (M * K * 2 bytes
+        // each) is at most 0.7 times the weight bytes that unit streams; else
+        // A is loaded along with the weight fragments.
+        if (bi::direct_alds_ok(static_cast<int>(in.M), static_cast<int>(in.K), fp4) &&
+            (fp4 || 10 * in.M * static_cast<int64_t>(cus) <= 7 * in.N)) {
+            // A in LDS.  8-column items when 16-column ones would leave fewer
+            // than two per compute unit.  One wavefront per item up to three
+            // per compute unit; beyond that a bf16 weight streams best from one
+            // wavefront per compute unit (fewer concurrent row streams in HBM),
+            // an NVFP4 one from three (its decode needs the SIMDs).
+            const int nb = (!fp4 && (in.N + 15) / 16 < 2 * static_cast<int64_t>(cus)) ? 8 : 16;
+            const int items = static_cast<int>((in.N + nb - 1) / nb);
+            int waves = items <= 3 * cus ? items : fp4 ? 3 * cus : cus;
+            if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
+            const int depth = opts ? opts->pipeline_depth : 0;
+            hipError_t e = bi::launch_direct_alds(in, fp4, nb, waves, cus, depth, static_cast<hipStream_t>(stream));
+            return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+        }
         if (b_mode == bi::OPND_BF16_ROWS) {
             // one wavefront per 16-column item, up to 16 per compute unit
             const int items = static_cast<int>((in.N + 15) / 16);
             const int grid = default_grid(items, cus, opts, 16);
             hipError_t e = bi::launch_direct(in, grid, static_cast<hipStream_t>(stream));
+            return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+        }
+        if (in.K % 128 == 0 && in.M <= 8) {
+            const int items = static_cast<int>((in.N + 15) / 16);
+            const int grid = default_grid(items, cus, opts, 16);
+            hipError_t e = bi::launch_direct_nvfp4(in, grid, static_cast<hipStream_t>(stream));
             return e == hipSuccess ? BI_OK : BI_ERR_HIP;
         }
         // 16-column items unless that leaves fewer than two per compute unit

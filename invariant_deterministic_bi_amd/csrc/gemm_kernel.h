@@ -50,6 +50,9 @@ __device__ void bi_raw_buffer_load_lds(bi_i32x4 rsrc,
 // outside the buffer's range reads zeros.
 __device__ bi_i32x4 bi_raw_buffer_load_b128(bi_i32x4 rsrc, int voffset, int soffset,
                                             int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+typedef int bi_i32x2 __attribute__((ext_vector_type(2)));
+__device__ bi_i32x2 bi_raw_buffer_load_b64(bi_i32x4 rsrc, int voffset, int soffset,
+                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
 
 namespace bi {
 namespace gemm_detail {
@@ -58,6 +61,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef bi_i32x4 i32x4;
+typedef bi_i32x2 i32x2;
 
 constexpr int kBK = 64;  // K columns per LDS stage (two 32-wide MFMA steps)
 constexpr int kRowBytes = kBK * 2;  // one staged operand row: eight 16-byte chunks
@@ -128,11 +132,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 
 // FP8 E4M3 (fn) byte (sign bit 7, exponent bits 6..3 with bias 7, mantissa
-// bits 2..0; exponent 0 is subnormal m/8 * 2^-6) as an fp32 value.
-__device__ __forceinline__ float e4m3_value(uint32_t s) {
-    const uint32_t e = (s >> 3) & 15u, m = s & 7u;
-    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-    return (s & 0x80u) ? -v : v;
+// bits 2..0; exponent 0 is subnormal m/8 * 2^-6; S.1111.111 is NaN) as an
+// fp32 value, by gfx950's FP8 convert, which implements exactly this format
+// (checked against the definition for all 256 bytes).  BYTE selects the byte
+// of the dword.
+template <int BYTE = 0>
+__device__ __forceinline__ float e4m3_value(uint32_t w) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)w, BYTE);
 }
 
 // Eight NVFP4 elements (one code dword, element 2j in the low nibble of byte

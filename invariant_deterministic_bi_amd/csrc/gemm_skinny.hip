@@ -417,6 +417,319 @@ hipError_t launch_ap(const GemmArgs &a, int d, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 weight, the same direct scheme.  The unit is a group of four 32-wide
+// chunks (128 K columns; K % 128 == 0).  Per group a lane loads 16 code bytes
+// (row r, chunk 4q + sub: the instruction covers 16 rows x 64 bytes) and the
+// row's 8 scale bytes.  The lane that holds chunk 4q + j's codes for row r is
+// (r, j), while the MFMA wants code dword s of that chunk in lane (r, s): a
+// 4 x 4 transpose across the four 16-lane rows, done with two 32-lane and two
+// 16-lane swaps.  Each lane then decodes its eight elements into the bf16
+// fragment as in the tiled kernel (FP4 pair convert, exact fp32 scale
+// multiply, top halves), so the MFMA operands are the same bf16 values.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void transpose4(uint32_t &x0, uint32_t &x1, uint32_t &x2, uint32_t &x3) {
+    // rows = 16-lane groups, registers = dwords: x_j row s <- x_s row j
+    auto a = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+    auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    x0 = c[0];
+    x1 = c[1];
+    x2 = d[0];
+    x3 = d[1];
+}
+
+// AP: A packed two chunks per load (M <= 8).  D: groups in flight (a divisor
+// of K / 128, chosen by the host).
+template <int AP, int D>
+__global__ __launch_bounds__(64) void direct_nvfp4_kernel(GemmArgs p) {
+    constexpr int AL = AP ? 2 : 4;  // A loads per group
+    const int lane = threadIdx.x;
+    const int r = lane & 15, sub = lane >> 4;
+    const int items = (p.N + 15) >> 4;
+    const int ng = p.K >> 7;
+    const int cpr = p.K >> 1, spr = p.K >> 4;  // code / scale bytes per weight row
+    const int my_items = (items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const i32x4 ra = make_rsrc(p.A, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
+    int a_lane[AL];
+#pragma unroll
+    for (int j = 0; j < AL; ++j) {
+        const int row = AP ? (r & 7) : r, ch = AP ? 2 * j + (r >> 3) : j;
+        a_lane[j] = row < p.M ? (int)(row * p.lda * 2) + 64 * ch + 16 * sub : kMark;
+    }
+    const int sshift = 8 * (sub >> 1);  // this lane's byte within each scale byte pair
+
+    int is_item = 0, is_g = 0;
+    i32x4 rc, rs;
+    int c_lane = kMark, s_lane = kMark;
+    auto set_item = [&]() {
+        const int n0 = ((int)blockIdx.x + is_item * (int)gridDim.x) * 16;
+        const int rows_b = is_item < my_items ? min(16, p.N - n0) : 0;
+        const int64_t b0 = rows_b > 0 ? n0 : 0;
+        rc = make_rsrc(static_cast<const uint8_t *>(p.B) + b0 * cpr, rows_b > 0 ? (uint32_t)(rows_b * cpr) : 0u);
+        rs = make_rsrc(static_cast<const uint8_t *>(p.B_scales) + b0 * spr,
+                       rows_b > 0 ? (uint32_t)(rows_b * spr) : 0u);
+        c_lane = r < rows_b ? r * cpr + 16 * sub : kMark;
+        s_lane = r < rows_b ? r * spr : kMark;
+    };
+    set_item();
+    auto issue = [&](i32x4 *av, i32x4 &cv, i32x2 &sv) {
+#pragma unroll
+        for (int j = 0; j < AL; ++j) av[j] = bi_raw_buffer_load_b128(ra, a_lane[j] + 256 * is_g, 0, 0);
+        cv = bi_raw_buffer_load_b128(rc, c_lane + 64 * is_g, 0, 0);
+        sv = bi_raw_buffer_load_b64(rs, s_lane + 8 * is_g, 0, 0);
+        if (++is_g == ng) {
+            is_g = 0;
+            ++is_item;
+            set_item();
+        }
+    };
+
+    i32x4 as[D][AL], cs[D];
+    i32x2 ss[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(as[d], cs[d], ss[d]);
+    uint16_t *Y = static_cast<uint16_t *>(p.Y);
+    for (int t = 0; t < my_items; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int gb = 0; gb < ng; gb += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                uint32_t y[4] = {(uint32_t)cs[d].x, (uint32_t)cs[d].y, (uint32_t)cs[d].z, (uint32_t)cs[d].w};
+                transpose4(y[0], y[1], y[2], y[3]);
+                // chunk j's scale: byte 2j + (sub >> 1) of the group's 8 scale bytes
+                const uint32_t s01 = (uint32_t)ss[d].x >> sshift, s23 = (uint32_t)ss[d].y >> sshift;
+                const float sc[4] = {e4m3_value<0>(s01), e4m3_value<2>(s01), e4m3_value<0>(s23),
+                                     e4m3_value<2>(s23)};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 w = decode8(y[j], sc[j]);
+                    const i32x4 wv = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+                    const i32x4 a = AP ? ((j & 1) ? ror8(as[d][j >> 1]) : as[d][j >> 1]) : as[d][j];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                  __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
+                }
+                issue(as[d], cs[d], ss[d]);
+            }
+        }
+        const int col = ((int)blockIdx.x + t * (int)gridDim.x) * 16 + r;
+        if (col < p.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * sub + i;
+                if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[i] * p.alpha);
+            }
+        }
+    }
+}
+
+template <int AP>
+hipError_t launch_nvfp4_ap(const GemmArgs &a, int d, int grid, hipStream_t s) {
+    switch (d) {
+        case 8: hipLaunchKernelGGL((direct_nvfp4_kernel<AP, 8>), dim3(grid), dim3(64), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((direct_nvfp4_kernel<AP, 4>), dim3(grid), dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((direct_nvfp4_kernel<AP, 2>), dim3(grid), dim3(64), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((direct_nvfp4_kernel<AP, 1>), dim3(grid), dim3(64), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Direct path with A in LDS.  The workgroup (1 to 4 wavefronts, each streaming
+// its own items) first copies A rows 0..M-1 into LDS by DMA, overlapping the
+// first weight prefetch, and every chunk's A fragment is then one LDS read:
+// the only global loads in the loop are the weight's (one 1 KB load per bf16
+// chunk; one code and one scale load per four NVFP4 chunks).  Used when the
+// padded A fits kALds bytes.  Row stride: whole 1 KB DMA blocks plus 16 bytes,
+// so the up to 16 rows of a fragment read fall in distinct bank groups.
+// ---------------------------------------------------------------------------
+constexpr int kALds = 144 * 1024;  // one workgroup (up to four wavefronts) per compute unit
+
+__device__ __forceinline__ int a_stride(int K) { return ((K * 2 + 1023) >> 10) * 1024 + 16; }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 rd_a(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return __builtin_bit_cast(i32x4, v);
+}
+template <int N, int U>
+__device__ __forceinline__ void wait_a(i32x4 (&a)[U]) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt field is 4 bits");
+    if constexpr (U == 2)
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a[0]), "+v"(a[1]) : "n"(N) : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(N) : "memory");
+}
+
+// FP4: NVFP4 weight, four-chunk units; else bf16, chunk pairs.  D: units in
+// flight (even; a divisor of the unit count, chosen by the host).
+// NB: output columns per item; 8 (bf16 only) loads a pair as one 8-row x
+// 128-byte instruction: rows 0..7 of chunk c in lanes 0..7 of each 16-lane
+// row, of chunk c + 1 in lanes 8..15, and a DPP rotation by eight lanes gives
+// chunk c + 1 its place; lanes 8..15 then carry columns that are not stored.
+template <bool FP4, int NB, int D>
+__global__ __launch_bounds__(256) void direct_alds_kernel(GemmArgs p) {
+    constexpr int U = FP4 ? 4 : 2;      // chunks per unit
+    constexpr int LPU = NB == 8 ? 1 : 2; // global loads per unit
+    static_assert(NB == 16 || (NB == 8 && !FP4), "8-column items are bf16 only");
+    static_assert(D % 2 == 0, "A fragments alternate between two register sets");
+    __shared__ __attribute__((aligned(1024))) char lds[kALds];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nwv = (int)(blockDim.x >> 6);
+    const int r = lane & 15, sub = lane >> 4;
+    const int items = (p.N + NB - 1) / NB;
+    const int nu = FP4 ? (p.K >> 7) : ((p.K + 63) >> 6);
+    const int slot = (int)blockIdx.x * nwv + w, slots = (int)gridDim.x * nwv;
+    const int my_items = slot < items ? (items - slot + slots - 1) / slots : 0;
+    const int stride = a_stride(p.K);
+
+    // 1. A rows by LDS DMA, 1 KB blocks shared out over the wavefronts
+    {
+        const i32x4 ra = make_rsrc(p.A, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
+        const int bpr = (p.K * 2 + 1023) >> 10;
+        for (int b = w; b < p.M * bpr; b += nwv) {
+            const int row = b / bpr, part = b - row * bpr;
+            const int k = part * 512 + lane * 8;
+            bi_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) uint32_t *)(lds + row * stride + part * 1024),
+                                   16, k < p.K ? (int)(row * p.lda * 2 + k * 2) : kMark, 0, 0, 0);
+        }
+    }
+
+    asm volatile("" ::: "memory");  // the weight loads below stay younger than the A copies
+
+    // 2. weight window (compiler-visible loads)
+    int is_item = 0, is_u = 0;
+    i32x4 rb, rs;
+    int w_lane = kMark, s_lane = kMark;
+    const int cpr = p.K >> 1, spr = p.K >> 4;
+    auto set_item = [&]() {
+        const int n0 = (slot + is_item * slots) * NB;
+        const int rows_b = is_item < my_items ? min(NB, p.N - n0) : 0;
+        const int64_t b0 = rows_b > 0 ? n0 : 0;
+        if constexpr (FP4) {
+            rb = make_rsrc(static_cast<const uint8_t *>(p.B) + b0 * cpr, rows_b > 0 ? (uint32_t)(rows_b * cpr) : 0u);
+            rs = make_rsrc(static_cast<const uint8_t *>(p.B_scales) + b0 * spr,
+                           rows_b > 0 ? (uint32_t)(rows_b * spr) : 0u);
+            w_lane = r < rows_b ? r * cpr + 16 * sub : kMark;
+            s_lane = r < rows_b ? r * spr : kMark;
+        } else {
+            rb = make_rsrc(static_cast<const uint16_t *>(p.B) + b0 * p.ldb,
+                           rows_b > 0 ? (uint32_t)(((int64_t)(rows_b - 1) * p.ldb + p.K) * 2) : 0u);
+            const int row = NB == 8 ? (r & 7) : r;
+            w_lane = row < rows_b ? (int)(row * p.ldb * 2) + (NB == 8 ? 64 * (r >> 3) : 0) + 16 * sub : kMark;
+        }
+    };
+    set_item();
+    const int kfull = p.K >> 6;  // bf16 pairs whose 64 columns all lie below K
+    auto issue = [&](i32x4 &x0, i32x4 &x1) {
+        if constexpr (FP4) {
+            x0 = bi_raw_buffer_load_b128(rb, w_lane + 64 * is_u, 0, 0);
+            const i32x2 s = bi_raw_buffer_load_b64(rs, s_lane + 8 * is_u, 0, 0);
+            x1 = i32x4{s.x, s.y, 0, 0};
+        } else if constexpr (NB == 8) {
+            int o = w_lane + 128 * is_u;
+            if (is_u >= kfull && 64 * is_u + 32 * (r >> 3) + 8 * sub >= p.K) o = kMark;
+            x0 = bi_raw_buffer_load_b128(rb, o, 0, 0);
+        } else {
+            int o0 = w_lane + 128 * is_u, o1 = o0 + 64;
+            if (is_u >= kfull) {
+                if (64 * is_u + 8 * sub >= p.K) o0 = kMark;
+                if (64 * is_u + 32 + 8 * sub >= p.K) o1 = kMark;
+            }
+            x0 = bi_raw_buffer_load_b128(rb, o0, 0, 0);
+            x1 = bi_raw_buffer_load_b128(rb, o1, 0, 0);
+        }
+        if (++is_u == nu) {
+            is_u = 0;
+            ++is_item;
+            set_item();
+        }
+    };
+    i32x4 ws0[D], ws1[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(ws0[d], ws1[d]);
+
+    // 3. this wavefront's A blocks are older than its D * LPU weight loads
+    wait_vmcnt<D * LPU>();
+    lds_barrier();
+
+    // 4. the items; A fragments read one unit ahead
+    const uint32_t a_base = lds_addr(lds) + (uint32_t)(min(r, p.M - 1) * stride) + 16 * sub;
+    i32x4 af[2][U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) af[0][j] = rd_a(a_base + 64 * j);
+    const int sshift = 8 * (sub >> 1);
+    uint16_t *Y = static_cast<uint16_t *>(p.Y);
+    for (int t = 0; t < my_items; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ub = 0; ub < nu; ub += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int un = (ub + d + 1 == nu) ? 0 : ub + d + 1;  // next unit (next item's first)
+#pragma unroll
+                for (int j = 0; j < U; ++j) af[(d + 1) & 1][j] = rd_a(a_base + 64 * (un * U + j));
+                wait_a<U, U>(af[d & 1]);
+                if constexpr (FP4) {
+                    uint32_t y[4] = {(uint32_t)ws0[d].x, (uint32_t)ws0[d].y, (uint32_t)ws0[d].z, (uint32_t)ws0[d].w};
+                    transpose4(y[0], y[1], y[2], y[3]);
+                    const uint32_t s01 = (uint32_t)ws1[d].x >> sshift, s23 = (uint32_t)ws1[d].y >> sshift;
+                    const float sc[4] = {e4m3_value<0>(s01), e4m3_value<2>(s01), e4m3_value<0>(s23),
+                                         e4m3_value<2>(s23)};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 q = decode8(y[j], sc[j]);
+                        const i32x4 wv = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[d & 1][j]),
+                                                                      __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
+                    }
+                } else {
+                    const i32x4 w1 = NB == 8 ? ror8(ws0[d]) : ws1[d];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[d & 1][0]),
+                                                                  __builtin_bit_cast(bf16x8, ws0[d]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[d & 1][1]),
+                                                                  __builtin_bit_cast(bf16x8, w1), acc, 0, 0, 0);
+                }
+                issue(ws0[d], ws1[d]);
+            }
+        }
+        const int col = (slot + t * slots) * NB + r;
+        if (r < NB && col < p.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * sub + i;
+                float v = acc[i];
+                if constexpr (FP4) v = v * p.alpha;
+                if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+template <bool FP4, int NB>
+hipError_t launch_alds(const GemmArgs &a, int d, int grid, int nwv, hipStream_t s) {
+    const dim3 b(64 * nwv);
+    switch (d) {
+        case 32:
+            if constexpr (NB == 8) {
+                hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 32>), dim3(grid), b, 0, s, a);
+                break;
+            }
+            return hipErrorInvalidValue;
+        case 16: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 16>), dim3(grid), b, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 8>), dim3(grid), b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 4>), dim3(grid), b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 2>), dim3(grid), b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace direct
 
 int direct_depth(int K) {
@@ -424,6 +737,44 @@ int direct_depth(int K) {
     int d = K >= 8192 ? 16 : 8;
     while (np % d) d >>= 1;
     return d;
+}
+
+bool direct_alds_fits(int M, int K) {
+    const int stride = ((K * 2 + 1023) / 1024) * 1024 + 16;
+    return (int64_t)M * stride <= direct::kALds;
+}
+
+// A in LDS: units of 2 (bf16) or 4 (NVFP4) chunks; D even, dividing the unit count.
+bool direct_alds_ok(int M, int K, bool fp4) {
+    const int nu = fp4 ? K / 128 : (K + 63) / 64;
+    return M >= 1 && M <= 16 && direct_alds_fits(M, K) && (fp4 ? K % 128 == 0 : true) && nu % 2 == 0;
+}
+
+hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, int nb, int waves, int cus, int depth,
+                              hipStream_t s) {
+    if (waves < 1 || cus < 1 || !direct_alds_ok(a.M, a.K, fp4) || (nb != 8 && nb != 16) || (fp4 && nb != 16))
+        return hipErrorInvalidValue;
+    const int nu = fp4 ? a.K / 128 : (a.K + 63) / 64;
+    const int dmax = nb == 8 ? 32 : 16;
+    int d = depth > 0 ? depth : fp4 ? 8 : (nb == 16 || a.K >= 8192) ? 16 : 8;
+    d = d > dmax ? dmax : d < 2 ? 2 : d;
+    while (d & (d - 1)) d &= d - 1;  // a power of two
+    while (nu % d) d >>= 1;
+    // at most one workgroup per compute unit (the A copy takes most of LDS)
+    int nwv = (waves + cus - 1) / cus;
+    nwv = nwv < 1 ? 1 : nwv > 4 ? 4 : nwv;
+    const int grid = (waves + nwv - 1) / nwv;
+    if (fp4) return direct::launch_alds<true, 16>(a, d, grid, nwv, s);
+    return nb == 8 ? direct::launch_alds<false, 8>(a, d, grid, nwv, s)
+                   : direct::launch_alds<false, 16>(a, d, grid, nwv, s);
+}
+
+hipError_t launch_direct_nvfp4(const GemmArgs &a, int grid, hipStream_t s) {
+    if (a.M < 1 || a.M > 16 || grid < 1 || a.K % 128 != 0) return hipErrorInvalidValue;
+    const int ng = a.K / 128;
+    int d = 8;
+    while (ng % d) d >>= 1;
+    return a.M <= 8 ? direct::launch_nvfp4_ap<1>(a, d, grid, s) : direct::launch_nvfp4_ap<0>(a, d, grid, s);
 }
 
 hipError_t launch_direct(const GemmArgs &a, int grid, hipStream_t s) {
