@@ -157,13 +157,13 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
             // one wavefront per 16-column item, up to 16 per compute unit
             const int items = static_cast<int>((in.N + 15) / 16);
             const int grid = default_grid(items, cus, opts, 16);
-            hipError_t e = bi::launch_direct(in, grid, static_cast<hipStream_t>(stream));
+            hipError_t e = bi::launch_direct(in, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
             return e == hipSuccess ? BI_OK : BI_ERR_HIP;
         }
         if (in.K % 128 == 0 && in.M <= 8) {
             const int items = static_cast<int>((in.N + 15) / 16);
             const int grid = default_grid(items, cus, opts, 16);
-            hipError_t e = bi::launch_direct_nvfp4(in, grid, static_cast<hipStream_t>(stream));
+            hipError_t e = bi::launch_direct_nvfp4(in, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
             return e == hipSuccess ? BI_OK : BI_ERR_HIP;
         }
         // 16-column items unless that leaves fewer than two per compute unit

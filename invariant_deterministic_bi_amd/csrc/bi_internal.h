@@ -83,9 +83,9 @@ hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &args, int grid, hip
 int skinny_lds_bytes(int b_mode, int M, int nb);
 // Direct path for 1 <= M <= 16, bf16 A and bf16 weight [N, K], batch 1: one
 // 64-thread workgroup per 16-column item, fragments loaded into registers.
-hipError_t launch_direct(const GemmArgs &args, int grid, hipStream_t stream);
+hipError_t launch_direct(const GemmArgs &args, int grid, int depth, hipStream_t stream);
 // The same for a raw NVFP4 weight (codes [N, K/2], scales [N, K/16]), K % 128 == 0.
-hipError_t launch_direct_nvfp4(const GemmArgs &args, int grid, hipStream_t stream);
+hipError_t launch_direct_nvfp4(const GemmArgs &args, int grid, int depth, hipStream_t stream);
 // Direct path with A staged in LDS once per workgroup (bf16 or raw NVFP4
 // weight), for shapes with direct_alds_ok; `waves` streaming wavefronts.
 bool direct_alds_ok(int M, int K, bool fp4);

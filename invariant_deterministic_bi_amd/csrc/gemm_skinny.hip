@@ -732,10 +732,12 @@ hipError_t launch_alds(const GemmArgs &a, int d, int grid, int nwv, hipStream_t 
 
 }  // namespace direct
 
-int direct_depth(int K) {
-    const int np = (K + 63) / 64;
-    int d = K >= 8192 ? 16 : 8;
-    while (np % d) d >>= 1;
+// A power of two <= dmax dividing `units`: `depth` if given, else `dflt`.
+static int pick_depth(int units, int depth, int dflt, int dmax) {
+    int d = depth > 0 ? depth : dflt;
+    d = d > dmax ? dmax : d;
+    while (d & (d - 1)) d &= d - 1;
+    while (units % d) d >>= 1;
     return d;
 }
 
@@ -755,11 +757,9 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, int nb, int waves, in
     if (waves < 1 || cus < 1 || !direct_alds_ok(a.M, a.K, fp4) || (nb != 8 && nb != 16) || (fp4 && nb != 16))
         return hipErrorInvalidValue;
     const int nu = fp4 ? a.K / 128 : (a.K + 63) / 64;
-    const int dmax = nb == 8 ? 32 : 16;
-    int d = depth > 0 ? depth : fp4 ? 8 : (nb == 16 || a.K >= 8192) ? 16 : 8;
-    d = d > dmax ? dmax : d < 2 ? 2 : d;
-    while (d & (d - 1)) d &= d - 1;  // a power of two
-    while (nu % d) d >>= 1;
+    const int d = pick_depth(nu, depth == 1 ? 2 : depth, fp4 ? 8 : (nb == 16 || a.K >= 8192) ? 16 : 8,
+                             nb == 8 ? 32 : 16);
+    if (d < 2) return hipErrorInvalidValue;  // the unit count is even (direct_alds_ok)
     // at most one workgroup per compute unit (the A copy takes most of LDS)
     int nwv = (waves + cus - 1) / cus;
     nwv = nwv < 1 ? 1 : nwv > 4 ? 4 : nwv;
@@ -769,17 +769,15 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, int nb, int waves, in
                    : direct::launch_alds<false, 16>(a, d, grid, nwv, s);
 }
 
-hipError_t launch_direct_nvfp4(const GemmArgs &a, int grid, hipStream_t s) {
+hipError_t launch_direct_nvfp4(const GemmArgs &a, int grid, int depth, hipStream_t s) {
     if (a.M < 1 || a.M > 16 || grid < 1 || a.K % 128 != 0) return hipErrorInvalidValue;
-    const int ng = a.K / 128;
-    int d = 8;
-    while (ng % d) d >>= 1;
+    const int d = pick_depth(a.K / 128, depth, 8, 8);
     return a.M <= 8 ? direct::launch_nvfp4_ap<1>(a, d, grid, s) : direct::launch_nvfp4_ap<0>(a, d, grid, s);
 }
 
-hipError_t launch_direct(const GemmArgs &a, int grid, hipStream_t s) {
+hipError_t launch_direct(const GemmArgs &a, int grid, int depth, hipStream_t s) {
     if (a.M < 1 || a.M > 16 || grid < 1) return hipErrorInvalidValue;
-    const int d = direct_depth(a.K);
+    const int d = pick_depth((a.K + 63) / 64, depth, a.K >= 8192 ? 16 : 8, 16);
     return a.M <= 8 ? direct::launch_ap<1>(a, d, grid, s) : direct::launch_ap<0>(a, d, grid, s);
 }
 

@@ -216,13 +216,14 @@ def test_every_tile_shape_gives_the_same_bits():
         gemm(Ad, Wd, tile_variant=len(shapes) + 1)
 
 
-@pytest.mark.parametrize("N,K", [(200, 544), (4100, 4128), (256, 96), (6144, 4096)])
+@pytest.mark.parametrize("N,K", [(200, 544), (4100, 4128), (256, 96), (6144, 4096), (8200, 512)])
 def test_small_m_path_matches_tiled_kernel(N, K):
-    """M <= 16 runs the skinny kernel (16-column work items, one wavefront
-    each).  Its rows must be bitwise the tiled kernel's (forced with
-    tile_variant) and the full-batch rows, for ragged N, K % 64 == 32 (the
-    trailing zero-filled chunk), a strided A and capped grids; and within the
-    oracle tolerance."""
+    """M <= 16 runs the direct kernels (8- or 16-column items streamed into
+    registers; A in LDS or loaded with the weight).  Their rows must be
+    bitwise the tiled kernel's (forced with tile_variant) and the full-batch
+    rows, for ragged N, K % 64 == 32 (the trailing zero-filled chunk), a
+    strided A, capped wavefront counts and every pipeline depth; and within
+    the oracle tolerance."""
     Mmax = 40
     W = inputs.randn_bf16((N, K), 0.02, tag=(951, N, K))
     Wd = dev(W)
@@ -238,15 +239,19 @@ def test_small_m_path_matches_tiled_kernel(N, K):
         assert np.array_equal(ys, yfull[:M]), f"skinny vs full batch, M={M}"
         for mw in (1, 5):
             assert np.array_equal(host(gemm(Ad[:M], Wd, max_workgroups=mw)), ys), (M, mw)
+        for depth in (1, 2, 4, 32):
+            assert np.array_equal(host(gemm(Ad[:M], Wd, pipeline_depth=depth)), ys), (M, depth)
     rows = [0, 4, 15]
     ref, s = oracle.gemm(A[rows], W)
     assert_within_tol(host(gemm(Ad[:16], Wd))[rows], ref, s, f"skinny N={N} K={K}")
 
 
-def test_small_m_nvfp4_path_matches_tiled_kernel():
-    """The NVFP4 weight through the skinny kernel (raw codes and scales,
-    decoded per lane) against the tiled kernel and the full batch."""
-    N, K = 1000, 4160
+@pytest.mark.parametrize("N,K", [(1000, 4160), (1000, 4096), (520, 1024)])
+def test_small_m_nvfp4_path_matches_tiled_kernel(N, K):
+    """The NVFP4 weight at M <= 16 (K % 128 == 0: codes and scales loaded
+    into registers, transposed across lanes and decoded per lane, A in LDS;
+    else the LDS-ring skinny kernel) against the tiled kernel and the full
+    batch, under capped wavefront counts and every pipeline depth."""
     x = inputs.rng(12345, 952).standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
     g = inputs.nvfp4_global_scale(x)
     Wq, Ws = inputs.nvfp4_quantize(x, g)
@@ -255,11 +260,14 @@ def test_small_m_nvfp4_path_matches_tiled_kernel():
     Ad, Wqd, Wsd = dev(A), dev(Wq), dev(Ws)
     note("skinny nvfp4 full")
     yfull = host(B.bi_nvfp4_gemm(Ad, Wqd, Wsd, alpha))
-    for M in (1, 2, 7, 16):
-        note(f"skinny nvfp4 M={M}")
+    for M in (1, 2, 7, 9, 16):
+        note(f"skinny nvfp4 N={N} K={K} M={M}")
         ys = host(B.bi_nvfp4_gemm(Ad[:M], Wqd, Wsd, alpha))
         yt = host(B.bi_nvfp4_gemm(Ad[:M], Wqd, Wsd, alpha, tile_variant=3))
         assert np.array_equal(ys, yt), f"skinny vs tiled, M={M}"
         assert np.array_equal(ys, yfull[:M]), f"skinny vs full batch, M={M}"
+        for mw, depth in ((1, 0), (7, 0), (0, 1), (0, 2), (0, 16)):
+            yo = host(B.bi_nvfp4_gemm(Ad[:M], Wqd, Wsd, alpha, max_workgroups=mw, pipeline_depth=depth))
+            assert np.array_equal(yo, ys), (M, mw, depth)
     ref, s = oracle.nvfp4_gemm(A[:3], None, Wq, Ws, alpha, K)
     assert_within_tol(host(B.bi_nvfp4_gemm(Ad[:3], Wqd, Wsd, alpha)), ref, s, "skinny nvfp4")
