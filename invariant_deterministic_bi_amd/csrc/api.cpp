@@ -82,7 +82,8 @@ constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offse
 int gemm_variant(int op, int64_t N, int64_t K) {
     (void)K;
     if (op == BI_OP_BMM) return 2;      // 256 x 128, 8 wavefronts
-    if (N >= 5120) return 12;           // 256 x 256, 8 wavefronts, 3-deep B ring
+    if (N >= 5120)                      // 256 x 256, 8 wavefronts: ping-pong schedule for the
+        return op == BI_OP_GEMM ? bi::kPingPongVariant : 12;  // bf16 GEMM, else 3-deep B ring
     if (N >= 2048) return 9;            // 256 x 128, 8 wavefronts, 3-deep A ring
     if (N >= 512) return 5;             // 128 x 64
     return 6;                           // 64 x 64
@@ -195,8 +196,11 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
     int per_cu = bi::kLdsPerCu / bi::tile_lds_bytes(t);
     if (per_cu < 1) per_cu = 1;
     const int grid = default_grid(a.num_tiles, cus, opts, per_cu);
-    hipError_t e = bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
-                                   static_cast<hipStream_t>(stream));
+    hipError_t e = (variant == bi::kPingPongVariant && a_mode == bi::OPND_BF16_ROWS &&
+                    b_mode == bi::OPND_BF16_ROWS && a.batch == 1)
+                       ? bi::launch_pingpong(a, grid, static_cast<hipStream_t>(stream))
+                       : bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
+                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 

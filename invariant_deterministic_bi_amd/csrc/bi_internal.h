@@ -40,7 +40,9 @@ constexpr TileShape kTileShapes[] = {
     {128, 128, 2, 2, 4, 4},   // 10
     {128, 128, 4, 2, 4, 4},   // 11
     {256, 256, 4, 2, 2, 3},   // 12
+    {256, 256, 2, 4, 2, 3},   // 13: ping-pong schedule (bf16 x bf16, batch 1; else as 12)
 };
+constexpr int kPingPongVariant = 13;
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 
 // LDS bytes of one workgroup: the two rings, or the padded bf16 output tile
@@ -81,6 +83,8 @@ hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmAr
 // (nb = 8 or 16).
 hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &args, int grid, hipStream_t stream);
 int skinny_lds_bytes(int b_mode, int M, int nb);
+// 256 x 256 tiles, eight wavefronts in a ping-pong schedule; bf16 x bf16, batch 1.
+hipError_t launch_pingpong(const GemmArgs &args, int grid, hipStream_t stream);
 // Direct path for 1 <= M <= 16, bf16 A and bf16 weight [N, K], batch 1: one
 // 64-thread workgroup per 16-column item, fragments loaded into registers.
 hipError_t launch_direct(const GemmArgs &args, int grid, int depth, hipStream_t stream);

@@ -830,7 +830,7 @@ hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
 
 template <int AM, int BMD>
 hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s) {
-    static_assert(kNumTileShapes == 13, "one case per compiled tile shape");
+    static_assert(kNumTileShapes == 14, "one case per compiled tile shape");
     switch (r.variant) {
         case 0: return launch_variant<AM, BMD, 0>(a, grid, s);
         case 1: return launch_variant<AM, BMD, 1>(a, grid, s);
@@ -845,6 +845,7 @@ hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStr
         case 10: return launch_variant<AM, BMD, 10>(a, grid, s);
         case 11: return launch_variant<AM, BMD, 11>(a, grid, s);
         case 12: return launch_variant<AM, BMD, 12>(a, grid, s);
+        case kPingPongVariant: return launch_variant<AM, BMD, 12>(a, grid, s);  // same shape, classic schedule
         default: return hipErrorInvalidValue;
     }
 }
