@@ -48,6 +48,8 @@ def _load():
     lib.oracle_nvfp4_gemm.restype = None
     lib.oracle_rmsnorm.argtypes = [_p, _i64, _p, ctypes.c_float, _i64, _i64, _p, _i64, _p]
     lib.oracle_rmsnorm.restype = None
+    lib.oracle_nvfp4_quant.argtypes = [_p, _i64, ctypes.c_float, _i64, _i64, _i64, _p, _p]
+    lib.oracle_nvfp4_quant.restype = None
     for name in ("oracle_e2m1_value", "oracle_e4m3_value", "oracle_bf16_value"):
         getattr(lib, name).argtypes = [ctypes.c_uint32]
         getattr(lib, name).restype = ctypes.c_double
@@ -182,3 +184,25 @@ def rmsnorm(X, gamma, eps, rows=None):
         _load().oracle_rmsnorm(_ptr(X), H, _ptr(gamma), float(np.float32(eps)), M, H,
                                _ptr(rows), nr, _ptr(Y))
     return Y
+
+
+def nvfp4_quant(X, global_scale):
+    """Row-local NVFP4 quantisation of bf16 activations X [M, K] (K % 16 == 0).
+
+    The quantiser named in the unit test of the vLLM PR #39912 summary page
+    (section "key source snippets"), in the fp32 reading spelled out in
+    oracle.c: per 16-element block, scale = nearest E4M3 to
+    min(fp32(fp32(amax * g) / 6), 448); codes = nearest E2M1 to
+    fp32(|x| * fp32(g / scale)), ties to even codes.  global_scale is rounded
+    to fp32 first, as the library receives it.  Returns (codes uint8
+    [M, K/2], scales uint8 [M, K/16]).
+    """
+    X = np.ascontiguousarray(_u16(X))
+    M, K = X.shape
+    assert K % 16 == 0
+    Q = np.zeros((M, K // 2), np.uint8)
+    S = np.zeros((M, K // 16), np.uint8)
+    if M and K:
+        _load().oracle_nvfp4_quant(_ptr(X), K, float(np.float32(global_scale)), M, K, K,
+                                   _ptr(Q), _ptr(S))
+    return Q, S

@@ -193,5 +193,79 @@ void oracle_rmsnorm(const uint16_t *X, int64_t ldx, const uint16_t *gamma, float
     }
 }
 
+/*
+ * NVFP4 quantiser of activations, row-local: the operation named
+ * scaled_fp4_quant(x, global_scale) -> (fp4 codes, block scales) in the vLLM
+ * PR #39912 unit test (summary page, section "key source snippets").  The
+ * pages name it without defining it; the reading used, step by step for
+ * each block of 16 consecutive elements of a row:
+ *   1. amax = the largest |x| of the block (bf16 values, exact);
+ *   2. v = (amax * g) / 6 with each operation rounded to fp32 (round to
+ *      nearest even), then min(v, 448): the block's largest magnitude is to
+ *      land on the largest E2M1 magnitude, 6, and 448 is the largest finite
+ *      E4M3 value;
+ *   3. the scale code is the E4M3 code whose value is nearest to v, ties to
+ *      the even code;
+ *   4. s = that code's value; when s == 0 every code of the block is 0;
+ *      otherwise r = g / s rounded to fp32, and for each element
+ *      w = |x| * r rounded to fp32;
+ *   5. the element code is the E2M1 magnitude code nearest to w, ties to the
+ *      even code, values beyond 6 giving 6; the sign bit is set for a
+ *      negative x whose magnitude code is not 0.
+ * The fp32 steps decide integers (the codes), so they are taken in the same
+ * precision as the GPU kernel takes them; the nearest-code searches are
+ * plain scans over every code.  Each row depends only on itself and g.
+ * Codes are packed two per byte, element 2j in the low nibble of byte j.
+ * Q: codes [M, K/2] with row stride ldq/2 bytes; S: scales [M, K/16] with
+ * row stride ldq/16 bytes; X: bf16 [M, K] with row stride ldx.
+ */
+static unsigned nearest_code(double v, double (*dec)(unsigned), unsigned ncodes) {
+    unsigned best = 0;
+    double bd = fabs(dec(0) - v);
+    for (unsigned c = 1; c < ncodes; c++) {
+        double d = fabs(dec(c) - v);
+        if (d < bd || (d == bd && (c & 1u) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return best;
+}
+
+void oracle_nvfp4_quant(const uint16_t *X, int64_t ldx, float g, int64_t M, int64_t K,
+                        int64_t ldq, uint8_t *Q, uint8_t *S) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; i++) {
+        const uint16_t *x = X + i * ldx;
+        uint8_t *q = Q + i * (ldq / 2), *sc = S + i * (ldq / 16);
+        for (int64_t b = 0; b < K / 16; b++) {
+            float amax = 0.0f;
+            for (int j = 0; j < 16; j++) {
+                float a = (float)fabs(bf16_value(x[16 * b + j]));
+                if (a > amax) amax = a;
+            }
+            float u = amax * g;
+            float v = u / 6.0f;
+            if (v > 448.0f) v = 448.0f;
+            unsigned scode = nearest_code((double)v, e4m3_value, 127);
+            float s = (float)e4m3_value(scode);
+            float r = (s != 0.0f) ? g / s : 0.0f;
+            unsigned codes[16];
+            for (int j = 0; j < 16; j++) {
+                double xv = bf16_value(x[16 * b + j]);
+                unsigned c = 0;
+                if (s != 0.0f) {
+                    float w = (float)fabs(xv) * r;
+                    c = nearest_code((double)w, e2m1_value, 8);
+                    if (c != 0 && signbit(xv)) c |= 8u;
+                }
+                codes[j] = c;
+            }
+            for (int j = 0; j < 8; j++) q[8 * b + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+            sc[b] = (uint8_t)scode;
+        }
+    }
+}
+
 /* Number of OpenMP threads the oracle will use (for reporting). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }

@@ -342,3 +342,170 @@ def test_quantiser_row_local_and_error_bound():
     # each element within half an e2m1 step of its block scale (plus scale rounding)
     blk_amax = np.repeat(np.abs(x).reshape(8, 4, 16).max(axis=2), 16, axis=1)
     assert np.all(np.abs(dec - x) <= blk_amax * 0.25 + 1e-12)
+
+
+# ---------------------------------------------------------------- NVFP4 quantiser (activations)
+#
+# oracle.nvfp4_quant is the row-local quantiser of the W4A4 path (the
+# scaled_fp4_quant step of the vLLM PR #39912 unit test, summary page,
+# section "key source snippets"), in the fp32 reading stated in oracle.c.
+# Pins: hand-worked examples, torch's own float8_e4m3fn rounding for the
+# scale, exact rational nearest-value search for both codes away from
+# decision midpoints, decode-then-requantise round trips, power-of-two
+# scaling and row independence.
+
+def _quant_examples():
+    out = {}
+    with open(os.path.join(GOLDEN, "nvfp4_quant_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, rest = [p.strip() for p in line.split(":", 1)]
+            lhs, rhs = [p.strip() for p in rest.split("=>")]
+            args = dict(tok.split("=", 1) for tok in lhs.split())
+            want = dict(tok.split("=", 1) for tok in rhs.split())
+            x = [float(v) for v in args["x"].split(",")]
+            codes = np.array([int(b, 16) for b in want["codes"].split(",")], np.uint8)
+            scales = np.array([int(b, 16) for b in want["scales"].split(",")], np.uint8)
+            out[name] = (float(args["g"]), x, codes, scales)
+    return out
+
+
+QUANT_EXAMPLES = _quant_examples()
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_EXAMPLES))
+def test_nvfp4_quant_worked_examples(name):
+    g, x, codes, scales = QUANT_EXAMPLES[name]
+    xb = bits([x])
+    assert np.array_equal(inputs.bf16_bits_to_f32(xb)[0], np.float32(x)), "example not exact in bf16"
+    q, s = oracle.nvfp4_quant(xb, g)
+    assert q[0].tolist() == codes.tolist(), (name, [hex(v) for v in q[0]])
+    assert s[0].tolist() == scales.tolist(), (name, [hex(v) for v in s[0]])
+
+
+def _e4m3_table():
+    return torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _e2m1_table():
+    return [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _nearest_exact(v, table):
+    """(code, distance to the nearest decision midpoint) for a Fraction v >= 0,
+    by exact scan: nearest table entry, ties to the even code."""
+    best, bd = 0, abs(Fraction(table[0]) - v)
+    for c in range(1, len(table)):
+        d = abs(Fraction(table[c]) - v)
+        if d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    mids = [(Fraction(table[c]) + Fraction(table[c + 1])) / 2 for c in range(len(table) - 1)]
+    return best, min(abs(v - m) for m in mids)
+
+
+def test_nvfp4_quant_scale_matches_torch_float8_rounding():
+    """The scale byte equals torch's own fp32 -> float8_e4m3fn conversion
+    (round to nearest even) of min(fp32(fp32(amax*g)/6), 448)."""
+    x = inputs.randn_bf16((64, 256), 1.0, tag=(31,))
+    xf = inputs.bf16_bits_to_f32(x)
+    for g in (np.float32(448 * 6 / np.abs(xf).max()), np.float32(1.0), np.float32(3.0e-3),
+              np.float32(0.37)):
+        q, s = oracle.nvfp4_quant(x, g)
+        amax = np.abs(xf).reshape(64, 16, 16).max(axis=2).astype(np.float32)
+        v = np.minimum((amax * g).astype(np.float32) / np.float32(6.0), np.float32(448.0)).astype(np.float32)
+        ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(s, ref), float(g)
+
+
+def test_nvfp4_quant_exact_rational_away_from_midpoints():
+    """Against exact arithmetic: the scale code is the E4M3 code nearest to
+    amax*g/6 and each element code the E2M1 code nearest to |x|*g/s, wherever
+    the exact value is not within 2^-20 (relative) of a decision midpoint, where
+    the fp32 roundings of the reading may legitimately move it."""
+    e4 = _e4m3_table()
+    e2 = _e2m1_table()
+    x = inputs.randn_bf16((12, 64), 1.0, tag=(32,))
+    xf = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    checked = skipped = 0
+    for g in (np.float32(448 * 6 / np.abs(xf).max()), np.float32(0.8), np.float32(2.0e-3)):
+        q, s = oracle.nvfp4_quant(x, g)
+        G = Fraction(float(g))
+        for i in range(x.shape[0]):
+            for b in range(x.shape[1] // 16):
+                blk = [Fraction(float(v)) for v in xf[i, 16 * b:16 * b + 16]]
+                amax = max(abs(v) for v in blk)
+                vstar = min(amax * G / 6, Fraction(448))
+                code, dist = _nearest_exact(vstar, e4)
+                if vstar > 0 and dist <= vstar * Fraction(1, 1 << 20):
+                    skipped += 1
+                    continue
+                assert s[i, b] == code, (float(g), i, b, float(vstar), s[i, b], code)
+                checked += 1
+                sv = Fraction(float(e4[code]))
+                for j, xv in enumerate(blk):
+                    k = 16 * b + j
+                    got = (q[i, k // 2] >> (4 * (k % 2))) & 15
+                    if sv == 0:
+                        assert got == 0
+                        continue
+                    w = abs(xv) * G / sv
+                    c, d = _nearest_exact(w, e2)
+                    if w > 0 and d <= w * Fraction(1, 1 << 20):
+                        skipped += 1
+                        continue
+                    want = c | (8 if (xv < 0 and c != 0) else 0)
+                    assert got == want, (float(g), i, k, float(w), got, want)
+                    checked += 1
+    assert checked > 1000 and skipped < checked // 100
+
+
+@pytest.mark.parametrize("g_exp", [-3, 0, 5])
+def test_nvfp4_quant_round_trip(g_exp):
+    """Decode then requantise: a block whose values are e2m1(q) * e4m3(c) / g,
+    with one element of magnitude 6 * e4m3(c) / g, quantises back to exactly
+    the codes q and the scale c (g a power of two keeps everything exact).
+    Code 8 (-0) comes back as 0."""
+    r = inputs.rng(12345, 33 + g_exp)
+    g = 2.0 ** g_exp
+    e2 = _e2m1_table()
+    e4 = _e4m3_table()
+    R, K = 40, 64
+    qs = r.integers(0, 16, size=(R, K))
+    qs[:, ::16] = np.where(r.integers(0, 2, size=(R, K // 16)), 7, 15)  # |code| 6 in every block
+    cs = r.integers(1, 127, size=(R, K // 16))
+    cs[0, :] = [1, 8, 56, 126]  # smallest subnormal, smallest normal, 1.0, 448
+    vals = np.empty((R, K))
+    for i in range(R):
+        for k in range(K):
+            mag = e2[qs[i, k] & 7] * e4[cs[i, k // 16]] / g
+            vals[i, k] = -mag if qs[i, k] & 8 else mag
+    xb = bits(vals)
+    assert np.array_equal(inputs.bf16_bits_to_f32(xb).astype(np.float64), vals)
+    q, s = oracle.nvfp4_quant(xb, g)
+    assert np.array_equal(s, cs.astype(np.uint8))
+    want = np.where(qs == 8, 0, qs)
+    assert np.array_equal(q & 15, want[:, 0::2]) and np.array_equal(q >> 4, want[:, 1::2])
+
+
+def test_nvfp4_quant_pow2_scaling_rows_and_zero():
+    x = inputs.randn_bf16((9, 128), 1.0, tag=(34,))
+    xf = inputs.bf16_bits_to_f32(x)
+    g = np.float32(448 * 6 / np.abs(xf).max())
+    q, s = oracle.nvfp4_quant(x, g)
+    # x * 2^p with g * 2^-p: every fp32 step is scaled exactly, codes unchanged
+    for p in (-4, 3):
+        q2, s2 = oracle.nvfp4_quant(bits(xf.astype(np.float64) * 2.0 ** p), g * np.float32(2.0 ** -p))
+        assert np.array_equal(q, q2) and np.array_equal(s, s2), p
+    # each row alone, and the rows reversed
+    for i in range(9):
+        qi, si = oracle.nvfp4_quant(x[i:i + 1], g)
+        assert np.array_equal(qi[0], q[i]) and np.array_equal(si[0], s[i])
+    qr, sr = oracle.nvfp4_quant(x[::-1].copy(), g)
+    assert np.array_equal(qr, q[::-1]) and np.array_equal(sr, s[::-1])
+    # a zero row gives zero bytes; negative zero gives code 0, not 8
+    z = np.zeros((1, 32), np.uint16)
+    z[0, 5] = 0x8000
+    qz, sz = oracle.nvfp4_quant(z, 3.0)
+    assert not qz.any() and not sz.any()
