@@ -369,6 +369,25 @@ def main():
             inv_checked += 1
             inv_passed += int(torch.equal(Y, ref16[:m]))
         del w4c, s4c
+        # NVFP4 activation quantiser at the step's M (K = 4096), and the W4A4
+        # GEMM it feeds (gate_up weight)
+        ga = inputs.nvfp4_global_scale(inputs.bf16_bits_to_f32(host["X2"]))
+        Aq, Aqs = B.bi_nvfp4_quant(t["X2"], ga)
+        us = timed(lambda r: B.bi_nvfp4_quant(t["X2"], ga, Aq, Aqs), 20)
+        byt = 2.0 * M * H + M * H / 2 + M * H / 16
+        gbs = byt / (us * 1e-6) / 1e9
+        sweep.append({"op": "nvfp4_quant", "M": M, "K": H, "us": round(us, 2), "GB/s": round(gbs, 1),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        q16, s16 = B.bi_nvfp4_quant(t["X2"][:16], ga)
+        inv_checked += 1
+        inv_passed += int(torch.equal(q16, Aq[:16]) and torch.equal(s16, Aqs[:16]))
+        alpha44 = float(np.float32(1.0) / (ga * g4))
+        Y44 = torch.empty((M, Ngu), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda r: B.bi_nvfp4_gemm(Aq, t["W4"], t["W4s"], alpha44, Y44, A_scales=Aqs), 10)
+        tf = flops["nvfp4_gate_up"] / (us * 1e-6) / 1e12
+        sweep.append({"op": "nvfp4_w4a4_gate_up", "M": M, "us": round(us, 2), "TFLOP/s": round(tf, 1),
+                      "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del Aq, Aqs, Y44
         # per-op figures at the step's M
         for name, fn, fl in [
             ("qkv", lambda r: B.bi_gemm(out["Xn"], t["Wqkv"], out["Yqkv"]), flops["qkv"]),

@@ -46,6 +46,8 @@
  *     dimension of 2^22 elements or more).  There is never a silent fallback to
  *     a non-invariant path: the fail-loud rule of the PR #51292 review thread.
  *   - BI_ERR_HIP: the HIP runtime refused the launch or a device query.
+ *   - BI_ERR_VALUE: a scalar argument outside its domain (a global scale
+ *     that is not a finite number > 0).
  */
 #ifndef BI_H
 #define BI_H
@@ -63,7 +65,8 @@ typedef enum bi_status {
     BI_ERR_ALIGN = 3,
     BI_ERR_ALIAS = 4,
     BI_ERR_UNSUPPORTED = 5,
-    BI_ERR_HIP = 6
+    BI_ERR_HIP = 6,
+    BI_ERR_VALUE = 7
 } bi_status;
 
 typedef enum bi_a_format {
@@ -75,7 +78,8 @@ typedef enum bi_op {
     BI_OP_GEMM = 0,
     BI_OP_BMM = 1,
     BI_OP_NVFP4_GEMM = 2,
-    BI_OP_RMSNORM = 3
+    BI_OP_RMSNORM = 3,
+    BI_OP_NVFP4_QUANT = 4
 } bi_op;
 
 /*
@@ -188,6 +192,39 @@ bi_status bi_nvfp4_gemm(const void *A, const void *A_scales, int a_fmt, int64_t 
 bi_status bi_rmsnorm(const void *X, int64_t ldx, const void *gamma, float eps, void *Y,
                      int64_t ldy, int64_t M, int64_t H, void *stream);
 
+/*
+ * bi_nvfp4_quant: row-local NVFP4 quantisation of bf16 activations, the
+ * scaled_fp4_quant(x, global_scale) -> (codes, block scales) step that feeds
+ * the W4A4 GEMM in the vLLM PR #39912 unit test (summary page, section "key
+ * source snippets").  The pages do not define it; per block of 16
+ * consecutive elements of a row this library computes, every step one IEEE
+ * fp32 operation with round to nearest even:
+ *   amax = max |x|;  v = min((amax * g) / 6, 448);
+ *   scale = the E4M3 (fn) code nearest to v, ties to the even code;
+ *   s = its value; if s == 0 every element code is 0, else r = g / s and each
+ *   element code is the E2M1 magnitude code nearest to |x| * r (ties to the
+ *   even code, saturating at 6), with the sign bit set for a negative x whose
+ *   magnitude code is not 0.
+ * Each row's bytes depend only on that row and g, so g must be fixed by the
+ * caller (computed once, e.g. from a calibration batch) and not recomputed
+ * per batch; then a row quantised alone equals the same row quantised inside
+ * any batch.  The output is the NVFP4 A operand of bi_nvfp4_gemm with
+ * a_fmt = BI_A_NVFP4 and lda = ldq.
+ *   X: bf16 [M,K], row stride ldx elements (ldx % 8 == 0), 16-byte aligned.
+ *   Q: codes uint8 [M,K/2], row stride ldq/2 bytes; element 2j of a row in
+ *      the low nibble of byte j, element 2j+1 in the high nibble.  4-byte
+ *      aligned.
+ *   Q_scales: uint8 [M,K/16], row stride ldq/16 bytes.
+ *   ldq >= K and ldq % 16 == 0 (BI_ERR_ALIGN otherwise; bi_nvfp4_gemm needs
+ *   ldq % 32 == 0 and 16-byte aligned buffers to consume the result);
+ *   K % 16 == 0.
+ *   g: the global scale, finite and > 0, else BI_ERR_VALUE.
+ *   Q and Q_scales must not overlap X or each other (BI_ERR_ALIAS).
+ *   M * K / 8 >= 2^30 is BI_ERR_UNSUPPORTED.
+ */
+bi_status bi_nvfp4_quant(const void *X, int64_t ldx, float g, void *Q, void *Q_scales,
+                         int64_t ldq, int64_t M, int64_t K, void *stream);
+
 /* The *_ex variants take launch options (may be NULL = defaults). */
 bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
                      int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream,
@@ -202,10 +239,15 @@ bi_status bi_nvfp4_gemm_ex(const void *A, const void *A_scales, int a_fmt, int64
 bi_status bi_rmsnorm_ex(const void *X, int64_t ldx, const void *gamma, float eps, void *Y,
                         int64_t ldy, int64_t M, int64_t H, void *stream,
                         const bi_launch_opts *opts);
+bi_status bi_nvfp4_quant_ex(const void *X, int64_t ldx, float g, void *Q, void *Q_scales,
+                            int64_t ldq, int64_t M, int64_t K, void *stream,
+                            const bi_launch_opts *opts);
 
 /*
  * bi_plan_query: the recipe the library uses for (op, N, K); for
- * BI_OP_RMSNORM pass H as N and 0 as K.  There is deliberately no M
+ * BI_OP_RMSNORM pass H as N and 0 as K; for BI_OP_NVFP4_QUANT pass K as N and
+ * 0 as K (threads = 256 per workgroup, chunks_per_thread = 1: one thread per
+ * 8 elements).  There is deliberately no M
  * argument: the recipe cannot depend on it.  Returns BI_ERR_SHAPE or
  * BI_ERR_UNSUPPORTED for keys the matching entry point would reject.
  * Host-only; makes no HIP call.

@@ -20,9 +20,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbi.so")
 
-BI_OK, BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_ALIGN, BI_ERR_ALIAS, BI_ERR_UNSUPPORTED, BI_ERR_HIP = range(7)
+(BI_OK, BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_ALIGN, BI_ERR_ALIAS, BI_ERR_UNSUPPORTED, BI_ERR_HIP,
+ BI_ERR_VALUE) = range(8)
 BI_A_BF16, BI_A_NVFP4 = 0, 1
-BI_OP_GEMM, BI_OP_BMM, BI_OP_NVFP4_GEMM, BI_OP_RMSNORM = range(4)
+BI_OP_GEMM, BI_OP_BMM, BI_OP_NVFP4_GEMM, BI_OP_RMSNORM, BI_OP_NVFP4_QUANT = range(5)
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -62,6 +63,8 @@ _SIGS = {
                          _i64, _i64, _p, _p],
     "bi_rmsnorm": [_p, _i64, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p],
     "bi_rmsnorm_ex": [_p, _i64, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p],
+    "bi_nvfp4_quant": [_p, _i64, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p],
+    "bi_nvfp4_quant_ex": [_p, _i64, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
 }
@@ -240,3 +243,27 @@ def bi_rmsnorm(X, gamma, eps, Y=None, *, stream=None, max_workgroups=0):
                              M, H, _stream(stream), _opts(max_workgroups))
     _raise(st, "bi_rmsnorm")
     return Y
+
+
+def bi_nvfp4_quant(X, g, Q=None, Q_scales=None, *, stream=None, max_workgroups=0):
+    """Row-local NVFP4 quantisation of bf16 X [M,K] with global scale g.
+
+    Returns (Q codes uint8 [M,K/2], Q_scales uint8 [M,K/16]), allocated with
+    torch if not given; they are the NVFP4 A operand of bi_nvfp4_gemm.
+    """
+    _check2d(X, "X")
+    M, K = X.shape
+    if Q is None:
+        Q = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if Q_scales is None:
+        Q_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=X.device)
+    if Q.dim() != 2 or Q.stride(1) != 1 or tuple(Q.shape) != (M, K // 2):
+        raise ValueError("Q must be [M,K/2] with unit last stride")
+    if Q_scales.dim() != 2 or Q_scales.stride(1) != 1 or tuple(Q_scales.shape) != (M, K // 16):
+        raise ValueError("Q_scales must be [M,K/16] with unit last stride")
+    if Q_scales.stride(0) * 8 != Q.stride(0) and M > 1:
+        raise ValueError("Q and Q_scales row strides must describe the same ldq")
+    st = lib().bi_nvfp4_quant_ex(_ptr(X), X.stride(0), float(g), _ptr(Q), _ptr(Q_scales),
+                                 Q.stride(0) * 2, M, K, _stream(stream), _opts(max_workgroups))
+    _raise(st, "bi_nvfp4_quant")
+    return Q, Q_scales

@@ -216,6 +216,7 @@ const char *bi_status_str(bi_status s) {
         case BI_ERR_ALIGN: return "BI_ERR_ALIGN: pointer or stride not 16-byte aligned";
         case BI_ERR_ALIAS: return "BI_ERR_ALIAS: output overlaps an input";
         case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: no batch-invariant plan for this shape";
+        case BI_ERR_VALUE: return "BI_ERR_VALUE: a scalar argument is outside its domain";
         case BI_ERR_HIP: return "BI_ERR_HIP: the HIP runtime reported an error";
     }
     return "unknown bi_status";
@@ -251,6 +252,16 @@ bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
             out->threads = T;
             out->waves = T / 64;
             out->chunks_per_thread = cpt;
+            return BI_OK;
+        }
+        case BI_OP_NVFP4_QUANT: {
+            if (N <= 0 || N % 16 != 0) return BI_ERR_SHAPE;
+            if (N > kI32Max) return BI_ERR_UNSUPPORTED;
+            std::memset(out, 0, sizeof *out);
+            out->op = op;
+            out->threads = 256;
+            out->waves = 4;
+            out->chunks_per_thread = 1;
             return BI_OK;
         }
     }
@@ -390,6 +401,47 @@ bi_status bi_rmsnorm_ex(const void *X, int64_t ldx, const void *gamma, float eps
 bi_status bi_rmsnorm(const void *X, int64_t ldx, const void *gamma, float eps, void *Y, int64_t ldy,
                      int64_t M, int64_t H, void *stream) {
     return bi_rmsnorm_ex(X, ldx, gamma, eps, Y, ldy, M, H, stream, nullptr);
+}
+
+bi_status bi_nvfp4_quant_ex(const void *X, int64_t ldx, float g, void *Q, void *Q_scales, int64_t ldq,
+                            int64_t M, int64_t K, void *stream, const bi_launch_opts *opts) {
+    if (M < 0 || K <= 0 || K % 16 != 0 || ldx < K || ldq < K) return BI_ERR_SHAPE;
+    if (!(g > 0.0f) || !(g <= 3.402823466e38f)) return BI_ERR_VALUE;
+    if (M > kI32Max || K > kI32Max || M * (K / 8) >= ((int64_t)1 << 30)) return BI_ERR_UNSUPPORTED;
+    if (M == 0) return BI_OK;
+    if (!X || !Q || !Q_scales) return BI_ERR_NULL;
+    // 16-byte loads of X; 4-byte code stores (row strides ldq/2 bytes); byte scale stores
+    if (!aligned16(X) || (reinterpret_cast<uintptr_t>(Q) & 3u) || ldx % 8 || ldq % 16) return BI_ERR_ALIGN;
+    const Range rx = mat_range(X, M, K, ldx, 2, 1);
+    const Range rq = mat_range(Q, M, K, ldq, 1, 2);
+    const Range rs = mat_range(Q_scales, M, K, ldq, 1, 16);
+    if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return BI_ERR_ALIAS;
+    int cus = 0;
+    bi_status st = device_cus(&cus);
+    if (st != BI_OK) return st;
+    bi::QuantArgs a{};
+    a.X = X; a.Q = Q; a.S = Q_scales;
+    a.ldx = ldx; a.ldq = ldq;
+    a.M = (int)M; a.K = (int)K;
+    a.halves = (int)(M * (K / 8));
+    {   // exact division by d = K / 8 for every dividend below 2^32
+        const uint64_t d = (uint64_t)(K / 8);
+        int l = 0;
+        while (((uint64_t)1 << l) < d) ++l;
+        a.shift = 32 + l;
+        a.magic = (((uint64_t)1 << a.shift) + d - 1) / d;
+    }
+    a.g = g;
+    // four half blocks per thread (the kernel's kU), at most 8 workgroups per compute unit
+    const int wgs = (int)(((int64_t)a.halves + 4 * 256 - 1) / (4 * 256));
+    const int grid = default_grid(wgs, cus, opts, 8);
+    hipError_t e = bi::launch_nvfp4_quant(a, grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+bi_status bi_nvfp4_quant(const void *X, int64_t ldx, float g, void *Q, void *Q_scales, int64_t ldq,
+                         int64_t M, int64_t K, void *stream) {
+    return bi_nvfp4_quant_ex(X, ldx, g, Q, Q_scales, ldq, M, K, stream, nullptr);
 }
 
 }  // extern "C"

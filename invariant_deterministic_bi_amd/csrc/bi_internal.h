@@ -41,6 +41,8 @@ constexpr TileShape kTileShapes[] = {
     {128, 128, 4, 2, 4, 4},   // 11
     {256, 256, 4, 2, 2, 3},   // 12
     {256, 256, 2, 4, 2, 3},   // 13: ping-pong schedule (bf16 x bf16, batch 1; else as 12)
+    {128, 128, 2, 2, 2, 2},   // 14: 64 KB of LDS, two workgroups per compute unit
+    {128, 128, 4, 2, 2, 2},   // 15: the same with eight wavefronts
 };
 constexpr int kPingPongVariant = 13;
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
@@ -107,5 +109,21 @@ struct RmsArgs {
 
 hipError_t launch_rmsnorm(int threads, int chunks_per_thread, const RmsArgs &args, int grid,
                           hipStream_t stream);
+
+struct QuantArgs {
+    const void *X;     // bf16 [M, K], row stride ldx elements
+    void *Q;           // codes, row stride ldq / 2 bytes
+    void *S;           // E4M3 scales, row stride ldq / 16 bytes
+    int64_t ldx, ldq;
+    int M, K;
+    int halves;        // M * K / 8: one thread per 8 elements
+    uint64_t magic;    // row of half block i = (i * magic) >> shift
+    int shift;
+    float g;           // global scale
+};
+
+// Row-local NVFP4 quantiser: 256-thread workgroups, a grid-stride loop over
+// the 8-element half blocks.
+hipError_t launch_nvfp4_quant(const QuantArgs &args, int grid, hipStream_t stream);
 
 }  // namespace bi

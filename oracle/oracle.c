@@ -256,6 +256,7 @@ void oracle_nvfp4_quant(const uint16_t *X, int64_t ldx, float g, int64_t M, int6
                 unsigned c = 0;
                 if (s != 0.0f) {
                     float w = (float)fabs(xv) * r;
+                    if (w > 6.0f) w = 6.0f;
                     c = nearest_code((double)w, e2m1_value, 8);
                     if (c != 0 && signbit(xv)) c |= 8u;
                 }

@@ -32,8 +32,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert B.status_str(s)
+    assert "VALUE" in B.status_str(B.BI_ERR_VALUE)
     assert "UNSUPPORTED" in B.status_str(B.BI_ERR_UNSUPPORTED)
     assert B.version().startswith("bi ")
 
@@ -147,3 +148,34 @@ def test_rmsnorm_validation():
     assert call(Y=A0 + 32) == B.BI_ERR_ALIAS      # partial overlap with X
     assert call(Y=B0) == B.BI_ERR_ALIAS           # overlaps gamma
     assert call(M=0, X=0, g=0, Y=0) == B.BI_OK
+
+
+def test_nvfp4_quant_plan():
+    p = B.plan_query(B.BI_OP_NVFP4_QUANT, 4096, 0)
+    assert p["threads"] == 256 and p["chunks_per_thread"] == 1
+    with pytest.raises(B.BiError) as e:
+        B.plan_query(B.BI_OP_NVFP4_QUANT, 4104, 0)
+    assert e.value.status == B.BI_ERR_SHAPE
+
+
+def test_nvfp4_quant_validation():
+    f = B.lib().bi_nvfp4_quant
+
+    def call(X=A0, ldx=4096, g=2.5, Q=B0, S=B0 + 0x100000, ldq=4096, M=4, K=4096):
+        return f(X, ldx, g, Q, S, ldq, M, K, None)
+    assert call(K=4088, ldx=4088, ldq=4096) == B.BI_ERR_SHAPE      # K % 16
+    assert call(ldx=4080) == B.BI_ERR_SHAPE                        # ldx < K
+    assert call(ldq=4080) == B.BI_ERR_SHAPE                        # ldq < K
+    assert call(M=-1) == B.BI_ERR_SHAPE
+    for bad_g in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(g=bad_g) == B.BI_ERR_VALUE, bad_g
+    assert call(X=0) == B.BI_ERR_NULL
+    assert call(S=0) == B.BI_ERR_NULL
+    assert call(ldq=4104) == B.BI_ERR_ALIGN                        # ldq % 16
+    assert call(ldx=4100) == B.BI_ERR_ALIGN                        # ldx % 8
+    assert call(X=A0 + 8) == B.BI_ERR_ALIGN
+    assert call(Q=B0 + 2) == B.BI_ERR_ALIGN
+    assert call(Q=A0 + 64) == B.BI_ERR_ALIAS                       # codes over X
+    assert call(S=B0 + 64) == B.BI_ERR_ALIAS                       # scales over codes
+    assert call(M=1 << 20, K=8192, ldx=8192, ldq=8192) == B.BI_ERR_UNSUPPORTED
+    assert call(M=0, X=0, Q=0, S=0) == B.BI_OK
