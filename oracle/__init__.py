@@ -50,6 +50,8 @@ def _load():
     lib.oracle_rmsnorm.restype = None
     lib.oracle_nvfp4_quant.argtypes = [_p, _i64, ctypes.c_float, _i64, _i64, _i64, _p, _p]
     lib.oracle_nvfp4_quant.restype = None
+    lib.oracle_reduce_rmsnorm.argtypes = [_p, _i64, _p, _p, ctypes.c_float, _i64, _i64, _p, _p, _p, _p]
+    lib.oracle_reduce_rmsnorm.restype = None
     for name in ("oracle_e2m1_value", "oracle_e4m3_value", "oracle_bf16_value"):
         getattr(lib, name).argtypes = [ctypes.c_uint32]
         getattr(lib, name).restype = ctypes.c_double
@@ -206,3 +208,32 @@ def nvfp4_quant(X, global_scale):
         _load().oracle_nvfp4_quant(_ptr(X), K, float(np.float32(global_scale)), M, K, K,
                                    _ptr(Q), _ptr(S))
     return Q, S
+
+
+def reduce_rmsnorm(partials, gamma, eps, residual=None):
+    """Fixed-order reduction of partial outputs followed by RMSNorm, fp64.
+
+    partials: bf16 bits [P, M, H] (the per-rank partial outputs of a
+    row-parallel layer); residual: bf16 bits [M, H] or None; gamma [H].
+    R = residual + sum_p partials[p]; Y = R * gamma / sqrt(mean_h R^2 + eps)
+    (the all-reduce + RMSNorm pair of the vLLM PR #51292 page, section
+    "Purpose").  eps is rounded to fp32 first.  Returns (R, SR, Y, SY):
+    SR = sum of |terms| of each R element, SY = |gamma| * SR / rms, the
+    scales of the tolerances.
+    """
+    P = np.ascontiguousarray(_u16(partials))
+    gamma = np.ascontiguousarray(_u16(gamma))
+    n, M, H = P.shape
+    assert gamma.shape == (H,)
+    res = None
+    if residual is not None:
+        res = np.ascontiguousarray(_u16(residual))
+        assert res.shape == (M, H)
+    R = np.zeros((M, H), np.float64)
+    SR = np.zeros((M, H), np.float64)
+    Y = np.zeros((M, H), np.float64)
+    SY = np.zeros((M, H), np.float64)
+    if M and H:
+        _load().oracle_reduce_rmsnorm(_ptr(P), n, _ptr(res), _ptr(gamma), float(np.float32(eps)),
+                                      M, H, _ptr(R), _ptr(SR), _ptr(Y), _ptr(SY))
+    return R, SR, Y, SY

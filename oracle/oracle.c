@@ -268,5 +268,49 @@ void oracle_nvfp4_quant(const uint16_t *X, int64_t ldx, float g, int64_t M, int6
     }
 }
 
+/*
+ * Fixed-order reduction of partial outputs followed by RMSNorm: the
+ * all-reduce + RMSNorm pair that the vLLM PR #51292 page fuses (section
+ * "Purpose"), and whose reduction it requires to run in one fixed order for
+ * every batch (the root-cause comment and the test plan: one distinct
+ * output over 8 runs).  On one GPU the P partial [M,H] outputs of a
+ * row-parallel layer are the inputs.  Plain definition, in fp64:
+ *   R[i][h] = residual[i][h] (if given) + sum_p P_p[i][h];
+ *   Y[i][h] = R[i][h] * gamma[h] / sqrt((1/H) * sum_h' R[i][h']^2 + eps).
+ * P holds the partials back to back, each bf16 [M,H] dense, P_p at P + p*M*H;
+ * residual is bf16 [M,H] dense or NULL.  SR gets sum |terms| of each R
+ * element, SY gets |gamma| * SR / sqrt(mean(R^2) + eps): the scales of the
+ * tolerances.
+ */
+void oracle_reduce_rmsnorm(const uint16_t *P, int64_t np, const uint16_t *residual,
+                           const uint16_t *gamma, float eps, int64_t M, int64_t H, double *R,
+                           double *SR, double *Y, double *SY) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; i++) {
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            double r = 0.0, sr = 0.0;
+            if (residual) {
+                r = bf16_value(residual[i * H + h]);
+                sr = fabs(r);
+            }
+            for (int64_t p = 0; p < np; p++) {
+                double v = bf16_value(P[(p * M + i) * H + h]);
+                r += v;
+                sr += fabs(v);
+            }
+            R[i * H + h] = r;
+            SR[i * H + h] = sr;
+            ss += r * r;
+        }
+        double denom = sqrt(ss / (double)H + (double)eps);
+        for (int64_t h = 0; h < H; h++) {
+            double g = bf16_value(gamma[h]);
+            Y[i * H + h] = R[i * H + h] * g / denom;
+            SY[i * H + h] = fabs(g) * SR[i * H + h] / denom;
+        }
+    }
+}
+
 /* Number of OpenMP threads the oracle will use (for reporting). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }

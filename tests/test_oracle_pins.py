@@ -509,3 +509,51 @@ def test_nvfp4_quant_pow2_scaling_rows_and_zero():
     z[0, 5] = 0x8000
     qz, sz = oracle.nvfp4_quant(z, 3.0)
     assert not qz.any() and not sz.any()
+
+
+# ---------------------------------------------------------------- reduction of partials + RMSNorm
+#
+# oracle.reduce_rmsnorm: R = residual + sum_p P_p, Y = RMSNorm(R) (the
+# all-reduce + RMSNorm pair of the vLLM PR #51292 page, section "Purpose").
+
+@pytest.mark.parametrize("name", ["reduce_rms_two", "reduce_rms_res"])
+def test_reduce_rmsnorm_worked_examples(name):
+    args, rhs = WORKED[name]
+    P = np.stack([bits([[float(v) for v in part.split(",")]]) for part in args["P"].split("|")])
+    res = None if args["res"] == "none" else bits([[float(v) for v in args["res"].split(",")]])
+    gam = bits([float(v) for v in args["gamma"].split(",")])
+    want = dict(tok.split("=", 1) for tok in rhs.split())
+    R, SR, Y, SY = oracle.reduce_rmsnorm(P, gam, float(args["eps"]), residual=res)
+    assert R[0].tolist() == [float(v) for v in want["R"].split(",")]
+    np.testing.assert_allclose(Y[0], [float(v) for v in want["Y"].split(",")], rtol=1e-15, atol=0)
+
+
+def test_reduce_rmsnorm_integer_exact_and_order():
+    """Integer partials: R equals numpy's int64 sum exactly, whatever the
+    order of the partials; the residual acts as one more partial."""
+    P = inputs.randint_bf16((5, 7, 64), -40, 40, tag=(40,))
+    res = inputs.randint_bf16((7, 64), -40, 40, tag=(41,))
+    gam = inputs.uniform_bf16((64,), 0.5, 1.5, tag=(42,))
+    Pi = inputs.bf16_bits_to_f32(P).astype(np.int64)
+    ri = inputs.bf16_bits_to_f32(res).astype(np.int64)
+    R, SR, Y, SY = oracle.reduce_rmsnorm(P, gam, 1e-6, residual=res)
+    assert np.array_equal(R, (Pi.sum(axis=0) + ri).astype(np.float64))
+    assert np.array_equal(SR, (np.abs(Pi).sum(axis=0) + np.abs(ri)).astype(np.float64))
+    R2, _, Y2, _ = oracle.reduce_rmsnorm(P[::-1].copy(), gam, 1e-6, residual=res)
+    assert np.array_equal(R2, R) and np.array_equal(Y2, Y)
+    R3, _, Y3, _ = oracle.reduce_rmsnorm(np.concatenate([res[None], P]), gam, 1e-6)
+    assert np.array_equal(R3, R) and np.array_equal(Y3, Y)
+
+
+def test_reduce_rmsnorm_single_partial_is_rmsnorm():
+    """One partial and no residual reduces to RMSNorm of that partial, and the
+    normalisation of R is RMSNorm's closed form (zero row -> 0)."""
+    X = inputs.randn_bf16((9, 512), tag=(43,))
+    X[4] = 0
+    gam = inputs.uniform_bf16((512,), 0.5, 1.5, tag=(44,))
+    R, SR, Y, SY = oracle.reduce_rmsnorm(X[None], gam, 1e-6)
+    assert np.array_equal(R, inputs.bf16_bits_to_f32(X).astype(np.float64))
+    assert np.array_equal(Y, oracle.rmsnorm(X, gam, 1e-6))
+    assert not Y[4].any()
+    # SY = |gamma| * SR / rms: with one partial SR = |x|, so SY = |Y|
+    np.testing.assert_allclose(SY, np.abs(Y), rtol=1e-15, atol=0)
