@@ -406,6 +406,20 @@ def main():
         gbs = (4.0 * M * H + 2.0 * H) / (us * 1e-6) / 1e9
         sweep.append({"op": "rmsnorm", "M": M, "H": H, "us": round(us, 2), "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        # fixed-order reduction of 8 per-rank partial outputs (a row-parallel
+        # layer's [M, 4096] at tensor-parallel degree 8) + residual, then RMSNorm
+        parts = [torch.randn((M, H), device=dev).to(torch.bfloat16) for _ in range(8)]
+        resid = torch.randn((M, H), device=dev).to(torch.bfloat16)
+        Rr, Yr = B.bi_reduce_rmsnorm(parts, t["g2"], eps, residual=resid)
+        us = timed(lambda r: B.bi_reduce_rmsnorm(parts, t["g2"], eps, resid, Rr, Yr), 20)
+        byt = 2.0 * M * H * (len(parts) + 3) + 2.0 * H
+        gbs = byt / (us * 1e-6) / 1e9
+        sweep.append({"op": "reduce8_rmsnorm", "M": M, "H": H, "us": round(us, 2), "GB/s": round(gbs, 1),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        R16, Y16 = B.bi_reduce_rmsnorm([q[:16] for q in parts], t["g2"], eps, residual=resid[:16])
+        inv_checked += 1
+        inv_passed += int(torch.equal(R16, Rr[:16]) and torch.equal(Y16, Yr[:16]))
+        del parts, resid, Rr, Yr
         # run-to-run: the step's outputs are identical over repeats
         snap = {k: v.clone() for k, v in out.items()}
         for _ in range(3):

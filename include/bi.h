@@ -79,7 +79,8 @@ typedef enum bi_op {
     BI_OP_BMM = 1,
     BI_OP_NVFP4_GEMM = 2,
     BI_OP_RMSNORM = 3,
-    BI_OP_NVFP4_QUANT = 4
+    BI_OP_NVFP4_QUANT = 4,
+    BI_OP_REDUCE_RMSNORM = 5
 } bi_op;
 
 /*
@@ -225,6 +226,35 @@ bi_status bi_rmsnorm(const void *X, int64_t ldx, const void *gamma, float eps, v
 bi_status bi_nvfp4_quant(const void *X, int64_t ldx, float g, void *Q, void *Q_scales,
                          int64_t ldq, int64_t M, int64_t K, void *stream);
 
+/*
+ * bi_reduce_rmsnorm: the one-GPU share of the all-reduce + RMSNorm pair that
+ * the vLLM PR #51292 page fuses (section "Purpose") and whose reduction must
+ * run in one fixed order for batch invariance (its root-cause comment: a
+ * size-dependent reduction path; its test plan: 8 identical runs, 1 distinct
+ * output).  The inputs are the n_partials partial outputs of a row-parallel
+ * layer (one per tensor-parallel rank), summed in rank order:
+ *   R[i][h] = bf16_rne( ((t_0 + t_1) + t_2) + ... ) in fp32, the terms t
+ *             being residual[i][h] (when residual != NULL) and then
+ *             partials[0][i][h], ..., partials[n_partials-1][i][h], each
+ *             widened exactly from bf16; the first term starts the sum;
+ *   Y = RMSNorm(R) by the very instruction sequence of bi_rmsnorm, so Y is
+ *       bitwise bi_rmsnorm(R, gamma, eps).
+ * Each element's sum order is fixed by n_partials alone, never by M, the
+ * grid or the row.  Changing the order of the partials may change bits;
+ * the rank order is the contract.
+ *   partials: HOST array of n_partials device pointers, each bf16 [M,H] with
+ *     row stride ldp; 1 <= n_partials <= 8 (BI_ERR_SHAPE otherwise).
+ *   residual: bf16 [M,H], row stride ldres, or NULL.
+ *   gamma: bf16 [H].  R, Y: bf16 [M,H], row strides ldr, ldy.
+ *   R may be the residual itself (same pointer and stride: an in-place
+ *   residual update); every other overlap between R, Y and the inputs is
+ *   BI_ERR_ALIAS.  H % 8 == 0 and H <= 32768, as for bi_rmsnorm.
+ */
+bi_status bi_reduce_rmsnorm(const void *const *partials, int n_partials, int64_t ldp,
+                            const void *residual, int64_t ldres, const void *gamma, float eps,
+                            void *R, int64_t ldr, void *Y, int64_t ldy, int64_t M, int64_t H,
+                            void *stream);
+
 /* The *_ex variants take launch options (may be NULL = defaults). */
 bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
                      int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream,
@@ -239,13 +269,18 @@ bi_status bi_nvfp4_gemm_ex(const void *A, const void *A_scales, int a_fmt, int64
 bi_status bi_rmsnorm_ex(const void *X, int64_t ldx, const void *gamma, float eps, void *Y,
                         int64_t ldy, int64_t M, int64_t H, void *stream,
                         const bi_launch_opts *opts);
+bi_status bi_reduce_rmsnorm_ex(const void *const *partials, int n_partials, int64_t ldp,
+                               const void *residual, int64_t ldres, const void *gamma, float eps,
+                               void *R, int64_t ldr, void *Y, int64_t ldy, int64_t M, int64_t H,
+                               void *stream, const bi_launch_opts *opts);
 bi_status bi_nvfp4_quant_ex(const void *X, int64_t ldx, float g, void *Q, void *Q_scales,
                             int64_t ldq, int64_t M, int64_t K, void *stream,
                             const bi_launch_opts *opts);
 
 /*
  * bi_plan_query: the recipe the library uses for (op, N, K); for
- * BI_OP_RMSNORM pass H as N and 0 as K; for BI_OP_NVFP4_QUANT pass K as N and
+ * BI_OP_RMSNORM and BI_OP_REDUCE_RMSNORM pass H as N and 0 as K (the two
+ * share one row recipe); for BI_OP_NVFP4_QUANT pass K as N and
  * 0 as K (threads = 256 per workgroup, chunks_per_thread = 1: one thread per
  * 8 elements).  There is deliberately no M
  * argument: the recipe cannot depend on it.  Returns BI_ERR_SHAPE or

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libbi.so")
 (BI_OK, BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_ALIGN, BI_ERR_ALIAS, BI_ERR_UNSUPPORTED, BI_ERR_HIP,
  BI_ERR_VALUE) = range(8)
 BI_A_BF16, BI_A_NVFP4 = 0, 1
-BI_OP_GEMM, BI_OP_BMM, BI_OP_NVFP4_GEMM, BI_OP_RMSNORM, BI_OP_NVFP4_QUANT = range(5)
+BI_OP_GEMM, BI_OP_BMM, BI_OP_NVFP4_GEMM, BI_OP_RMSNORM, BI_OP_NVFP4_QUANT, BI_OP_REDUCE_RMSNORM = range(6)
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -65,6 +65,10 @@ _SIGS = {
     "bi_rmsnorm_ex": [_p, _i64, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p],
     "bi_nvfp4_quant": [_p, _i64, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p],
     "bi_nvfp4_quant_ex": [_p, _i64, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p],
+    "bi_reduce_rmsnorm": [ctypes.POINTER(_p), ctypes.c_int, _i64, _p, _i64, _p, ctypes.c_float, _p,
+                          _i64, _p, _i64, _i64, _i64, _p],
+    "bi_reduce_rmsnorm_ex": [ctypes.POINTER(_p), ctypes.c_int, _i64, _p, _i64, _p, ctypes.c_float,
+                             _p, _i64, _p, _i64, _i64, _i64, _p, _p],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
 }
@@ -267,3 +271,38 @@ def bi_nvfp4_quant(X, g, Q=None, Q_scales=None, *, stream=None, max_workgroups=0
                                  Q.stride(0) * 2, M, K, _stream(stream), _opts(max_workgroups))
     _raise(st, "bi_nvfp4_quant")
     return Q, Q_scales
+
+
+def bi_reduce_rmsnorm(partials, gamma, eps, residual=None, R=None, Y=None, *, stream=None,
+                      max_workgroups=0):
+    """R = residual + partials[0] + ... (fp32, this order, one bf16 rounding);
+    Y = RMSNorm(R).  partials: a list of bf16 [M,H] tensors with one common
+    row stride.  Returns (R, Y); R may be the residual tensor (in place)."""
+    if not partials:
+        raise ValueError("at least one partial")
+    for t in partials:
+        _check2d(t, "partial")
+    M, H = partials[0].shape
+    ldp = partials[0].stride(0)
+    for t in partials:
+        if tuple(t.shape) != (M, H) or t.stride(0) != ldp:
+            raise ValueError("partials must share shape and row stride")
+    if gamma.dim() != 1 or gamma.shape[0] != H or not gamma.is_contiguous():
+        raise ValueError("gamma must be a dense [H] vector")
+    if residual is not None:
+        _check2d(residual, "residual")
+        if tuple(residual.shape) != (M, H):
+            raise ValueError("residual must be [M,H]")
+    if R is None:
+        R = torch.empty((M, H), dtype=torch.bfloat16, device=partials[0].device)
+    if Y is None:
+        Y = torch.empty((M, H), dtype=torch.bfloat16, device=partials[0].device)
+    _check2d(R, "R")
+    _check2d(Y, "Y")
+    arr = (ctypes.c_void_p * len(partials))(*[t.data_ptr() for t in partials])
+    st = lib().bi_reduce_rmsnorm_ex(arr, len(partials), ldp, _ptr(residual),
+                                    residual.stride(0) if residual is not None else 0, _ptr(gamma),
+                                    float(eps), _ptr(R), R.stride(0), _ptr(Y), Y.stride(0), M, H,
+                                    _stream(stream), _opts(max_workgroups))
+    _raise(st, "bi_reduce_rmsnorm")
+    return R, Y

@@ -244,7 +244,8 @@ bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
             fill_tile_plan(op, gemm_variant(op, N, K), out);
             return BI_OK;
         }
-        case BI_OP_RMSNORM: {
+        case BI_OP_RMSNORM:
+        case BI_OP_REDUCE_RMSNORM: {
             int T = 0, cpt = 0;
             if (!rms_shape(N, &T, &cpt)) return N > 32768 && N % 8 == 0 ? BI_ERR_UNSUPPORTED : BI_ERR_SHAPE;
             std::memset(out, 0, sizeof *out);
@@ -442,6 +443,64 @@ bi_status bi_nvfp4_quant_ex(const void *X, int64_t ldx, float g, void *Q, void *
 bi_status bi_nvfp4_quant(const void *X, int64_t ldx, float g, void *Q, void *Q_scales, int64_t ldq,
                          int64_t M, int64_t K, void *stream) {
     return bi_nvfp4_quant_ex(X, ldx, g, Q, Q_scales, ldq, M, K, stream, nullptr);
+}
+
+bi_status bi_reduce_rmsnorm_ex(const void *const *partials, int n_partials, int64_t ldp,
+                               const void *residual, int64_t ldres, const void *gamma, float eps,
+                               void *R, int64_t ldr, void *Y, int64_t ldy, int64_t M, int64_t H,
+                               void *stream, const bi_launch_opts *opts) {
+    int T = 0, cpt = 0;
+    if (M < 0 || H <= 0 || H % 8 != 0) return BI_ERR_SHAPE;
+    if (n_partials < 1 || n_partials > bi::kMaxPartials) return BI_ERR_SHAPE;
+    if (ldp < H || ldr < H || ldy < H || (residual && ldres < H)) return BI_ERR_SHAPE;
+    if (!rms_shape(H, &T, &cpt)) return BI_ERR_UNSUPPORTED;
+    if (M > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (M == 0) return BI_OK;
+    if (!partials || !gamma || !R || !Y) return BI_ERR_NULL;
+    for (int q = 0; q < n_partials; ++q)
+        if (!partials[q]) return BI_ERR_NULL;
+    if (!aligned16(gamma) || !aligned16(R) || !aligned16(Y) || ldp % 8 || ldr % 8 || ldy % 8 ||
+        (residual && (!aligned16(residual) || ldres % 8)))
+        return BI_ERR_ALIGN;
+    for (int q = 0; q < n_partials; ++q)
+        if (!aligned16(partials[q])) return BI_ERR_ALIGN;
+    const Range rr = mat_range(R, M, H, ldr, 2, 1);
+    const Range ry = mat_range(Y, M, H, ldy, 2, 1);
+    const Range rg = mat_range(gamma, 1, H, H, 2, 1);
+    if (overlap(rr, ry) || overlap(rr, rg) || overlap(ry, rg)) return BI_ERR_ALIAS;
+    for (int q = 0; q < n_partials; ++q) {
+        const Range rp = mat_range(partials[q], M, H, ldp, 2, 1);
+        if (overlap(rr, rp) || overlap(ry, rp)) return BI_ERR_ALIAS;
+    }
+    if (residual) {
+        const Range rs = mat_range(residual, M, H, ldres, 2, 1);
+        const bool in_place = (residual == R && ldres == ldr);
+        if ((!in_place && overlap(rr, rs)) || overlap(ry, rs)) return BI_ERR_ALIAS;
+    }
+    int cus = 0;
+    bi_status st = device_cus(&cus);
+    if (st != BI_OK) return st;
+    bi::ReduceRmsArgs a{};
+    for (int q = 0; q < n_partials; ++q) a.P[q] = partials[q];
+    a.np = n_partials;
+    a.ldp = ldp;
+    a.res = residual;
+    a.ldres = residual ? ldres : 0;
+    a.gamma = gamma;
+    a.R = R; a.Y = Y;
+    a.ldr = ldr; a.ldy = ldy;
+    a.M = (int)M; a.H = (int)H; a.eps = eps;
+    const int grid = default_grid((int)M, cus, opts, 16);
+    hipError_t e = bi::launch_reduce_rmsnorm(T, cpt, a, grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+bi_status bi_reduce_rmsnorm(const void *const *partials, int n_partials, int64_t ldp,
+                            const void *residual, int64_t ldres, const void *gamma, float eps,
+                            void *R, int64_t ldr, void *Y, int64_t ldy, int64_t M, int64_t H,
+                            void *stream) {
+    return bi_reduce_rmsnorm_ex(partials, n_partials, ldp, residual, ldres, gamma, eps, R, ldr, Y, ldy,
+                                M, H, stream, nullptr);
 }
 
 }  // extern "C"

@@ -110,6 +110,27 @@ struct RmsArgs {
 hipError_t launch_rmsnorm(int threads, int chunks_per_thread, const RmsArgs &args, int grid,
                           hipStream_t stream);
 
+constexpr int kMaxPartials = 8;
+
+struct ReduceRmsArgs {
+    const void *P[kMaxPartials];  // np partial outputs, bf16 [M, H], row stride ldp
+    int np;
+    int64_t ldp;
+    const void *res;              // residual bf16 [M, H] (row stride ldres) or NULL
+    int64_t ldres;
+    const void *gamma;
+    void *R;                      // reduced rows, bf16 [M, H], row stride ldr
+    void *Y;                      // RMSNorm(R), bf16 [M, H], row stride ldy
+    int64_t ldr, ldy;
+    int M, H;
+    float eps;
+};
+
+// Same threads / chunks per thread as RMSNorm for H (the row normalisation
+// is RMSNorm's own code).
+hipError_t launch_reduce_rmsnorm(int threads, int chunks_per_thread, const ReduceRmsArgs &args,
+                                 int grid, hipStream_t stream);
+
 struct QuantArgs {
     const void *X;     // bf16 [M, K], row stride ldx elements
     void *Q;           // codes, row stride ldq / 2 bytes

@@ -179,3 +179,33 @@ def test_nvfp4_quant_validation():
     assert call(S=B0 + 64) == B.BI_ERR_ALIAS                       # scales over codes
     assert call(M=1 << 20, K=8192, ldx=8192, ldq=8192) == B.BI_ERR_UNSUPPORTED
     assert call(M=0, X=0, Q=0, S=0) == B.BI_OK
+
+
+def test_reduce_rmsnorm_plan_matches_rmsnorm():
+    for H in (512, 4096, 1000):
+        assert B.plan_query(B.BI_OP_REDUCE_RMSNORM, H, 0)["threads"] == B.plan_query(B.BI_OP_RMSNORM, H, 0)["threads"]
+
+
+def test_reduce_rmsnorm_validation():
+    f = B.lib().bi_reduce_rmsnorm
+    P0, P1, RES, G, R, Y = 0x10000000, 0x11000000, 0x12000000, 0x13000000, 0x14000000, 0x15000000
+
+    def call(parts=(P0, P1), n=None, ldp=4096, res=RES, ldres=4096, g=G, R=R, ldr=4096, Y=Y,
+             ldy=4096, M=4, H=4096):
+        arr = (ctypes.c_void_p * max(1, len(parts)))(*parts) if parts is not None else None
+        return f(arr, len(parts) if n is None else n, ldp, res, ldres, g, 1e-6, R, ldr, Y, ldy, M, H, None)
+    assert call(n=0) == B.BI_ERR_SHAPE
+    assert call(parts=(P0,) * 9) == B.BI_ERR_SHAPE              # more than 8 partials
+    assert call(H=4100, ldp=4104, ldres=4104, ldr=4104, ldy=4104) == B.BI_ERR_SHAPE
+    assert call(ldp=2048) == B.BI_ERR_SHAPE
+    assert call(H=65536, ldp=65536, ldres=65536, ldr=65536, ldy=65536) == B.BI_ERR_UNSUPPORTED
+    assert call(parts=(P0, 0)) == B.BI_ERR_NULL
+    assert call(Y=0) == B.BI_ERR_NULL
+    assert call(parts=(P0, P1 + 8)) == B.BI_ERR_ALIGN
+    assert call(res=RES + 8) == B.BI_ERR_ALIGN
+    assert call(R=P1 + 64) == B.BI_ERR_ALIAS                     # R over a partial
+    assert call(Y=R + 1024) == B.BI_ERR_ALIAS                    # Y over R
+    assert call(Y=RES) == B.BI_ERR_ALIAS                         # Y over the residual
+    assert call(R=RES + 64) == B.BI_ERR_ALIAS                    # partial overlap with the residual
+    assert call(res=0, ldres=0, M=0) == B.BI_OK
+    assert call(parts=(0, 0), M=0, g=0, R=0, Y=0) == B.BI_OK
