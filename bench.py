@@ -125,15 +125,22 @@ def summarize(dirs, out, command):
                 lines.append(f"{r['Name'][:150]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                              f"{float(r['TotalDurationNs']):.0f} | {float(r.get('Percentage', 0) or 0):.2f}")
         for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
-            groups = {}
+            groups, every = {}, {}
             for r in csv.DictReader(open(path)):
+                g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
                 if GATE_UP_KERNEL in r["Kernel_Name"]:
-                    g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-                    groups.setdefault(g, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                    groups.setdefault(g, []).append(dur)
+                every.setdefault((r["Kernel_Name"][:110], g), []).append(dur)
             if groups:
                 lines.append(f"# {GATE_UP_KERNEL} by grid size (threads): calls | avg ns")
                 for g, v in sorted(groups.items()):
                     lines.append(f"grid_{g}_calls_avg_ns: {len(v)} | {sum(v) / len(v):.0f}")
+            if every:
+                lines.append("# every kernel by grid size (threads), largest total first: "
+                             "name | grid | calls | avg ns | min ns")
+                for (n, g), v in sorted(every.items(), key=lambda kv: -sum(kv[1]))[:60]:
+                    lines.append(f"{n} | {g} | {len(v)} | {sum(v) / len(v):.0f} | {min(v)}")
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(path)):
                 name = r["Kernel_Name"]
