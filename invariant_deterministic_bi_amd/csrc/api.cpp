@@ -177,6 +177,20 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         hipError_t e = bi::launch_skinny(b_mode, nb, in, grid, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? BI_OK : BI_ERR_HIP;
     }
+    // BMM with a short reduction: the streaming kernel (its own recipe, chosen
+    // from K alone; a forced tile_variant keeps the tiled kernel, same bits)
+    if (op == BI_OP_BMM && bi::bmm_short_k_ok(in.K) && !(opts && opts->tile_variant != 0)) {
+        const int64_t units = static_cast<int64_t>(in.batch) * ((in.N + 127) / 128);
+        if (units > kI32Max) return BI_ERR_UNSUPPORTED;
+        int cus = 0;
+        bi_status st = device_cus(&cus);
+        if (st != BI_OK) return st;
+        int per_cu = bi::kLdsPerCu / bi::bmm_short_k_lds_bytes(in.K);
+        per_cu = per_cu > 2 ? 2 : (per_cu < 1 ? 1 : per_cu);
+        const int grid = default_grid(static_cast<int>(units), cus, opts, per_cu);
+        hipError_t e = bi::launch_bmm_short_k(in, grid, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+    }
     int variant = gemm_variant(op, in.N, in.K);
     if (opts && opts->tile_variant != 0) {
         if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;
@@ -241,6 +255,21 @@ bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
             if (op == BI_OP_NVFP4_GEMM ? (K % 32 != 0) : (K % 8 != 0)) return BI_ERR_SHAPE;
             if (op == BI_OP_BMM && N % 8 != 0) return BI_ERR_SHAPE;
             if (N > kI32Max || K > kI32Max) return BI_ERR_UNSUPPORTED;
+            if (op == BI_OP_BMM && bi::bmm_short_k_ok(static_cast<int>(K))) {
+                // the streaming BMM kernel: 64 x 128 tiles, the whole K staged
+                std::memset(out, 0, sizeof *out);
+                out->op = op;
+                out->bm = 64;
+                out->bn = 128;
+                out->bk = static_cast<int32_t>(K);
+                out->mfma_m = 16;
+                out->mfma_n = 16;
+                out->mfma_k = 32;
+                out->waves = 4;
+                out->lds_stages = 1;
+                out->threads = 256;
+                return BI_OK;
+            }
             fill_tile_plan(op, gemm_variant(op, N, K), out);
             return BI_OK;
         }

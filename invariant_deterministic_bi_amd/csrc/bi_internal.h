@@ -85,6 +85,13 @@ hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmAr
 // (nb = 8 or 16).
 hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &args, int grid, hipStream_t stream);
 int skinny_lds_bytes(int b_mode, int M, int nb);
+// BMM with a short reduction (K = 64, 128 or 256), B [K, N]: one workgroup
+// per (head, 128-column block) keeps the transposed B block in LDS and
+// streams 64-row tiles of A; four wavefronts.  Same bits as every tiled
+// variant.
+bool bmm_short_k_ok(int K);
+int bmm_short_k_lds_bytes(int K);
+hipError_t launch_bmm_short_k(const GemmArgs &args, int grid, hipStream_t stream);
 // 256 x 256 tiles, eight wavefronts in a ping-pong schedule; bf16 x bf16, batch 1.
 hipError_t launch_pingpong(const GemmArgs &args, int grid, hipStream_t stream);
 // Direct path for 1 <= M <= 16, bf16 A and bf16 weight [N, K], batch 1: one

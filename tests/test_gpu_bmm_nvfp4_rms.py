@@ -238,3 +238,39 @@ def test_tile_shapes_bmm_and_nvfp4():
         note(f"nvfp4 tile variant {v}")
         for rep in range(3):   # repeated: a timing-dependent LDS race shows as a rare mismatch
             assert np.array_equal(host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha, tile_variant=v)), y), (v, rep)
+
+
+@pytest.mark.parametrize("H,M,K,N", [(5, 70, 64, 200), (3, 33, 128, 512), (2, 129, 256, 136),
+                                     (128, 1, 128, 512), (7, 1000, 128, 264)])
+def test_bmm_short_k_kernel(H, M, K, N):
+    """The streaming BMM kernel (K in {64, 128, 256}): integer inputs give
+    bf16_rne(exact) bit for bit, Gaussian inputs stay within the oracle's
+    tolerance, and the bits equal those of every tiled variant (the same
+    per-element MFMA chain), whatever the heads, rows and grid."""
+    Ai = inputs.randint_bf16((H, M, K), -3, 3, tag=(150, K))
+    Wi = inputs.randint_bf16((H, K, N), -3, 3, tag=(151, K))
+    ref, _ = oracle.bmm(Ai, Wi)
+    note(f"bmm short-K integer H={H} M={M} K={K} N={N}")
+    assert np.array_equal(host(B.bi_bmm(dev(Ai), dev(Wi))), rne_bf16_of_exact(ref))
+    A = inputs.randn_bf16((H, M, K), tag=(152, K))
+    W = inputs.randn_bf16((H, K, N), tag=(153, K))
+    Ad, Wd = dev(A), dev(W)
+    note(f"bmm short-K gaussian H={H} M={M} K={K} N={N}")
+    y = host(B.bi_bmm(Ad, Wd))
+    hs = sorted({0, H - 1})
+    ref, s = oracle.bmm(A[hs][:, :min(M, 64)], W[hs])
+    assert_within_tol(y[hs][:, :min(M, 64)], ref, s, "bmm short-K")
+    for v in (2, 3, 10):        # 256x128, 128x128, 128x128 (4x2 waves) tiled kernels
+        note(f"bmm short-K vs tile variant {v}")
+        assert np.array_equal(host(B.bi_bmm(Ad, Wd, tile_variant=v)), y), v
+    for mw in (1, 3, 8, 1000):
+        assert np.array_equal(host(B.bi_bmm(Ad, Wd, max_workgroups=mw)), y), mw
+    if M > 1:
+        assert np.array_equal(host(B.bi_bmm(Ad[:, :1].contiguous(), Wd)), y[:, :1])
+        rows = inputs.rng(12345, 154).permutation(M)[:max(1, M // 3)]
+        r = torch.from_numpy(rows).cuda()
+        assert np.array_equal(host(B.bi_bmm(Ad[:, r].contiguous(), Wd)), y[:, rows])
+    if H > 1:
+        assert np.array_equal(host(B.bi_bmm(Ad[H - 1:], Wd[H - 1:])), y[H - 1:])
+    outs = {host(B.bi_bmm(Ad, Wd)).tobytes() for _ in range(4)}
+    assert len(outs) == 1
