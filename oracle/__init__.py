@@ -52,6 +52,8 @@ def _load():
     lib.oracle_nvfp4_quant.restype = None
     lib.oracle_reduce_rmsnorm.argtypes = [_p, _i64, _p, _p, ctypes.c_float, _i64, _i64, _p, _p, _p, _p]
     lib.oracle_reduce_rmsnorm.restype = None
+    lib.oracle_grouped_gemm.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _p, _p]
+    lib.oracle_grouped_gemm.restype = None
     for name in ("oracle_e2m1_value", "oracle_e4m3_value", "oracle_bf16_value"):
         getattr(lib, name).argtypes = [ctypes.c_uint32]
         getattr(lib, name).restype = ctypes.c_double
@@ -237,3 +239,21 @@ def reduce_rmsnorm(partials, gamma, eps, residual=None):
         _load().oracle_reduce_rmsnorm(_ptr(P), n, _ptr(res), _ptr(gamma), float(np.float32(eps)),
                                       M, H, _ptr(R), _ptr(SR), _ptr(Y), _ptr(SY))
     return R, SR, Y, SY
+
+
+def grouped_gemm(A, W, offsets):
+    """Mixture-of-experts grouped GEMM: rows offsets[e] .. offsets[e+1]-1 of
+    A [T, K] (bf16 bits) use expert e's weight W[e] [N, K];
+    y[t, j] = sum_k A[t, k] * W[e(t), j, k].  Returns (y, s) [T, N] fp64."""
+    A = np.ascontiguousarray(_u16(A))
+    W = np.ascontiguousarray(_u16(W))
+    off = np.ascontiguousarray(np.asarray(offsets, np.int64))
+    T, K = A.shape
+    E, N, K2 = W.shape
+    assert K == K2 and off.shape == (E + 1,) and off[0] == 0 and off[-1] == T
+    assert np.all(np.diff(off) >= 0)
+    Y = np.zeros((T, N), np.float64)
+    S = np.zeros((T, N), np.float64)
+    if T and N:
+        _load().oracle_grouped_gemm(_ptr(A), K, _ptr(W), K, N * K, _ptr(off), E, N, K, _ptr(Y), _ptr(S))
+    return Y, S

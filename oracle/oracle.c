@@ -312,5 +312,37 @@ void oracle_reduce_rmsnorm(const uint16_t *P, int64_t np, const uint16_t *residu
     }
 }
 
+/*
+ * Grouped (mixture-of-experts) GEMM: rows of A are grouped by expert, rows
+ * offsets[e] .. offsets[e+1]-1 belonging to expert e, and
+ *   Y[t][j] = sum_{k<K} A[t][k] * W_e[j][k]   for t in expert e's rows,
+ * W_e the bf16 [N,K] weight of expert e at W + e*sW (row stride ldw).  The
+ * vLLM batch-invariance user guide lists mixture-of-experts layers among the
+ * operations that must not change with batch composition; the row count of
+ * each expert is exactly what changes with it.  Y and S are dense [T, N]
+ * (T = offsets[E]); S gets sum_k |a*w|.
+ */
+void oracle_grouped_gemm(const uint16_t *A, int64_t lda, const uint16_t *W, int64_t ldw, int64_t sW,
+                         const int64_t *offsets, int64_t E, int64_t N, int64_t K, double *Y,
+                         double *S) {
+    for (int64_t e = 0; e < E; e++) {
+        const int64_t t0 = offsets[e], t1 = offsets[e + 1];
+#pragma omp parallel for collapse(2) schedule(static)
+        for (int64_t t = t0; t < t1; t++) {
+            for (int64_t j = 0; j < N; j++) {
+                const uint16_t *a = A + t * lda, *w = W + e * sW + j * ldw;
+                double y = 0.0, s = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    double p = bf16_value(a[k]) * bf16_value(w[k]);
+                    y += p;
+                    s += fabs(p);
+                }
+                Y[t * N + j] = y;
+                S[t * N + j] = s;
+            }
+        }
+    }
+}
+
 /* Number of OpenMP threads the oracle will use (for reporting). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }

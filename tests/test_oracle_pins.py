@@ -557,3 +557,34 @@ def test_reduce_rmsnorm_single_partial_is_rmsnorm():
     assert not Y[4].any()
     # SY = |gamma| * SR / rms: with one partial SR = |x|, so SY = |Y|
     np.testing.assert_allclose(SY, np.abs(Y), rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- grouped (MoE) GEMM
+
+def test_grouped_gemm_worked_example():
+    args, rhs = WORKED["grouped_two_experts"]
+    A = bits(_parse_matrix(args["A"]))
+    W = np.stack([bits(_parse_matrix(w)) for w in args["W"].split("|")])
+    off = [int(v) for v in args["off"].split(",")]
+    y, s = oracle.grouped_gemm(A, W, off)
+    assert y.tolist() == _parse_matrix(rhs)
+
+
+def test_grouped_gemm_integer_exact_empty_groups_and_single_expert():
+    """Integer inputs against numpy int64 per-expert matmuls, with empty
+    experts; one expert covering every row is the plain GEMM."""
+    T, N, K = 40, 24, 64
+    off = [0, 0, 7, 7, 30, 40]          # experts 0 and 2 empty
+    E = len(off) - 1
+    A = inputs.randint_bf16((T, K), -3, 3, tag=(60,))
+    W = inputs.randint_bf16((E, N, K), -3, 3, tag=(61,))
+    Ai = inputs.bf16_bits_to_f32(A).astype(np.int64)
+    Wi = inputs.bf16_bits_to_f32(W).astype(np.int64)
+    y, s = oracle.grouped_gemm(A, W, off)
+    for e in range(E):
+        rows = slice(off[e], off[e + 1])
+        assert np.array_equal(y[rows], (Ai[rows] @ Wi[e].T).astype(np.float64))
+        assert np.array_equal(s[rows], (np.abs(Ai[rows]) @ np.abs(Wi[e]).T).astype(np.float64))
+    y1, s1 = oracle.grouped_gemm(A, W[3:4], [0, T])
+    g, gs = oracle.gemm(A, W[3])
+    assert np.array_equal(y1, g) and np.array_equal(s1, gs)
