@@ -413,6 +413,22 @@ def main():
         gbs = (4.0 * M * H + 2.0 * H) / (us * 1e-6) / 1e9
         sweep.append({"op": "rmsnorm", "M": M, "H": H, "us": round(us, 2), "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        # grouped (mixture-of-experts) GEMM: the step's M tokens routed to 8
+        # experts of [4096, 4096] with seeded, uneven group sizes
+        E = 8
+        sizes = np.bincount(inputs.rng(12345, 20).integers(0, E, M), minlength=E)
+        offs = torch.tensor(np.concatenate([[0], np.cumsum(sizes)]), dtype=torch.int64, device=dev)
+        We = torch.randn((E, H, H), device=dev).mul_(0.02).to(torch.bfloat16)
+        Ye = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        us = timed(lambda r: B.bi_grouped_gemm(t["Ao"], We, offs, Ye), 10)
+        tf = 2.0 * M * H * H / (us * 1e-6) / 1e12
+        sweep.append({"op": "grouped_gemm_8x4096x4096", "M": M, "group_sizes": sizes.tolist(),
+                      "us": round(us, 2), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        e0 = int(np.argmax(sizes > 0))
+        t0 = int(np.sum(sizes[:e0]))
+        inv_checked += 1
+        inv_passed += int(torch.equal(B.bi_gemm(t["Ao"][t0:t0 + 1], We[e0]), Ye[t0:t0 + 1]))
+        del We, Ye, offs
         # fixed-order reduction of 8 per-rank partial outputs (a row-parallel
         # layer's [M, 4096] at tensor-parallel degree 8) + residual, then RMSNorm
         parts = [torch.randn((M, H), device=dev).to(torch.bfloat16) for _ in range(8)]

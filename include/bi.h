@@ -80,7 +80,8 @@ typedef enum bi_op {
     BI_OP_NVFP4_GEMM = 2,
     BI_OP_RMSNORM = 3,
     BI_OP_NVFP4_QUANT = 4,
-    BI_OP_REDUCE_RMSNORM = 5
+    BI_OP_REDUCE_RMSNORM = 5,
+    BI_OP_GROUPED_GEMM = 6
 } bi_op;
 
 /*
@@ -255,6 +256,30 @@ bi_status bi_reduce_rmsnorm(const void *const *partials, int n_partials, int64_t
                             void *R, int64_t ldr, void *Y, int64_t ldy, int64_t M, int64_t H,
                             void *stream);
 
+/*
+ * bi_grouped_gemm: the grouped GEMM of a mixture-of-experts layer.  The
+ * vLLM-Ascend "Batch Invariance" guide lists MoE layers among the operations
+ * whose results must not depend on batch composition; what batch
+ * composition changes there is how many tokens each expert receives.  Rows
+ * group_offsets[e] .. group_offsets[e+1]-1 of A (tokens sorted by expert) are
+ * multiplied by expert e's weight:
+ *   Y[t] = A[t] . W_e^T, W_e = bf16 [N,K] at W + e*sW (row stride ldw).
+ * Each row is computed exactly as bi_gemm computes it for (N, K) -- the same
+ * tile recipe, MFMA chain and K order -- so Y[t] is bitwise bi_gemm of row t
+ * alone with W_e, whatever the other groups' sizes.
+ *   A: bf16 [T,K], row stride lda.  Y: bf16 [T,N], row stride ldy.
+ *   group_offsets: DEVICE int64 [E+1], group_offsets[0] = 0, ascending,
+ *     group_offsets[E] = T; it is read only by the kernel (no host sync), which
+ *     clamps every offset to [0, T], so malformed offsets never reach memory
+ *     outside A and Y (their rows are then unspecified).  8-byte aligned.
+ *   E >= 1 experts; sW >= (N-1)*ldw + K when E > 1; K % 8 == 0.  T == 0 is
+ *   a no-op.  Work is E * ceil(T/bm) * ceil(N/bn) tiles, those beyond an
+ *   expert's rows exiting at once.
+ */
+bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int64_t sW, void *Y,
+                          int64_t ldy, const int64_t *group_offsets, int64_t E, int64_t T, int64_t N,
+                          int64_t K, void *stream);
+
 /* The *_ex variants take launch options (may be NULL = defaults). */
 bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
                      int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream,
@@ -273,6 +298,9 @@ bi_status bi_reduce_rmsnorm_ex(const void *const *partials, int n_partials, int6
                                const void *residual, int64_t ldres, const void *gamma, float eps,
                                void *R, int64_t ldr, void *Y, int64_t ldy, int64_t M, int64_t H,
                                void *stream, const bi_launch_opts *opts);
+bi_status bi_grouped_gemm_ex(const void *A, int64_t lda, const void *W, int64_t ldw, int64_t sW, void *Y,
+                             int64_t ldy, const int64_t *group_offsets, int64_t E, int64_t T, int64_t N,
+                             int64_t K, void *stream, const bi_launch_opts *opts);
 bi_status bi_nvfp4_quant_ex(const void *X, int64_t ldx, float g, void *Q, void *Q_scales,
                             int64_t ldq, int64_t M, int64_t K, void *stream,
                             const bi_launch_opts *opts);

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libbi.so")
 (BI_OK, BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_ALIGN, BI_ERR_ALIAS, BI_ERR_UNSUPPORTED, BI_ERR_HIP,
  BI_ERR_VALUE) = range(8)
 BI_A_BF16, BI_A_NVFP4 = 0, 1
-BI_OP_GEMM, BI_OP_BMM, BI_OP_NVFP4_GEMM, BI_OP_RMSNORM, BI_OP_NVFP4_QUANT, BI_OP_REDUCE_RMSNORM = range(6)
+(BI_OP_GEMM, BI_OP_BMM, BI_OP_NVFP4_GEMM, BI_OP_RMSNORM, BI_OP_NVFP4_QUANT, BI_OP_REDUCE_RMSNORM,
+ BI_OP_GROUPED_GEMM) = range(7)
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -69,6 +70,8 @@ _SIGS = {
                           _i64, _p, _i64, _i64, _i64, _p],
     "bi_reduce_rmsnorm_ex": [ctypes.POINTER(_p), ctypes.c_int, _i64, _p, _i64, _p, ctypes.c_float,
                              _p, _i64, _p, _i64, _i64, _i64, _p, _p],
+    "bi_grouped_gemm": [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
+    "bi_grouped_gemm_ex": [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
 }
@@ -306,3 +309,25 @@ def bi_reduce_rmsnorm(partials, gamma, eps, residual=None, R=None, Y=None, *, st
                                     _stream(stream), _opts(max_workgroups))
     _raise(st, "bi_reduce_rmsnorm")
     return R, Y
+
+
+def bi_grouped_gemm(A, W, offsets, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
+    """Mixture-of-experts grouped GEMM: rows offsets[e] .. offsets[e+1]-1 of
+    A [T,K] use W[e] [N,K]; offsets is a device int64 tensor [E+1]."""
+    _check2d(A, "A")
+    if W.dim() != 3 or W.stride(2) != 1:
+        raise ValueError("W must be [E,N,K] with unit last stride")
+    T, K = A.shape
+    E, N, K2 = W.shape
+    if K2 != K:
+        raise ValueError("A and W disagree on K")
+    if offsets.dtype != torch.int64 or offsets.dim() != 1 or offsets.shape[0] != E + 1 or not offsets.is_cuda:
+        raise ValueError("offsets must be a device int64 tensor of E+1 entries")
+    if Y is None:
+        Y = torch.empty((T, N), dtype=torch.bfloat16, device=A.device)
+    _check2d(Y, "Y")
+    st = lib().bi_grouped_gemm_ex(_ptr(A), A.stride(0), _ptr(W), W.stride(1), W.stride(0), _ptr(Y),
+                                  Y.stride(0), _ptr(offsets), E, T, N, K, _stream(stream),
+                                  _opts(max_workgroups, tile_variant))
+    _raise(st, "bi_grouped_gemm")
+    return Y

@@ -81,6 +81,7 @@ constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offse
 // shape is the one with the best balance of the two for that N.
 int gemm_variant(int op, int64_t N, int64_t K) {
     (void)K;
+    if (op == BI_OP_GROUPED_GEMM) op = BI_OP_GEMM;  // the dense GEMM's recipe
     if (op == BI_OP_BMM) return 2;      // 256 x 128, 8 wavefronts
     if (N >= 5120)                      // 256 x 256, 8 wavefronts: ping-pong schedule for the
         return op == BI_OP_GEMM ? bi::kPingPongVariant : 12;  // bf16 GEMM, else 3-deep B ring
@@ -129,7 +130,7 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
     // streams 16-column blocks of the weight with no barrier.  It runs the
     // same per-element MFMA chain as the tiled kernel (bits are identical);
     // a forced tile_variant keeps the tiled kernel so the two can be compared.
-    if (op != BI_OP_BMM && in.M <= 16 && a_mode == bi::OPND_BF16_ROWS &&
+    if ((op == BI_OP_GEMM || op == BI_OP_NVFP4_GEMM) && in.M <= 16 && a_mode == bi::OPND_BF16_ROWS &&
         (b_mode == bi::OPND_BF16_ROWS || b_mode == bi::OPND_NVFP4_RAW) &&
         !(opts && opts->tile_variant != 0)) {
         int cus = 0;
@@ -210,7 +211,7 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
     int per_cu = bi::kLdsPerCu / bi::tile_lds_bytes(t);
     if (per_cu < 1) per_cu = 1;
     const int grid = default_grid(a.num_tiles, cus, opts, per_cu);
-    hipError_t e = (variant == bi::kPingPongVariant && a_mode == bi::OPND_BF16_ROWS &&
+    hipError_t e = (variant == bi::kPingPongVariant && a_mode == bi::OPND_BF16_ROWS && !a.group_off &&
                     b_mode == bi::OPND_BF16_ROWS && a.batch == 1)
                        ? bi::launch_pingpong(a, grid, static_cast<hipStream_t>(stream))
                        : bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
@@ -250,7 +251,8 @@ bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
     switch (op) {
         case BI_OP_GEMM:
         case BI_OP_BMM:
-        case BI_OP_NVFP4_GEMM: {
+        case BI_OP_NVFP4_GEMM:
+        case BI_OP_GROUPED_GEMM: {
             if (N <= 0 || K <= 0) return BI_ERR_SHAPE;
             if (op == BI_OP_NVFP4_GEMM ? (K % 32 != 0) : (K % 8 != 0)) return BI_ERR_SHAPE;
             if (op == BI_OP_BMM && N % 8 != 0) return BI_ERR_SHAPE;
@@ -530,6 +532,39 @@ bi_status bi_reduce_rmsnorm(const void *const *partials, int n_partials, int64_t
                             void *stream) {
     return bi_reduce_rmsnorm_ex(partials, n_partials, ldp, residual, ldres, gamma, eps, R, ldr, Y, ldy,
                                 M, H, stream, nullptr);
+}
+
+bi_status bi_grouped_gemm_ex(const void *A, int64_t lda, const void *W, int64_t ldw, int64_t sW, void *Y,
+                             int64_t ldy, const int64_t *group_offsets, int64_t E, int64_t T, int64_t N,
+                             int64_t K, void *stream, const bi_launch_opts *opts) {
+    if (T < 0 || E <= 0 || N <= 0 || K <= 0 || K % 8 != 0) return BI_ERR_SHAPE;
+    if (lda < K || ldw < K || ldy < N || (E > 1 && sW < (N - 1) * ldw + K) || sW < 0) return BI_ERR_SHAPE;
+    if (T > kI32Max || N > kI32Max || K > kI32Max || E > kI32Max || lda >= kMaxLd || ldw >= kMaxLd)
+        return BI_ERR_UNSUPPORTED;
+    if (T == 0) return BI_OK;
+    if (!A || !W || !Y || !group_offsets) return BI_ERR_NULL;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || (reinterpret_cast<uintptr_t>(group_offsets) & 7u) ||
+        lda % 8 || ldw % 8 || sW % 8)
+        return BI_ERR_ALIGN;
+    const Range ry = mat_range(Y, T, N, ldy, 2, 1);
+    const Range rw = mat_range(W, 1, (E - 1) * sW + (N - 1) * ldw + K, 0, 2, 1);
+    const Range ro = mat_range(group_offsets, 1, E + 1, 0, 8, 1);
+    if (overlap(ry, mat_range(A, T, K, lda, 2, 1)) || overlap(ry, rw) || overlap(ry, ro)) return BI_ERR_ALIAS;
+    GemmArgs a{};
+    a.A = A; a.B = W; a.Y = Y;
+    a.lda = lda; a.ldb = ldw; a.ldy = ldy;
+    a.sB = sW;
+    a.M = (int)T; a.N = (int)N; a.K = (int)K; a.batch = (int)E;
+    a.alpha = 1.0f;
+    a.group_off = group_offsets;
+    a.total_rows = T;
+    return run_gemm(bi::OPND_BF16_ROWS, bi::OPND_BF16_ROWS, BI_OP_GROUPED_GEMM, a, stream, opts);
+}
+
+bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int64_t sW, void *Y,
+                          int64_t ldy, const int64_t *group_offsets, int64_t E, int64_t T, int64_t N,
+                          int64_t K, void *stream) {
+    return bi_grouped_gemm_ex(A, lda, W, ldw, sW, Y, ldy, group_offsets, E, T, N, K, stream, nullptr);
 }
 
 }  // extern "C"

@@ -75,6 +75,12 @@ struct GemmArgs {
     int num_tiles;
     float alpha;
     int use_alpha;
+    // Grouped GEMM (mixture of experts): when set, head e is expert e, whose
+    // rows are group_off[e] .. group_off[e+1]-1 of A and Y (device int64
+    // [batch+1], clamped to [0, total_rows]); M is then total_rows, the bound
+    // of any group, and B's head stride sB is the expert stride.
+    const int64_t *group_off;
+    int64_t total_rows;
 };
 
 // Launchers; they return hipSuccess or the launch error.

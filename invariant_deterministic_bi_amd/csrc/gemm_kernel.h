@@ -778,32 +778,43 @@ __global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
         const char *Ab = static_cast<const char *>(p.A) + bh * p.sA * elem_bytes_x2<AMODE>() / 2;
         const char *Bb = static_cast<const char *>(p.B) + bh * p.sB * elem_bytes_x2<BMODE>() / 2;
         uint16_t *Yb = static_cast<uint16_t *>(p.Y) + bh * p.sY;
+        GemmArgs q = p;
+        if (p.group_off) {
+            // expert bh's rows: a tile past them has nothing to do (uniform)
+            int64_t o0 = p.group_off[bh], o1 = p.group_off[bh + 1];
+            o0 = o0 < 0 ? 0 : (o0 > p.total_rows ? p.total_rows : o0);
+            o1 = o1 < o0 ? o0 : (o1 > p.total_rows ? p.total_rows : o1);
+            q.M = static_cast<int>(o1 - o0);
+            if (m0 >= q.M) continue;
+            Ab = static_cast<const char *>(p.A) + o0 * p.lda * elem_bytes_x2<AMODE>() / 2;
+            Yb = static_cast<uint16_t *>(p.Y) + o0 * p.ldy;
+        }
 
         // live 16-row blocks of this wavefront's sub-tile, rounded up to the
         // next instantiated count (wave-uniform)
-        const int rows_left = p.M - m0 - wm * WTM;
+        const int rows_left = q.M - m0 - wm * WTM;
         const int nlive = rows_left <= 0 ? 0 : min(FM, (rows_left + 15) / 16);
         // Compact tiles (valid rows all in the first 16) re-lay the LDS for
         // deep weight prefetch.  The raw-NVFP4 256-column instance skips it:
         // its deep raw ring does not fit the register file beside the full
         // path, and M <= 16 calls take the skinny kernel anyway.  Such tiles
         // run the full path with one live block (same bits).
-        if (p.M - m0 <= 16 && !(BMODE == OPND_NVFP4_RAW && BN >= 256)) {
+        if (q.M - m0 <= 16 && !(BMODE == OPND_NVFP4_RAW && BN >= 256)) {
             // every valid row of the tile is in wavefront row 0's first block
             if (wm == 0)
-                run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1, true>(p, lds, m0, n0, Ab, Bb, Yb);
+                run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1, true>(q, lds, m0, n0, Ab, Bb, Yb);
             else
-                run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0, true>(p, lds, m0, n0, Ab, Bb, Yb);
+                run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0, true>(q, lds, m0, n0, Ab, Bb, Yb);
         } else if (nlive == 0)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0, false>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 0, false>(q, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive == 1 || FM == 1)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1, false>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, 1, false>(q, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive <= 2 || FM == 2)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 2 ? FM : 2), false>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 2 ? FM : 2), false>(q, lds, m0, n0, Ab, Bb, Yb);
         else if (nlive <= 4 || FM <= 4)
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 4 ? FM : 4), false>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, (FM < 4 ? FM : 4), false>(q, lds, m0, n0, Ab, Bb, Yb);
         else
-            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, FM, false>(p, lds, m0, n0, Ab, Bb, Yb);
+            run_tile<BM, BN, WGM, WGN, SA, SB, AMODE, BMODE, FM, false>(q, lds, m0, n0, Ab, Bb, Yb);
     }
 }
 

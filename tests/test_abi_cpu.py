@@ -209,3 +209,28 @@ def test_reduce_rmsnorm_validation():
     assert call(R=RES + 64) == B.BI_ERR_ALIAS                    # partial overlap with the residual
     assert call(res=0, ldres=0, M=0) == B.BI_OK
     assert call(parts=(0, 0), M=0, g=0, R=0, Y=0) == B.BI_OK
+
+
+def test_grouped_gemm_plan_is_the_gemm_plan():
+    for N, K in ((6144, 4096), (4096, 4096), (512, 1024)):
+        g, q = B.plan_query(B.BI_OP_GEMM, N, K), B.plan_query(B.BI_OP_GROUPED_GEMM, N, K)
+        g.pop("op"), q.pop("op")
+        assert g == q
+
+
+def test_grouped_gemm_validation():
+    f = B.lib().bi_grouped_gemm
+    OFF = 0x7000000
+
+    def call(A=A0, lda=512, W=B0, ldw=512, sW=256 * 512, Y=Y0, ldy=256, off=OFF, E=4, T=40, N=256, K=512):
+        return f(A, lda, W, ldw, sW, Y, ldy, off, E, T, N, K, None)
+    assert call(E=0) == B.BI_ERR_SHAPE
+    assert call(K=12, lda=16, ldw=16) == B.BI_ERR_SHAPE
+    assert call(sW=1000) == B.BI_ERR_SHAPE                       # experts overlap
+    assert call(T=-1) == B.BI_ERR_SHAPE
+    assert call(off=0) == B.BI_ERR_NULL
+    assert call(off=OFF + 4) == B.BI_ERR_ALIGN
+    assert call(A=A0 + 8) == B.BI_ERR_ALIGN
+    assert call(Y=B0 + 64) == B.BI_ERR_ALIAS                     # Y over an expert weight
+    assert call(Y=A0 + 1024) == B.BI_ERR_ALIAS
+    assert call(T=0, A=0, W=0, Y=0, off=0) == B.BI_OK
