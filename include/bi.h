@@ -273,8 +273,9 @@ bi_status bi_reduce_rmsnorm(const void *const *partials, int n_partials, int64_t
  *     clamps every offset to [0, T], so malformed offsets never reach memory
  *     outside A and Y (their rows are then unspecified).  8-byte aligned.
  *   E >= 1 experts; sW >= (N-1)*ldw + K when E > 1; K % 8 == 0.  T == 0 is
- *   a no-op.  Work is E * ceil(T/bm) * ceil(N/bn) tiles, those beyond an
- *   expert's rows exiting at once.
+ *   a no-op.  The kernel enumerates only the experts' non-empty tiles (at most
+ *   (ceil(T/bm) + E) * ceil(N/bn)), so any routing spreads evenly over the
+ *   persistent grid.
  */
 bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int64_t sW, void *Y,
                           int64_t ldy, const int64_t *group_offsets, int64_t E, int64_t T, int64_t N,

@@ -202,7 +202,10 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
     GemmArgs a = in;
     a.tiles_m = static_cast<int>((a.M + t.bm - 1) / t.bm);
     a.tiles_n = static_cast<int>((a.N + t.bn - 1) / t.bn);
-    const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n * a.batch;
+    // grouped: the experts' non-empty tiles are enumerated compactly, at most
+    // (ceil(T / bm) + E) * tiles_n of them
+    const int64_t tiles = a.group_off ? (static_cast<int64_t>(a.tiles_m) + a.batch) * a.tiles_n
+                                      : static_cast<int64_t>(a.tiles_m) * a.tiles_n * a.batch;
     if (tiles > kI32Max) return BI_ERR_UNSUPPORTED;
     a.num_tiles = static_cast<int>(tiles);
     int cus = 0;

@@ -769,26 +769,53 @@ __global__ __launch_bounds__(WGM *WGN * 64, 1) void gemm_kernel(GemmArgs p) {
     const bool spread = (G % 8) == 0;
     const int slot = spread ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
 
+    // Grouped mode: tiles are enumerated compactly, expert by expert, each
+    // expert holding ceil(rows / BM) * tiles_n of them; L only grows, so the
+    // walk over the experts' row ranges is resumed, not restarted (scalar,
+    // wave-uniform).  num_tiles is the host's bound (ceil(T / BM) + E) *
+    // tiles_n; a workgroup stops at the first L past the real total.
+    int g_e = 0;
+    int64_t g_pref = 0, g_o0 = 0, g_o1 = 0;
+    auto g_range = [&](int e) {
+        int64_t o0 = p.group_off[e], o1 = p.group_off[e + 1];
+        o0 = o0 < 0 ? 0 : (o0 > p.total_rows ? p.total_rows : o0);
+        o1 = o1 < o0 ? o0 : (o1 > p.total_rows ? p.total_rows : o1);
+        g_o0 = o0;
+        g_o1 = o1;
+    };
+    if (p.group_off) g_range(0);
+
     for (int base = 0; base < p.num_tiles; base += G) {
         const int L = base + slot;
         if (L >= p.num_tiles) break;
         int bh, tm, tn;
-        tile_coords(L, p.tiles_m, p.tiles_n, bh, tm, tn);
-        const int m0 = tm * BM, n0 = tn * BN;
-        const char *Ab = static_cast<const char *>(p.A) + bh * p.sA * elem_bytes_x2<AMODE>() / 2;
-        const char *Bb = static_cast<const char *>(p.B) + bh * p.sB * elem_bytes_x2<BMODE>() / 2;
-        uint16_t *Yb = static_cast<uint16_t *>(p.Y) + bh * p.sY;
         GemmArgs q = p;
+        const char *Ab, *Bb;
+        uint16_t *Yb;
         if (p.group_off) {
-            // expert bh's rows: a tile past them has nothing to do (uniform)
-            int64_t o0 = p.group_off[bh], o1 = p.group_off[bh + 1];
-            o0 = o0 < 0 ? 0 : (o0 > p.total_rows ? p.total_rows : o0);
-            o1 = o1 < o0 ? o0 : (o1 > p.total_rows ? p.total_rows : o1);
-            q.M = static_cast<int>(o1 - o0);
-            if (m0 >= q.M) continue;
-            Ab = static_cast<const char *>(p.A) + o0 * p.lda * elem_bytes_x2<AMODE>() / 2;
-            Yb = static_cast<uint16_t *>(p.Y) + o0 * p.ldy;
+            for (;;) {
+                const int64_t nt = ((g_o1 - g_o0 + BM - 1) / BM) * p.tiles_n;
+                if (L < g_pref + nt) break;
+                g_pref += nt;
+                if (++g_e >= p.batch) break;
+                g_range(g_e);
+            }
+            if (g_e >= p.batch) break;
+            const int l = static_cast<int>(L - g_pref);
+            bh = g_e;
+            tm = l / p.tiles_n;
+            tn = l - tm * p.tiles_n;
+            q.M = static_cast<int>(g_o1 - g_o0);
+            Ab = static_cast<const char *>(p.A) + g_o0 * p.lda * elem_bytes_x2<AMODE>() / 2;
+            Bb = static_cast<const char *>(p.B) + bh * p.sB * elem_bytes_x2<BMODE>() / 2;
+            Yb = static_cast<uint16_t *>(p.Y) + g_o0 * p.ldy;
+        } else {
+            tile_coords(L, p.tiles_m, p.tiles_n, bh, tm, tn);
+            Ab = static_cast<const char *>(p.A) + bh * p.sA * elem_bytes_x2<AMODE>() / 2;
+            Bb = static_cast<const char *>(p.B) + bh * p.sB * elem_bytes_x2<BMODE>() / 2;
+            Yb = static_cast<uint16_t *>(p.Y) + bh * p.sY;
         }
+        const int m0 = tm * BM, n0 = tn * BN;
 
         // live 16-row blocks of this wavefront's sub-tile, rounded up to the
         // next instantiated count (wave-uniform)

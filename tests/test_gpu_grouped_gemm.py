@@ -21,7 +21,8 @@ def offsets_dev(off):
 @pytest.mark.parametrize("E,N,K,sizes", [(8, 512, 1024, [3, 0, 40, 1, 17, 0, 300, 9]),
                                          (4, 6144, 4096, [1, 129, 0, 70]),
                                          (1, 6144, 512, [33]),
-                                         (3, 200, 544, [5, 16, 1])])
+                                         (3, 200, 544, [5, 16, 1]),
+                                         (64, 256, 512, [0] * 20 + [1, 2000] + [0] * 30 + [5] + [0] * 11)])
 def test_grouped_parity_and_rows_alone(E, N, K, sizes):
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     T = int(off[-1])
