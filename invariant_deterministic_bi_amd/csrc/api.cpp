@@ -81,7 +81,14 @@ constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offse
 // shape is the one with the best balance of the two for that N.
 int gemm_variant(int op, int64_t N, int64_t K) {
     (void)K;
-    if (op == BI_OP_GROUPED_GEMM) op = BI_OP_GEMM;  // the dense GEMM's recipe
+    // Grouped GEMM: every expert adds a partial m-tile, so wide n-tiles (fewer
+    // tiles per expert) pay off sooner than for one dense GEMM; every tile
+    // shape gives the same bits, so each row is still bitwise bi_gemm's.
+    if (op == BI_OP_GROUPED_GEMM) {
+        if (N >= 2048) return 12;        // 256 x 256, classic schedule
+        if (N >= 512) return 11;         // 128 x 128, 8 wavefronts
+        op = BI_OP_GEMM;
+    }
     if (op == BI_OP_BMM) return 2;      // 256 x 128, 8 wavefronts
     if (N >= 5120)                      // 256 x 256, 8 wavefronts: ping-pong schedule for the
         return op == BI_OP_GEMM ? bi::kPingPongVariant : 12;  // bf16 GEMM, else 3-deep B ring

@@ -211,11 +211,16 @@ def test_reduce_rmsnorm_validation():
     assert call(parts=(0, 0), M=0, g=0, R=0, Y=0) == B.BI_OK
 
 
-def test_grouped_gemm_plan_is_the_gemm_plan():
-    for N, K in ((6144, 4096), (4096, 4096), (512, 1024)):
+def test_grouped_gemm_plan_shares_the_gemm_chain():
+    """The grouped GEMM's tile may differ from the dense one (every tile shape
+    gives the same bits), but the MFMA block and K step are the same, and the
+    plan is a function of (N, K) alone."""
+    for N, K in ((6144, 4096), (4096, 4096), (1536, 4096), (256, 1024)):
         g, q = B.plan_query(B.BI_OP_GEMM, N, K), B.plan_query(B.BI_OP_GROUPED_GEMM, N, K)
-        g.pop("op"), q.pop("op")
-        assert g == q
+        for key in ("mfma_m", "mfma_n", "mfma_k", "bk"):
+            assert g[key] == q[key]
+        assert q == B.plan_query(B.BI_OP_GROUPED_GEMM, N, K)
+    assert B.plan_query(B.BI_OP_GROUPED_GEMM, 4096, 4096)["bn"] == 256
 
 
 def test_grouped_gemm_validation():
