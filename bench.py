@@ -155,7 +155,7 @@ def summarize(dirs, out, command):
         mean = {k: sum(v) / len(v) for k, v in acc.items()}
         fetch = {g: m for (kind, cn, g), m in mean.items() if kind == "gemm" and cn == "FETCH_SIZE"}
         gate_grid = max(fetch, key=fetch.get) if fetch else None
-        lines.append("# counters, mean per dispatch (KiB)")
+        lines.append("# counters, mean per dispatch (FETCH_SIZE and WRITE_SIZE in KiB, others as read)")
         for (kind, cn, g), m in sorted(mean.items()):
             tag = f"{kind}_grid{g}" if kind == "gemm" else kind
             lines.append(f"{tag}_{cn}_per_dispatch: {m:.1f}")
@@ -174,6 +174,14 @@ def summarize(dirs, out, command):
                 parts += 1
         if parts == 2:
             lines.append(f"traffic_bytes_per_launch: {total:.0f}")
+        g = gate_grid if gate_grid is not None else (max(k[2] for k in mean if k[0] == "gemm")
+                                                       if any(k[0] == "gemm" for k in mean) else None)
+        lds_c, lds_a = mean.get(("gemm", "SQ_LDS_BANK_CONFLICT", g)), mean.get(("gemm", "SQ_LDS_IDX_ACTIVE", g))
+        if lds_c is not None and lds_a:
+            lines.append(f"gate_up_lds_bank_conflict_over_lds_active: {lds_c / lds_a:.4f}")
+        mf, busy = mean.get(("gemm", "SQ_VALU_MFMA_BUSY_CYCLES", g)), mean.get(("gemm", "SQ_BUSY_CYCLES", g))
+        if mf is not None and busy:
+            lines.append(f"gate_up_mfma_busy_over_sq_busy: {mf / busy:.4f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
