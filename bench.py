@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 CALIB_BYTES = 512 << 20     # bytes read (and written) by one calibration copy
-GATE_UP_KERNEL = "pingpong_kernel"   # bf16 GEMM, 256x256 tile, ping-pong schedule
+GATE_UP_KERNEL = "pingpong_kernel<256>"   # bf16 GEMM, 256x256 tile, ping-pong schedule
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_M2048_counters.txt")
 
 
@@ -104,8 +104,8 @@ def read_counters_summary():
 def summarize(dirs, out, command):
     """Condense rocprofv3 CSV output (kernel stats, counters) into text.
 
-    The gate_up GEMM shares its kernel instance with other GEMMs of the step
-    (same tile shape), so its dispatches are told apart by grid size: per
+    The gate_up GEMM's kernel instance (the 256x256 ping-pong kernel) may
+    serve other GEMMs too, so its dispatches are grouped by grid size: per
     grid size the kernel trace gives the mean duration and the counters the
     mean per dispatch, and the gate_up group is the one with the largest
     FETCH_SIZE (the largest weight).  Each counter of that group is scaled by

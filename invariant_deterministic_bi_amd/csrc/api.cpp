@@ -90,6 +90,9 @@ int gemm_variant(int op, int64_t N, int64_t K) {
         op = BI_OP_GEMM;
     }
     if (op == BI_OP_BMM) return 2;      // 256 x 128, 8 wavefronts
+    // 256 x 192 for 5120 <= N < 12288: one more tile per 768 columns keeps
+    // N = 6144 at 256 tiles for 2048 rows (one per compute unit) instead of 192
+    if (op == BI_OP_GEMM && N >= 5120 && N < 12288) return bi::kPingPong192Variant;
     if (N >= 5120)                      // 256 x 256, 8 wavefronts: ping-pong schedule for the
         return op == BI_OP_GEMM ? bi::kPingPongVariant : 12;  // bf16 GEMM, else 3-deep B ring
     if (N >= 2048) return 9;            // 256 x 128, 8 wavefronts, 3-deep A ring
@@ -221,9 +224,10 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
     int per_cu = bi::kLdsPerCu / bi::tile_lds_bytes(t);
     if (per_cu < 1) per_cu = 1;
     const int grid = default_grid(a.num_tiles, cus, opts, per_cu);
-    hipError_t e = (variant == bi::kPingPongVariant && a_mode == bi::OPND_BF16_ROWS && !a.group_off &&
-                    b_mode == bi::OPND_BF16_ROWS && a.batch == 1)
-                       ? bi::launch_pingpong(a, grid, static_cast<hipStream_t>(stream))
+    const bool pp = (variant == bi::kPingPongVariant || variant == bi::kPingPong192Variant) &&
+                    a_mode == bi::OPND_BF16_ROWS && !a.group_off && b_mode == bi::OPND_BF16_ROWS &&
+                    a.batch == 1;
+    hipError_t e = pp ? bi::launch_pingpong(a, t.bn, grid, static_cast<hipStream_t>(stream))
                        : bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;

@@ -43,8 +43,11 @@ constexpr TileShape kTileShapes[] = {
     {256, 256, 2, 4, 2, 3},   // 13: ping-pong schedule (bf16 x bf16, batch 1; else as 12)
     {128, 128, 2, 2, 2, 2},   // 14: 64 KB of LDS, two workgroups per compute unit
     {128, 128, 4, 2, 2, 2},   // 15: the same with eight wavefronts
+    {256, 192, 4, 2, 2, 3},   // 16: 256 x 192, classic schedule
+    {256, 192, 2, 4, 2, 3},   // 17: 256 x 192, ping-pong schedule (bf16 x bf16, batch 1; else as 16)
 };
 constexpr int kPingPongVariant = 13;
+constexpr int kPingPong192Variant = 17;
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 
 // LDS bytes of one workgroup: the two rings, or the padded bf16 output tile
@@ -99,7 +102,7 @@ bool bmm_short_k_ok(int K);
 int bmm_short_k_lds_bytes(int K);
 hipError_t launch_bmm_short_k(const GemmArgs &args, int grid, hipStream_t stream);
 // 256 x 256 tiles, eight wavefronts in a ping-pong schedule; bf16 x bf16, batch 1.
-hipError_t launch_pingpong(const GemmArgs &args, int grid, hipStream_t stream);
+hipError_t launch_pingpong(const GemmArgs &args, int bn, int grid, hipStream_t stream);
 // Direct path for 1 <= M <= 16, bf16 A and bf16 weight [N, K], batch 1: one
 // 64-thread workgroup per 16-column item, fragments loaded into registers.
 hipError_t launch_direct(const GemmArgs &args, int grid, int depth, hipStream_t stream);

@@ -1,5 +1,7 @@
-// Batch-invariant bf16 GEMM, 256 x 256 tiles, eight wavefronts in a
-// ping-pong schedule (tile variant 14 of the plan table).
+// Batch-invariant bf16 GEMM, 256 x BN tiles (BN = 256 or 192), eight
+// wavefronts in a ping-pong schedule.  At BN = 192 each wavefront owns a
+// 128 x 48 block and issues three B loads per memory phase instead of four;
+// everything else below is written for BN = 256.
 //
 // The two wavefronts that share a SIMD (w and w + 4) belong to different
 // groups: group 0 (wavefronts 0..3) owns output rows 0..127 of the tile and
@@ -35,13 +37,23 @@ namespace pingpong {
 
 using namespace gemm_detail;
 
-constexpr int kBM = 256, kBN = 256, kNT = 512;
+constexpr int kBM = 256, kNT = 512;
 constexpr int kHalf = 128 * kRowBytes;    // one 64-column stage of 128 rows: 16 KB
-constexpr int kBStage = 256 * kRowBytes;  // 32 KB
 constexpr int kOffA0 = 0, kOffA1 = 2 * kHalf, kOffB = 4 * kHalf;
-constexpr int kLds = 4 * kHalf + 3 * kBStage;  // 160 KB
-constexpr int kCStride = kBN * 2 + 16;         // padded bf16 output row in LDS
-static_assert(kBM * kCStride <= kLds, "the output tile is staged in the ring space");
+
+// What depends on the tile width BN (256 or 192 columns).
+template <int BN>
+struct Shape {
+    static constexpr int FN = BN / 64;            // 16-column blocks per wavefront
+    static constexpr int BW = BN / 8;             // B rows per wavefront per memory phase
+    static constexpr int BL = BW / 8;             // B DMA instructions per memory phase
+    static constexpr int LOADS = 4 + BL;          // DMA instructions per memory phase
+    static constexpr int BStage = BN * kRowBytes;
+    static constexpr int Lds = 4 * kHalf + 3 * BStage;  // 160 KB at BN = 256, 136 KB at 192
+    static constexpr int CStride = BN * 2 + 16;   // padded bf16 output row in LDS
+    static_assert(BN == 256 || BN == 192, "tile widths of the ping-pong schedule");
+    static_assert(kBM * CStride <= Lds, "the output tile is staged in the ring space");
+};
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -89,8 +101,11 @@ __device__ __forceinline__ void dma8(const i32x4 &rs, char *tile, const DmaLane 
                            0, 0, 0);
 }
 
+template <int BN>
 __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) char lds[kLds];
+    using S = Shape<BN>;
+    constexpr int FN = S::FN;
+    __shared__ __attribute__((aligned(1024))) char lds[S::Lds];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = wave >> 2, j = wave & 3;  // group, column strip
@@ -105,10 +120,10 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
         if (L >= p.num_tiles) break;
         int bh, tm, tn;
         tile_coords(L, p.tiles_m, p.tiles_n, bh, tm, tn);
-        const int m0 = tm * kBM, n0 = tn * kBN;
+        const int m0 = tm * kBM, n0 = tn * BN;
         const uint16_t *Ab = static_cast<const uint16_t *>(p.A) + (int64_t)m0 * p.lda;
         const uint16_t *Bb = static_cast<const uint16_t *>(p.B) + (int64_t)n0 * p.ldb;
-        const int rows_a = min(kBM, p.M - m0), rows_b = min(kBN, p.N - n0);
+        const int rows_a = min(kBM, p.M - m0), rows_b = min(BN, p.N - n0);
         const i32x4 ra = make_rsrc(Ab, (uint32_t)(((int64_t)(rows_a - 1) * p.lda + p.K) * 2));
         const i32x4 rb = make_rsrc(Bb, (uint32_t)(((int64_t)(rows_b - 1) * p.ldb + p.K) * 2));
         DmaLane dla, dlb;
@@ -121,56 +136,74 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
         // and B rows 0..127 of stage t + 3.  Each wavefront takes 32 rows of
         // each.  Stages past the last issue zero-filling loads into the slot
         // they would use, which nobody reads.
+        // B rows rb0, rb0 + 8, ... of one stage: BL instructions.  Bit 3 of
+        // an 8-row group's first row selects the DMA lane offsets; rb0 is
+        // b_row0 + BW * j, so at BW = 24 it alternates with j's parity.
+        auto dma_b = [&](char *b_tile, int rb0, int k0, bool live) {
+            if constexpr (S::BL == 4) {
+                dma8<0>(rb, b_tile, dlb, rb0, k0, p.K, rows_b, p.ldb, live);
+                dma8<1>(rb, b_tile, dlb, rb0 + 8, k0, p.K, rows_b, p.ldb, live);
+                dma8<0>(rb, b_tile, dlb, rb0 + 16, k0, p.K, rows_b, p.ldb, live);
+                dma8<1>(rb, b_tile, dlb, rb0 + 24, k0, p.K, rows_b, p.ldb, live);
+            } else if (j & 1) {
+                dma8<1>(rb, b_tile, dlb, rb0, k0, p.K, rows_b, p.ldb, live);
+                dma8<0>(rb, b_tile, dlb, rb0 + 8, k0, p.K, rows_b, p.ldb, live);
+                dma8<1>(rb, b_tile, dlb, rb0 + 16, k0, p.K, rows_b, p.ldb, live);
+            } else {
+                dma8<0>(rb, b_tile, dlb, rb0, k0, p.K, rows_b, p.ldb, live);
+                dma8<1>(rb, b_tile, dlb, rb0 + 8, k0, p.K, rows_b, p.ldb, live);
+                dma8<0>(rb, b_tile, dlb, rb0 + 16, k0, p.K, rows_b, p.ldb, live);
+            }
+        };
         auto issue = [&](int t) {
             const int sa = t + 2, sbb = g ? t + 2 : t + 3;
             const int a_row0 = g ? 0 : 128;   // tile row of the A half this group loads
-            const int b_row0 = g ? 128 : 0;
+            const int b_row0 = g ? BN / 2 : 0;
             // the A half buffer holds its 128 rows as rows 0..127
             char *a_tile = lds + (g ? kOffA0 : kOffA1) + (sa & 1) * kHalf - a_row0 * kRowBytes;
-            char *b_tile = lds + kOffB + (sbb % 3) * kBStage;
-            const int ra0 = a_row0 + 32 * j, rb0 = b_row0 + 32 * j;
+            char *b_tile = lds + kOffB + (sbb % 3) * S::BStage;
+            const int ra0 = a_row0 + 32 * j, rb0 = b_row0 + S::BW * j;
             dma8<0>(ra, a_tile, dla, ra0, sa * kBK, p.K, rows_a, p.lda, sa < nk);
             dma8<1>(ra, a_tile, dla, ra0 + 8, sa * kBK, p.K, rows_a, p.lda, sa < nk);
             dma8<0>(ra, a_tile, dla, ra0 + 16, sa * kBK, p.K, rows_a, p.lda, sa < nk);
             dma8<1>(ra, a_tile, dla, ra0 + 24, sa * kBK, p.K, rows_a, p.lda, sa < nk);
-            dma8<0>(rb, b_tile, dlb, rb0, sbb * kBK, p.K, rows_b, p.ldb, sbb < nk);
-            dma8<1>(rb, b_tile, dlb, rb0 + 8, sbb * kBK, p.K, rows_b, p.ldb, sbb < nk);
-            dma8<0>(rb, b_tile, dlb, rb0 + 16, sbb * kBK, p.K, rows_b, p.ldb, sbb < nk);
-            dma8<1>(rb, b_tile, dlb, rb0 + 24, sbb * kBK, p.K, rows_b, p.ldb, sbb < nk);
+            dma_b(b_tile, rb0, sbb * kBK, sbb < nk);
         };
 
         // This wavefront's fragments of one stage: fa[K step][16-row block],
         // fb[K step][16-column block].
-        u32x4 fa[2][8], fb[2][4];
-        f32x4 acc[8][4];
+        u32x4 fa[2][8], fb[2][4];  // fb[..][3] unused at BN = 192
+        f32x4 acc[8][FN];
 #pragma unroll
         for (int fm = 0; fm < 8; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // Fragment reads of stage s.  Rows 16 apart share swz (it reads a
         // row's low four bits), so one address per operand and K step serves
         // all its blocks, the block offset going in the instruction.
         const int r16 = lane & 15;
         const uint32_t a_lane = lds0 + (g ? kOffA1 : kOffA0) + r16 * kRowBytes;
-        const uint32_t b_lane = lds0 + kOffB + (64 * j + r16) * kRowBytes;
+        const uint32_t b_lane = lds0 + kOffB + ((BN / 4) * j + r16) * kRowBytes;
         const uint32_t sw0 = swz(r16, lane >> 4) * 16, sw1 = swz(r16, 4 + (lane >> 4)) * 16;
 #define BI_PP_READ(s)                                                                          \
     do {                                                                                       \
         const uint32_t a0 = a_lane + ((s) & 1) * kHalf + sw0, a1 = a_lane + ((s) & 1) * kHalf + sw1; \
-        const uint32_t b0 = b_lane + ((s) % 3) * kBStage + sw0, b1 = b_lane + ((s) % 3) * kBStage + sw1; \
+        const uint32_t b0 = b_lane + ((s) % 3) * S::BStage + sw0, b1 = b_lane + ((s) % 3) * S::BStage + sw1; \
         fa[0][0] = rd128<0 * 2048>(a0); fa[0][1] = rd128<1 * 2048>(a0);                      \
         fa[0][2] = rd128<2 * 2048>(a0); fa[0][3] = rd128<3 * 2048>(a0);                      \
         fa[0][4] = rd128<4 * 2048>(a0); fa[0][5] = rd128<5 * 2048>(a0);                      \
         fa[0][6] = rd128<6 * 2048>(a0); fa[0][7] = rd128<7 * 2048>(a0);                      \
         fb[0][0] = rd128<0 * 2048>(b0); fb[0][1] = rd128<1 * 2048>(b0);                      \
-        fb[0][2] = rd128<2 * 2048>(b0); fb[0][3] = rd128<3 * 2048>(b0);                      \
+        fb[0][2] = rd128<2 * 2048>(b0);                                                      \
+        if constexpr (FN == 4) fb[0][3] = rd128<3 * 2048>(b0);                               \
         fa[1][0] = rd128<0 * 2048>(a1); fa[1][1] = rd128<1 * 2048>(a1);                      \
         fa[1][2] = rd128<2 * 2048>(a1); fa[1][3] = rd128<3 * 2048>(a1);                      \
         fa[1][4] = rd128<4 * 2048>(a1); fa[1][5] = rd128<5 * 2048>(a1);                      \
         fa[1][6] = rd128<6 * 2048>(a1); fa[1][7] = rd128<7 * 2048>(a1);                      \
         fb[1][0] = rd128<0 * 2048>(b1); fb[1][1] = rd128<1 * 2048>(b1);                      \
-        fb[1][2] = rd128<2 * 2048>(b1); fb[1][3] = rd128<3 * 2048>(b1);                      \
+        fb[1][2] = rd128<2 * 2048>(b1);                                                      \
+        if constexpr (FN == 4) fb[1][3] = rd128<3 * 2048>(b1);                               \
     } while (0)
 // The reads are complete, and the compiler may not use their registers
 // before this point.
@@ -183,14 +216,15 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
                      : "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fa[1][2]), "+v"(fa[1][3]),         \
                        "+v"(fa[1][4]), "+v"(fa[1][5]), "+v"(fa[1][6]), "+v"(fa[1][7])::"memory"); \
         asm volatile(""                                                                        \
-                     : "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[0][2]), "+v"(fb[0][3]),         \
-                       "+v"(fb[1][0]), "+v"(fb[1][1]), "+v"(fb[1][2]), "+v"(fb[1][3])::"memory"); \
+                     : "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[0][2]),                         \
+                       "+v"(fb[1][0]), "+v"(fb[1][1]), "+v"(fb[1][2])::"memory");              \
+        if constexpr (FN == 4) asm volatile("" : "+v"(fb[0][3]), "+v"(fb[1][3])::"memory");    \
     } while (0)
 #define BI_PP_COMPUTE()                                                                        \
     do {                                                                                       \
         _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                       \
         _Pragma("unroll") for (int fm = 0; fm < 8; ++fm)                                       \
-        _Pragma("unroll") for (int fn = 0; fn < 4; ++fn)                                       \
+        _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                      \
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                             \
                 __builtin_bit_cast(bf16x8, fa[ks][fm]), __builtin_bit_cast(bf16x8, fb[ks][fn]), \
                 acc[fm][fn], 0, 0, 0);                                                         \
@@ -200,12 +234,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
         // first half of B(2)); group 0's step -3 loads only B(0)'s first half
         // (its A1(-1) half is a stage that does not exist).  Then everything
         // lands, and group 0 reads its fragments of stage 0.
-        if (g == 0) {
-            dma8<0>(rb, lds + kOffB, dlb, 32 * j, 0, p.K, rows_b, p.ldb, nk > 0);
-            dma8<1>(rb, lds + kOffB, dlb, 32 * j + 8, 0, p.K, rows_b, p.ldb, nk > 0);
-            dma8<0>(rb, lds + kOffB, dlb, 32 * j + 16, 0, p.K, rows_b, p.ldb, nk > 0);
-            dma8<1>(rb, lds + kOffB, dlb, 32 * j + 24, 0, p.K, rows_b, p.ldb, nk > 0);
-        }
+        if (g == 0) dma_b(lds + kOffB, S::BW * j, 0, nk > 0);
         issue(-2);
         issue(-1);
         wait_vmcnt<0>();
@@ -227,7 +256,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
             BI_PP_READ(0);
             issue(0);
             BI_PP_SETTLE();
-            wait_vmcnt<8>();
+            wait_vmcnt<S::LOADS>();
             lds_barrier();
         }
         // sched_barrier(0) keeps the compiler from moving MFMAs (which touch
@@ -241,7 +270,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
             BI_PP_READ(t + 1);
             issue(t + g);
             BI_PP_SETTLE();
-            wait_vmcnt<8>();
+            wait_vmcnt<S::LOADS>();
             __builtin_amdgcn_sched_barrier(0);
             lds_barrier();
         }
@@ -260,22 +289,22 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
 #pragma unroll
         for (int fm = 0; fm < 8; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn) {
-                const int col = 64 * j + fn * 16 + (lane & 15);
+            for (int fn = 0; fn < FN; ++fn) {
+                const int col = (BN / 4) * j + fn * 16 + (lane & 15);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 128 * g + fm * 16 + (lane >> 4) * 4 + i;
-                    *reinterpret_cast<uint16_t *>(ct + row * kCStride + col * 2) =
+                    *reinterpret_cast<uint16_t *>(ct + row * S::CStride + col * 2) =
                         (uint16_t)f32_to_bf16_rne(acc[fm][fn][i]);
                 }
             }
         __syncthreads();
-        constexpr int CPR = kBN / 8;
+        constexpr int CPR = BN / 8;
         uint16_t *Yb = static_cast<uint16_t *>(p.Y);
         for (int q = tid; q < rows_a * CPR; q += kNT) {
             const int row = q / CPR, c8 = q % CPR;
             const int col = n0 + c8 * 8;
-            const uint4 v = *reinterpret_cast<const uint4 *>(ct + row * kCStride + c8 * 16);
+            const uint4 v = *reinterpret_cast<const uint4 *>(ct + row * S::CStride + c8 * 16);
             uint16_t *dst = Yb + (int64_t)(m0 + row) * p.ldy + col;
             if (col + 8 <= p.N && (((uintptr_t)dst) & 15) == 0) {
                 *reinterpret_cast<uint4 *>(dst) = v;
@@ -292,9 +321,14 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
 
 }  // namespace pingpong
 
-hipError_t launch_pingpong(const GemmArgs &a, int grid, hipStream_t s) {
-    if (a.batch != 1 || grid < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pingpong::pingpong_kernel, dim3(grid), dim3(pingpong::kNT), 0, s, a);
+hipError_t launch_pingpong(const GemmArgs &a, int bn, int grid, hipStream_t s) {
+    if (a.batch != 1 || grid < 1 || a.group_off) return hipErrorInvalidValue;
+    if (bn == 256)
+        hipLaunchKernelGGL(pingpong::pingpong_kernel<256>, dim3(grid), dim3(pingpong::kNT), 0, s, a);
+    else if (bn == 192)
+        hipLaunchKernelGGL(pingpong::pingpong_kernel<192>, dim3(grid), dim3(pingpong::kNT), 0, s, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

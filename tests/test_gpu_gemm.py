@@ -216,25 +216,27 @@ def test_every_tile_shape_gives_the_same_bits():
         gemm(Ad, Wd, tile_variant=len(shapes) + 1)
 
 
-def test_pingpong_schedule_matches_classic_schedule():
-    """The ping-pong 256 x 256 kernel (tile variant 14) against the classic
-    256 x 256 schedule (variant 13): ragged M and N, K % 64 == 32, several
-    grid caps, each run repeated (a phase-ordering race would show as a rare
-    mismatch)."""
+@pytest.mark.parametrize("pp,classic,bn", [(14, 13, 256), (18, 17, 192)])
+def test_pingpong_schedule_matches_classic_schedule(pp, classic, bn):
+    """The ping-pong kernels (256 x 256: tile variant 14; 256 x 192: 18)
+    against the classic schedule of the same shape (13; 17): ragged M and N,
+    K % 64 == 32, several grid caps, each run repeated (a phase-ordering race
+    would show as a rare mismatch)."""
     shapes = B.tile_shapes()
-    pp = 14
-    assert shapes[pp - 1]["bm"] == 256 and shapes[pp - 1]["bn"] == 256
-    for (M, N, K) in [(1000, 2600, 4160), (513, 1300, 2080), (2048, 6144, 4096)]:
+    assert shapes[pp - 1]["bm"] == 256 and shapes[pp - 1]["bn"] == bn
+    assert shapes[classic - 1]["bm"] == 256 and shapes[classic - 1]["bn"] == bn
+    for (M, N, K) in [(1000, 2600, 4160), (513, 1300, 2080), (2048, 6144, 4096), (77, 200, 544)]:
         A = inputs.randn_bf16((M, K), tag=(75, M, N))
         W = inputs.randn_bf16((N, K), 0.02, tag=(76, M, N))
         Ad, Wd = dev(A), dev(W)
-        y = host(gemm(Ad, Wd, tile_variant=13))
+        y = host(gemm(Ad, Wd, tile_variant=classic))
         for mw in (0, 7, 64):
             for rep in range(2):
-                note(f"pingpong M={M} N={N} K={K} grid cap {mw} rep {rep}")
+                note(f"pingpong {bn} M={M} N={N} K={K} grid cap {mw} rep {rep}")
                 assert np.array_equal(host(gemm(Ad, Wd, tile_variant=pp, max_workgroups=mw)), y), (M, N, K, mw, rep)
-    ref, s = oracle.gemm(A[[0, 511, 2047]], W)
-    assert_within_tol(host(gemm(Ad, Wd, tile_variant=pp))[[0, 511, 2047]], ref, s, "pingpong")
+        if M == 2048:
+            ref, s = oracle.gemm(A[[0, 511, 2047]], W)
+            assert_within_tol(host(gemm(Ad, Wd, tile_variant=pp))[[0, 511, 2047]], ref, s, "pingpong")
 
 
 @pytest.mark.parametrize("N,K", [(200, 544), (4100, 4128), (256, 96), (6144, 4096), (8200, 512)])
