@@ -224,7 +224,8 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
     int per_cu = bi::kLdsPerCu / bi::tile_lds_bytes(t);
     if (per_cu < 1) per_cu = 1;
     const int grid = default_grid(a.num_tiles, cus, opts, per_cu);
-    const bool pp = (variant == bi::kPingPongVariant || variant == bi::kPingPong192Variant) &&
+    const bool pp = (variant == bi::kPingPongVariant || variant == bi::kPingPong192Variant ||
+                     variant == bi::kPingPong128Variant) &&
                     a_mode == bi::OPND_BF16_ROWS && !a.group_off && b_mode == bi::OPND_BF16_ROWS &&
                     a.batch == 1;
     hipError_t e = pp ? bi::launch_pingpong(a, t.bn, grid, static_cast<hipStream_t>(stream))

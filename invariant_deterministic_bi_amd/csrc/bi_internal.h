@@ -45,9 +45,11 @@ constexpr TileShape kTileShapes[] = {
     {128, 128, 4, 2, 2, 2},   // 15: the same with eight wavefronts
     {256, 192, 4, 2, 2, 3},   // 16: 256 x 192, classic schedule
     {256, 192, 2, 4, 2, 3},   // 17: 256 x 192, ping-pong schedule (bf16 x bf16, batch 1; else as 16)
+    {256, 128, 2, 4, 2, 3},   // 18: 256 x 128, ping-pong schedule (bf16 x bf16, batch 1; else as 9)
 };
 constexpr int kPingPongVariant = 13;
 constexpr int kPingPong192Variant = 17;
+constexpr int kPingPong128Variant = 18;
 constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 
 // LDS bytes of one workgroup: the two rings, or the padded bf16 output tile

@@ -868,7 +868,7 @@ hipError_t launch_variant(const GemmArgs &a, int grid, hipStream_t s) {
 
 template <int AM, int BMD>
 hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStream_t s) {
-    static_assert(kNumTileShapes == 18, "one case per compiled tile shape");
+    static_assert(kNumTileShapes == 19, "one case per compiled tile shape");
     switch (r.variant) {
         case 0: return launch_variant<AM, BMD, 0>(a, grid, s);
         case 1: return launch_variant<AM, BMD, 1>(a, grid, s);
@@ -888,6 +888,7 @@ hipError_t launch_modes(const GemmRecipe &r, const GemmArgs &a, int grid, hipStr
         case 15: return launch_variant<AM, BMD, 15>(a, grid, s);
         case 16: return launch_variant<AM, BMD, 16>(a, grid, s);
         case kPingPong192Variant: return launch_variant<AM, BMD, 16>(a, grid, s);  // same shape, classic schedule
+        case kPingPong128Variant: return launch_variant<AM, BMD, 9>(a, grid, s);   // same shape, classic schedule
         default: return hipErrorInvalidValue;
     }
 }

@@ -1,7 +1,7 @@
-// Batch-invariant bf16 GEMM, 256 x BN tiles (BN = 256 or 192), eight
-// wavefronts in a ping-pong schedule.  At BN = 192 each wavefront owns a
-// 128 x 48 block and issues three B loads per memory phase instead of four;
-// everything else below is written for BN = 256.
+// Batch-invariant bf16 GEMM, 256 x BN tiles (BN = 256, 192 or 128), eight
+// wavefronts in a ping-pong schedule.  Below BN = 256 each wavefront owns a
+// 128 x BN/4 block and issues BN/64 B loads per memory phase instead of
+// four; everything else below is written for BN = 256.
 //
 // The two wavefronts that share a SIMD (w and w + 4) belong to different
 // groups: group 0 (wavefronts 0..3) owns output rows 0..127 of the tile and
@@ -51,7 +51,7 @@ struct Shape {
     static constexpr int BStage = BN * kRowBytes;
     static constexpr int Lds = 4 * kHalf + 3 * BStage;  // 160 KB at BN = 256, 136 KB at 192
     static constexpr int CStride = BN * 2 + 16;   // padded bf16 output row in LDS
-    static_assert(BN == 256 || BN == 192, "tile widths of the ping-pong schedule");
+    static_assert(BN == 256 || BN == 192 || BN == 128, "tile widths of the ping-pong schedule");
     static_assert(kBM * CStride <= Lds, "the output tile is staged in the ring space");
 };
 
@@ -145,6 +145,9 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
                 dma8<1>(rb, b_tile, dlb, rb0 + 8, k0, p.K, rows_b, p.ldb, live);
                 dma8<0>(rb, b_tile, dlb, rb0 + 16, k0, p.K, rows_b, p.ldb, live);
                 dma8<1>(rb, b_tile, dlb, rb0 + 24, k0, p.K, rows_b, p.ldb, live);
+            } else if constexpr (S::BL == 2) {
+                dma8<0>(rb, b_tile, dlb, rb0, k0, p.K, rows_b, p.ldb, live);
+                dma8<1>(rb, b_tile, dlb, rb0 + 8, k0, p.K, rows_b, p.ldb, live);
             } else if (j & 1) {
                 dma8<1>(rb, b_tile, dlb, rb0, k0, p.K, rows_b, p.ldb, live);
                 dma8<0>(rb, b_tile, dlb, rb0 + 8, k0, p.K, rows_b, p.ldb, live);
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
 
         // This wavefront's fragments of one stage: fa[K step][16-row block],
         // fb[K step][16-column block].
-        u32x4 fa[2][8], fb[2][4];  // fb[..][3] unused at BN = 192
+        u32x4 fa[2][8], fb[2][4];  // fb[..][FN..3] unused below BN = 256
         f32x4 acc[8][FN];
 #pragma unroll
         for (int fm = 0; fm < 8; ++fm)
@@ -195,14 +198,14 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
         fa[0][4] = rd128<4 * 2048>(a0); fa[0][5] = rd128<5 * 2048>(a0);                      \
         fa[0][6] = rd128<6 * 2048>(a0); fa[0][7] = rd128<7 * 2048>(a0);                      \
         fb[0][0] = rd128<0 * 2048>(b0); fb[0][1] = rd128<1 * 2048>(b0);                      \
-        fb[0][2] = rd128<2 * 2048>(b0);                                                      \
+        if constexpr (FN >= 3) fb[0][2] = rd128<2 * 2048>(b0);                               \
         if constexpr (FN == 4) fb[0][3] = rd128<3 * 2048>(b0);                               \
         fa[1][0] = rd128<0 * 2048>(a1); fa[1][1] = rd128<1 * 2048>(a1);                      \
         fa[1][2] = rd128<2 * 2048>(a1); fa[1][3] = rd128<3 * 2048>(a1);                      \
         fa[1][4] = rd128<4 * 2048>(a1); fa[1][5] = rd128<5 * 2048>(a1);                      \
         fa[1][6] = rd128<6 * 2048>(a1); fa[1][7] = rd128<7 * 2048>(a1);                      \
         fb[1][0] = rd128<0 * 2048>(b1); fb[1][1] = rd128<1 * 2048>(b1);                      \
-        fb[1][2] = rd128<2 * 2048>(b1);                                                      \
+        if constexpr (FN >= 3) fb[1][2] = rd128<2 * 2048>(b1);                               \
         if constexpr (FN == 4) fb[1][3] = rd128<3 * 2048>(b1);                               \
     } while (0)
 // The reads are complete, and the compiler may not use their registers
@@ -215,9 +218,8 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
         asm volatile(""                                                                        \
                      : "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fa[1][2]), "+v"(fa[1][3]),         \
                        "+v"(fa[1][4]), "+v"(fa[1][5]), "+v"(fa[1][6]), "+v"(fa[1][7])::"memory"); \
-        asm volatile(""                                                                        \
-                     : "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[0][2]),                         \
-                       "+v"(fb[1][0]), "+v"(fb[1][1]), "+v"(fb[1][2])::"memory");              \
+        asm volatile("" : "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[1][0]), "+v"(fb[1][1])::"memory"); \
+        if constexpr (FN >= 3) asm volatile("" : "+v"(fb[0][2]), "+v"(fb[1][2])::"memory");    \
         if constexpr (FN == 4) asm volatile("" : "+v"(fb[0][3]), "+v"(fb[1][3])::"memory");    \
     } while (0)
 #define BI_PP_COMPUTE()                                                                        \
@@ -327,6 +329,8 @@ hipError_t launch_pingpong(const GemmArgs &a, int bn, int grid, hipStream_t s) {
         hipLaunchKernelGGL(pingpong::pingpong_kernel<256>, dim3(grid), dim3(pingpong::kNT), 0, s, a);
     else if (bn == 192)
         hipLaunchKernelGGL(pingpong::pingpong_kernel<192>, dim3(grid), dim3(pingpong::kNT), 0, s, a);
+    else if (bn == 128)
+        hipLaunchKernelGGL(pingpong::pingpong_kernel<128>, dim3(grid), dim3(pingpong::kNT), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -216,10 +216,11 @@ def test_every_tile_shape_gives_the_same_bits():
         gemm(Ad, Wd, tile_variant=len(shapes) + 1)
 
 
-@pytest.mark.parametrize("pp,classic,bn", [(14, 13, 256), (18, 17, 192)])
+@pytest.mark.parametrize("pp,classic,bn", [(14, 13, 256), (18, 17, 192), (19, 10, 128)])
 def test_pingpong_schedule_matches_classic_schedule(pp, classic, bn):
-    """The ping-pong kernels (256 x 256: tile variant 14; 256 x 192: 18)
-    against the classic schedule of the same shape (13; 17): ragged M and N,
+    """The ping-pong kernels (256 x 256: tile variant 14; 256 x 192: 18;
+    256 x 128: 19) against the classic schedule of the same shape (13; 17;
+    10): ragged M and N,
     K % 64 == 32, several grid caps, each run repeated (a phase-ordering race
     would show as a rare mismatch)."""
     shapes = B.tile_shapes()
