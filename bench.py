@@ -15,9 +15,10 @@ of the step over the measured step time).  `roofline` is for the dominant
 kernel, the bf16 gate_up GEMM; its duration is measured with HIP events on
 the stream it is launched on, and `traffic` comes from the committed
 counter summary in profiles/ when that was taken with the current kernel
-sources.  `sweep` adds per-op figures at M = 1 and 16 (HBM GB/s with >= 1
-GiB of rotating weight copies, so the 256 MB last-level cache cannot serve
-them) and at the step's M.  `invariance` counts bitwise checks of small-M
+sources.  `sweep` adds per-op figures at M = 1, 16, 64, 256 and 1024 for the dense
+linears (HBM GB/s and TFLOP/s with >= 1 GiB of rotating weight copies, so
+the 256 MB last-level cache cannot serve them), at M = 1 and 16 for the NVFP4
+GEMM, and at the step's M for every op.  `invariance` counts bitwise checks of small-M
 rows against the step's rows and of repeated steps.  `cpu_baseline` times
 the fp64 oracle on a bounded sample of the same step.
 
@@ -352,20 +353,22 @@ def main():
                  ("down", t["Wdn"], t["Adn"], out["Ydn"], Kdn)]
         for name, W, Afull, Yfull, K in specs:
             N = W.shape[0]
-            ref16 = Yfull[:16].clone()
+            ref = Yfull[:1024].clone()
             ncopy = max(2, int(np.ceil((1 << 30) / (W.numel() * 2))))
             copies = [W] + [W.clone() for _ in range(ncopy - 1)]
-            for m in (1, 16):
+            for m in (1, 16, 64, 256, 1024):
                 A = Afull[:m]
                 Y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
-                us = timed(lambda r: B.bi_gemm(A, copies[r % ncopy], Y), 20 * ncopy)
+                us = timed(lambda r: B.bi_gemm(A, copies[r % ncopy], Y), (20 if m <= 64 else 4) * ncopy)
                 byt = 2.0 * (m * K + N * K + m * N)
                 gbs = byt / (us * 1e-6) / 1e9
+                tf = 2.0 * m * N * K / (us * 1e-6) / 1e12
                 sweep.append({"op": name, "N": N, "K": K, "M": m, "us": round(us, 2),
                               "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                              "TFLOP/s": round(2.0 * m * N * K / (us * 1e-6) / 1e12, 3)})
+                              "TFLOP/s": round(tf, 3), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+                # rows 0 .. m-1 computed with M = m equal the step's rows
                 inv_checked += 1
-                inv_passed += int(torch.equal(Y, ref16[:m]))
+                inv_passed += int(torch.equal(Y, ref[:m]))
             del copies
             torch.cuda.empty_cache()
         # NVFP4 gate_up at M = 1, 16 (rotating weight copies)
