@@ -319,21 +319,25 @@ __device__ __forceinline__ i32x4 ror8(const i32x4 &v) {  // lane i <- lane i ^ 8
 }
 
 // AP: A packed two chunks per instruction (M <= 8).  D: chunk pairs in flight
-// (a divisor of the pair count ceil(K / 64), chosen by the host).
-template <int AP, int D>
+// (a divisor of the pair count ceil(K / 64), chosen by the host).  RB: 16-row
+// blocks of A (M <= 16 * RB); each block has its own accumulator and runs the
+// same chain, one MFMA per chunk, against the same weight fragments.
+template <int AP, int D, int RB = 1>
 __global__ __launch_bounds__(64) void direct_kernel(GemmArgs p) {
-    constexpr int AL = AP ? 1 : 2;  // A loads per pair; the weight takes two
+    static_assert(RB == 1 || !AP, "two-chunk A packing is for M <= 8");
+    constexpr int AL = AP ? 1 : 2 * RB;  // A loads per pair; the weight takes two
     const int lane = threadIdx.x;
     const int r = lane & 15, sub = lane >> 4;
     const int items = (p.N + 15) >> 4;
     const int np = (p.K + 63) >> 6;  // chunk pairs: 2 * ceil(K / 64) chunks
     const int my_items = (items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const i32x4 ra = make_rsrc(p.A, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
-    // byte offset of a lane's 16 bytes within pair 0, and its first K column
+    // byte offset of a lane's 16 bytes within pair 0, and its first K column;
+    // load j is row block j / 2, chunk j % 2 (unpacked)
     int a_lane[AL], a_kl[AL];
 #pragma unroll
     for (int j = 0; j < AL; ++j) {
-        const int row = AP ? (r & 7) : r, ch = AP ? (r >> 3) : j;
+        const int row = AP ? (r & 7) : r + 16 * (j >> 1), ch = AP ? (r >> 3) : (j & 1);
         a_lane[j] = row < p.M ? (int)(row * p.lda * 2) + 64 * ch + 16 * sub : kMark;
         a_kl[j] = 32 * ch + 8 * sub;
     }
@@ -380,26 +384,34 @@ __global__ __launch_bounds__(64) void direct_kernel(GemmArgs p) {
     for (int d = 0; d < D; ++d) issue(as[d], ws[d]);
     uint16_t *Y = static_cast<uint16_t *>(p.Y);
     for (int t = 0; t < my_items; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int pb = 0; pb < np; pb += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                const i32x4 a1 = AP ? ror8(as[d][0]) : as[d][AL - 1];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as[d][0]),
-                                                              __builtin_bit_cast(bf16x8, ws[d][0]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                              __builtin_bit_cast(bf16x8, ws[d][1]), acc, 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    const i32x4 a0 = as[d][AP ? 0 : 2 * b];
+                    const i32x4 a1 = AP ? ror8(as[d][0]) : as[d][2 * b + 1];
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                                     __builtin_bit_cast(bf16x8, ws[d][0]), acc[b], 0, 0, 0);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                                     __builtin_bit_cast(bf16x8, ws[d][1]), acc[b], 0, 0, 0);
+                }
                 issue(as[d], ws[d]);
             }
         }
-        // lane holds rows 4*sub .. 4*sub+3 of column n0 + r
+        // lane holds rows 16*b + 4*sub .. +3 of column n0 + r
         const int col = ((int)blockIdx.x + t * (int)gridDim.x) * 16 + r;
         if (col < p.N) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * sub + i;
-                if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[i]);
-            }
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * b + 4 * sub + i;
+                    if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[b][i]);
+                }
         }
     }
 }
@@ -412,6 +424,19 @@ hipError_t launch_ap(const GemmArgs &a, int d, int grid, hipStream_t s) {
         case 4: hipLaunchKernelGGL((direct_kernel<AP, 4>), dim3(grid), dim3(64), 0, s, a); break;
         case 2: hipLaunchKernelGGL((direct_kernel<AP, 2>), dim3(grid), dim3(64), 0, s, a); break;
         case 1: hipLaunchKernelGGL((direct_kernel<AP, 1>), dim3(grid), dim3(64), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// RB row blocks (M <= 16 * RB), unpacked A; the register budget caps D.
+template <int RB>
+hipError_t launch_rb(const GemmArgs &a, int d, int grid, hipStream_t s) {
+    switch (d) {
+        case 8: hipLaunchKernelGGL((direct_kernel<0, 8, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((direct_kernel<0, 4, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((direct_kernel<0, 2, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((direct_kernel<0, 1, RB>), dim3(grid), dim3(64), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -776,7 +801,9 @@ hipError_t launch_direct_nvfp4(const GemmArgs &a, int grid, int depth, hipStream
 }
 
 hipError_t launch_direct(const GemmArgs &a, int grid, int depth, hipStream_t s) {
-    if (a.M < 1 || a.M > 16 || grid < 1) return hipErrorInvalidValue;
+    if (a.M < 1 || a.M > 64 || grid < 1) return hipErrorInvalidValue;
+    if (a.M > 32) return direct::launch_rb<4>(a, pick_depth((a.K + 63) / 64, depth, 4, 4), grid, s);
+    if (a.M > 16) return direct::launch_rb<2>(a, pick_depth((a.K + 63) / 64, depth, 8, 8), grid, s);
     const int d = pick_depth((a.K + 63) / 64, depth, a.K >= 8192 ? 16 : 8, 16);
     return a.M <= 8 ? direct::launch_ap<1>(a, d, grid, s) : direct::launch_ap<0>(a, d, grid, s);
 }

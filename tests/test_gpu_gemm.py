@@ -242,20 +242,21 @@ def test_pingpong_schedule_matches_classic_schedule(pp, classic, bn):
 
 @pytest.mark.parametrize("N,K", [(200, 544), (4100, 4128), (256, 96), (6144, 4096), (8200, 512)])
 def test_small_m_path_matches_tiled_kernel(N, K):
-    """M <= 16 runs the direct kernels (8- or 16-column items streamed into
-    registers; A in LDS or loaded with the weight).  Their rows must be
+    """M <= 64 runs the direct kernels (8- or 16-column items streamed into
+    registers; A in LDS or loaded with the weight; above 16 rows, two or
+    four 16-row blocks of A per weight fragment).  Their rows must be
     bitwise the tiled kernel's (forced with tile_variant) and the full-batch
     rows, for ragged N, K % 64 == 32 (the trailing zero-filled chunk), a
     strided A, capped wavefront counts and every pipeline depth; and within
     the oracle tolerance."""
-    Mmax = 40
+    Mmax = 72
     W = inputs.randn_bf16((N, K), 0.02, tag=(951, N, K))
     Wd = dev(W)
     Ad = dev(inputs.randn_bf16((Mmax, K + 24), tag=(950, N, K)))[:, :K]   # row stride K + 24
     A = host(Ad)
     note(f"skinny N={N} K={K} full")
     yfull = host(gemm(Ad, Wd))
-    for M in (1, 2, 3, 5, 8, 9, 16):
+    for M in (1, 2, 3, 5, 8, 9, 16, 17, 31, 32, 33, 40):
         note(f"skinny N={N} K={K} M={M}")
         ys = host(gemm(Ad[:M], Wd))
         yt = host(gemm(Ad[:M], Wd, tile_variant=1))
@@ -265,9 +266,18 @@ def test_small_m_path_matches_tiled_kernel(N, K):
             assert np.array_equal(host(gemm(Ad[:M], Wd, max_workgroups=mw)), ys), (M, mw)
         for depth in (1, 2, 4, 32):
             assert np.array_equal(host(gemm(Ad[:M], Wd, pipeline_depth=depth)), ys), (M, depth)
+    for M in (48, 64):
+        note(f"skinny N={N} K={K} M={M}")
+        ys = host(gemm(Ad[:M], Wd))
+        assert np.array_equal(ys, host(gemm(Ad[:M], Wd, tile_variant=1))), f"skinny vs tiled, M={M}"
+        assert np.array_equal(ys, yfull[:M]), f"skinny vs full batch, M={M}"
+        assert np.array_equal(host(gemm(Ad[:M], Wd, max_workgroups=3)), ys), M
     rows = [0, 4, 15]
     ref, s = oracle.gemm(A[rows], W)
     assert_within_tol(host(gemm(Ad[:16], Wd))[rows], ref, s, f"skinny N={N} K={K}")
+    rows = [16, 33, 63]
+    ref, s = oracle.gemm(A[rows], W)
+    assert_within_tol(host(gemm(Ad[:64], Wd))[rows], ref, s, f"direct 64 rows N={N} K={K}")
 
 
 @pytest.mark.parametrize("N,K", [(1000, 4160), (1000, 4096), (520, 1024)])
