@@ -17,7 +17,7 @@ the stream it is launched on, and `traffic` comes from the committed
 counter summary in profiles/ when that was taken with the current kernel
 sources.  `sweep` adds per-op figures at M = 1, 16, 64, 256 and 1024 for the dense
 linears (HBM GB/s and TFLOP/s with >= 1 GiB of rotating weight copies, so
-the 256 MB last-level cache cannot serve them), at M = 1 and 16 for the NVFP4
+the 256 MB last-level cache cannot serve them), at M = 1, 16 and 64 for the NVFP4
 GEMM, and at the step's M for every op.  `invariance` counts bitwise checks of small-M
 rows against the step's rows and of repeated steps.  `cpu_baseline` times
 the fp64 oracle on a bounded sample of the same step.
@@ -375,8 +375,8 @@ def main():
         ncopy = 8
         w4c = [t["W4"]] + [t["W4"].clone() for _ in range(ncopy - 1)]
         s4c = [t["W4s"]] + [t["W4s"].clone() for _ in range(ncopy - 1)]
-        ref16 = out["Y4"][:16].clone()
-        for m in (1, 16):
+        ref16 = out["Y4"][:64].clone()
+        for m in (1, 16, 64):
             A = out["Xn2"][:m]
             Y = torch.empty((m, Ngu), dtype=torch.bfloat16, device=dev)
             us = timed(lambda r: B.bi_nvfp4_gemm(A, w4c[r % ncopy], s4c[r % ncopy], alpha4, Y), 24)

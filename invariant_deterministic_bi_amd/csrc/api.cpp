@@ -218,6 +218,20 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         hipError_t e = bi::launch_direct(in, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? BI_OK : BI_ERR_HIP;
     }
+    // NVFP4 weight, bf16 A, 16 < M <= 64, K % 128 == 0: the register-streaming
+    // NVFP4 kernel with two or four 16-row blocks; each decoded weight
+    // fragment feeds every block's chain (the tiled kernel's).
+    if (op == BI_OP_NVFP4_GEMM && in.M > 16 && in.M <= 64 && in.K % 128 == 0 &&
+        a_mode == bi::OPND_BF16_ROWS && b_mode == bi::OPND_NVFP4_RAW && !(opts && opts->tile_variant != 0)) {
+        int cus = 0;
+        bi_status st = device_cus(&cus);
+        if (st != BI_OK) return st;
+        const int items = static_cast<int>((in.N + 15) / 16);
+        const int grid = default_grid(items, cus, opts, 16);
+        hipError_t e = bi::launch_direct_nvfp4(in, grid, opts ? opts->pipeline_depth : 0,
+                                               static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+    }
     int variant = gemm_variant(op, in.N, in.K);
     if (opts && opts->tile_variant != 0) {
         if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;

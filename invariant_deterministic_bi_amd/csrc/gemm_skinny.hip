@@ -466,10 +466,12 @@ __device__ __forceinline__ void transpose4(uint32_t &x0, uint32_t &x1, uint32_t 
 }
 
 // AP: A packed two chunks per load (M <= 8).  D: groups in flight (a divisor
-// of K / 128, chosen by the host).
-template <int AP, int D>
+// of K / 128, chosen by the host).  RB: 16-row blocks of A (M <= 16 * RB);
+// each decoded weight fragment feeds every block's chain.
+template <int AP, int D, int RB = 1>
 __global__ __launch_bounds__(64) void direct_nvfp4_kernel(GemmArgs p) {
-    constexpr int AL = AP ? 2 : 4;  // A loads per group
+    static_assert(RB == 1 || !AP, "two-chunk A packing is for M <= 8");
+    constexpr int AL = AP ? 2 : 4 * RB;  // A loads per group: load j is block j / 4, chunk j % 4
     const int lane = threadIdx.x;
     const int r = lane & 15, sub = lane >> 4;
     const int items = (p.N + 15) >> 4;
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(64) void direct_nvfp4_kernel(GemmArgs p) {
     int a_lane[AL];
 #pragma unroll
     for (int j = 0; j < AL; ++j) {
-        const int row = AP ? (r & 7) : r, ch = AP ? 2 * j + (r >> 3) : j;
+        const int row = AP ? (r & 7) : r + 16 * (j >> 2), ch = AP ? 2 * j + (r >> 3) : (j & 3);
         a_lane[j] = row < p.M ? (int)(row * p.lda * 2) + 64 * ch + 16 * sub : kMark;
     }
     const int sshift = 8 * (sub >> 1);  // this lane's byte within each scale byte pair
@@ -517,7 +519,9 @@ __global__ __launch_bounds__(64) void direct_nvfp4_kernel(GemmArgs p) {
     for (int d = 0; d < D; ++d) issue(as[d], cs[d], ss[d]);
     uint16_t *Y = static_cast<uint16_t *>(p.Y);
     for (int t = 0; t < my_items; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int gb = 0; gb < ng; gb += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
@@ -531,9 +535,12 @@ __global__ __launch_bounds__(64) void direct_nvfp4_kernel(GemmArgs p) {
                 for (int j = 0; j < 4; ++j) {
                     const uint4 w = decode8(y[j], sc[j]);
                     const i32x4 wv = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
-                    const i32x4 a = AP ? ((j & 1) ? ror8(as[d][j >> 1]) : as[d][j >> 1]) : as[d][j];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                  __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < RB; ++b) {
+                        const i32x4 a = AP ? ((j & 1) ? ror8(as[d][j >> 1]) : as[d][j >> 1]) : as[d][4 * b + j];
+                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                         __builtin_bit_cast(bf16x8, wv), acc[b], 0, 0, 0);
+                    }
                 }
                 issue(as[d], cs[d], ss[d]);
             }
@@ -541,12 +548,25 @@ __global__ __launch_bounds__(64) void direct_nvfp4_kernel(GemmArgs p) {
         const int col = ((int)blockIdx.x + t * (int)gridDim.x) * 16 + r;
         if (col < p.N) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * sub + i;
-                if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[i] * p.alpha);
-            }
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * b + 4 * sub + i;
+                    if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[b][i] * p.alpha);
+                }
         }
     }
+}
+
+template <int RB>
+hipError_t launch_nvfp4_rb(const GemmArgs &a, int d, int grid, hipStream_t s) {
+    switch (d) {
+        case 4: hipLaunchKernelGGL((direct_nvfp4_kernel<0, 4, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((direct_nvfp4_kernel<0, 2, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((direct_nvfp4_kernel<0, 1, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int AP>
@@ -795,7 +815,9 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, int nb, int waves, in
 }
 
 hipError_t launch_direct_nvfp4(const GemmArgs &a, int grid, int depth, hipStream_t s) {
-    if (a.M < 1 || a.M > 16 || grid < 1 || a.K % 128 != 0) return hipErrorInvalidValue;
+    if (a.M < 1 || a.M > 64 || grid < 1 || a.K % 128 != 0) return hipErrorInvalidValue;
+    if (a.M > 32) return direct::launch_nvfp4_rb<4>(a, pick_depth(a.K / 128, depth, 2, 2), grid, s);
+    if (a.M > 16) return direct::launch_nvfp4_rb<2>(a, pick_depth(a.K / 128, depth, 4, 4), grid, s);
     const int d = pick_depth(a.K / 128, depth, 8, 8);
     return a.M <= 8 ? direct::launch_nvfp4_ap<1>(a, d, grid, s) : direct::launch_nvfp4_ap<0>(a, d, grid, s);
 }

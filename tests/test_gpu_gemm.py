@@ -284,17 +284,19 @@ def test_small_m_path_matches_tiled_kernel(N, K):
 def test_small_m_nvfp4_path_matches_tiled_kernel(N, K):
     """The NVFP4 weight at M <= 16 (K % 128 == 0: codes and scales loaded
     into registers, transposed across lanes and decoded per lane, A in LDS;
-    else the LDS-ring skinny kernel) against the tiled kernel and the full
-    batch, under capped wavefront counts and every pipeline depth."""
+    else the LDS-ring skinny kernel), and at 16 < M <= 64 with K % 128 == 0
+    (the register kernel with two or four 16-row blocks of A), against the
+    tiled kernel and the full batch (M = 80, tiled), under capped wavefront
+    counts and every pipeline depth."""
     x = inputs.rng(12345, 952).standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
     g = inputs.nvfp4_global_scale(x)
     Wq, Ws = inputs.nvfp4_quantize(x, g)
     alpha = float(np.float32(1.0) / g)
-    A = inputs.randn_bf16((48, K), tag=(953,))
+    A = inputs.randn_bf16((80, K), tag=(953,))
     Ad, Wqd, Wsd = dev(A), dev(Wq), dev(Ws)
     note("skinny nvfp4 full")
     yfull = host(B.bi_nvfp4_gemm(Ad, Wqd, Wsd, alpha))
-    for M in (1, 2, 7, 9, 16):
+    for M in (1, 2, 7, 9, 16, 17, 32, 33, 64):
         note(f"skinny nvfp4 N={N} K={K} M={M}")
         ys = host(B.bi_nvfp4_gemm(Ad[:M], Wqd, Wsd, alpha))
         yt = host(B.bi_nvfp4_gemm(Ad[:M], Wqd, Wsd, alpha, tile_variant=3))
