@@ -113,12 +113,13 @@ typedef struct bi_plan {
  * tests and for tuning sweeps; production calls pass NULL.
  *   max_workgroups: cap on the persistent grid (0 = the library's default,
  *     the device's compute-unit count times the tiles one unit holds); for
- *     the GEMMs at M <= 16 (no tile_variant), a cap on the streaming
- *     wavefronts.
+ *     the GEMMs served by the streaming kernels (M <= 16; 16 < M <= 64 for
+ *     bf16 weights with N <= 12288 and for NVFP4 weights with K % 128 == 0;
+ *     no tile_variant), a cap on the streaming wavefronts.
  *   tile_variant: GEMM family only; 0 = the plan's tile shape, v > 0 = the
  *     compiled tile shape v-1 (see bi_tile_shape).  BI_ERR_SHAPE if out of
  *     range.
- *   pipeline_depth: GEMMs at M <= 16 only; weight load units in flight per
+ *   pipeline_depth: the streaming kernels only; weight load units in flight per
  *     wavefront (0 = the library's choice; otherwise rounded down to a
  *     supported power of two that divides the unit count).
  */
