@@ -113,9 +113,9 @@ typedef struct bi_plan {
  * tests and for tuning sweeps; production calls pass NULL.
  *   max_workgroups: cap on the persistent grid (0 = the library's default,
  *     the device's compute-unit count times the tiles one unit holds); for
- *     the GEMMs served by the streaming kernels (M <= 16; 16 < M <= 64 for
- *     bf16 weights with N <= 12288 and for NVFP4 weights with K % 128 == 0;
- *     no tile_variant), a cap on the streaming wavefronts.
+ *     the GEMMs served by the streaming kernels (M <= 16; up to M = 128 for
+ *     bf16 weights with N <= 12288 and to M = 64 for NVFP4 weights with
+ *     K % 128 == 0; no tile_variant), a cap on the streaming wavefronts.
  *   tile_variant: GEMM family only; 0 = the plan's tile shape, v > 0 = the
  *     compiled tile shape v-1 (see bi_tile_shape).  BI_ERR_SHAPE if out of
  *     range.

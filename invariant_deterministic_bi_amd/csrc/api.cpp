@@ -202,13 +202,13 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         hipError_t e = bi::launch_bmm_short_k(in, grid, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? BI_OK : BI_ERR_HIP;
     }
-    // bf16 GEMM with 16 < M <= 64 and N <= 12288: the same register-streaming
-    // kernel with two or four 16-row blocks (one weight fragment feeds each
-    // block's chain), so every compute unit streams 16-column items as at
+    // bf16 GEMM with 16 < M <= 128 and N <= 12288: the same register-streaming
+    // kernel with two, four or eight 16-row blocks (one weight fragment feeds
+    // each block's chain), so every compute unit streams 16-column items as at
     // M <= 16 instead of N / bn workgroups; the bits are the tiled kernel's.
     // Each item re-reads A from L2 (M * K * 2 bytes), so wider weights, whose
     // tiles already fill the chip, keep the tiled kernel.
-    if (op == BI_OP_GEMM && in.M > 16 && in.M <= 64 && in.N <= 12288 && a_mode == bi::OPND_BF16_ROWS &&
+    if (op == BI_OP_GEMM && in.M > 16 && in.M <= 128 && in.N <= 12288 && a_mode == bi::OPND_BF16_ROWS &&
         b_mode == bi::OPND_BF16_ROWS && in.batch == 1 && !in.group_off && !(opts && opts->tile_variant != 0)) {
         int cus = 0;
         bi_status st = device_cus(&cus);

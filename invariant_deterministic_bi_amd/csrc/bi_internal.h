@@ -105,9 +105,9 @@ int bmm_short_k_lds_bytes(int K);
 hipError_t launch_bmm_short_k(const GemmArgs &args, int grid, hipStream_t stream);
 // 256 x 256 tiles, eight wavefronts in a ping-pong schedule; bf16 x bf16, batch 1.
 hipError_t launch_pingpong(const GemmArgs &args, int bn, int grid, hipStream_t stream);
-// Direct path for 1 <= M <= 64, bf16 A and bf16 weight [N, K], batch 1: one
+// Direct path for 1 <= M <= 128, bf16 A and bf16 weight [N, K], batch 1: one
 // 64-thread workgroup per 16-column item, fragments loaded into registers
-// (one, two or four 16-row blocks of A).
+// (one, two, four or eight 16-row blocks of A).
 hipError_t launch_direct(const GemmArgs &args, int grid, int depth, hipStream_t stream);
 // The same for a raw NVFP4 weight (codes [N, K/2], scales [N, K/16]), K % 128 == 0.
 hipError_t launch_direct_nvfp4(const GemmArgs &args, int grid, int depth, hipStream_t stream);

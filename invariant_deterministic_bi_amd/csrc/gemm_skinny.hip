@@ -429,12 +429,15 @@ hipError_t launch_ap(const GemmArgs &a, int d, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-// RB row blocks (M <= 16 * RB), unpacked A; the register budget caps D.
+// RB row blocks (M <= 16 * RB), unpacked A; the register budget caps D at
+// 16 / RB chunk pairs (A takes 8 * RB registers per pair).
 template <int RB>
 hipError_t launch_rb(const GemmArgs &a, int d, int grid, hipStream_t s) {
+    constexpr int DMAX = 16 / RB;
+    if (d > DMAX) return hipErrorInvalidValue;
     switch (d) {
-        case 8: hipLaunchKernelGGL((direct_kernel<0, 8, RB>), dim3(grid), dim3(64), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((direct_kernel<0, 4, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        case 8: if constexpr (DMAX >= 8) hipLaunchKernelGGL((direct_kernel<0, 8, RB>), dim3(grid), dim3(64), 0, s, a); break;
+        case 4: if constexpr (DMAX >= 4) hipLaunchKernelGGL((direct_kernel<0, 4, RB>), dim3(grid), dim3(64), 0, s, a); break;
         case 2: hipLaunchKernelGGL((direct_kernel<0, 2, RB>), dim3(grid), dim3(64), 0, s, a); break;
         case 1: hipLaunchKernelGGL((direct_kernel<0, 1, RB>), dim3(grid), dim3(64), 0, s, a); break;
         default: return hipErrorInvalidValue;
@@ -823,7 +826,8 @@ hipError_t launch_direct_nvfp4(const GemmArgs &a, int grid, int depth, hipStream
 }
 
 hipError_t launch_direct(const GemmArgs &a, int grid, int depth, hipStream_t s) {
-    if (a.M < 1 || a.M > 64 || grid < 1) return hipErrorInvalidValue;
+    if (a.M < 1 || a.M > 128 || grid < 1) return hipErrorInvalidValue;
+    if (a.M > 64) return direct::launch_rb<8>(a, pick_depth((a.K + 63) / 64, depth, 2, 2), grid, s);
     if (a.M > 32) return direct::launch_rb<4>(a, pick_depth((a.K + 63) / 64, depth, 4, 4), grid, s);
     if (a.M > 16) return direct::launch_rb<2>(a, pick_depth((a.K + 63) / 64, depth, 8, 8), grid, s);
     const int d = pick_depth((a.K + 63) / 64, depth, a.K >= 8192 ? 16 : 8, 16);

@@ -249,7 +249,7 @@ def test_small_m_path_matches_tiled_kernel(N, K):
     rows, for ragged N, K % 64 == 32 (the trailing zero-filled chunk), a
     strided A, capped wavefront counts and every pipeline depth; and within
     the oracle tolerance."""
-    Mmax = 72
+    Mmax = 136
     W = inputs.randn_bf16((N, K), 0.02, tag=(951, N, K))
     Wd = dev(W)
     Ad = dev(inputs.randn_bf16((Mmax, K + 24), tag=(950, N, K)))[:, :K]   # row stride K + 24
@@ -266,7 +266,7 @@ def test_small_m_path_matches_tiled_kernel(N, K):
             assert np.array_equal(host(gemm(Ad[:M], Wd, max_workgroups=mw)), ys), (M, mw)
         for depth in (1, 2, 4, 32):
             assert np.array_equal(host(gemm(Ad[:M], Wd, pipeline_depth=depth)), ys), (M, depth)
-    for M in (48, 64):
+    for M in (48, 64, 65, 100, 128):
         note(f"skinny N={N} K={K} M={M}")
         ys = host(gemm(Ad[:M], Wd))
         assert np.array_equal(ys, host(gemm(Ad[:M], Wd, tile_variant=1))), f"skinny vs tiled, M={M}"
