@@ -54,6 +54,8 @@ def _load():
     lib.oracle_reduce_rmsnorm.restype = None
     lib.oracle_grouped_gemm.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _p, _p]
     lib.oracle_grouped_gemm.restype = None
+    lib.oracle_mla_decode.argtypes = [_p, _p, _p, ctypes.c_float, _i64, _i64, _i64, _i64, _i64, _p, _p]
+    lib.oracle_mla_decode.restype = None
     for name in ("oracle_e2m1_value", "oracle_e4m3_value", "oracle_bf16_value"):
         getattr(lib, name).argtypes = [ctypes.c_uint32]
         getattr(lib, name).restype = ctypes.c_double
@@ -257,3 +259,24 @@ def grouped_gemm(A, W, offsets):
     if T and N:
         _load().oracle_grouped_gemm(_ptr(A), K, _ptr(W), K, N * K, _ptr(off), E, N, K, _ptr(Y), _ptr(S))
     return Y, S
+
+
+def mla_decode(q, kv, lens, scale, Dv):
+    """Decode attention over a latent KV cache, fp64 plain definition:
+    s_t = scale * q . kv_t (all Dqk components), p = softmax(s) over the
+    request's L_b tokens, o = sum_t p_t * kv_t[:Dv].  q bf16 [B, H, Dqk],
+    kv bf16 [B, Lmax, Dqk], lens [B].  scale is rounded to fp32 first.
+    Returns (o, s) [B, H, Dv], s = sum_t p_t |v_t| (tolerance scale)."""
+    q = np.ascontiguousarray(_u16(q))
+    kv = np.ascontiguousarray(_u16(kv))
+    lens = np.ascontiguousarray(np.asarray(lens, np.int64))
+    B, H, Dqk = q.shape
+    B2, Lmax, D2 = kv.shape
+    assert B == B2 and Dqk == D2 and lens.shape == (B,) and 0 < Dv <= Dqk
+    assert np.all((lens >= 0) & (lens <= Lmax))
+    O = np.zeros((B, H, Dv), np.float64)
+    S = np.zeros((B, H, Dv), np.float64)
+    if B and H:
+        _load().oracle_mla_decode(_ptr(q), _ptr(kv), _ptr(lens), float(np.float32(scale)), B, H, Lmax,
+                                  Dqk, Dv, _ptr(O), _ptr(S))
+    return O, S

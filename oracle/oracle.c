@@ -344,5 +344,58 @@ void oracle_grouped_gemm(const uint16_t *A, int64_t lda, const uint16_t *W, int6
     }
 }
 
+/*
+ * Decode attention over a latent (MLA-absorbed) KV cache: the attention step
+ * the vLLM batch-invariance tracking issue lists (MLA backends) and the
+ * vLLM-Ascend guide requires to be deterministic.  Plain definition, fp64,
+ * for request b with L_b cached tokens and head h:
+ *   s_t = scale * sum_{d < Dqk} q[b][h][d] * kv[b][t][d],   t < L_b;
+ *   p_t = exp(s_t - max_t s_t);
+ *   o[b][h][c] = sum_t p_t * kv[b][t][c] / sum_t p_t,       c < Dv (Dv <= Dqk:
+ *   the value is the first Dv components of the cached latent).
+ * q is bf16 [B, H, Dqk] dense; kv is bf16 [B, Lmax, Dqk] dense; lens [B].
+ * O and S are dense [B, H, Dv]; S gets sum_t p_t |v_t[c]| / sum_t p_t, the
+ * scale of the tolerance.  A request with L_b == 0 gives O = S = 0.
+ */
+void oracle_mla_decode(const uint16_t *q, const uint16_t *kv, const int64_t *lens, float scale,
+                       int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, double *O,
+                       double *S) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; b++) {
+        for (int64_t h = 0; h < H; h++) {
+            const int64_t L = lens[b];
+            const uint16_t *qq = q + (b * H + h) * Dqk;
+            double *o = O + (b * H + h) * Dv, *sv = S + (b * H + h) * Dv;
+            for (int64_t c = 0; c < Dv; c++) o[c] = sv[c] = 0.0;
+            if (L <= 0) continue;
+            double smax = -INFINITY;
+            for (int64_t t = 0; t < L; t++) {
+                const uint16_t *k = kv + (b * Lmax + t) * Dqk;
+                double dot = 0.0;
+                for (int64_t d = 0; d < Dqk; d++) dot += bf16_value(qq[d]) * bf16_value(k[d]);
+                double st = (double)scale * dot;
+                if (st > smax) smax = st;
+            }
+            double l = 0.0;
+            for (int64_t t = 0; t < L; t++) {
+                const uint16_t *k = kv + (b * Lmax + t) * Dqk;
+                double dot = 0.0;
+                for (int64_t d = 0; d < Dqk; d++) dot += bf16_value(qq[d]) * bf16_value(k[d]);
+                double pt = exp((double)scale * dot - smax);
+                l += pt;
+                for (int64_t c = 0; c < Dv; c++) {
+                    double v = bf16_value(k[c]);
+                    o[c] += pt * v;
+                    sv[c] += pt * fabs(v);
+                }
+            }
+            for (int64_t c = 0; c < Dv; c++) {
+                o[c] /= l;
+                sv[c] /= l;
+            }
+        }
+    }
+}
+
 /* Number of OpenMP threads the oracle will use (for reporting). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }

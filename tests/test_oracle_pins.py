@@ -588,3 +588,54 @@ def test_grouped_gemm_integer_exact_empty_groups_and_single_expert():
     y1, s1 = oracle.grouped_gemm(A, W[3:4], [0, T])
     g, gs = oracle.gemm(A, W[3])
     assert np.array_equal(y1, g) and np.array_equal(s1, gs)
+
+
+# ---------------------------------------------------------------- MLA decode attention
+
+@pytest.mark.parametrize("name", ["attn_uniform", "attn_two"])
+def test_mla_decode_worked_examples(name):
+    args, rhs = WORKED[name]
+    q = bits([[[float(v) for v in args["q"].split(",")]]])
+    kv = bits([_parse_matrix(args["kv"])])
+    o, s = oracle.mla_decode(q, kv, [kv.shape[1]], float(args["scale"]), int(args["Dv"]))
+    assert math.isclose(o[0, 0, 0], float(rhs), rel_tol=1e-15)
+
+
+def test_mla_decode_closed_forms_and_bruteforce():
+    """One token: o = v exactly.  Identical keys: o = mean of the values.
+    Token order does not matter.  Against a direct numpy softmax in fp64 on
+    a small random case.  A zero-length request gives zeros."""
+    r = inputs.rng(12345, 70)
+    H, Dqk, Dv, L = 3, 40, 24, 9
+    q = inputs.randn_bf16((2, H, Dqk), tag=(71,))
+    kv = inputs.randn_bf16((2, L, Dqk), tag=(72,))
+    qf = inputs.bf16_bits_to_f32(q).astype(np.float64)
+    kvf = inputs.bf16_bits_to_f32(kv).astype(np.float64)
+    scale = 0.125
+    o, s = oracle.mla_decode(q, kv, [L, 1], scale, Dv)
+    # request 1 has a single token: o = v_0 exactly, for every head
+    assert np.array_equal(o[1], np.broadcast_to(kvf[1, 0, :Dv], (H, Dv)))
+    # request 0 against numpy
+    sc = scale * np.einsum("hd,td->ht", qf[0], kvf[0])
+    p = np.exp(sc - sc.max(axis=1, keepdims=True))
+    ref = (p @ kvf[0, :, :Dv]) / p.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(o[0], ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s[0], (p @ np.abs(kvf[0, :, :Dv])) / p.sum(axis=1, keepdims=True),
+                               rtol=1e-12, atol=1e-12)
+    # token order
+    perm = r.permutation(L)
+    o2, _ = oracle.mla_decode(q, kv[:, perm], [L, 1] if perm[0] == 0 else [L, 1], scale, Dv)
+    np.testing.assert_allclose(o2[0], o[0], rtol=1e-12, atol=1e-13)
+    # identical keys: uniform weights, o = mean of the values
+    kv_same = kv.copy()
+    kv_same[0, :, Dv:] = kv[0, 0, Dv:]
+    kv_same[0, :, :Dv] = 0
+    kv_same[0, :, :Dv] = inputs.randint_bf16((L, Dv), -8, 8, tag=(73,))
+    qz = q.copy()
+    qz[0, :, :Dv] = 0            # scores then depend on the shared components only
+    o3, _ = oracle.mla_decode(qz, kv_same, [L, 1], scale, Dv)
+    mean = inputs.bf16_bits_to_f32(kv_same[0, :, :Dv]).astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(o3[0], np.broadcast_to(mean, (H, Dv)), rtol=1e-13, atol=1e-13)
+    # empty request
+    o4, s4 = oracle.mla_decode(q, kv, [0, 1], scale, Dv)
+    assert not o4[0].any() and not s4[0].any()
