@@ -454,6 +454,25 @@ def main():
         inv_checked += 1
         inv_passed += int(torch.equal(R16, Rr[:16]) and torch.equal(Y16, Yr[:16]))
         del parts, resid, Rr, Yr
+        # decode attention over a latent cache: 64 requests of 1024..4096
+        # tokens (seeded), 16 heads, Dqk 576 (512 latent + 64 rotary), Dv 512
+        Bq, Hq, Dqk, Dv, Lmx = 64, 16, 576, 512, 4096
+        lens_np = inputs.rng(12345, 21).integers(1024, Lmx + 1, Bq).astype(np.int32)
+        qa = torch.randn((Bq, Hq, Dqk), device=dev).to(torch.bfloat16)
+        kva = torch.randn((Bq, Lmx, Dqk), device=dev).to(torch.bfloat16)
+        lens_d = torch.from_numpy(lens_np).to(dev)
+        oa = B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv)
+        us = timed(lambda r: B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv, oa), 10)
+        byt = 2.0 * int(lens_np.sum()) * Dqk + 2.0 * Bq * Hq * (Dqk + Dv) + 4.0 * Bq
+        gbs = byt / (us * 1e-6) / 1e9
+        sweep.append({"op": "mla_decode", "B": Bq, "H": Hq, "Dqk": Dqk, "Dv": Dv,
+                      "tokens": int(lens_np.sum()), "us": round(us, 2), "GB/s": round(gbs, 1),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        o1 = B.bi_mla_decode(qa[3:4].contiguous(), kva[3:4].contiguous(), lens_d[3:4].contiguous(),
+                             1.0 / 192 ** 0.5, Dv)
+        inv_checked += 1
+        inv_passed += int(torch.equal(o1[0], oa[3]))
+        del qa, kva, oa, o1
         # run-to-run: the step's outputs are identical over repeats
         snap = {k: v.clone() for k, v in out.items()}
         for _ in range(3):

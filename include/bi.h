@@ -282,6 +282,37 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
                           int64_t ldy, const int64_t *group_offsets, int64_t E, int64_t T, int64_t N,
                           int64_t K, void *stream);
 
+/*
+ * bi_mla_decode: one decode step of attention over a latent KV cache, the
+ * MLA form in which the key and value projections are absorbed into the
+ * query and output (the vLLM batch-invariance tracking issue lists the MLA
+ * attention backends among the operators batch-invariant mode must cover;
+ * the vLLM-Ascend "Batch Invariance" guide requires deterministic attention).
+ * Every cached token t < L_b of request b holds one latent row kv_t of Dqk
+ * components, used whole as the key and its first Dv components as the
+ * value:
+ *   s_t = scale * (q . kv_t),  p = softmax over t < L_b of s,
+ *   out[b][h] = sum over t of p_t * kv_t[0:Dv].
+ * One workgroup computes one (request, head) over all of the request's
+ * tokens, with no split of the KV walk, in an order fixed by L_b, Dqk and
+ * Dv alone: out[b][h] is bitwise the same whatever other requests share the
+ * call, whatever their lengths, B, H and the launch options.  In fp32:
+ * scores are fma chains over d ascending, weights the hardware exp2 of
+ * (s_t - max s) * log2(e), the value sum four fixed token-strided fma chains
+ * added in a fixed order, one division by the weight sum, bf16 round to
+ * nearest even.
+ *   q: bf16 [B,H,Dqk] dense.  kv: bf16 [B,Lmax,Dqk] dense (request b's
+ *     cache is Lmax contiguous rows; rows at or past L_b are never read).
+ *   lens: DEVICE int32 [B], 4-byte aligned; read only by the kernel, which
+ *     clamps each to [0, Lmax].  A request with L_b = 0 gets zeros.
+ *   out: bf16 [B,H,Dv] dense; must not overlap q, kv or lens.
+ *   Dqk % 8 == 0, Dqk <= 1024; Dv % 8 == 0, Dv <= Dqk, Dv <= 1024;
+ *   Lmax <= 16384 (the weights live in LDS).  q, kv, out 16-byte aligned.
+ *   scale finite (BI_ERR_VALUE otherwise).  B == 0 or H == 0 is a no-op.
+ */
+bi_status bi_mla_decode(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
+                        int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream);
+
 /* The *_ex variants take launch options (may be NULL = defaults). */
 bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
                      int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream,
@@ -306,6 +337,9 @@ bi_status bi_grouped_gemm_ex(const void *A, int64_t lda, const void *W, int64_t 
 bi_status bi_nvfp4_quant_ex(const void *X, int64_t ldx, float g, void *Q, void *Q_scales,
                             int64_t ldq, int64_t M, int64_t K, void *stream,
                             const bi_launch_opts *opts);
+bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
+                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream,
+                           const bi_launch_opts *opts);
 
 /*
  * bi_plan_query: the recipe the library uses for (op, N, K); for

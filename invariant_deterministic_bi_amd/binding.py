@@ -72,6 +72,8 @@ _SIGS = {
                              _p, _i64, _p, _i64, _i64, _i64, _p, _p],
     "bi_grouped_gemm": [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
     "bi_grouped_gemm_ex": [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p],
+    "bi_mla_decode": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p],
+    "bi_mla_decode_ex": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p, _p],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
 }
@@ -331,3 +333,26 @@ def bi_grouped_gemm(A, W, offsets, Y=None, *, stream=None, max_workgroups=0, til
                                   _opts(max_workgroups, tile_variant))
     _raise(st, "bi_grouped_gemm")
     return Y
+
+
+def bi_mla_decode(q, kv, lens, scale, Dv, out=None, *, stream=None, max_workgroups=0):
+    """Decode attention over a latent KV cache: q bf16 [B,H,Dqk], kv bf16
+    [B,Lmax,Dqk], lens a device int32 tensor [B]; returns out bf16 [B,H,Dv]
+    = softmax(scale * q . kv^T) . kv[..., :Dv] per request and head."""
+    for t, name in ((q, "q"), (kv, "kv")):
+        if t.dim() != 3 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a dense 3-d bf16 tensor")
+    B, H, Dqk = q.shape
+    B2, Lmax, D2 = kv.shape
+    if B2 != B or D2 != Dqk:
+        raise ValueError("q and kv disagree on B or Dqk")
+    if lens.dtype != torch.int32 or lens.dim() != 1 or lens.shape[0] != B or not lens.is_cuda:
+        raise ValueError("lens must be a device int32 tensor of B entries")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=q.device)
+    if tuple(out.shape) != (B, H, Dv) or not out.is_contiguous():
+        raise ValueError("out must be a dense [B,H,Dv] tensor")
+    st = lib().bi_mla_decode_ex(_ptr(q), _ptr(kv), _ptr(lens), float(scale), _ptr(out), B, H, Lmax, Dqk, Dv,
+                                _stream(stream), _opts(max_workgroups))
+    _raise(st, "bi_mla_decode")
+    return out

@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libbi.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "gemm_dispatch.hip", "gemm_bf16.hip", "gemm_kn.hip", "gemm_nvfp4.hip",
            "gemm_nvfp4raw.hip", "gemm_nvfp4a.hip", "gemm_skinny.hip", "gemm_pingpong.hip",
-           "rmsnorm.hip", "nvfp4_quant.hip", "bmm.hip"]
+           "rmsnorm.hip", "nvfp4_quant.hip", "bmm.hip",
+           "mla_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -612,4 +612,38 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
     return bi_grouped_gemm_ex(A, lda, W, ldw, sW, Y, ldy, group_offsets, E, T, N, K, stream, nullptr);
 }
 
+bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
+                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream,
+                           const bi_launch_opts *opts) {
+    if (B < 0 || H < 0 || Lmax < 0 || Dqk <= 0 || Dv <= 0 || Dv > Dqk) return BI_ERR_SHAPE;
+    if (Dqk % 8 || Dv % 8) return BI_ERR_SHAPE;
+    if (Dqk > bi::kMlaMaxDqk || Dv > bi::kMlaMaxDv || Lmax > bi::kMlaMaxTokens) return BI_ERR_UNSUPPORTED;
+    if (B > kI32Max || H > kI32Max || B * H > kI32Max) return BI_ERR_UNSUPPORTED;
+    if (!(scale == scale) || scale > 3.402823466e38f || scale < -3.402823466e38f) return BI_ERR_VALUE;
+    if (B == 0 || H == 0) return BI_OK;
+    if (!q || !kv || !lens || !out) return BI_ERR_NULL;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lens) & 3u))
+        return BI_ERR_ALIGN;
+    const Range ro = mat_range(out, B * H, Dv, Dv, 2, 1);
+    if (overlap(ro, mat_range(q, B * H, Dqk, Dqk, 2, 1)) || overlap(ro, mat_range(lens, 1, B, B, 4, 1)) ||
+        (Lmax > 0 && overlap(ro, mat_range(kv, B * Lmax, Dqk, Dqk, 2, 1))))
+        return BI_ERR_ALIAS;
+    int cus = 0;
+    bi_status st = device_cus(&cus);
+    if (st != BI_OK) return st;
+    bi::MlaArgs a{};
+    a.q = q; a.kv = kv; a.lens = lens; a.out = out;
+    a.B = (int)B; a.H = (int)H; a.Lmax = (int)Lmax; a.Dqk = (int)Dqk; a.Dv = (int)Dv;
+    a.scale = scale;
+    const int per_cu = bi::mla_token_capacity(a.Lmax) == 4096 ? 4 : 1;
+    const int grid = default_grid((int)(B * H), cus, opts, per_cu);
+    hipError_t e = bi::launch_mla_decode(a, grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+bi_status bi_mla_decode(const void *q, const void *kv, const int32_t *lens, float scale, void *out, int64_t B,
+                        int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream) {
+    return bi_mla_decode_ex(q, kv, lens, scale, out, B, H, Lmax, Dqk, Dv, stream, nullptr);
+}
+
 }  // extern "C"

@@ -166,4 +166,20 @@ struct QuantArgs {
 // the 8-element half blocks.
 hipError_t launch_nvfp4_quant(const QuantArgs &args, int grid, hipStream_t stream);
 
+// Decode attention over a latent KV cache (one workgroup per request and
+// head, no KV split).
+constexpr int kMlaMaxTokens = 16384;  // the weights live in LDS
+constexpr int kMlaMaxDqk = 1024;
+constexpr int kMlaMaxDv = 1024;
+struct MlaArgs {
+    const void *q;        // bf16 [B, H, Dqk]
+    const void *kv;       // bf16 [B, Lmax, Dqk]
+    const int32_t *lens;  // device int32 [B], clamped to [0, Lmax]
+    void *out;            // bf16 [B, H, Dv]
+    int B, H, Lmax, Dqk, Dv;
+    float scale;
+};
+int mla_token_capacity(int Lmax);  // 0 when Lmax is too large
+hipError_t launch_mla_decode(const MlaArgs &args, int grid, hipStream_t stream);
+
 }  // namespace bi

@@ -65,3 +65,26 @@ def reduce_rms_y_extra(R_ref, gamma_bits, eps):
     rms = np.sqrt(np.mean(R * R, axis=-1, keepdims=True) + float(np.float32(eps)))
     g = np.abs(bf16_to_f64(gamma_bits))
     return 0.5 * ulp_bf16(R) * g / rms
+
+
+def mla_rel_bound(q_bits, kv_bits, lens, scale):
+    """First-order rounding bound of the fp32 decode attention, as a multiple
+    c[b,h] of S = sum_t p_t |v_t| / sum_t p_t, from the inputs alone (u =
+    2^-24).  A weight's relative error is at most that of its score
+    (Dqk*u*A, A = |scale| * max_t sum_d |q_d kv_td|), of the exp2 argument
+    (u*|s - m| <= 2u*A) and of exp2 itself (2u); it moves the output by at
+    most twice that times S.  The value chains (L/4 + 3 steps) and the weight
+    sum (L + 8 steps) add (5L/4 + 11)*u, the division u.  Returns
+    max(1e-3, 1.01 * c), broadcast over Dv."""
+    qf = np.abs(bf16_to_f64(q_bits))
+    kf = np.abs(bf16_to_f64(kv_bits))
+    Bn, H, Dqk = qf.shape
+    u = 2.0 ** -24
+    c = np.zeros((Bn, H, 1))
+    for b in range(Bn):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        A = abs(float(scale)) * np.max(qf[b] @ kf[b, :L].T, axis=1)
+        c[b, :, 0] = 2 * (Dqk * u * A + 2 * u * A + 2 * u) + (1.25 * L + 11) * u + u
+    return np.maximum(1e-3, 1.01 * c)

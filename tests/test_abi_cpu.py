@@ -239,3 +239,27 @@ def test_grouped_gemm_validation():
     assert call(Y=B0 + 64) == B.BI_ERR_ALIAS                     # Y over an expert weight
     assert call(Y=A0 + 1024) == B.BI_ERR_ALIAS
     assert call(T=0, A=0, W=0, Y=0, off=0) == B.BI_OK
+
+
+def test_mla_decode_validation():
+    f = B.lib().bi_mla_decode
+    Q0, KV0, LN0, O0 = 0x1000000, 0x2000000, 0x6000000, 0x7000000
+
+    def call(q=Q0, kv=KV0, lens=LN0, scale=0.04, out=O0, Bn=4, H=16, Lmax=1024, Dqk=576, Dv=512):
+        return f(q, kv, lens, scale, out, Bn, H, Lmax, Dqk, Dv, None)
+    assert call(Dqk=572) == B.BI_ERR_SHAPE                      # Dqk % 8
+    assert call(Dv=500) == B.BI_ERR_SHAPE                       # Dv % 8
+    assert call(Dv=584) == B.BI_ERR_SHAPE                       # Dv > Dqk
+    assert call(Bn=-1) == B.BI_ERR_SHAPE
+    assert call(Lmax=-1) == B.BI_ERR_SHAPE
+    assert call(Dqk=1032, Dv=512) == B.BI_ERR_UNSUPPORTED
+    assert call(Lmax=16385) == B.BI_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == B.BI_ERR_VALUE
+    assert call(scale=float("inf")) == B.BI_ERR_VALUE
+    assert call(lens=0) == B.BI_ERR_NULL
+    assert call(q=Q0 + 8) == B.BI_ERR_ALIGN
+    assert call(lens=LN0 + 2) == B.BI_ERR_ALIGN
+    assert call(out=Q0 + 1024) == B.BI_ERR_ALIAS                 # out over q
+    assert call(out=KV0 + 4096) == B.BI_ERR_ALIAS                # out over the cache
+    assert call(Bn=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
+    assert call(H=0, q=0, kv=0, lens=0, out=0) == B.BI_OK

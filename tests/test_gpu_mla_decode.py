@@ -1,0 +1,135 @@
+"""GPU parity and invariance tests of bi_mla_decode, decode attention over a
+latent KV cache: each (request, head) output must match the fp64 oracle
+within the derived bound, and be bitwise the same alone, in any batch, with
+any head subset, grid cap or cache capacity."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_deterministic_bi_amd import inputs
+from invariant_deterministic_bi_amd import binding as B
+from harness import assert_within_tol, mla_rel_bound, rne_bf16_of_exact, bf16_to_f64
+from gpu_util import dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def lens_dev(lens):
+    return torch.tensor(np.asarray(lens, np.int32), dtype=torch.int32, device="cuda")
+
+
+def check_parity(o_bits, q, kv, lens, scale, Dv, what):
+    ref, s = oracle.mla_decode(q, kv, lens, scale, Dv)
+    c = mla_rel_bound(q, kv, lens, scale)
+    # assert_within_tol adds 1e-3*S; the extra term lifts the bound to c*S
+    assert_within_tol(o_bits, ref, s, what, extra=(c - 1e-3) * s)
+
+
+@pytest.mark.parametrize("lens,H,Dqk,Dv,Lmax", [([1, 37, 300, 0, 1029], 16, 576, 512, 1100),
+                                                ([4096, 2500], 16, 576, 512, 4096),
+                                                ([7, 64, 255, 256, 257], 3, 64, 64, 260),
+                                                ([5, 0, 13], 2, 8, 8, 16),
+                                                ([200, 33], 4, 1024, 1024, 200)])
+def test_mla_decode_parity_and_requests_alone(lens, H, Dqk, Dv, Lmax):
+    Bn = len(lens)
+    scale = 1.0 / math.sqrt(192.0)
+    q = inputs.randn_bf16((Bn, H, Dqk), 1.0, tag=(500, Dqk, Lmax))
+    kv = inputs.randn_bf16((Bn, Lmax, Dqk), 1.0, tag=(501, Dqk, Lmax))
+    qd, kvd = dev(q), dev(kv)
+    note(f"mla_decode lens={lens} H={H} Dqk={Dqk} Dv={Dv} Lmax={Lmax}")
+    o = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
+    check_parity(o, q, kv, lens, scale, Dv, "mla_decode")
+    for b in range(Bn):
+        if lens[b] == 0:
+            assert not o[b].any(), b
+        # the request alone, with only its own cache rows
+        Lb = max(lens[b], 1)
+        alone = host(B.bi_mla_decode(qd[b:b + 1].contiguous(), kvd[b:b + 1, :Lb].contiguous(),
+                                     lens_dev([lens[b]]), scale, Dv))
+        assert np.array_equal(alone[0], o[b]), b
+    # one head alone
+    h = H - 1
+    one = host(B.bi_mla_decode(qd[:, h:h + 1].contiguous(), kvd, lens_dev(lens), scale, Dv))
+    assert np.array_equal(one[:, 0], o[:, h])
+    for mw in (1, 7):
+        assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, max_workgroups=mw)), o)
+    outs = {host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv)).tobytes() for _ in range(3)}
+    assert len(outs) == 1
+
+
+def test_mla_decode_batch_composition_and_capacity():
+    """A request's output is the same bits inside batches of other requests of
+    other lengths, and whether the cache layout holds 4096 or 5000 rows per
+    request (the kernel's two LDS capacities)."""
+    H, Dqk, Dv = 16, 576, 512
+    scale = 0.0721
+    q = inputs.randn_bf16((6, H, Dqk), 1.0, tag=(510,))
+    kv = inputs.randn_bf16((6, 4096, Dqk), 1.0, tag=(511,))
+    lens = [3000, 1, 4096, 517, 0, 2048]
+    qd, kvd = dev(q), dev(kv)
+    note("mla_decode batch composition")
+    full = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
+    # sub-batches in another order
+    idx = [5, 2, 0]
+    sub = host(B.bi_mla_decode(qd[idx].contiguous(), kvd[idx].contiguous(), lens_dev([lens[i] for i in idx]),
+                               scale, Dv))
+    for j, i in enumerate(idx):
+        assert np.array_equal(sub[j], full[i]), i
+    # the same requests in a 5000-row layout
+    big = torch.zeros((6, 5000, Dqk), dtype=torch.bfloat16, device="cuda")
+    big[:, :4096] = kvd
+    wide = host(B.bi_mla_decode(qd, big, lens_dev(lens), scale, Dv))
+    assert np.array_equal(wide, full)
+    # sampled parity of the whole batch
+    check_parity(full[[0, 2, 5]], q[[0, 2, 5]], kv[[0, 2, 5]], [lens[i] for i in (0, 2, 5)], scale, Dv,
+                 "mla_decode batch")
+
+
+def test_mla_decode_long_request():
+    """The 16384-token capacity: one request of 16384 tokens, parity."""
+    H, Dqk, Dv, L = 4, 576, 512, 16384
+    scale = 1.0 / math.sqrt(192.0)
+    q = inputs.randn_bf16((1, H, Dqk), 1.0, tag=(520,))
+    kv = inputs.randn_bf16((1, L, Dqk), 1.0, tag=(521,))
+    note("mla_decode L=16384")
+    o = host(B.bi_mla_decode(dev(q), dev(kv), lens_dev([L]), scale, Dv))
+    check_parity(o, q, kv, [L], scale, Dv, "mla_decode long")
+
+
+def test_mla_decode_exact_cases():
+    """scale 0 makes every weight exactly 1: the output is the exact mean of
+    the value rows, bf16-rounded once (integer values, L a power of two).  A
+    one-token request returns its value row exactly."""
+    H, Dqk, Dv = 4, 128, 64
+    q = inputs.randn_bf16((3, H, Dqk), 1.0, tag=(530,))
+    kv = inputs.randint_bf16((3, 1024, Dqk), -3, 3, tag=(531,))
+    lens = [1024, 1, 256]
+    note("mla_decode exact cases")
+    o = host(B.bi_mla_decode(dev(q), dev(kv), lens_dev(lens), 0.0, Dv))
+    v = bf16_to_f64(kv)
+    for b, L in enumerate(lens):
+        mean = v[b, :L, :Dv].sum(axis=0) / L
+        exp = rne_bf16_of_exact(np.broadcast_to(mean, (H, Dv)))
+        assert np.array_equal(o[b], exp), b
+    # a one-token request with a nonzero scale still returns v_0 exactly
+    o1 = host(B.bi_mla_decode(dev(q), dev(kv), lens_dev([1, 1, 1]), 0.37, Dv))
+    for b in range(3):
+        assert np.array_equal(o1[b], np.broadcast_to(kv[b, 0, :Dv], (H, Dv))), b
+
+
+def test_mla_decode_lens_clamped_and_empty():
+    """lens outside [0, Lmax] are clamped by the kernel; B == 0 is a no-op."""
+    H, Dqk, Dv, Lmax = 2, 64, 32, 40
+    q = inputs.randn_bf16((3, H, Dqk), 1.0, tag=(540,))
+    kv = inputs.randn_bf16((3, Lmax, Dqk), 1.0, tag=(541,))
+    qd, kvd = dev(q), dev(kv)
+    note("mla_decode clamped lens")
+    o = host(B.bi_mla_decode(qd, kvd, lens_dev([-5, 1000, 17]), 0.125, Dv))
+    ref = host(B.bi_mla_decode(qd, kvd, lens_dev([0, Lmax, 17]), 0.125, Dv))
+    assert np.array_equal(o, ref)
+    assert not o[0].any()
+    e = B.bi_mla_decode(qd[:0], kvd[:0], lens_dev([]), 0.125, Dv)
+    assert e.shape == (0, H, Dv)
