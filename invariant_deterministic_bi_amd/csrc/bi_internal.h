@@ -179,7 +179,8 @@ struct MlaArgs {
     int B, H, Lmax, Dqk, Dv;
     float scale;
 };
-int mla_token_capacity(int Lmax);  // 0 when Lmax is too large
+int mla_token_capacity(int Lmax);     // VALU kernel's LDS capacity; 0 when Lmax is too large
+int mla_mfma_variant(int Dqk, int Dv);  // 0: the VALU kernel serves (Dqk, Dv)
 hipError_t launch_mla_decode(const MlaArgs &args, int grid, hipStream_t stream);
 
 }  // namespace bi

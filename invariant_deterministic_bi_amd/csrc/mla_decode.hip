@@ -1,20 +1,34 @@
 // Batch-invariant decode attention over a latent (MLA-absorbed) KV cache.
 // The vLLM batch-invariance tracking issue lists the MLA attention backends
 // among the operators batch-invariant mode must cover, and the vLLM-Ascend
-// guide requires deterministic attention kernels.  For request b (L_b cached
-// tokens) and head h the kernel computes, in this order:
-//   s_t = (fp32 fma chain from 0 over d ascending of q[d] * kv_t[d]) * scale,
-//         one thread per token;
-//   m   = max over t of s_t (order-free);
-//   p_t = exp2((s_t - m) * log2(e)), the hardware exp2;
-//   l   = sum of p_t: thread i sums tokens i, i+256, ... ascending, then a
-//         64-lane xor butterfly, then the four wave partials in wave order;
-//   o[c] = bf16_rne(u[c] / l) with u[c] = ((u0 + u1) + u2) + u3, where wave
-//         w's u_w[c] is the fp32 fma chain over tokens t = w, w+4, w+8, ...
-//         ascending of p_t * v_t[c] and v_t is the first Dv components of kv_t.
-// One workgroup computes one (b, h) over all of the request's tokens: there
-// is no KV split, so every step above depends only on L_b, Dqk and Dv --
-// never on the other requests, the batch size, the grid or the launch.
+// guide requires deterministic attention kernels.  Request b holds L_b
+// cached latent rows kv_t (Dqk components; the first Dv are the value).
+// Every (request, head) result is computed over all of the request's tokens
+// by one workgroup, with no split of the KV walk across workgroups, in an
+// order fixed by L_b, Dqk and Dv alone -- never by the other requests, the
+// batch size, the head count, the grid or the launch.  Two kernels, chosen
+// by (Dqk, Dv) only:
+//
+// MFMA kernel (Dqk <= 32*KC, Dv <= 128*VB for a compiled (KC, VB)): one
+// workgroup per (request, group of 16 heads), four wavefronts.  Wave w takes
+// the 32-token blocks w, w+4, w+8, ... ascending and keeps, per head, a
+// running max m, a weight sum l and an fp32 value accumulator O:
+//   S^T = K . Q^T        16x16x32 bf16 MFMA, tokens as rows, heads as
+//                        columns, Dqk in ascending 32-wide chunks; times scale;
+//   m' = max(m, block max);  alpha = exp2((m - m') * log2 e);
+//   p_t = exp2((s_t - m') * log2 e)  (hardware exp2; 0 past L_b);
+//   l = alpha * l + the lane's p_t in a fixed order;
+//   O^T = alpha * O^T + V^T . P_hi^T + V^T . P_lo^T, where P_hi = bf16(p)
+//                        and P_lo = bf16(p - P_hi) (the pair carries p to
+//                        about 2^-18 relative), V^T transposed in registers.
+// The four waves' (m, l, O) are then merged in wave order with the factors
+// exp2((m_w - M) * log2 e), M the largest m_w, and o = bf16_rne(O / l).
+//
+// VALU kernel (other shapes): one workgroup per (request, head); one thread
+// per token computes the score as an fp32 fma chain over d ascending, the
+// weights are exp2((s_t - max s) * log2 e), their sum a fixed butterfly, and
+// wave w accumulates p_t * v_t over tokens w, w+4, ... as fp32 fma chains,
+// merged ((u0 + u1) + u2) + u3 and divided by the sum.
 
 #include "bi_internal.h"
 
@@ -44,7 +58,7 @@ struct MlaLds {
 };
 
 template <int LT>
-__global__ __launch_bounds__(kNT) void mla_decode_kernel(MlaArgs a) {
+__global__ __launch_bounds__(kNT) void mla_valu_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) MlaLds<LT> s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int Dqk = a.Dqk, Dv = a.Dv, nc = Dqk >> 3, ng = Dv >> 3;
@@ -139,18 +153,216 @@ __global__ __launch_bounds__(kNT) void mla_decode_kernel(MlaArgs a) {
     }
 }
 
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kNW = 4;                    // wavefronts per workgroup (MFMA kernel)
+constexpr int kQStride = kMlaMaxDqk + 8;  // LDS row of Q, padded: 16 rows conflict-free
+
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int KC, int VB>
+__global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t qs[16 * kQStride];
+    __shared__ float ob[VB * 128][17];  // merged O^T: [dim][head], padded
+    __shared__ float mred[kNW][16], lred[kNW][16], lfin[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int Dqk = a.Dqk, Dv = a.Dv, H = a.H;
+    const int HG = (H + 15) >> 4;
+    const int qrow = (Dqk + 31) & ~31;  // Q columns staged (zero past Dqk)
+    const int64_t units = (int64_t)a.B * HG;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int b = (int)(u / HG), h0 = (int)(u % HG) * 16;
+        int L = a.lens[b];
+        L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
+        const uint16_t *kvb = static_cast<const uint16_t *>(a.kv) + (int64_t)b * a.Lmax * Dqk;
+        const uint16_t *qb = static_cast<const uint16_t *>(a.q) + ((int64_t)b * H + h0) * Dqk;
+
+        __syncthreads();  // the previous unit's readers of qs, ob and lfin are done
+        for (int i = tid; i < 16 * (qrow >> 3); i += kNW * 64) {
+            const int h = i / (qrow >> 3), d = (i % (qrow >> 3)) * 8;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (h0 + h < H && d < Dqk) v = *reinterpret_cast<const uint4 *>(qb + (int64_t)h * Dqk + d);
+            *reinterpret_cast<uint4 *>(qs + h * kQStride + d) = v;
+        }
+        __syncthreads();
+
+        f32x4_t o[VB][8];
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[vb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_part = 0.f;
+        const int nblk = (L + 31) >> 5;
+        for (int kb = w; kb < nblk; kb += kNW) {
+            const int t0 = kb * 32;
+            // scores: lane holds tokens t0 + 16hb + 4g + i of head r16
+            f32x4_t sacc[2];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int t = t0 + 16 * hb + r16;
+                const uint16_t *row = kvb + (int64_t)t * Dqk;
+                uint4 kk[KC];
+#pragma unroll
+                for (int c = 0; c < KC; ++c) {
+                    const int d = 32 * c + 8 * g;
+                    kk[c] = (t < L && d < Dqk) ? *reinterpret_cast<const uint4 *>(row + d) : make_uint4(0, 0, 0, 0);
+                }
+                sacc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < KC; ++c) {
+                    const uint4 qq = *reinterpret_cast<const uint4 *>(qs + r16 * kQStride + 32 * c + 8 * g);
+                    sacc[hb] = mfma16(kk[c], qq, sacc[hb]);
+                }
+            }
+            float sv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
+                sv[k] = t < L ? sacc[k >> 2][k & 3] * a.scale : -INFINITY;
+            }
+            float bm = sv[0];
+#pragma unroll
+            for (int k = 1; k < 8; ++k) bm = fmaxf(bm, sv[k]);
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const float m_new = fmaxf(m_run, bm);  // finite: token t0 < L is in the block
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+            m_run = m_new;
+            float pv[8];
+            l_part *= alpha;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                pv[k] = __builtin_amdgcn_exp2f((sv[k] - m_new) * kLog2e);
+                l_part += pv[k];
+            }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t h0b = to_bf16_rne(pv[2 * q]), h1b = to_bf16_rne(pv[2 * q + 1]);
+                const uint32_t l0b = to_bf16_rne(pv[2 * q] - __uint_as_float(h0b << 16));
+                const uint32_t l1b = to_bf16_rne(pv[2 * q + 1] - __uint_as_float(h1b << 16));
+                hi[q] = h0b | (h1b << 16);
+                lo[q] = l0b | (l1b << 16);
+            }
+            const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[vb][j] *= alpha;
+            // values: lane loads its group's 8 tokens x 8 dims (128 vb + 8 r16 ..)
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb) {
+                const int d = 128 * vb + 8 * r16;
+                uint32_t wv[8][4];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
+                    const uint4 v = (t < L && d < Dv) ? *reinterpret_cast<const uint4 *>(kvb + (int64_t)t * Dqk + d)
+                                                      : make_uint4(0, 0, 0, 0);
+                    wv[k][0] = v.x; wv[k][1] = v.y; wv[k][2] = v.z; wv[k][3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    // V^T row (dim d + j) over the 8 tokens, in the order of pv
+                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                    const int wd = j >> 1;
+                    const uint4 av = make_uint4(__builtin_amdgcn_perm(wv[1][wd], wv[0][wd], sel),
+                                                __builtin_amdgcn_perm(wv[3][wd], wv[2][wd], sel),
+                                                __builtin_amdgcn_perm(wv[5][wd], wv[4][wd], sel),
+                                                __builtin_amdgcn_perm(wv[7][wd], wv[6][wd], sel));
+                    o[vb][j] = mfma16(av, phi, o[vb][j]);
+                    o[vb][j] = mfma16(av, plo, o[vb][j]);
+                }
+            }
+        }
+
+        // merge the waves in wave order
+        float lw = l_part;
+        lw += __shfl_xor(lw, 16, 64);
+        lw += __shfl_xor(lw, 32, 64);
+        if (g == 0) {
+            mred[w][r16] = m_run;
+            lred[w][r16] = lw;
+        }
+        __syncthreads();
+        float M = mred[0][r16];
+#pragma unroll
+        for (int v = 1; v < kNW; ++v) M = fmaxf(M, mred[v][r16]);
+        if (L > 0) {
+            const float f = __builtin_amdgcn_exp2f((m_run - M) * kLog2e);
+            if (tid < 16) {
+                float lt = __builtin_amdgcn_exp2f((mred[0][tid] - M) * kLog2e) * lred[0][tid];
+#pragma unroll
+                for (int v = 1; v < kNW; ++v)
+                    lt = __builtin_fmaf(__builtin_amdgcn_exp2f((mred[v][tid] - M) * kLog2e), lred[v][tid], lt);
+                lfin[tid] = lt;
+            }
+            for (int v = 0; v < kNW; ++v) {
+                if (w == v) {
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                float &dst = ob[128 * vb + 8 * (4 * g + i) + j][r16];
+                                dst = v == 0 ? f * o[vb][j][i] : __builtin_fmaf(f, o[vb][j][i], dst);
+                            }
+                }
+                __syncthreads();
+            }
+        }
+        // out[b][h0 + h][8c .. 8c + 7]
+        uint16_t *ob_out = static_cast<uint16_t *>(a.out) + ((int64_t)b * H + h0) * Dv;
+        for (int i = tid; i < 16 * (Dv >> 3); i += kNW * 64) {
+            const int h = i / (Dv >> 3), c = i % (Dv >> 3);
+            if (h0 + h >= H) continue;
+            uint32_t r[4] = {0u, 0u, 0u, 0u};
+            if (L > 0) {
+                const float l = lfin[h];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    r[q] = to_bf16_rne(ob[8 * c + 2 * q][h] / l) | (to_bf16_rne(ob[8 * c + 2 * q + 1][h] / l) << 16);
+            }
+            *reinterpret_cast<uint4 *>(ob_out + (int64_t)h * Dv + 8 * c) = make_uint4(r[0], r[1], r[2], r[3]);
+        }
+    }
+}
+
 }  // namespace
 
 int mla_token_capacity(int Lmax) { return Lmax <= 4096 ? 4096 : (Lmax <= kMlaMaxTokens ? kMlaMaxTokens : 0); }
+
+// The compiled (KC, VB) of the MFMA kernel for (Dqk, Dv), or 0 (VALU kernel).
+int mla_mfma_variant(int Dqk, int Dv) {
+    const int kc = (Dqk + 31) / 32, vb = (Dv + 127) / 128;
+    if (kc == 18 && vb == 4) return 1;
+    if (kc == 4 && vb == 1) return 2;
+    if (kc == 2 && vb == 1) return 3;
+    return 0;
+}
 
 hipError_t launch_mla_decode(const MlaArgs &a, int grid, hipStream_t st) {
     if (grid < 1 || a.Dqk <= 0 || a.Dqk % 8 || a.Dqk > kMlaMaxDqk || a.Dv <= 0 || a.Dv % 8 ||
         a.Dv > a.Dqk || a.Dv > kMlaMaxDv || a.Lmax < 0)
         return hipErrorInvalidValue;
+    switch (mla_mfma_variant(a.Dqk, a.Dv)) {
+        case 1: hipLaunchKernelGGL((mla_mfma_kernel<18, 4>), dim3(grid), dim3(kNW * 64), 0, st, a); return hipGetLastError();
+        case 2: hipLaunchKernelGGL((mla_mfma_kernel<4, 1>), dim3(grid), dim3(kNW * 64), 0, st, a); return hipGetLastError();
+        case 3: hipLaunchKernelGGL((mla_mfma_kernel<2, 1>), dim3(grid), dim3(kNW * 64), 0, st, a); return hipGetLastError();
+        default: break;
+    }
     switch (mla_token_capacity(a.Lmax)) {
-        case 4096: hipLaunchKernelGGL(mla_decode_kernel<4096>, dim3(grid), dim3(kNT), 0, st, a); break;
+        case 4096: hipLaunchKernelGGL(mla_valu_kernel<4096>, dim3(grid), dim3(kNT), 0, st, a); break;
         case kMlaMaxTokens:
-            hipLaunchKernelGGL(mla_decode_kernel<kMlaMaxTokens>, dim3(grid), dim3(kNT), 0, st, a);
+            hipLaunchKernelGGL(mla_valu_kernel<kMlaMaxTokens>, dim3(grid), dim3(kNT), 0, st, a);
             break;
         default: return hipErrorInvalidValue;
     }

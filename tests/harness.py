@@ -74,8 +74,10 @@ def mla_rel_bound(q_bits, kv_bits, lens, scale):
     (Dqk*u*A, A = |scale| * max_t sum_d |q_d kv_td|), of the exp2 argument
     (u*|s - m| <= 2u*A) and of exp2 itself (2u); it moves the output by at
     most twice that times S.  The value chains (L/4 + 3 steps) and the weight
-    sum (L + 8 steps) add (5L/4 + 11)*u, the division u.  Returns
-    max(1e-3, 1.01 * c), broadcast over Dv."""
+    sum (L + 8 steps) add (5L/4 + 11)*u, the division u.  The matrix-core
+    path adds the split of each weight into two bf16 parts (2^-18 relative,
+    twice) and one rescaling per 32-token block and per merged wave
+    ((L/32 + 8)*u).  Returns max(1e-3, 1.01 * c), broadcast over Dv."""
     qf = np.abs(bf16_to_f64(q_bits))
     kf = np.abs(bf16_to_f64(kv_bits))
     Bn, H, Dqk = qf.shape
@@ -86,5 +88,6 @@ def mla_rel_bound(q_bits, kv_bits, lens, scale):
         if L == 0:
             continue
         A = abs(float(scale)) * np.max(qf[b] @ kf[b, :L].T, axis=1)
-        c[b, :, 0] = 2 * (Dqk * u * A + 2 * u * A + 2 * u) + (1.25 * L + 11) * u + u
+        c[b, :, 0] = (2 * (Dqk * u * A + 2 * u * A + 2 * u + 2.0 ** -18) + (1.25 * L + 11) * u + u
+                      + (L / 32 + 8) * u)
     return np.maximum(1e-3, 1.01 * c)
