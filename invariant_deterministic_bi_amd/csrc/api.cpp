@@ -635,8 +635,12 @@ bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, f
     a.q = q; a.kv = kv; a.lens = lens; a.out = out;
     a.B = (int)B; a.H = (int)H; a.Lmax = (int)Lmax; a.Dqk = (int)Dqk; a.Dv = (int)Dv;
     a.scale = scale;
-    const int per_cu = bi::mla_token_capacity(a.Lmax) == 4096 ? 4 : 1;
-    const int grid = default_grid((int)(B * H), cus, opts, per_cu);
+    // work units: (request, 16-head group) for the MFMA kernel, one
+    // workgroup per compute unit; (request, head) for the VALU kernel
+    const bool mfma = bi::mla_mfma_variant(a.Dqk, a.Dv) != 0;
+    const int64_t units = mfma ? B * ((H + 15) / 16) : B * H;
+    const int per_cu = mfma ? 1 : (bi::mla_token_capacity(a.Lmax) == 4096 ? 4 : 1);
+    const int grid = default_grid((int)units, cus, opts, per_cu);
     hipError_t e = bi::launch_mla_decode(a, grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
