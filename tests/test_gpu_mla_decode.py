@@ -32,7 +32,9 @@ def check_parity(o_bits, q, kv, lens, scale, Dv, what):
                                                 ([4096, 2500], 16, 576, 512, 4096),
                                                 ([7, 64, 255, 256, 257], 3, 64, 64, 260),
                                                 ([5, 0, 13], 2, 8, 8, 16),
-                                                ([200, 33], 4, 1024, 1024, 200)])
+                                                ([200, 33], 4, 1024, 1024, 200),
+                                                ([100, 7, 64], 20, 576, 512, 128),
+                                                ([33, 1], 5, 128, 64, 40)])
 def test_mla_decode_parity_and_requests_alone(lens, H, Dqk, Dv, Lmax):
     Bn = len(lens)
     scale = 1.0 / math.sqrt(192.0)
