@@ -135,3 +135,24 @@ def test_mla_decode_lens_clamped_and_empty():
     assert not o[0].any()
     e = B.bi_mla_decode(qd[:0], kvd[:0], lens_dev([]), 0.125, Dv)
     assert e.shape == (0, H, Dv)
+
+
+def test_mla_decode_bench_configuration_sampled():
+    """The timed workload's launch configuration: 64 requests of 1024..4096
+    tokens (the same seeded lengths), 16 heads, Dqk 576, Dv 512, Lmax 4096.
+    Sampled requests are checked against the oracle, and each alone is
+    bitwise its row of the batch."""
+    Bn, H, Dqk, Dv, Lmax = 64, 16, 576, 512, 4096
+    lens = inputs.rng(12345, 21).integers(1024, Lmax + 1, Bn).astype(np.int32)
+    scale = 1.0 / 192 ** 0.5
+    q = inputs.randn_bf16((Bn, H, Dqk), 1.0, tag=(550,))
+    kv = inputs.randn_bf16((Bn, Lmax, Dqk), 1.0, tag=(551,))
+    qd, kvd = dev(q), dev(kv)
+    note("mla_decode bench configuration B=64 H=16 Lmax=4096")
+    o = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
+    pick = [0, int(np.argmax(lens)), int(np.argmin(lens)), Bn - 1]
+    check_parity(o[pick], q[pick], kv[pick], lens[pick], scale, Dv, "mla_decode bench config")
+    for b in pick:
+        alone = host(B.bi_mla_decode(qd[b:b + 1].contiguous(), kvd[b:b + 1].contiguous(), lens_dev(lens[b:b + 1]),
+                                     scale, Dv))
+        assert np.array_equal(alone[0], o[b]), b
