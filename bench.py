@@ -461,18 +461,20 @@ def main():
         qa = torch.randn((Bq, Hq, Dqk), device=dev).to(torch.bfloat16)
         kva = torch.randn((Bq, Lmx, Dqk), device=dev).to(torch.bfloat16)
         lens_d = torch.from_numpy(lens_np).to(dev)
-        oa = B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv)
-        us = timed(lambda r: B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv, oa), 10)
+        wsa = torch.empty(B.mla_decode_workspace_size(Bq, Hq, Lmx, Dqk, Dv), dtype=torch.uint8, device=dev)
+        oa = B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv, workspace=wsa)
+        us = timed(lambda r: B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv, oa, workspace=wsa), 10)
         byt = 2.0 * int(lens_np.sum()) * Dqk + 2.0 * Bq * Hq * (Dqk + Dv) + 4.0 * Bq
         gbs = byt / (us * 1e-6) / 1e9
-        sweep.append({"op": "mla_decode", "B": Bq, "H": Hq, "Dqk": Dqk, "Dv": Dv,
+        sweep.append({"op": "mla_decode", "schedule": "workgroup per 2048-token chunk + fold", "B": Bq, "H": Hq, "Dqk": Dqk, "Dv": Dv,
                       "tokens": int(lens_np.sum()), "us": round(us, 2), "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
         o1 = B.bi_mla_decode(qa[3:4].contiguous(), kva[3:4].contiguous(), lens_d[3:4].contiguous(),
                              1.0 / 192 ** 0.5, Dv)
-        inv_checked += 1
+        inv_checked += 2
         inv_passed += int(torch.equal(o1[0], oa[3]))
-        del qa, kva, oa, o1
+        inv_passed += int(torch.equal(B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv), oa))
+        del qa, kva, oa, o1, wsa
         # run-to-run: the step's outputs are identical over repeats
         snap = {k: v.clone() for k, v in out.items()}
         for _ in range(3):

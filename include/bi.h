@@ -293,25 +293,41 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
  * value:
  *   s_t = scale * (q . kv_t),  p = softmax over t < L_b of s,
  *   out[b][h] = sum over t of p_t * kv_t[0:Dv].
- * One workgroup computes one (request, head) over all of the request's
- * tokens, with no split of the KV walk, in an order fixed by L_b, Dqk and
- * Dv alone: out[b][h] is bitwise the same whatever other requests share the
- * call, whatever their lengths, B, H and the launch options.  In fp32:
- * scores are fma chains over d ascending, weights the hardware exp2 of
- * (s_t - max s) * log2(e), the value sum four fixed token-strided fma chains
- * added in a fixed order, one division by the weight sum, bf16 round to
- * nearest even.
+ * The order of every sum is fixed by L_b, Dqk and Dv alone: out[b][h] is
+ * bitwise the same whatever other requests share the call, whatever their
+ * lengths, B, H, the launch options and whether a workspace is passed.
+ * In fp32: scores are MFMA (or fma) chains over d ascending, weights the
+ * hardware exp2 of (s_t - running max) * log2(e), the weighted values summed
+ * per 2048-token chunk in a fixed order and the chunks folded in ascending
+ * order, one division by the weight sum, bf16 round to nearest even.
  *   q: bf16 [B,H,Dqk] dense.  kv: bf16 [B,Lmax,Dqk] dense (request b's
  *     cache is Lmax contiguous rows; rows at or past L_b are never read).
- *   lens: DEVICE int32 [B], 4-byte aligned; read only by the kernel, which
- *     clamps each to [0, Lmax].  A request with L_b = 0 gets zeros.
+ *   lens: DEVICE int32 [B], 4-byte aligned; read only by the kernels, which
+ *     clamp each to [0, Lmax].  A request with L_b = 0 gets zeros.
  *   out: bf16 [B,H,Dv] dense; must not overlap q, kv or lens.
+ *   workspace: NULL, or caller-owned device memory of at least
+ *     bi_mla_decode_workspace_size() bytes, 16-byte aligned, overlapping
+ *     nothing else (BI_ERR_SHAPE if too small).  With it, and when the
+ *     (request, 16-head group) pairs are fewer than the device's compute
+ *     units, every 2048-token chunk of every request gets its own workgroup
+ *     and a second kernel folds the chunks: the same bits, more of the chip
+ *     busy.  Its contents need no initialisation and are clobbered.
  *   Dqk % 8 == 0, Dqk <= 1024; Dv % 8 == 0, Dv <= Dqk, Dv <= 1024;
- *   Lmax <= 16384 (the weights live in LDS).  q, kv, out 16-byte aligned.
- *   scale finite (BI_ERR_VALUE otherwise).  B == 0 or H == 0 is a no-op.
+ *   Lmax <= 16384.  q, kv, out 16-byte aligned.  scale finite
+ *   (BI_ERR_VALUE otherwise).  B == 0 or H == 0 is a no-op.
  */
 bi_status bi_mla_decode(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
-                        int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream);
+                        int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *workspace,
+                        int64_t workspace_bytes, void *stream);
+
+/*
+ * bi_mla_decode_workspace_size: *bytes = the workspace bi_mla_decode uses
+ * for this shape (0 when the shape is served without one; a workspace
+ * passed then is ignored).  Validates the shape as bi_mla_decode does.
+ * Host-only; makes no HIP call.
+ */
+bi_status bi_mla_decode_workspace_size(int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv,
+                                       int64_t *bytes);
 
 /* The *_ex variants take launch options (may be NULL = defaults). */
 bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
@@ -338,8 +354,8 @@ bi_status bi_nvfp4_quant_ex(const void *X, int64_t ldx, float g, void *Q, void *
                             int64_t ldq, int64_t M, int64_t K, void *stream,
                             const bi_launch_opts *opts);
 bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
-                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream,
-                           const bi_launch_opts *opts);
+                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *workspace,
+                           int64_t workspace_bytes, void *stream, const bi_launch_opts *opts);
 
 /*
  * bi_plan_query: the recipe the library uses for (op, N, K); for

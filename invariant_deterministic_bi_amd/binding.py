@@ -72,8 +72,9 @@ _SIGS = {
                              _p, _i64, _p, _i64, _i64, _i64, _p, _p],
     "bi_grouped_gemm": [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
     "bi_grouped_gemm_ex": [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p],
-    "bi_mla_decode": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p],
-    "bi_mla_decode_ex": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p, _p],
+    "bi_mla_decode": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _p],
+    "bi_mla_decode_ex": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "bi_mla_decode_workspace_size": [_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_int64)],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
 }
@@ -335,10 +336,21 @@ def bi_grouped_gemm(A, W, offsets, Y=None, *, stream=None, max_workgroups=0, til
     return Y
 
 
-def bi_mla_decode(q, kv, lens, scale, Dv, out=None, *, stream=None, max_workgroups=0):
+def mla_decode_workspace_size(B, H, Lmax, Dqk, Dv) -> int:
+    """Bytes of workspace bi_mla_decode uses for this shape (0: none)."""
+    n = ctypes.c_int64(0)
+    _raise(lib().bi_mla_decode_workspace_size(B, H, Lmax, Dqk, Dv, ctypes.byref(n)), "bi_mla_decode_workspace_size")
+    return int(n.value)
+
+
+def bi_mla_decode(q, kv, lens, scale, Dv, out=None, *, workspace=None, stream=None, max_workgroups=0):
     """Decode attention over a latent KV cache: q bf16 [B,H,Dqk], kv bf16
     [B,Lmax,Dqk], lens a device int32 tensor [B]; returns out bf16 [B,H,Dv]
-    = softmax(scale * q . kv^T) . kv[..., :Dv] per request and head."""
+    = softmax(scale * q . kv^T) . kv[..., :Dv] per request and head.
+    workspace: None (one workgroup per request), True (allocate one with
+    torch), or a device tensor of at least mla_decode_workspace_size bytes
+    (one workgroup per 2048-token chunk when the request and head groups
+    leave compute units idle); the bits are the same."""
     for t, name in ((q, "q"), (kv, "kv")):
         if t.dim() != 3 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_contiguous():
             raise ValueError(f"{name} must be a dense 3-d bf16 tensor")
@@ -352,7 +364,12 @@ def bi_mla_decode(q, kv, lens, scale, Dv, out=None, *, stream=None, max_workgrou
         out = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=q.device)
     if tuple(out.shape) != (B, H, Dv) or not out.is_contiguous():
         raise ValueError("out must be a dense [B,H,Dv] tensor")
+    if workspace is True:
+        workspace = torch.empty(max(16, mla_decode_workspace_size(B, H, Lmax, Dqk, Dv)), dtype=torch.uint8,
+                                device=q.device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace),
+                                                           workspace.numel() * workspace.element_size())
     st = lib().bi_mla_decode_ex(_ptr(q), _ptr(kv), _ptr(lens), float(scale), _ptr(out), B, H, Lmax, Dqk, Dv,
-                                _stream(stream), _opts(max_workgroups))
+                                ws_ptr, ws_bytes, _stream(stream), _opts(max_workgroups))
     _raise(st, "bi_mla_decode")
     return out

@@ -612,42 +612,71 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
     return bi_grouped_gemm_ex(A, lda, W, ldw, sW, Y, ldy, group_offsets, E, T, N, K, stream, nullptr);
 }
 
-bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
-                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream,
-                           const bi_launch_opts *opts) {
-    if (B < 0 || H < 0 || Lmax < 0 || Dqk <= 0 || Dv <= 0 || Dv > Dqk) return BI_ERR_SHAPE;
-    if (Dqk % 8 || Dv % 8) return BI_ERR_SHAPE;
+bi_status bi_mla_decode_workspace_size(int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv,
+                                       int64_t *bytes) {
+    if (!bytes) return BI_ERR_NULL;
+    *bytes = 0;
+    if (B < 0 || H < 0 || Lmax < 0 || Dqk <= 0 || Dv <= 0 || Dv > Dqk || Dqk % 8 || Dv % 8) return BI_ERR_SHAPE;
     if (Dqk > bi::kMlaMaxDqk || Dv > bi::kMlaMaxDv || Lmax > bi::kMlaMaxTokens) return BI_ERR_UNSUPPORTED;
     if (B > kI32Max || H > kI32Max || B * H > kI32Max) return BI_ERR_UNSUPPORTED;
+    *bytes = bi::mla_workspace_bytes((int)B, (int)H, (int)Lmax, (int)Dqk, (int)Dv);
+    return BI_OK;
+}
+
+bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
+                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *workspace,
+                           int64_t workspace_bytes, void *stream, const bi_launch_opts *opts) {
+    int64_t need = 0;
+    bi_status st = bi_mla_decode_workspace_size(B, H, Lmax, Dqk, Dv, &need);
+    if (st != BI_OK) return st;
     if (!(scale == scale) || scale > 3.402823466e38f || scale < -3.402823466e38f) return BI_ERR_VALUE;
+    if (workspace && need > 0 && workspace_bytes < need) return BI_ERR_SHAPE;
     if (B == 0 || H == 0) return BI_OK;
     if (!q || !kv || !lens || !out) return BI_ERR_NULL;
-    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lens) & 3u))
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lens) & 3u) ||
+        (workspace && !aligned16(workspace)))
         return BI_ERR_ALIGN;
+    const bool use_ws = workspace && need > 0;
     const Range ro = mat_range(out, B * H, Dv, Dv, 2, 1);
-    if (overlap(ro, mat_range(q, B * H, Dqk, Dqk, 2, 1)) || overlap(ro, mat_range(lens, 1, B, B, 4, 1)) ||
-        (Lmax > 0 && overlap(ro, mat_range(kv, B * Lmax, Dqk, Dqk, 2, 1))))
-        return BI_ERR_ALIAS;
+    const Range rq = mat_range(q, B * H, Dqk, Dqk, 2, 1);
+    const Range rl = mat_range(lens, 1, B, B, 4, 1);
+    const Range rk = Lmax > 0 ? mat_range(kv, B * Lmax, Dqk, Dqk, 2, 1) : Range{0, 0};
+    if (overlap(ro, rq) || overlap(ro, rl) || overlap(ro, rk)) return BI_ERR_ALIAS;
+    if (use_ws) {
+        const Range rw = mat_range(workspace, 1, need, need, 1, 1);
+        if (overlap(rw, ro) || overlap(rw, rq) || overlap(rw, rl) || overlap(rw, rk)) return BI_ERR_ALIAS;
+    }
     int cus = 0;
-    bi_status st = device_cus(&cus);
+    st = device_cus(&cus);
     if (st != BI_OK) return st;
+    // The chunked schedule pays for its fold only when the (request, head
+    // group) units alone leave compute units idle; both give the same bits.
+    const int64_t groups = B * ((H + 15) / 16);
+    const bool split = use_ws && groups < cus;
     bi::MlaArgs a{};
     a.q = q; a.kv = kv; a.lens = lens; a.out = out;
     a.B = (int)B; a.H = (int)H; a.Lmax = (int)Lmax; a.Dqk = (int)Dqk; a.Dv = (int)Dv;
     a.scale = scale;
-    // work units: (request, 16-head group) for the MFMA kernel, one
+    a.ws = split ? static_cast<float *>(workspace) : nullptr;
+    a.nchunk = split ? (int)((Lmax + bi::kMlaChunk - 1) / bi::kMlaChunk) : 0;
+    // work units: (request, 16-head group[, chunk]) for the MFMA kernel, one
     // workgroup per compute unit; (request, head) for the VALU kernel
     const bool mfma = bi::mla_mfma_variant(a.Dqk, a.Dv) != 0;
-    const int64_t units = mfma ? B * ((H + 15) / 16) : B * H;
+    const int64_t units = mfma ? groups * (split ? a.nchunk : 1) : B * H;
+    if (units > kI32Max) return BI_ERR_UNSUPPORTED;
     const int per_cu = mfma ? 1 : (bi::mla_token_capacity(a.Lmax) == 4096 ? 4 : 1);
     const int grid = default_grid((int)units, cus, opts, per_cu);
-    hipError_t e = bi::launch_mla_decode(a, grid, static_cast<hipStream_t>(stream));
+    const int64_t fold_blocks = (groups * 16 * Dv + 255) / 256;  // one thread per output element
+    const int fold_grid = (int)(fold_blocks < (int64_t)cus * 8 ? fold_blocks : (int64_t)cus * 8);
+    hipError_t e = bi::launch_mla_decode(a, grid, fold_grid < 1 ? 1 : fold_grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
 bi_status bi_mla_decode(const void *q, const void *kv, const int32_t *lens, float scale, void *out, int64_t B,
-                        int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream) {
-    return bi_mla_decode_ex(q, kv, lens, scale, out, B, H, Lmax, Dqk, Dv, stream, nullptr);
+                        int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *workspace, int64_t workspace_bytes,
+                        void *stream) {
+    return bi_mla_decode_ex(q, kv, lens, scale, out, B, H, Lmax, Dqk, Dv, workspace, workspace_bytes, stream,
+                            nullptr);
 }
 
 }  // extern "C"

@@ -171,6 +171,7 @@ hipError_t launch_nvfp4_quant(const QuantArgs &args, int grid, hipStream_t strea
 constexpr int kMlaMaxTokens = 16384;  // the weights live in LDS
 constexpr int kMlaMaxDqk = 1024;
 constexpr int kMlaMaxDv = 1024;
+constexpr int kMlaChunk = 2048;  // tokens per chunk of the MFMA kernel's fold
 struct MlaArgs {
     const void *q;        // bf16 [B, H, Dqk]
     const void *kv;       // bf16 [B, Lmax, Dqk]
@@ -178,9 +179,12 @@ struct MlaArgs {
     void *out;            // bf16 [B, H, Dv]
     int B, H, Lmax, Dqk, Dv;
     float scale;
+    float *ws;   // chunk partials (one workgroup per chunk), or null (one per request)
+    int nchunk;  // chunks per (request, head group) in ws: ceil(Lmax / kMlaChunk)
 };
 int mla_token_capacity(int Lmax);     // VALU kernel's LDS capacity; 0 when Lmax is too large
 int mla_mfma_variant(int Dqk, int Dv);  // 0: the VALU kernel serves (Dqk, Dv)
-hipError_t launch_mla_decode(const MlaArgs &args, int grid, hipStream_t stream);
+int64_t mla_workspace_bytes(int B, int H, int Lmax, int Dqk, int Dv);  // 0: no workspace used
+hipError_t launch_mla_decode(const MlaArgs &args, int grid, int fold_grid, hipStream_t stream);
 
 }  // namespace bi

@@ -245,8 +245,9 @@ def test_mla_decode_validation():
     f = B.lib().bi_mla_decode
     Q0, KV0, LN0, O0 = 0x1000000, 0x2000000, 0x6000000, 0x7000000
 
-    def call(q=Q0, kv=KV0, lens=LN0, scale=0.04, out=O0, Bn=4, H=16, Lmax=1024, Dqk=576, Dv=512):
-        return f(q, kv, lens, scale, out, Bn, H, Lmax, Dqk, Dv, None)
+    def call(q=Q0, kv=KV0, lens=LN0, scale=0.04, out=O0, Bn=4, H=16, Lmax=1024, Dqk=576, Dv=512, ws=None,
+             wsb=0):
+        return f(q, kv, lens, scale, out, Bn, H, Lmax, Dqk, Dv, ws, wsb, None)
     assert call(Dqk=572) == B.BI_ERR_SHAPE                      # Dqk % 8
     assert call(Dv=500) == B.BI_ERR_SHAPE                       # Dv % 8
     assert call(Dv=584) == B.BI_ERR_SHAPE                       # Dv > Dqk
@@ -263,3 +264,16 @@ def test_mla_decode_validation():
     assert call(out=KV0 + 4096) == B.BI_ERR_ALIAS                # out over the cache
     assert call(Bn=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
     assert call(H=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
+    need = B.mla_decode_workspace_size(4, 16, 1024, 576, 512)
+    assert need == 4 * 1 * 1 * (32 + 16 * 512) * 4                 # 1 chunk of 2048 tokens
+    WS0 = 0x8000000
+    assert call(ws=WS0, wsb=need - 4) == B.BI_ERR_SHAPE            # too small
+    assert call(ws=WS0 + 8, wsb=need) == B.BI_ERR_ALIGN
+    assert call(ws=KV0 + 4096, wsb=need) == B.BI_ERR_ALIAS          # over the cache
+    assert call(ws=O0 - 64, wsb=need) == B.BI_ERR_ALIAS             # runs into out
+    assert call(Bn=0, q=0, kv=0, lens=0, out=0, ws=WS0, wsb=need) == B.BI_OK
+    # shapes served by the VALU kernel use no workspace
+    assert B.mla_decode_workspace_size(4, 16, 1024, 1024, 1024) == 0
+    assert B.mla_decode_workspace_size(4, 20, 5000, 576, 512) == 4 * 2 * 3 * (32 + 16 * 512) * 4
+    with pytest.raises(B.BiError):
+        B.mla_decode_workspace_size(4, 16, 1024, 572, 512)

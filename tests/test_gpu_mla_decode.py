@@ -44,6 +44,8 @@ def test_mla_decode_parity_and_requests_alone(lens, H, Dqk, Dv, Lmax):
     note(f"mla_decode lens={lens} H={H} Dqk={Dqk} Dv={Dv} Lmax={Lmax}")
     o = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
     check_parity(o, q, kv, lens, scale, Dv, "mla_decode")
+    # one workgroup per 2048-token chunk plus the fold: the same bits
+    assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, workspace=True)), o)
     for b in range(Bn):
         if lens[b] == 0:
             assert not o[b].any(), b
@@ -99,6 +101,8 @@ def test_mla_decode_long_request():
     note("mla_decode L=16384")
     o = host(B.bi_mla_decode(dev(q), dev(kv), lens_dev([L]), scale, Dv))
     check_parity(o, q, kv, [L], scale, Dv, "mla_decode long")
+    ow = host(B.bi_mla_decode(dev(q), dev(kv), lens_dev([L]), scale, Dv, workspace=True))
+    assert np.array_equal(ow, o)
 
 
 def test_mla_decode_exact_cases():
@@ -152,7 +156,15 @@ def test_mla_decode_bench_configuration_sampled():
     o = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
     pick = [0, int(np.argmax(lens)), int(np.argmin(lens)), Bn - 1]
     check_parity(o[pick], q[pick], kv[pick], lens[pick], scale, Dv, "mla_decode bench config")
+    ws = torch.empty(B.mla_decode_workspace_size(Bn, H, Lmax, Dqk, Dv), dtype=torch.uint8, device="cuda")
+    assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, workspace=ws)), o)
+    for mw in (1, 37):
+        assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, workspace=ws,
+                                                   max_workgroups=mw)), o)
     for b in pick:
         alone = host(B.bi_mla_decode(qd[b:b + 1].contiguous(), kvd[b:b + 1].contiguous(), lens_dev(lens[b:b + 1]),
                                      scale, Dv))
+        assert np.array_equal(alone[0], o[b]), b
+        alone = host(B.bi_mla_decode(qd[b:b + 1].contiguous(), kvd[b:b + 1].contiguous(), lens_dev(lens[b:b + 1]),
+                                     scale, Dv, workspace=True))
         assert np.array_equal(alone[0], o[b]), b
