@@ -466,7 +466,7 @@ def main():
         us = timed(lambda r: B.bi_mla_decode(qa, kva, lens_d, 1.0 / 192 ** 0.5, Dv, oa, workspace=wsa), 10)
         byt = 2.0 * int(lens_np.sum()) * Dqk + 2.0 * Bq * Hq * (Dqk + Dv) + 4.0 * Bq
         gbs = byt / (us * 1e-6) / 1e9
-        sweep.append({"op": "mla_decode", "schedule": "workgroup per 2048-token chunk + fold", "B": Bq, "H": Hq, "Dqk": Dqk, "Dv": Dv,
+        sweep.append({"op": "mla_decode", "schedule": "workgroup per 1024-token chunk + fold", "B": Bq, "H": Hq, "Dqk": Dqk, "Dv": Dv,
                       "tokens": int(lens_np.sum()), "us": round(us, 2), "GB/s": round(gbs, 1),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
         o1 = B.bi_mla_decode(qa[3:4].contiguous(), kva[3:4].contiguous(), lens_d[3:4].contiguous(),

@@ -298,7 +298,7 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
  * lengths, B, H, the launch options and whether a workspace is passed.
  * In fp32: scores are MFMA (or fma) chains over d ascending, weights the
  * hardware exp2 of (s_t - running max) * log2(e), the weighted values summed
- * per 2048-token chunk in a fixed order and the chunks folded in ascending
+ * per 1024-token chunk in a fixed order and the chunks folded in ascending
  * order, one division by the weight sum, bf16 round to nearest even.
  *   q: bf16 [B,H,Dqk] dense.  kv: bf16 [B,Lmax,Dqk] dense (request b's
  *     cache is Lmax contiguous rows; rows at or past L_b are never read).
@@ -309,7 +309,7 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
  *     bi_mla_decode_workspace_size() bytes, 16-byte aligned, overlapping
  *     nothing else (BI_ERR_SHAPE if too small).  With it, and when the
  *     (request, 16-head group) pairs are fewer than the device's compute
- *     units, every 2048-token chunk of every request gets its own workgroup
+ *     units, every 1024-token chunk of every request gets its own workgroup
  *     and a second kernel folds the chunks: the same bits, more of the chip
  *     busy.  Its contents need no initialisation and are clobbered.
  *   Dqk % 8 == 0, Dqk <= 1024; Dv % 8 == 0, Dv <= Dqk, Dv <= 1024;

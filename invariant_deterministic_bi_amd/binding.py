@@ -349,7 +349,7 @@ def bi_mla_decode(q, kv, lens, scale, Dv, out=None, *, workspace=None, stream=No
     = softmax(scale * q . kv^T) . kv[..., :Dv] per request and head.
     workspace: None (one workgroup per request), True (allocate one with
     torch), or a device tensor of at least mla_decode_workspace_size bytes
-    (one workgroup per 2048-token chunk when the request and head groups
+    (one workgroup per 1024-token chunk when the request and head groups
     leave compute units idle); the bits are the same."""
     for t, name in ((q, "q"), (kv, "kv")):
         if t.dim() != 3 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_contiguous():

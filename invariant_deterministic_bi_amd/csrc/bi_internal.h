@@ -171,7 +171,7 @@ hipError_t launch_nvfp4_quant(const QuantArgs &args, int grid, hipStream_t strea
 constexpr int kMlaMaxTokens = 16384;  // the weights live in LDS
 constexpr int kMlaMaxDqk = 1024;
 constexpr int kMlaMaxDv = 1024;
-constexpr int kMlaChunk = 2048;  // tokens per chunk of the MFMA kernel's fold
+constexpr int kMlaChunk = 1024;  // tokens per chunk of the MFMA kernel's fold
 struct MlaArgs {
     const void *q;        // bf16 [B, H, Dqk]
     const void *kv;       // bf16 [B, Lmax, Dqk]

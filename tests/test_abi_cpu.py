@@ -265,7 +265,7 @@ def test_mla_decode_validation():
     assert call(Bn=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
     assert call(H=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
     need = B.mla_decode_workspace_size(4, 16, 1024, 576, 512)
-    assert need == 4 * 1 * 1 * (32 + 16 * 512) * 4                 # 1 chunk of 2048 tokens
+    assert need == 4 * 1 * 1 * (32 + 16 * 512) * 4                 # 1 chunk of 1024 tokens
     WS0 = 0x8000000
     assert call(ws=WS0, wsb=need - 4) == B.BI_ERR_SHAPE            # too small
     assert call(ws=WS0 + 8, wsb=need) == B.BI_ERR_ALIGN
@@ -274,6 +274,6 @@ def test_mla_decode_validation():
     assert call(Bn=0, q=0, kv=0, lens=0, out=0, ws=WS0, wsb=need) == B.BI_OK
     # shapes served by the VALU kernel use no workspace
     assert B.mla_decode_workspace_size(4, 16, 1024, 1024, 1024) == 0
-    assert B.mla_decode_workspace_size(4, 20, 5000, 576, 512) == 4 * 2 * 3 * (32 + 16 * 512) * 4
+    assert B.mla_decode_workspace_size(4, 20, 5000, 576, 512) == 4 * 2 * 5 * (32 + 16 * 512) * 4
     with pytest.raises(B.BiError):
         B.mla_decode_workspace_size(4, 16, 1024, 572, 512)

@@ -44,7 +44,7 @@ def test_mla_decode_parity_and_requests_alone(lens, H, Dqk, Dv, Lmax):
     note(f"mla_decode lens={lens} H={H} Dqk={Dqk} Dv={Dv} Lmax={Lmax}")
     o = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
     check_parity(o, q, kv, lens, scale, Dv, "mla_decode")
-    # one workgroup per 2048-token chunk plus the fold: the same bits
+    # one workgroup per 1024-token chunk plus the fold: the same bits
     assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, workspace=True)), o)
     for b in range(Bn):
         if lens[b] == 0:
