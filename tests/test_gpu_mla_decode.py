@@ -168,3 +168,23 @@ def test_mla_decode_bench_configuration_sampled():
         alone = host(B.bi_mla_decode(qd[b:b + 1].contiguous(), kvd[b:b + 1].contiguous(), lens_dev(lens[b:b + 1]),
                                      scale, Dv, workspace=True))
         assert np.array_equal(alone[0], o[b]), b
+
+
+def test_mla_decode_moving_max():
+    """Scores that rise (or fall) along the sequence make the running max
+    change in every 32-token block and every chunk, so every rescale and
+    every chunk fold is exercised; parity, and the same bits with and
+    without the workspace."""
+    H, Dqk, Dv, L = 16, 576, 512, 3000
+    q = inputs.randn_bf16((2, H, Dqk), 0.5, tag=(560,))
+    kv = inputs.randn_bf16((2, L, Dqk), 0.5, tag=(561,))
+    ramp = np.linspace(-6.0, 6.0, L)
+    q[:, :, Dqk - 1] = inputs.to_bf16_bits(np.full((2, H), 4.0))
+    kv[0, :, Dqk - 1] = inputs.to_bf16_bits(ramp)          # rising scores
+    kv[1, :, Dqk - 1] = inputs.to_bf16_bits(ramp[::-1])    # falling scores
+    scale = 1.0 / math.sqrt(192.0)
+    qd, kvd = dev(q), dev(kv)
+    note("mla_decode moving max")
+    o = host(B.bi_mla_decode(qd, kvd, lens_dev([L, L]), scale, Dv))
+    check_parity(o, q, kv, [L, L], scale, Dv, "mla_decode moving max")
+    assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev([L, L]), scale, Dv, workspace=True)), o)
