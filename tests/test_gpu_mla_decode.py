@@ -188,3 +188,40 @@ def test_mla_decode_moving_max():
     o = host(B.bi_mla_decode(qd, kvd, lens_dev([L, L]), scale, Dv))
     check_parity(o, q, kv, [L, L], scale, Dv, "mla_decode moving max")
     assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev([L, L]), scale, Dv, workspace=True)), o)
+
+
+def test_absorbed_mla_decode_pipeline_request_alone():
+    """The absorbed MLA decode step end to end, three library calls: the
+    query's no-rope part times W_UK per head (bi_bmm, [H, B, 128] x [H, 128,
+    512]), joined with its rope part into the 576-wide latent query; attention
+    over the latent cache (bi_mla_decode, with and without the workspace);
+    the latent output times W_UV per head (bi_bmm, [H, B, 512] x [H, 512,
+    128]).  Each request run alone gives bitwise its rows of the batch."""
+    Bn, H, L = 8, 16, 2500
+    lens = inputs.rng(12345, 570).integers(1, L + 1, Bn).astype(np.int32)
+    q_nope = dev(inputs.randn_bf16((Bn, H, 128), 1.0, tag=(571,)))
+    q_pe = dev(inputs.randn_bf16((Bn, H, 64), 1.0, tag=(572,)))
+    w_uk = dev(inputs.randn_bf16((H, 128, 512), 0.09, tag=(573,)))
+    w_uv = dev(inputs.randn_bf16((H, 512, 128), 0.05, tag=(574,)))
+    kv = dev(inputs.randn_bf16((Bn, L, 576), 1.0, tag=(575,)))
+    scale = 1.0 / math.sqrt(192.0)
+
+    def step(rows, workspace):
+        qn = q_nope[rows].permute(1, 0, 2).contiguous()                      # [H, b, 128]
+        q_lat = B.bi_bmm(qn, w_uk).permute(1, 0, 2)                          # [b, H, 512] view
+        q = torch.cat([q_lat, q_pe[rows]], dim=2).contiguous()               # [b, H, 576]
+        o_lat = B.bi_mla_decode(q, kv[rows].contiguous(), lens_dev(lens[rows]), scale, 512,
+                                workspace=workspace)
+        return B.bi_bmm(o_lat.permute(1, 0, 2).contiguous(), w_uv)           # [H, b, 128]
+
+    note("absorbed MLA decode pipeline")
+    allr = list(range(Bn))
+    full = host(step(allr, None))
+    assert np.array_equal(host(step(allr, True)), full)
+    for b in (0, 3, Bn - 1):
+        alone = host(step([b], None))
+        assert np.array_equal(alone[:, 0], full[:, b]), b
+    sub = [6, 1, 4]
+    part = host(step(sub, True))
+    for j, b in enumerate(sub):
+        assert np.array_equal(part[:, j], full[:, b]), b
