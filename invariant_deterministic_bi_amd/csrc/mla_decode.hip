@@ -36,6 +36,7 @@
 // merged ((u0 + u1) + u2) + u3 and divided by the sum.
 
 #include "bi_internal.h"
+#include "gemm_kernel.h"  // buffer-resource loads (zeros past the range, no branch)
 
 namespace bi {
 namespace {
@@ -165,6 +166,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kNW = 4;                    // wavefronts per workgroup (MFMA kernel)
 constexpr int kQStride = kMlaMaxDqk + 8;  // LDS row of Q, padded: 16 rows conflict-free
 
+constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range: loads read zeros
+
+// 16 bytes at byte offset `off` of the buffer `r`, or zeros past its range.
+__device__ __forceinline__ uint4 rload16(gemm_detail::i32x4 r, int off) {
+    return __builtin_bit_cast(uint4, bi_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -221,6 +229,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
         __syncthreads();
 
         const int nblk = (L + 31) >> 5;
+        // the request's L cached rows; rows at or past L read as zeros
+        const gemm_detail::i32x4 rkv = gemm_detail::make_rsrc(kvb, (uint32_t)L * (uint32_t)Dqk * 2u);
         for (int c = c0; c < c1; ++c) {
             f32x4_t o[VB][8];
 #pragma unroll
@@ -236,12 +246,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
                     const int t = t0 + 16 * hb + r16;
-                    const uint16_t *row = kvb + (int64_t)t * Dqk;
                     uint4 kk[KC];
 #pragma unroll
                     for (int cc = 0; cc < KC; ++cc) {
                         const int d = 32 * cc + 8 * g;
-                        kk[cc] = (t < L && d < Dqk) ? *reinterpret_cast<const uint4 *>(row + d) : make_uint4(0, 0, 0, 0);
+                        kk[cc] = rload16(rkv, d < Dqk ? (t * Dqk + d) * 2 : kOutOfRange);
                     }
                     sacc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -294,8 +303,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
-                        const uint4 v = (t < L && d < Dv) ? *reinterpret_cast<const uint4 *>(kvb + (int64_t)t * Dqk + d)
-                                                          : make_uint4(0, 0, 0, 0);
+                        const uint4 v = rload16(rkv, d < Dv ? (t * Dqk + d) * 2 : kOutOfRange);
                         wv[k][0] = v.x; wv[k][1] = v.y; wv[k][2] = v.z; wv[k][3] = v.w;
                     }
 #pragma unroll
