@@ -662,7 +662,7 @@ bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, f
     // work units: (request, 16-head group[, chunk]) for the MFMA kernel, one
     // workgroup per compute unit; (request, head) for the VALU kernel
     const bool mfma = bi::mla_mfma_variant(a.Dqk, a.Dv) != 0;
-    const int64_t units = mfma ? groups * (split ? a.nchunk : 1) : B * H;
+    const int64_t units = mfma ? bi::mla_mfma_units(B * (split ? a.nchunk : 1), (int)((H + 15) / 16)) : B * H;
     if (units > kI32Max) return BI_ERR_UNSUPPORTED;
     const int per_cu = mfma ? 1 : (bi::mla_token_capacity(a.Lmax) == 4096 ? 4 : 1);
     const int grid = default_grid((int)units, cus, opts, per_cu);

@@ -184,6 +184,11 @@ struct MlaArgs {
 };
 int mla_token_capacity(int Lmax);     // VALU kernel's LDS capacity; 0 when Lmax is too large
 int mla_mfma_variant(int Dqk, int Dv);  // 0: the VALU kernel serves (Dqk, Dv)
+// Work units of the MFMA kernel: `keys` (requests, or request chunks) padded
+// to a multiple of 8, times the head groups.
+__host__ __device__ inline int64_t mla_mfma_units(int64_t keys, int head_groups) {
+    return (keys + 7) / 8 * 8 * head_groups;
+}
 int64_t mla_workspace_bytes(int B, int H, int Lmax, int Dqk, int Dv);  // 0: no workspace used
 hipError_t launch_mla_decode(const MlaArgs &args, int grid, int fold_grid, hipStream_t stream);
 

@@ -206,15 +206,24 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
     const int Dqk = a.Dqk, Dv = a.Dv, H = a.H;
     const int HG = (H + 15) >> 4;
     const int qrow = (Dqk + 31) & ~31;  // Q columns staged (zero past Dqk)
-    const int ncu = a.ws ? a.nchunk : 1;  // chunks per (request, head group) in the unit index
-    const int64_t units = (int64_t)a.B * HG * ncu;
+    // A key is a request (or a request's chunk); its head groups read the same
+    // cache rows.  Units are ordered so that a key's head groups get the same
+    // unit index mod 8 -- the same XCD, and so one L2, when the grid is a
+    // multiple of 8 (workgroups are dealt to the XCDs round-robin).
+    const int ncu = a.ws ? a.nchunk : 1;  // chunks per request in the key
+    const int64_t keys = (int64_t)a.B * ncu;
+    const int64_t units = mla_mfma_units(keys, HG);
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-        const int64_t bhg = u / ncu;
-        const int b = (int)(bhg / HG), h0 = (int)(bhg % HG) * 16;
+        const int64_t grp = u / (8 * HG);
+        const int r = (int)(u - grp * 8 * HG);
+        const int64_t key = grp * 8 + (r & 7);
+        if (key >= keys) continue;  // padding of the last group of 8 keys (uniform per workgroup)
+        const int hg = r >> 3;
+        const int b = (int)(key / ncu), h0 = hg * 16;
         int L = a.lens[b];
         L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
         const int nc = (L + kMlaChunk - 1) / kMlaChunk;
-        const int c0 = a.ws ? (int)(u % ncu) : 0, c1 = a.ws ? c0 + 1 : nc;
+        const int c0 = a.ws ? (int)(key % ncu) : 0, c1 = a.ws ? c0 + 1 : nc;
         if (c0 >= nc && a.ws) continue;  // a chunk past the request's end (uniform per workgroup)
         const uint16_t *kvb = static_cast<const uint16_t *>(a.kv) + (int64_t)b * a.Lmax * Dqk;
         const uint16_t *qb = static_cast<const uint16_t *>(a.q) + ((int64_t)b * H + h0) * Dqk;
@@ -358,7 +367,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
             }
             if (a.ws) {
                 // this chunk's partial: m[16], l[16], O[Dv][16]
-                float *pw = a.ws + u * (32 + 16 * (int64_t)Dv);
+                float *pw = a.ws + (((int64_t)b * HG + hg) * ncu + c) * (32 + 16 * (int64_t)Dv);
                 if (tid < 16) {
                     pw[tid] = mch[tid];
                     pw[16 + tid] = lch[tid];
