@@ -251,22 +251,23 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
             for (int kb = c * (kMlaChunk / 32) + w; kb < kb_end; kb += kNW) {
                 const int t0 = kb * 32;
                 // scores: lane holds tokens t0 + 16hb + 4g + i of head r16
-                f32x4_t sacc[2];
+                f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+                uint4 kk[2][KC];
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
                     const int t = t0 + 16 * hb + r16;
-                    uint4 kk[KC];
 #pragma unroll
                     for (int cc = 0; cc < KC; ++cc) {
                         const int d = 32 * cc + 8 * g;
-                        kk[cc] = rload16(rkv, d < Dqk ? (t * Dqk + d) * 2 : kOutOfRange);
+                        kk[hb][cc] = rload16(rkv, d < Dqk ? (t * Dqk + d) * 2 : kOutOfRange);
                     }
-                    sacc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+                // each Q chunk is read from LDS once and feeds both halves' chains
 #pragma unroll
-                    for (int cc = 0; cc < KC; ++cc) {
-                        const uint4 qq = *reinterpret_cast<const uint4 *>(qs + r16 * kQStride + 32 * cc + 8 * g);
-                        sacc[hb] = mfma16(kk[cc], qq, sacc[hb]);
-                    }
+                for (int cc = 0; cc < KC; ++cc) {
+                    const uint4 qq = *reinterpret_cast<const uint4 *>(qs + r16 * kQStride + 32 * cc + 8 * g);
+                    sacc[0] = mfma16(kk[0][cc], qq, sacc[0]);
+                    sacc[1] = mfma16(kk[1][cc], qq, sacc[1]);
                 }
                 float sv[8];
 #pragma unroll
