@@ -262,6 +262,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
                         kk[hb][cc] = rload16(rkv, d < Dqk ? (t * Dqk + d) * 2 : kOutOfRange);
                     }
                 }
+                // the first value block's loads go out before the score MFMAs
+                uint32_t wv0[8][4];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
+                    const uint4 v = rload16(rkv, 8 * r16 < Dv ? (t * Dqk + 8 * r16) * 2 : kOutOfRange);
+                    wv0[k][0] = v.x; wv0[k][1] = v.y; wv0[k][2] = v.z; wv0[k][3] = v.w;
+                }
                 // each Q chunk is read from LDS once and feeds both halves' chains
 #pragma unroll
                 for (int cc = 0; cc < KC; ++cc) {
@@ -312,6 +320,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
                     uint32_t wv[8][4];
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
+                        if (vb == 0) {
+                            wv[k][0] = wv0[k][0]; wv[k][1] = wv0[k][1]; wv[k][2] = wv0[k][2]; wv[k][3] = wv0[k][3];
+                            continue;
+                        }
                         const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
                         const uint4 v = rload16(rkv, d < Dv ? (t * Dqk + d) * 2 : kOutOfRange);
                         wv[k][0] = v.x; wv[k][1] = v.y; wv[k][2] = v.z; wv[k][3] = v.w;
