@@ -313,32 +313,42 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
                 for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) o[vb][j] *= alpha;
-                // values: lane loads its group's 8 tokens x 8 dims (128 vb + 8 r16 ..)
+                // values: lane loads its group's 8 tokens x 8 dims (128 vb + 8 r16 ..);
+                // block vb + 1's loads go out before block vb's MFMAs
+                uint32_t wcur[8][4];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) wcur[k][e] = wv0[k][e];
 #pragma unroll
                 for (int vb = 0; vb < VB; ++vb) {
-                    const int d = 128 * vb + 8 * r16;
-                    uint32_t wv[8][4];
+                    uint32_t wnext[8][4];
+                    if (vb + 1 < VB) {
+                        const int dn = 128 * (vb + 1) + 8 * r16;
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        if (vb == 0) {
-                            wv[k][0] = wv0[k][0]; wv[k][1] = wv0[k][1]; wv[k][2] = wv0[k][2]; wv[k][3] = wv0[k][3];
-                            continue;
+                        for (int k = 0; k < 8; ++k) {
+                            const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
+                            const uint4 v = rload16(rkv, dn < Dv ? (t * Dqk + dn) * 2 : kOutOfRange);
+                            wnext[k][0] = v.x; wnext[k][1] = v.y; wnext[k][2] = v.z; wnext[k][3] = v.w;
                         }
-                        const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
-                        const uint4 v = rload16(rkv, d < Dv ? (t * Dqk + d) * 2 : kOutOfRange);
-                        wv[k][0] = v.x; wv[k][1] = v.y; wv[k][2] = v.z; wv[k][3] = v.w;
                     }
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        // V^T row (dim d + j) over the 8 tokens, in the order of pv
+                        // V^T row (dim 128 vb + 8 r16 + j) over the 8 tokens, in the order of pv
                         const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
                         const int wd = j >> 1;
-                        const uint4 av = make_uint4(__builtin_amdgcn_perm(wv[1][wd], wv[0][wd], sel),
-                                                    __builtin_amdgcn_perm(wv[3][wd], wv[2][wd], sel),
-                                                    __builtin_amdgcn_perm(wv[5][wd], wv[4][wd], sel),
-                                                    __builtin_amdgcn_perm(wv[7][wd], wv[6][wd], sel));
+                        const uint4 av = make_uint4(__builtin_amdgcn_perm(wcur[1][wd], wcur[0][wd], sel),
+                                                    __builtin_amdgcn_perm(wcur[3][wd], wcur[2][wd], sel),
+                                                    __builtin_amdgcn_perm(wcur[5][wd], wcur[4][wd], sel),
+                                                    __builtin_amdgcn_perm(wcur[7][wd], wcur[6][wd], sel));
                         o[vb][j] = mfma16(av, phi, o[vb][j]);
                         o[vb][j] = mfma16(av, plo, o[vb][j]);
+                    }
+                    if (vb + 1 < VB) {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) wcur[k][e] = wnext[k][e];
                     }
                 }
             }
