@@ -296,10 +296,13 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
  * The order of every sum is fixed by L_b, Dqk and Dv alone: out[b][h] is
  * bitwise the same whatever other requests share the call, whatever their
  * lengths, B, H, the launch options and whether a workspace is passed.
- * In fp32: scores are MFMA (or fma) chains over d ascending, weights the
- * hardware exp2 of (s_t - running max) * log2(e), the weighted values summed
- * per 1024-token chunk in a fixed order and the chunks folded in ascending
- * order, one division by the weight sum, bf16 round to nearest even.
+ * In fp32, for Dqk in 545..576 with Dv in 385..512 (DeepSeek's 576 / 512),
+ * Dqk in 97..128 or 33..64 with Dv <= 128 (the matrix-core kernel):
+ * scores are MFMA chains over d ascending, weights the hardware exp2 of
+ * (s_t - running max) * log2(e), the weighted values summed per 1024-token
+ * chunk in a fixed order and the chunks folded in ascending order, one
+ * division by the weight sum, bf16 round to nearest even.  Other shapes use
+ * fp32 fma chains with one max over the whole request and no chunks.
  *   q: bf16 [B,H,Dqk] dense.  kv: bf16 [B,Lmax,Dqk] dense (request b's
  *     cache is Lmax contiguous rows; rows at or past L_b are never read).
  *   lens: DEVICE int32 [B], 4-byte aligned; read only by the kernels, which
