@@ -34,7 +34,10 @@ def check_parity(o_bits, q, kv, lens, scale, Dv, what):
                                                 ([5, 0, 13], 2, 8, 8, 16),
                                                 ([200, 33], 4, 1024, 1024, 200),
                                                 ([100, 7, 64], 20, 576, 512, 128),
-                                                ([33, 1], 5, 128, 64, 40)])
+                                                ([33, 1], 5, 128, 64, 40),
+                                                # matrix-core kernel with a partial last K chunk and value block
+                                                ([50, 1100, 0], 16, 568, 392, 1200),
+                                                ([9, 70], 3, 40, 24, 80)])
 def test_mla_decode_parity_and_requests_alone(lens, H, Dqk, Dv, Lmax):
     Bn = len(lens)
     scale = 1.0 / math.sqrt(192.0)
