@@ -138,24 +138,6 @@ def test_nvfp4_equals_bf16_gemm_on_decoded_weights():
     assert np.array_equal(y4, yb)
 
 
-def test_nvfp4_config_parity_and_invariance():
-    """W[24576,4096] quantised from N(0,0.02); A bf16 N(0,1), M up to 4096."""
-    N, K, Mmax = 24576, 4096, 4096
-    W, Ws, g = _nvfp4_weights(N, K, (125,))
-    alpha = float(np.float32(1.0) / g)
-    A = inputs.randn_bf16((Mmax, K), tag=(126,))
-    Ad, Wd, Wsd = dev(A), dev(W), dev(Ws)
-    note("nvfp4 M=4096")
-    yfull = host(B.bi_nvfp4_gemm(Ad, Wd, Wsd, alpha))
-    rows = np.array([0, 1, 2, 1000, Mmax - 1])
-    ref, s = oracle.nvfp4_gemm(A, None, W, Ws, alpha, K, rows=rows)
-    assert_within_tol(yfull[rows], ref, s, "nvfp4 sampled rows")
-    for M in (1, 2, 4, 16, 64, 256, 1024):
-        note(f"nvfp4 M={M}")
-        y = host(B.bi_nvfp4_gemm(Ad[:M], Wd, Wsd, alpha))
-        assert np.array_equal(y, yfull[:M]), f"M={M}"
-
-
 def test_nvfp4_activation_rows_quantised_alone():
     """W4A4: a row quantised alone with the batch's global scale gives the
     same codes, hence the same output row."""
@@ -188,7 +170,7 @@ def test_rmsnorm_parity_and_invariance(H, Mmax):
     note(f"rmsnorm H={H} M={Mmax}")
     y = host(B.bi_rmsnorm(Xd, gd, eps))
     assert_within_tol(y, ref, np.abs(ref), f"rmsnorm H={H}")
-    for M in sorted({1, 2, 7, Mmax // 2}):
+    for M in sorted({1 << i for i in range(Mmax.bit_length()) if (1 << i) < Mmax} | {7, Mmax // 2}):
         yM = host(B.bi_rmsnorm(Xd[:M], gd, eps))
         assert np.array_equal(yM, y[:M])
     perm = inputs.rng(12345, 132).permutation(Mmax)

@@ -69,8 +69,8 @@ def test_mla_decode_parity_and_requests_alone(lens, H, Dqk, Dv, Lmax):
 
 def test_mla_decode_batch_composition_and_capacity():
     """A request's output is the same bits inside batches of other requests of
-    other lengths, and whether the cache layout holds 4096 or 5000 rows per
-    request (the kernel's two LDS capacities)."""
+    other lengths, and whether the dense cache layout holds 4096 or 5000 rows
+    per request (matrix-core kernel, Dqk 576 / Dv 512)."""
     H, Dqk, Dv = 16, 576, 512
     scale = 0.0721
     q = inputs.randn_bf16((6, H, Dqk), 1.0, tag=(510,))
@@ -228,3 +228,37 @@ def test_absorbed_mla_decode_pipeline_request_alone():
     part = host(step(sub, True))
     for j, b in enumerate(sub):
         assert np.array_equal(part[:, j], full[:, b]), b
+
+
+@pytest.mark.parametrize("Dqk,Dv", [(256, 256), (1024, 1024)])
+def test_mla_decode_fp32_kernel_large_capacity(Dqk, Dv):
+    """Shapes the fp32 (VALU) kernel serves, at its larger LDS capacity
+    (Lmax above 4096 keeps up to 16384 weights per workgroup): parity; each
+    request alone; the requests of at most 4096 tokens bitwise the same in a
+    4096-row layout (the smaller capacity) as in the 5000-row one; and one
+    request of 16384 tokens."""
+    H, Lmax = 4, 5000
+    lens = [5000, 4096, 1, 0, 3000]
+    Bn = len(lens)
+    scale = 1.0 / math.sqrt(192.0)
+    q = inputs.randn_bf16((Bn, H, Dqk), 1.0, tag=(580, Dqk))
+    kv = inputs.randn_bf16((Bn, Lmax, Dqk), 1.0, tag=(581, Dqk))
+    qd, kvd = dev(q), dev(kv)
+    note(f"mla_decode fp32 kernel Dqk={Dqk} Lmax={Lmax}")
+    o = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
+    check_parity(o, q, kv, lens, scale, Dv, "mla_decode fp32 kernel Lmax 5000")
+    assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, workspace=True)), o)
+    for b in range(Bn):
+        alone = host(B.bi_mla_decode(qd[b:b + 1].contiguous(), kvd[b:b + 1].contiguous(), lens_dev([lens[b]]),
+                                     scale, Dv))
+        assert np.array_equal(alone[0], o[b]), b
+    small = [1, 2, 3, 4]
+    narrow = host(B.bi_mla_decode(qd[small].contiguous(), kvd[small, :4096].contiguous(),
+                                  lens_dev([lens[i] for i in small]), scale, Dv))
+    assert np.array_equal(narrow, o[small])
+    L = 16384
+    q1 = inputs.randn_bf16((1, H, Dqk), 1.0, tag=(582, Dqk))
+    kv1 = inputs.randn_bf16((1, L, Dqk), 1.0, tag=(583, Dqk))
+    note(f"mla_decode fp32 kernel Dqk={Dqk} L={L}")
+    o1 = host(B.bi_mla_decode(dev(q1), dev(kv1), lens_dev([L]), scale, Dv))
+    check_parity(o1, q1, kv1, [L], scale, Dv, "mla_decode fp32 kernel L 16384")
