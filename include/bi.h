@@ -332,6 +332,30 @@ bi_status bi_mla_decode(const void *q, const void *kv, const int32_t *lens, floa
 bi_status bi_mla_decode_workspace_size(int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv,
                                        int64_t *bytes);
 
+/*
+ * bi_mla_decode_noalloc: bi_mla_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It takes no workspace and calls no
+ * allocator: when the chunked schedule applies (fewer (request, 16-head
+ * group) pairs than compute units and a shape with a nonzero
+ * bi_mla_decode_workspace_size), its chunk partials go to a scratch array
+ * the library holds on each GPU, BI_MLA_SCRATCH_BYTES (32 MiB) large,
+ * reserved when the library's code is loaded on that GPU and kept until
+ * the process ends.  The outputs are bitwise those of bi_mla_decode.
+ *   Arguments, layouts, ownership and the other errors are bi_mla_decode's.
+ *   BI_ERR_UNSUPPORTED when the chunked schedule would need more than
+ *   BI_MLA_SCRATCH_BYTES (workspace size above it and fewer pairs than
+ *   compute units); the caller can then use bi_mla_decode with a workspace.
+ *   Every call on one GPU shares that GPU's array and overwrites it; calls
+ *   that overlap in time on one GPU (e.g. on two streams) race and give
+ *   undefined results.  Calls on one stream are ordered and safe.  The
+ *   array needs no initialisation: every partial is written before it is
+ *   read within the call.
+ */
+#define BI_MLA_SCRATCH_BYTES ((int64_t)32 << 20)
+bi_status bi_mla_decode_noalloc(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
+                                int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream);
+
 /* The *_ex variants take launch options (may be NULL = defaults). */
 bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y,
                      int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream,

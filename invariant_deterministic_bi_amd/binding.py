@@ -74,6 +74,7 @@ _SIGS = {
     "bi_grouped_gemm_ex": [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p],
     "bi_mla_decode": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _p],
     "bi_mla_decode_ex": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "bi_mla_decode_noalloc": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _i64, _i64, _p],
     "bi_mla_decode_workspace_size": [_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_int64)],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
@@ -372,4 +373,29 @@ def bi_mla_decode(q, kv, lens, scale, Dv, out=None, *, workspace=None, stream=No
     st = lib().bi_mla_decode_ex(_ptr(q), _ptr(kv), _ptr(lens), float(scale), _ptr(out), B, H, Lmax, Dqk, Dv,
                                 ws_ptr, ws_bytes, _stream(stream), _opts(max_workgroups))
     _raise(st, "bi_mla_decode")
+    return out
+
+
+MLA_SCRATCH_BYTES = 32 << 20  # BI_MLA_SCRATCH_BYTES
+
+
+def bi_mla_decode_noalloc(q, kv, lens, scale, Dv, out):
+    """bi_mla_decode without a workspace and without any allocation: the
+    chunked schedule's partials go to the library's per-GPU scratch array.
+    `out` (bf16 [B,H,Dv], dense) must be given: nothing is allocated here
+    either."""
+    for t, name in ((q, "q"), (kv, "kv")):
+        if t.dim() != 3 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a dense 3-d bf16 tensor")
+    B, H, Dqk = q.shape
+    B2, Lmax, D2 = kv.shape
+    if B2 != B or D2 != Dqk:
+        raise ValueError("q and kv disagree on B or Dqk")
+    if lens.dtype != torch.int32 or lens.dim() != 1 or lens.shape[0] != B or not lens.is_cuda:
+        raise ValueError("lens must be a device int32 tensor of B entries")
+    if tuple(out.shape) != (B, H, Dv) or not out.is_contiguous():
+        raise ValueError("out must be a dense [B,H,Dv] tensor")
+    st = lib().bi_mla_decode_noalloc(_ptr(q), _ptr(kv), _ptr(lens), float(scale), _ptr(out), B, H, Lmax, Dqk,
+                                     Dv, _stream(None))
+    _raise(st, "bi_mla_decode_noalloc")
     return out

@@ -623,29 +623,48 @@ bi_status bi_mla_decode_workspace_size(int64_t B, int64_t H, int64_t Lmax, int64
     return BI_OK;
 }
 
-bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
-                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *workspace,
-                           int64_t workspace_bytes, void *stream, const bi_launch_opts *opts) {
-    int64_t need = 0;
-    bi_status st = bi_mla_decode_workspace_size(B, H, Lmax, Dqk, Dv, &need);
+}  // extern "C"
+
+namespace {
+
+// Host-side validation shared by the decode-attention entry points; *need is
+// the workspace size of the shape.  BI_OK with B == 0 or H == 0 means a no-op.
+bi_status mla_check(const void *q, const void *kv, const int32_t *lens, float scale, void *out, int64_t B,
+                    int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *workspace, int64_t workspace_bytes,
+                    int64_t *need) {
+    bi_status st = bi_mla_decode_workspace_size(B, H, Lmax, Dqk, Dv, need);
     if (st != BI_OK) return st;
     if (!(scale == scale) || scale > 3.402823466e38f || scale < -3.402823466e38f) return BI_ERR_VALUE;
-    if (workspace && need > 0 && workspace_bytes < need) return BI_ERR_SHAPE;
+    if (workspace && *need > 0 && workspace_bytes < *need) return BI_ERR_SHAPE;
     if (B == 0 || H == 0) return BI_OK;
     if (!q || !kv || !lens || !out) return BI_ERR_NULL;
     if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lens) & 3u) ||
         (workspace && !aligned16(workspace)))
         return BI_ERR_ALIGN;
-    const bool use_ws = workspace && need > 0;
     const Range ro = mat_range(out, B * H, Dv, Dv, 2, 1);
     const Range rq = mat_range(q, B * H, Dqk, Dqk, 2, 1);
     const Range rl = mat_range(lens, 1, B, B, 4, 1);
     const Range rk = Lmax > 0 ? mat_range(kv, B * Lmax, Dqk, Dqk, 2, 1) : Range{0, 0};
     if (overlap(ro, rq) || overlap(ro, rl) || overlap(ro, rk)) return BI_ERR_ALIAS;
-    if (use_ws) {
-        const Range rw = mat_range(workspace, 1, need, need, 1, 1);
+    if (workspace && *need > 0) {
+        const Range rw = mat_range(workspace, 1, *need, *need, 1, 1);
         if (overlap(rw, ro) || overlap(rw, rq) || overlap(rw, rl) || overlap(rw, rk)) return BI_ERR_ALIAS;
     }
+    return BI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
+                           int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *workspace,
+                           int64_t workspace_bytes, void *stream, const bi_launch_opts *opts) {
+    int64_t need = 0;
+    bi_status st = mla_check(q, kv, lens, scale, out, B, H, Lmax, Dqk, Dv, workspace, workspace_bytes, &need);
+    if (st != BI_OK) return st;
+    if (B == 0 || H == 0) return BI_OK;
+    const bool use_ws = workspace && need > 0;
     int cus = 0;
     st = device_cus(&cus);
     if (st != BI_OK) return st;
@@ -670,6 +689,28 @@ bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, f
     const int fold_grid = (int)(fold_blocks < (int64_t)cus * 8 ? fold_blocks : (int64_t)cus * 8);
     hipError_t e = bi::launch_mla_decode(a, grid, fold_grid < 1 ? 1 : fold_grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+bi_status bi_mla_decode_noalloc(const void *q, const void *kv, const int32_t *lens, float scale, void *out,
+                                int64_t B, int64_t H, int64_t Lmax, int64_t Dqk, int64_t Dv, void *stream) {
+    int64_t need = 0;
+    bi_status st = mla_check(q, kv, lens, scale, out, B, H, Lmax, Dqk, Dv, nullptr, 0, &need);
+    if (st != BI_OK || B == 0 || H == 0) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != BI_OK) return st;
+    // The chunked schedule, the only one that needs scratch, runs exactly when
+    // bi_mla_decode with a workspace would run it: fewer (request, head group)
+    // pairs than compute units.  Its partials then go to the library's array.
+    void *ws = nullptr;
+    if (need > 0 && B * ((H + 15) / 16) < cus) {
+        if (need > bi::kMlaScratchBytes) return BI_ERR_UNSUPPORTED;
+        float *p = nullptr;
+        if (bi::mla_scratch(&p) != hipSuccess) return BI_ERR_HIP;
+        ws = p;
+    }
+    return bi_mla_decode_ex(q, kv, lens, scale, out, B, H, Lmax, Dqk, Dv, ws, ws ? bi::kMlaScratchBytes : 0, stream,
+                            nullptr);
 }
 
 bi_status bi_mla_decode(const void *q, const void *kv, const int32_t *lens, float scale, void *out, int64_t B,

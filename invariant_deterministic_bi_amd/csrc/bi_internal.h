@@ -190,6 +190,11 @@ __host__ __device__ inline int64_t mla_mfma_units(int64_t keys, int head_groups)
     return (keys + 7) / 8 * 8 * head_groups;
 }
 int64_t mla_workspace_bytes(int B, int H, int Lmax, int Dqk, int Dv);  // 0: no workspace used
+// The library-held chunk-partial scratch of bi_mla_decode_noalloc: its size,
+// and its device address on the current device (looked up once per device).
+constexpr int64_t kMlaScratchBytes = (int64_t)32 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t mla_scratch(float **out);
 hipError_t launch_mla_decode(const MlaArgs &args, int grid, int fold_grid, hipStream_t stream);
 
 }  // namespace bi

@@ -35,6 +35,8 @@
 // wave w accumulates p_t * v_t over tokens w, w+4, ... as fp32 fma chains,
 // merged ((u0 + u1) + u2) + u3 and divided by the sum.
 
+#include <atomic>
+
 #include "bi_internal.h"
 #include "gemm_kernel.h"  // buffer-resource loads (zeros past the range, no branch)
 
@@ -456,7 +458,34 @@ __global__ __launch_bounds__(256) void mla_fold_kernel(MlaArgs a) {
     }
 }
 
+std::atomic<float *> g_scratch_ptr[kMaxDevices];
+
 }  // namespace
+
+// Library-held scratch for callers that cannot allocate: the chunk partials
+// of the chunked schedule, kMlaScratchBytes per GPU, held from the code
+// object's load until the process ends.  Host code must never pass this
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// uses the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device in mla_scratch.
+static __device__ __align__(256) float scratch[kMlaScratchBytes / sizeof(float)];
+
+hipError_t mla_scratch(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // with `dev` current: each GPU holds its own copy of the array
+        e = hipGetSymbolAddress(reinterpret_cast<void **>(&p), HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 int mla_token_capacity(int Lmax) { return Lmax <= 4096 ? 4096 : (Lmax <= kMlaMaxTokens ? kMlaMaxTokens : 0); }
 

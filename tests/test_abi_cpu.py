@@ -277,3 +277,23 @@ def test_mla_decode_validation():
     assert B.mla_decode_workspace_size(4, 20, 5000, 576, 512) == 4 * 2 * 5 * (32 + 16 * 512) * 4
     with pytest.raises(B.BiError):
         B.mla_decode_workspace_size(4, 16, 1024, 572, 512)
+
+
+def test_mla_decode_noalloc_validation():
+    """The no-allocation decode entry point validates like bi_mla_decode
+    before it touches the device or its scratch array."""
+    f = B.lib().bi_mla_decode_noalloc
+    Q0, KV0, LN0, O0 = 0x1000000, 0x2000000, 0x6000000, 0x7000000
+
+    def call(q=Q0, kv=KV0, lens=LN0, scale=0.04, out=O0, Bn=4, H=16, Lmax=1024, Dqk=576, Dv=512):
+        return f(q, kv, lens, scale, out, Bn, H, Lmax, Dqk, Dv, None)
+    assert call(Dqk=572) == B.BI_ERR_SHAPE
+    assert call(Dv=584) == B.BI_ERR_SHAPE
+    assert call(Lmax=16385) == B.BI_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == B.BI_ERR_VALUE
+    assert call(lens=0) == B.BI_ERR_NULL
+    assert call(q=Q0 + 8) == B.BI_ERR_ALIGN
+    assert call(out=KV0 + 4096) == B.BI_ERR_ALIAS
+    assert call(Bn=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
+    assert call(H=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
+    assert B.MLA_SCRATCH_BYTES == 32 << 20
