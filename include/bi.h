@@ -11,22 +11,28 @@
  *     snippets", test_nvfp4_gemm_batch_invariance) and the vLLM PR #51292 page
  *     checks run to run (section "Test Plan": 8 identical runs, 1 distinct
  *     output).
- *   - How each output is computed depends on the operation and on (N, K)
- *     (H for RMSNorm) only, never on M: one tile shape, one MFMA instruction,
- *     one ascending K order, no split-K, no stream-K, no atomics.  M changes
- *     only the number of tiles and the tail masks.  The PR #39912 page calls
- *     the M-bucketed kernel configurations the thing batch-invariant mode must
+ *   - The arithmetic of each output depends on the operation and on (N, K)
+ *     (H for RMSNorm) only, never on M: one MFMA instruction, one ascending
+ *     K order, one lane accumulating each output over the whole K range,
+ *     no split-K, no stream-K, no atomics.  The PR #39912 page calls the
+ *     M-bucketed kernel configurations the thing batch-invariant mode must
  *     avoid (section "implementation breakdown": only the default config with
  *     a persistent scheduler), and the PR #51292 page names size-gated kernel
- *     selection as the bug class (root-cause comment).
+ *     selection as the bug class (root-cause comment).  Which kernel runs
+ *     that arithmetic does depend on M: the tiled kernel of bi_plan_query's
+ *     tile shape, or at small M a streaming kernel that spreads column items
+ *     of the weight over the whole chip.  bi_plan_regimes lists every such
+ *     choice and its row range; all of them give the same bits.
  *   - There is no mode switch and no environment variable: invariance is
  *     unconditional (the PR #39912 page lists a cached mode flag as a risk,
  *     section "risks and impact").
  *
  * Memory and streams:
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *     never allocates, frees or keeps device memory, and keeps no per-call
- *     state; calls are thread-safe.
+ *     never allocates or frees device memory and keeps no per-call state;
+ *     calls are thread-safe.  The one memory it holds is the scratch array
+ *     of bi_mla_decode_noalloc (BI_MLA_SCRATCH_BYTES per GPU, reserved with
+ *     the library's code).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without synchronising.  Kernel faults surface at
  *     the caller's next synchronisation.
@@ -395,6 +401,57 @@ bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, f
  * Host-only; makes no HIP call.
  */
 bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out);
+
+/*
+ * The kernels that serve the GEMM family.  Each runs the per-element chain
+ * of bi_plan_query's recipe for (N, K) -- one 16x16x32 bf16 MFMA per 32-wide
+ * K chunk in ascending order from +0, fp32 accumulation by one lane for the
+ * whole K range, (alpha x) then bf16 round to nearest even -- so a row's bits
+ * do not depend on which kernel computes it.
+ */
+typedef enum bi_kernel_kind {
+    BI_KERNEL_TILED = 0,           /* persistent tiled kernel, bm x bn tiles (classic schedule) */
+    BI_KERNEL_TILED_PINGPONG = 1,  /* the same tile, wavefronts alternating load and MFMA phases */
+    BI_KERNEL_STREAM_A_LDS = 2,    /* weight streamed into registers in column items, A staged in LDS */
+    BI_KERNEL_STREAM_REG = 3,      /* weight and A fragments streamed into registers, column items */
+    BI_KERNEL_STREAM_RING = 4,     /* weight streamed through a per-wavefront LDS ring, column items */
+    BI_KERNEL_BMM_STREAM = 5       /* BMM: a 128-column B block kept in LDS, A streamed in 64-row tiles */
+} bi_kernel_kind;
+
+/*
+ * One row range of the kernel choice: calls with m_min <= M <= m_max run
+ * `kernel` (m_max = 2^31-1: no bound).  row_blocks: 16-row MFMA blocks of A
+ * that each weight fragment feeds (tiled: bm / 16); cols: output columns per
+ * work item (tiled: bn); a_pairs: 1 when one load carries A rows 0-7 of two
+ * K chunks; a_rows_staged: rows of A the LDS-ring kernel stages (4, 8, 16).
+ */
+typedef struct bi_regime {
+    int32_t kernel;
+    int32_t m_min, m_max;
+    int32_t row_blocks;
+    int32_t cols;
+    int32_t a_pairs;
+    int32_t a_rows_staged;
+    int32_t reserved;
+} bi_regime;
+
+/*
+ * bi_plan_regimes: every kernel an (op, N, K) call can run, with the row
+ * ranges that select it, in ascending M; they cover M >= 1 with no gap.
+ * This is the host's whole kernel-choice rule: the choice depends on M as
+ * well as (op, N, K) -- a departure from a single tile per (N, K) -- and
+ * never changes an output bit (every kernel runs the same chain; the
+ * bitwise tests cross every edge listed here).
+ *   a_fmt: BI_A_BF16, or BI_A_NVFP4 for an NVFP4 A (BI_OP_NVFP4_GEMM only).
+ *   cus: compute units of the device the calls run on (one of the edges,
+ *     the A-in-LDS limit 10 * M * cus <= 7 * N, depends on it), or 0 for the
+ *     current device (one HIP attribute query).
+ *   out: room for `capacity` entries; *count = the number of regimes
+ *   (BI_ERR_SHAPE, with *count set, when capacity is too small).
+ *   Ops other than the GEMM family: BI_ERR_UNSUPPORTED.
+ */
+bi_status bi_plan_regimes(int op, int64_t N, int64_t K, int a_fmt, int cus, bi_regime *out, int capacity,
+                          int *count);
 
 /*
  * bi_tile_shape: describe compiled tile shape v (0-based) of the GEMM

@@ -40,6 +40,17 @@ class BiPlan(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
 
 
+class BiRegime(ctypes.Structure):
+    _fields_ = [("kernel", _i32), ("m_min", _i32), ("m_max", _i32), ("row_blocks", _i32), ("cols", _i32),
+                ("a_pairs", _i32), ("a_rows_staged", _i32), ("reserved", _i32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+KERNEL_KINDS = ("tiled", "tiled_pingpong", "stream_a_lds", "stream_reg", "stream_ring", "bmm_stream")
+
+
 class BiLaunchOpts(ctypes.Structure):
     _fields_ = [("max_workgroups", _i32), ("tile_variant", _i32), ("pipeline_depth", _i32),
                 ("reserved", _i32 * 5)]
@@ -78,6 +89,8 @@ _SIGS = {
     "bi_mla_decode_workspace_size": [_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_int64)],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
+    "bi_plan_regimes": [ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(BiRegime),
+                        ctypes.c_int, ctypes.POINTER(ctypes.c_int)],
 }
 
 
@@ -117,6 +130,23 @@ def plan_query(op: int, N: int, K: int) -> dict:
     if st != BI_OK:
         raise BiError(st, "bi_plan_query")
     return pl.as_dict()
+
+
+def plan_regimes(op: int, N: int, K: int, a_fmt: int = BI_A_BF16, cus: int = 0) -> list:
+    """Every kernel an (op, N, K) call can run and the row ranges that select
+    it (bi_plan_regimes), as dicts with a 'kind' name added."""
+    cap = 64
+    arr = (BiRegime * cap)()
+    n = ctypes.c_int(0)
+    st = lib().bi_plan_regimes(int(op), int(N), int(K), int(a_fmt), int(cus), arr, cap, ctypes.byref(n))
+    if st != BI_OK:
+        raise BiError(st, "bi_plan_regimes")
+    out = []
+    for i in range(n.value):
+        d = arr[i].as_dict()
+        d["kind"] = KERNEL_KINDS[d["kernel"]]
+        out.append(d)
+    return out
 
 
 def tile_shapes() -> list:

@@ -1,13 +1,16 @@
 // C-ABI layer of libbi: argument validation, the (op, N, K) -> recipe table,
-// persistent-grid sizing and kernel launch.  Declarations and the contract
-// are in include/bi.h.
+// the kernel regimes, persistent-grid sizing and kernel launch.
+// Declarations and the contract are in include/bi.h.
 //
-// Nothing here looks at M except to size the grid, mask tails and validate
-// pointers: the recipe comes from bi_plan_query(op, N, K), which has no M
-// argument.  This is the batch-invariant kernel-selection rule: the vLLM PR
-// #39912 summary page (section "implementation breakdown") pins the default
-// config instead of the M-bucketed ones, and the vLLM PR #51292 page's
-// root-cause comment names size-gated selection as the failure mode.
+// The per-element recipe -- the MFMA instruction, the K order, the
+// accumulator and the epilogue -- depends on (op, N, K) only.  The kernel
+// that runs it does depend on M: the tiled kernel of bi_plan_query's shape,
+// or, at small M, a streaming kernel (classify() below; the ranges are
+// listed by bi_plan_regimes).  The vLLM PR #39912 summary page (section
+// "implementation breakdown") pins one default config instead of M-bucketed
+// ones, and the vLLM PR #51292 page's root-cause comment names size-gated
+// selection as the failure mode; here every kernel a shape can take runs the
+// identical per-element chain, and the bitwise tests walk every regime edge.
 
 #include <atomic>
 #include <cstdint>
@@ -134,109 +137,90 @@ int default_grid(int tiles, int cus, const bi_launch_opts *opts, int per_cu) {
     return tiles < cap ? tiles : cap;
 }
 
-bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *stream,
-                   const bi_launch_opts *opts) {
-    // M <= 16: every valid row fits one 16-row MFMA block; the skinny kernel
-    // streams 16-column blocks of the weight with no barrier.  It runs the
-    // same per-element MFMA chain as the tiled kernel (bits are identical);
-    // a forced tile_variant keeps the tiled kernel so the two can be compared.
-    if ((op == BI_OP_GEMM || op == BI_OP_NVFP4_GEMM) && in.M <= 16 && a_mode == bi::OPND_BF16_ROWS &&
-        (b_mode == bi::OPND_BF16_ROWS || b_mode == bi::OPND_NVFP4_RAW) &&
-        !(opts && opts->tile_variant != 0)) {
-        int cus = 0;
-        bi_status st = device_cus(&cus);
-        if (st != BI_OK) return st;
-        const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
+// ---------------------------------------------------------------------------
+// Kernel regimes of the GEMM family.  Every kernel below runs the same
+// per-element chain -- one 16x16x32 bf16 MFMA per 32-wide K chunk, K
+// ascending from +0, one fp32 accumulator per output owned by one lane for
+// the whole K range, (alpha x) then bf16 RNE -- so each gives the tiled
+// kernel's bits.  Which one runs is chosen on the host from the row count M
+// as well as (op, N, K): at M <= 16 (and to 128 rows for bf16 weights of
+// N <= 12288, to 64 for NVFP4 weights) a streaming kernel spreads 8- or
+// 16-column items of the weight over every compute unit, which the per-(N,K)
+// tile cannot do at small M.  This departs from a single tile per (N, K); it
+// is kept safe by that identical chain and by bitwise tests at every regime
+// edge of every configured (N, K).  classify() is the whole rule: run_gemm
+// dispatches on it and bi_plan_regimes() enumerates it.
+// ---------------------------------------------------------------------------
+struct Regime {
+    int kind;   // bi_kernel_kind
+    int rb;     // 16-row MFMA blocks of A per weight fragment (tiled: bm / 16)
+    int ap;     // one load carries A rows 0-7 of two K chunks (M <= 8)
+    int ma;     // rows of A staged by the LDS-ring kernel (4, 8 or 16)
+    int cols;   // output columns per item (tiled: bn)
+    int variant;  // tiled: index into kTileShapes
+    bool operator==(const Regime &o) const {
+        return kind == o.kind && rb == o.rb && ap == o.ap && ma == o.ma && cols == o.cols && variant == o.variant;
+    }
+};
+
+constexpr int64_t kStreamMaxRows = 128;  // above this every call takes the tiled kernel
+
+Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch, bool grouped, int cus,
+                int64_t M) {
+    const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
+    const bool stream_modes = a_mode == bi::OPND_BF16_ROWS && (b_mode == bi::OPND_BF16_ROWS || fp4);
+    if ((op == BI_OP_GEMM || op == BI_OP_NVFP4_GEMM) && M <= 16 && stream_modes) {
         // A in LDS when its copy into every compute unit (M * K * 2 bytes
         // each) is at most 0.7 times the weight bytes that unit streams; else
-        // A is loaded along with the weight fragments.
-        if (bi::direct_alds_ok(static_cast<int>(in.M), static_cast<int>(in.K), fp4) &&
-            (fp4 || 10 * in.M * static_cast<int64_t>(cus) <= 7 * in.N)) {
-            // A in LDS.  8-column items when 16-column ones would leave fewer
-            // than two per compute unit.  One wavefront per item up to three
-            // per compute unit; beyond that a bf16 weight streams best from one
-            // wavefront per compute unit (fewer concurrent row streams in HBM),
-            // an NVFP4 one from three (its decode needs the SIMDs).
-            const int nb = (!fp4 && (in.N + 15) / 16 < 2 * static_cast<int64_t>(cus)) ? 8 : 16;
-            const int items = static_cast<int>((in.N + nb - 1) / nb);
-            int waves = items <= 3 * cus ? items : fp4 ? 3 * cus : cus;
-            if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
-            const int depth = opts ? opts->pipeline_depth : 0;
-            hipError_t e = bi::launch_direct_alds(in, fp4, nb, waves, cus, depth, static_cast<hipStream_t>(stream));
-            return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+        // A is loaded along with the weight fragments.  8-column items when
+        // 16-column ones would leave fewer than two per compute unit.
+        if (bi::direct_alds_ok(static_cast<int>(M), static_cast<int>(K), fp4) && (fp4 || 10 * M * cus <= 7 * N)) {
+            const int nb = (!fp4 && (N + 15) / 16 < 2 * static_cast<int64_t>(cus)) ? 8 : 16;
+            return {BI_KERNEL_STREAM_A_LDS, 1, 0, 0, nb, -1};
         }
-        if (b_mode == bi::OPND_BF16_ROWS) {
-            // one wavefront per 16-column item, up to 16 per compute unit
-            const int items = static_cast<int>((in.N + 15) / 16);
-            const int grid = default_grid(items, cus, opts, 16);
-            hipError_t e = bi::launch_direct(in, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
-            return e == hipSuccess ? BI_OK : BI_ERR_HIP;
-        }
-        if (in.K % 128 == 0 && in.M <= 8) {
-            const int items = static_cast<int>((in.N + 15) / 16);
-            const int grid = default_grid(items, cus, opts, 16);
-            hipError_t e = bi::launch_direct_nvfp4(in, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
-            return e == hipSuccess ? BI_OK : BI_ERR_HIP;
-        }
-        // 16-column items unless that leaves fewer than two per compute unit
-        const int nb = (in.N + 15) / 16 >= 2 * static_cast<int64_t>(cus) ? 16 : 8;
-        const int items = static_cast<int>((in.N + nb - 1) / nb);
-        int per_cu = bi::kLdsPerCu / bi::skinny_lds_bytes(b_mode, static_cast<int>(in.M), nb);
-        if (per_cu > 8) per_cu = 8;
-        if (per_cu < 1) per_cu = 1;
-        const int grid = default_grid(items, cus, opts, per_cu);
-        hipError_t e = bi::launch_skinny(b_mode, nb, in, grid, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+        if (b_mode == bi::OPND_BF16_ROWS) return {BI_KERNEL_STREAM_REG, 1, M <= 8 ? 1 : 0, 0, 16, -1};
+        if (K % 128 == 0 && M <= 8) return {BI_KERNEL_STREAM_REG, 1, 1, 0, 16, -1};
+        const int nb = (N + 15) / 16 >= 2 * static_cast<int64_t>(cus) ? 16 : 8;
+        return {BI_KERNEL_STREAM_RING, 1, 0, M <= 4 ? 4 : M <= 8 ? 8 : 16, nb, -1};
     }
-    // BMM with a short reduction: the streaming kernel (its own recipe, chosen
-    // from K alone; a forced tile_variant keeps the tiled kernel, same bits)
-    if (op == BI_OP_BMM && bi::bmm_short_k_ok(in.K) && !(opts && opts->tile_variant != 0)) {
-        const int64_t units = static_cast<int64_t>(in.batch) * ((in.N + 127) / 128);
-        if (units > kI32Max) return BI_ERR_UNSUPPORTED;
-        int cus = 0;
-        bi_status st = device_cus(&cus);
-        if (st != BI_OK) return st;
-        int per_cu = bi::kLdsPerCu / bi::bmm_short_k_lds_bytes(in.K);
-        per_cu = per_cu > 2 ? 2 : (per_cu < 1 ? 1 : per_cu);
-        const int grid = default_grid(static_cast<int>(units), cus, opts, per_cu);
-        hipError_t e = bi::launch_bmm_short_k(in, grid, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? BI_OK : BI_ERR_HIP;
-    }
-    // bf16 GEMM with 16 < M <= 128 and N <= 12288: the same register-streaming
+    // BMM with a short reduction: the streaming BMM kernel for every M (its
+    // own recipe, chosen from K alone)
+    if (op == BI_OP_BMM && bi::bmm_short_k_ok(static_cast<int>(K))) return {BI_KERNEL_BMM_STREAM, 4, 0, 0, 128, -1};
+    // bf16 GEMM with 16 < M <= 128 and N <= 12288: the register-streaming
     // kernel with two, four or eight 16-row blocks (one weight fragment feeds
-    // each block's chain), so every compute unit streams 16-column items as at
-    // M <= 16 instead of N / bn workgroups; the bits are the tiled kernel's.
-    // Each item re-reads A from L2 (M * K * 2 bytes), so wider weights, whose
-    // tiles already fill the chip, keep the tiled kernel.
-    if (op == BI_OP_GEMM && in.M > 16 && in.M <= 128 && in.N <= 12288 && a_mode == bi::OPND_BF16_ROWS &&
-        b_mode == bi::OPND_BF16_ROWS && in.batch == 1 && !in.group_off && !(opts && opts->tile_variant != 0)) {
-        int cus = 0;
-        bi_status st = device_cus(&cus);
-        if (st != BI_OK) return st;
-        const int items = static_cast<int>((in.N + 15) / 16);
-        const int grid = default_grid(items, cus, opts, 16);
-        hipError_t e = bi::launch_direct(in, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+    // each block's chain).  Each item re-reads A from L2 (M * K * 2 bytes),
+    // so wider weights, whose tiles already fill the chip, keep the tiled
+    // kernel.
+    if (op == BI_OP_GEMM && M > 16 && M <= kStreamMaxRows && N <= 12288 && a_mode == bi::OPND_BF16_ROWS &&
+        b_mode == bi::OPND_BF16_ROWS && batch == 1 && !grouped)
+        return {BI_KERNEL_STREAM_REG, M > 64 ? 8 : M > 32 ? 4 : 2, 0, 0, 16, -1};
+    // NVFP4 weight, bf16 A, 16 < M <= 64, K % 128 == 0: the NVFP4 register
+    // kernel with two or four 16-row blocks; each decoded fragment feeds every
+    // block's chain.
+    if (op == BI_OP_NVFP4_GEMM && M > 16 && M <= 64 && K % 128 == 0 && a_mode == bi::OPND_BF16_ROWS && fp4)
+        return {BI_KERNEL_STREAM_REG, M > 32 ? 4 : 2, 0, 0, 16, -1};
+    const int v = gemm_variant(op, N, K);
+    const bi::TileShape &t = bi::kTileShapes[v];
+    const bool pp = (v == bi::kPingPongVariant || v == bi::kPingPong192Variant || v == bi::kPingPong128Variant) &&
+                    a_mode == bi::OPND_BF16_ROWS && b_mode == bi::OPND_BF16_ROWS && batch == 1 && !grouped;
+    return {pp ? BI_KERNEL_TILED_PINGPONG : BI_KERNEL_TILED, t.bm / 16, 0, 0, t.bn, v};
+}
+
+// Operand modes of an op as its entry point sets them.
+void op_modes(int op, int a_fmt, int64_t K, int *a_mode, int *b_mode) {
+    *a_mode = bi::OPND_BF16_ROWS;
+    *b_mode = bi::OPND_BF16_ROWS;
+    if (op == BI_OP_BMM) *b_mode = bi::OPND_BF16_KN;
+    if (op == BI_OP_NVFP4_GEMM) {
+        *a_mode = a_fmt == BI_A_BF16 ? bi::OPND_BF16_ROWS : bi::OPND_NVFP4_ROWS;
+        // weight bytes by LDS DMA into a raw ring when the scale rows are
+        // dword-aligned (K % 64 == 0); otherwise through registers (same bits)
+        *b_mode = (*a_mode == bi::OPND_BF16_ROWS && K % 64 == 0) ? bi::OPND_NVFP4_RAW : bi::OPND_NVFP4_ROWS;
     }
-    // NVFP4 weight, bf16 A, 16 < M <= 64, K % 128 == 0: the register-streaming
-    // NVFP4 kernel with two or four 16-row blocks; each decoded weight
-    // fragment feeds every block's chain (the tiled kernel's).
-    if (op == BI_OP_NVFP4_GEMM && in.M > 16 && in.M <= 64 && in.K % 128 == 0 &&
-        a_mode == bi::OPND_BF16_ROWS && b_mode == bi::OPND_NVFP4_RAW && !(opts && opts->tile_variant != 0)) {
-        int cus = 0;
-        bi_status st = device_cus(&cus);
-        if (st != BI_OK) return st;
-        const int items = static_cast<int>((in.N + 15) / 16);
-        const int grid = default_grid(items, cus, opts, 16);
-        hipError_t e = bi::launch_direct_nvfp4(in, grid, opts ? opts->pipeline_depth : 0,
-                                               static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? BI_OK : BI_ERR_HIP;
-    }
-    int variant = gemm_variant(op, in.N, in.K);
-    if (opts && opts->tile_variant != 0) {
-        if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;
-        variant = opts->tile_variant - 1;
-    }
+}
+
+bi_status launch_tiled(int a_mode, int b_mode, int op, int variant, const GemmArgs &in, void *stream,
+                       const bi_launch_opts *opts, int cus) {
     const bi::TileShape &t = bi::kTileShapes[variant];
     if (op == BI_OP_BMM && (t.bn % 8 != 0)) return BI_ERR_UNSUPPORTED;
     GemmArgs a = in;
@@ -248,9 +232,6 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
                                       : static_cast<int64_t>(a.tiles_m) * a.tiles_n * a.batch;
     if (tiles > kI32Max) return BI_ERR_UNSUPPORTED;
     a.num_tiles = static_cast<int>(tiles);
-    int cus = 0;
-    bi_status st = device_cus(&cus);
-    if (st != BI_OK) return st;
     int per_cu = bi::kLdsPerCu / bi::tile_lds_bytes(t);
     if (per_cu < 1) per_cu = 1;
     const int grid = default_grid(a.num_tiles, cus, opts, per_cu);
@@ -259,8 +240,64 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
                     a_mode == bi::OPND_BF16_ROWS && !a.group_off && b_mode == bi::OPND_BF16_ROWS &&
                     a.batch == 1;
     hipError_t e = pp ? bi::launch_pingpong(a, t.bn, grid, static_cast<hipStream_t>(stream))
-                       : bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
-                                         static_cast<hipStream_t>(stream));
+                      : bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *stream,
+                   const bi_launch_opts *opts) {
+    int cus = 0;
+    bi_status st = device_cus(&cus);
+    if (st != BI_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int depth = opts ? opts->pipeline_depth : 0;
+    // a forced tile_variant keeps the tiled kernel, so the kernels can be compared
+    if (opts && opts->tile_variant != 0) {
+        if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;
+        return launch_tiled(a_mode, b_mode, op, opts->tile_variant - 1, in, stream, opts, cus);
+    }
+    const Regime r = classify(op, a_mode, b_mode, in.N, in.K, in.batch, in.group_off != nullptr, cus, in.M);
+    hipError_t e = hipSuccess;
+    switch (r.kind) {
+        case BI_KERNEL_STREAM_A_LDS: {
+            // one wavefront per item up to three per compute unit; beyond that
+            // a bf16 weight streams best from one wavefront per compute unit
+            // (fewer concurrent row streams in HBM), an NVFP4 one from three
+            // (its decode needs the SIMDs)
+            const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
+            const int items = static_cast<int>((in.N + r.cols - 1) / r.cols);
+            int waves = items <= 3 * cus ? items : fp4 ? 3 * cus : cus;
+            if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
+            e = bi::launch_direct_alds(in, fp4, r.cols, waves, cus, depth, s);
+            break;
+        }
+        case BI_KERNEL_STREAM_REG: {
+            // one wavefront per 16-column item, up to 16 per compute unit
+            const int items = static_cast<int>((in.N + 15) / 16);
+            const int grid = default_grid(items, cus, opts, 16);
+            e = b_mode == bi::OPND_NVFP4_RAW ? bi::launch_direct_nvfp4(in, r.rb, r.ap, grid, depth, s)
+                                             : bi::launch_direct(in, r.rb, r.ap, grid, depth, s);
+            break;
+        }
+        case BI_KERNEL_STREAM_RING: {
+            const int items = static_cast<int>((in.N + r.cols - 1) / r.cols);
+            int per_cu = bi::kLdsPerCu / bi::skinny_lds_bytes(b_mode, static_cast<int>(in.M), r.cols);
+            per_cu = per_cu > 8 ? 8 : per_cu < 1 ? 1 : per_cu;
+            e = bi::launch_skinny(b_mode, r.cols, r.ma, in, default_grid(items, cus, opts, per_cu), s);
+            break;
+        }
+        case BI_KERNEL_BMM_STREAM: {
+            const int64_t units = static_cast<int64_t>(in.batch) * ((in.N + 127) / 128);
+            if (units > kI32Max) return BI_ERR_UNSUPPORTED;
+            int per_cu = bi::kLdsPerCu / bi::bmm_short_k_lds_bytes(in.K);
+            per_cu = per_cu > 2 ? 2 : (per_cu < 1 ? 1 : per_cu);
+            e = bi::launch_bmm_short_k(in, default_grid(static_cast<int>(units), cus, opts, per_cu), s);
+            break;
+        }
+        default:
+            return launch_tiled(a_mode, b_mode, op, r.variant, in, stream, opts, cus);
+    }
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
@@ -343,6 +380,52 @@ bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
         }
     }
     return BI_ERR_UNSUPPORTED;
+}
+
+bi_status bi_plan_regimes(int op, int64_t N, int64_t K, int a_fmt, int cus, bi_regime *out, int capacity,
+                          int *count) {
+    if (!count || (capacity > 0 && !out)) return BI_ERR_NULL;
+    *count = 0;
+    if (op != BI_OP_GEMM && op != BI_OP_BMM && op != BI_OP_NVFP4_GEMM && op != BI_OP_GROUPED_GEMM)
+        return BI_ERR_UNSUPPORTED;
+    if (a_fmt != BI_A_BF16 && a_fmt != BI_A_NVFP4) return BI_ERR_SHAPE;
+    if (a_fmt == BI_A_NVFP4 && op != BI_OP_NVFP4_GEMM) return BI_ERR_SHAPE;
+    bi_plan plan;
+    bi_status st = bi_plan_query(op, N, K, &plan);
+    if (st != BI_OK) return st;
+    if (cus < 0) return BI_ERR_SHAPE;
+    if (cus == 0) {
+        st = device_cus(&cus);
+        if (st != BI_OK) return st;
+    }
+    int a_mode = 0, b_mode = 0;
+    op_modes(op, a_fmt, K, &a_mode, &b_mode);
+    // classify() is constant above kStreamMaxRows rows: walk M up to there
+    // and merge equal neighbours into row ranges
+    int n = 0;
+    Regime prev{};
+    for (int64_t M = 1; M <= kStreamMaxRows + 1; ++M) {
+        const Regime r = classify(op, a_mode, b_mode, N, K, 1, op == BI_OP_GROUPED_GEMM, cus, M);
+        if (M > 1 && r == prev) {
+            if (n <= capacity) out[n - 1].m_max = static_cast<int32_t>(M);
+            continue;
+        }
+        if (n < capacity) {
+            bi_regime &g = out[n];
+            std::memset(&g, 0, sizeof g);
+            g.kernel = r.kind;
+            g.m_min = g.m_max = static_cast<int32_t>(M);
+            g.row_blocks = r.rb;
+            g.cols = r.cols;
+            g.a_pairs = r.ap;
+            g.a_rows_staged = r.ma;
+        }
+        ++n;
+        prev = r;
+    }
+    if (n <= capacity) out[n - 1].m_max = static_cast<int32_t>(kI32Max);
+    *count = n;
+    return n <= capacity ? BI_OK : BI_ERR_SHAPE;
 }
 
 bi_status bi_gemm_ex(const void *A, int64_t lda, const void *B, int64_t ldb, void *Y, int64_t ldy,

@@ -91,10 +91,10 @@ struct GemmArgs {
 // Launchers; they return hipSuccess or the launch error.
 hipError_t launch_gemm(int a_mode, int b_mode, const GemmRecipe &r, const GemmArgs &args,
                        int grid, hipStream_t stream);
-// Skinny path for 1 <= M <= 16, bf16 A, weight OPND_BF16_ROWS or
-// OPND_NVFP4_RAW, batch 1; one 64-thread workgroup per nb-column block
-// (nb = 8 or 16).
-hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &args, int grid, hipStream_t stream);
+// Skinny path for 1 <= M <= ma <= 16 (ma = 4, 8 or 16 rows of A staged),
+// bf16 A, weight OPND_BF16_ROWS or OPND_NVFP4_RAW, batch 1; one 64-thread
+// workgroup per nb-column block (nb = 8 or 16).
+hipError_t launch_skinny(int b_mode, int nb, int ma, const GemmArgs &args, int grid, hipStream_t stream);
 int skinny_lds_bytes(int b_mode, int M, int nb);
 // BMM with a short reduction (K = 64, 128 or 256), B [K, N]: one workgroup
 // per (head, 128-column block) keeps the transposed B block in LDS and
@@ -105,12 +105,14 @@ int bmm_short_k_lds_bytes(int K);
 hipError_t launch_bmm_short_k(const GemmArgs &args, int grid, hipStream_t stream);
 // 256 x 256 tiles, eight wavefronts in a ping-pong schedule; bf16 x bf16, batch 1.
 hipError_t launch_pingpong(const GemmArgs &args, int bn, int grid, hipStream_t stream);
-// Direct path for 1 <= M <= 128, bf16 A and bf16 weight [N, K], batch 1: one
-// 64-thread workgroup per 16-column item, fragments loaded into registers
-// (one, two, four or eight 16-row blocks of A).
-hipError_t launch_direct(const GemmArgs &args, int grid, int depth, hipStream_t stream);
-// The same for a raw NVFP4 weight (codes [N, K/2], scales [N, K/16]), K % 128 == 0.
-hipError_t launch_direct_nvfp4(const GemmArgs &args, int grid, int depth, hipStream_t stream);
+// Direct path for 1 <= M <= 16 * rb, bf16 A and bf16 weight [N, K], batch 1:
+// one 64-thread workgroup per 16-column item, fragments loaded into
+// registers, each weight fragment feeding rb = 1, 2, 4 or 8 16-row blocks of
+// A; ap = 1 (rb = 1, M <= 8): one load carries A rows 0-7 of two K chunks.
+hipError_t launch_direct(const GemmArgs &args, int rb, int ap, int grid, int depth, hipStream_t stream);
+// The same for a raw NVFP4 weight (codes [N, K/2], scales [N, K/16]), K % 128
+// == 0, rb = 1, 2 or 4.
+hipError_t launch_direct_nvfp4(const GemmArgs &args, int rb, int ap, int grid, int depth, hipStream_t stream);
 // Direct path with A staged in LDS once per workgroup (bf16 or raw NVFP4
 // weight), for shapes with direct_alds_ok; `waves` streaming wavefronts.
 bool direct_alds_ok(int M, int K, bool fp4);

@@ -251,10 +251,13 @@ hipError_t launch_ma(const GemmArgs &a, int grid, hipStream_t s) {
 }
 
 template <int BMODE, int NB>
-hipError_t launch_mode(const GemmArgs &a, int grid, hipStream_t s) {
-    if (a.M <= 4) return launch_ma<4, BMODE, NB>(a, grid, s);
-    if (a.M <= 8) return launch_ma<8, BMODE, NB>(a, grid, s);
-    return launch_ma<16, BMODE, NB>(a, grid, s);
+hipError_t launch_mode(const GemmArgs &a, int ma, int grid, hipStream_t s) {
+    switch (ma) {
+        case 4: return launch_ma<4, BMODE, NB>(a, grid, s);
+        case 8: return launch_ma<8, BMODE, NB>(a, grid, s);
+        case 16: return launch_ma<16, BMODE, NB>(a, grid, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int BMODE, int NB>
@@ -270,14 +273,14 @@ int skinny_lds_bytes(int b_mode, int M, int nb) {
     return raw ? skinny::lds_of<OPND_NVFP4_RAW, 16>(M) : skinny::lds_of<OPND_BF16_ROWS, 16>(M);
 }
 
-hipError_t launch_skinny(int b_mode, int nb, const GemmArgs &a, int grid, hipStream_t s) {
-    if (a.M < 1 || a.M > 16 || (nb != 8 && nb != 16)) return hipErrorInvalidValue;
+hipError_t launch_skinny(int b_mode, int nb, int ma, const GemmArgs &a, int grid, hipStream_t s) {
+    if (a.M < 1 || a.M > ma || ma > 16 || (nb != 8 && nb != 16)) return hipErrorInvalidValue;
     if (b_mode == OPND_BF16_ROWS)
-        return nb == 8 ? skinny::launch_mode<OPND_BF16_ROWS, 8>(a, grid, s)
-                       : skinny::launch_mode<OPND_BF16_ROWS, 16>(a, grid, s);
+        return nb == 8 ? skinny::launch_mode<OPND_BF16_ROWS, 8>(a, ma, grid, s)
+                       : skinny::launch_mode<OPND_BF16_ROWS, 16>(a, ma, grid, s);
     if (b_mode == OPND_NVFP4_RAW)
-        return nb == 8 ? skinny::launch_mode<OPND_NVFP4_RAW, 8>(a, grid, s)
-                       : skinny::launch_mode<OPND_NVFP4_RAW, 16>(a, grid, s);
+        return nb == 8 ? skinny::launch_mode<OPND_NVFP4_RAW, 8>(a, ma, grid, s)
+                       : skinny::launch_mode<OPND_NVFP4_RAW, 16>(a, ma, grid, s);
     return hipErrorInvalidValue;
 }
 
@@ -817,21 +820,32 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, int nb, int waves, in
                    : direct::launch_alds<false, 16>(a, d, grid, nwv, s);
 }
 
-hipError_t launch_direct_nvfp4(const GemmArgs &a, int grid, int depth, hipStream_t s) {
-    if (a.M < 1 || a.M > 64 || grid < 1 || a.K % 128 != 0) return hipErrorInvalidValue;
-    if (a.M > 32) return direct::launch_nvfp4_rb<4>(a, pick_depth(a.K / 128, depth, 2, 2), grid, s);
-    if (a.M > 16) return direct::launch_nvfp4_rb<2>(a, pick_depth(a.K / 128, depth, 4, 4), grid, s);
-    const int d = pick_depth(a.K / 128, depth, 8, 8);
-    return a.M <= 8 ? direct::launch_nvfp4_ap<1>(a, d, grid, s) : direct::launch_nvfp4_ap<0>(a, d, grid, s);
+hipError_t launch_direct_nvfp4(const GemmArgs &a, int rb, int ap, int grid, int depth, hipStream_t s) {
+    if (a.M < 1 || a.M > 16 * rb || grid < 1 || a.K % 128 != 0 || (ap && (rb != 1 || a.M > 8)))
+        return hipErrorInvalidValue;
+    switch (rb) {
+        case 4: return direct::launch_nvfp4_rb<4>(a, pick_depth(a.K / 128, depth, 2, 2), grid, s);
+        case 2: return direct::launch_nvfp4_rb<2>(a, pick_depth(a.K / 128, depth, 4, 4), grid, s);
+        case 1: {
+            const int d = pick_depth(a.K / 128, depth, 8, 8);
+            return ap ? direct::launch_nvfp4_ap<1>(a, d, grid, s) : direct::launch_nvfp4_ap<0>(a, d, grid, s);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_direct(const GemmArgs &a, int grid, int depth, hipStream_t s) {
-    if (a.M < 1 || a.M > 128 || grid < 1) return hipErrorInvalidValue;
-    if (a.M > 64) return direct::launch_rb<8>(a, pick_depth((a.K + 63) / 64, depth, 2, 2), grid, s);
-    if (a.M > 32) return direct::launch_rb<4>(a, pick_depth((a.K + 63) / 64, depth, 4, 4), grid, s);
-    if (a.M > 16) return direct::launch_rb<2>(a, pick_depth((a.K + 63) / 64, depth, 8, 8), grid, s);
-    const int d = pick_depth((a.K + 63) / 64, depth, a.K >= 8192 ? 16 : 8, 16);
-    return a.M <= 8 ? direct::launch_ap<1>(a, d, grid, s) : direct::launch_ap<0>(a, d, grid, s);
+hipError_t launch_direct(const GemmArgs &a, int rb, int ap, int grid, int depth, hipStream_t s) {
+    if (a.M < 1 || a.M > 16 * rb || grid < 1 || (ap && (rb != 1 || a.M > 8))) return hipErrorInvalidValue;
+    switch (rb) {
+        case 8: return direct::launch_rb<8>(a, pick_depth((a.K + 63) / 64, depth, 2, 2), grid, s);
+        case 4: return direct::launch_rb<4>(a, pick_depth((a.K + 63) / 64, depth, 4, 4), grid, s);
+        case 2: return direct::launch_rb<2>(a, pick_depth((a.K + 63) / 64, depth, 8, 8), grid, s);
+        case 1: {
+            const int d = pick_depth((a.K + 63) / 64, depth, a.K >= 8192 ? 16 : 8, 16);
+            return ap ? direct::launch_ap<1>(a, d, grid, s) : direct::launch_ap<0>(a, d, grid, s);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace bi

@@ -297,3 +297,45 @@ def test_mla_decode_noalloc_validation():
     assert call(Bn=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
     assert call(H=0, q=0, kv=0, lens=0, out=0) == B.BI_OK
     assert B.MLA_SCRATCH_BYTES == 32 << 20
+
+
+@pytest.mark.parametrize("op,N,K,a_fmt", [(B.BI_OP_GEMM, 256, 512, 0), (B.BI_OP_GEMM, 6144, 4096, 0),
+                                          (B.BI_OP_GEMM, 4096, 4096, 0), (B.BI_OP_GEMM, 24576, 4096, 0),
+                                          (B.BI_OP_GEMM, 4096, 12288, 0), (B.BI_OP_NVFP4_GEMM, 24576, 4096, 0),
+                                          (B.BI_OP_NVFP4_GEMM, 24576, 4096, 1), (B.BI_OP_NVFP4_GEMM, 1000, 4160, 0),
+                                          (B.BI_OP_BMM, 512, 128, 0), (B.BI_OP_GROUPED_GEMM, 4096, 4096, 0)])
+def test_plan_regimes_cover_every_m(op, N, K, a_fmt):
+    """The kernel-choice table covers M >= 1 without gaps or overlaps; its
+    last range is the tiled kernel of bi_plan_query's shape (or the
+    streaming BMM kernel), unbounded above; streaming ranges end by 128 rows."""
+    for cus in (80, 256, 304):
+        regs = B.plan_regimes(op, N, K, a_fmt, cus=cus)
+        assert regs[0]["m_min"] == 1 and regs[-1]["m_max"] == 2 ** 31 - 1
+        for a, b in zip(regs, regs[1:]):
+            assert b["m_min"] == a["m_max"] + 1
+            assert a != b
+        last = regs[-1]
+        plan = B.plan_query(op, N, K)
+        if last["kind"] != "bmm_stream":
+            assert last["kind"] in ("tiled", "tiled_pingpong")
+            assert (last["row_blocks"] * 16, last["cols"]) == (plan["bm"], plan["bn"])
+            assert last["m_min"] <= 129
+        for r in regs[:-1]:
+            assert r["kind"].startswith("stream") and r["m_max"] <= 128
+        if a_fmt == 1 or op == B.BI_OP_GROUPED_GEMM:
+            assert len(regs) == 1                     # no streaming kernel serves these
+
+
+def test_plan_regimes_edges_and_errors():
+    # the A-in-LDS limit 10 * M * cus <= 7 * N moves with the compute-unit count
+    r = B.plan_regimes(B.BI_OP_GEMM, 4096, 4096, cus=256)
+    assert (r[0]["kind"], r[0]["m_max"], r[1]["kind"]) == ("stream_a_lds", 11, "stream_reg")
+    r = B.plan_regimes(B.BI_OP_GEMM, 4096, 4096, cus=128)
+    assert (r[0]["kind"], r[0]["m_max"]) == ("stream_a_lds", 16)
+    arr = (B.BiRegime * 1)()
+    n = B.ctypes.c_int(0)
+    st = B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4096, 0, 256, arr, 1, B.ctypes.byref(n))
+    assert st == B.BI_ERR_SHAPE and n.value == 6
+    assert B.lib().bi_plan_regimes(B.BI_OP_RMSNORM, 4096, 0, 0, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_UNSUPPORTED
+    assert B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4096, 1, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_SHAPE
+    assert B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4100, 0, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_SHAPE

@@ -163,15 +163,14 @@ def test_w4a4_config_tile_variants_and_grid():
 
 # ------------------------------------------------------------ regime edges
 
-def _regime_ms(N):
-    """M values around every place the host changes the streaming kernel or
-    its launch: 8/9 (one load carries A rows 0-7), the A-in-LDS limit
-    10 M #CU <= 7 N, 16/17 (one 16-row block), 32/33, 64/65 and 128/129 (the
-    row blocks of the register kernels), 255/256/257 (one 256-row M-tile)."""
-    lds = (7 * N) // (10 * _cus())
-    ms = set(range(1, 21)) | {31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257}
-    ms |= {m for m in (lds - 1, lds, lds + 1) if m >= 1}
-    return sorted(ms)
+def _regime_ms(op, N, K, a_fmt=B.BI_A_BF16, mmax=300):
+    """M values on both sides of every edge bi_plan_regimes lists for (op,
+    N, K) on this device (the kernel choice changes there), plus 1 and the
+    256-row M-tile edges."""
+    ms = {1, 2, 255, 256, 257}
+    for r in B.plan_regimes(op, N, K, a_fmt):
+        ms |= {r["m_min"], r["m_min"] + 1, r["m_max"], r["m_max"] + 1}
+    return sorted(m for m in ms if 1 <= m <= mmax)
 
 
 CONFIG_NK = [(256, 512), (6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
@@ -179,16 +178,17 @@ CONFIG_NK = [(256, 512), (6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288
 
 @pytest.mark.parametrize("N,K", CONFIG_NK)
 def test_regime_edges_bf16(N, K):
-    """Every configuration's (N, K), M walked across every host-side kernel
-    regime edge: each M's rows are bitwise the forced tiled kernel's (tile
-    shape 0, 256 x 256) and the M = 300 batch's prefix."""
+    """Every configuration's (N, K), M walked across every edge of the
+    kernel choice that bi_plan_regimes lists: each M's rows are bitwise the
+    forced tiled kernel's (tile shape 0, 256 x 256) and the M = 300 batch's
+    prefix."""
     Mmax = 300
     A = inputs.randn_bf16((Mmax, K), tag=(710, N, K))
     W = inputs.randn_bf16((N, K), 0.02, tag=(711, N, K))
     Ad, Wd = dev(A), dev(W)
     note(f"regime edges bf16 N={N} K={K} M={Mmax}")
     yfull = B.bi_gemm(Ad, Wd)
-    for M in _regime_ms(N):
+    for M in _regime_ms(B.BI_OP_GEMM, N, K):
         note(f"regime edges bf16 N={N} K={K} M={M}")
         y = B.bi_gemm(Ad[:M], Wd)
         assert torch.equal(y, yfull[:M]), f"M={M} vs batch"
@@ -199,8 +199,8 @@ def test_regime_edges_bf16(N, K):
 
 def test_regime_edges_nvfp4():
     """The NVFP4 configuration's (24576, 4096), bf16 A: M across every edge
-    of the streaming kernels (8/9, 16/17, 64/65) bitwise equal to the forced
-    256 x 256 tiled kernel (the plan's shape) and the batch prefix."""
+    bi_plan_regimes lists, bitwise equal to the forced 256 x 256 tiled
+    kernel (the plan's shape) and the batch prefix."""
     N, K, Mmax = 24576, 4096, 300
     W, Ws, g = _nvfp4_weights(N, K, (125,))
     alpha = float(np.float32(1.0) / g)
@@ -208,7 +208,7 @@ def test_regime_edges_nvfp4():
     Ad, Wd, Wsd = dev(A), dev(W), dev(Ws)
     note("regime edges nvfp4 M=300")
     yfull = B.bi_nvfp4_gemm(Ad, Wd, Wsd, alpha)
-    for M in _regime_ms(N):
+    for M in _regime_ms(B.BI_OP_NVFP4_GEMM, N, K):
         note(f"regime edges nvfp4 M={M}")
         y = B.bi_nvfp4_gemm(Ad[:M], Wd, Wsd, alpha)
         assert torch.equal(y, yfull[:M]), f"M={M} vs batch"
