@@ -125,9 +125,11 @@ typedef struct bi_plan {
  *   tile_variant: GEMM family only; 0 = the plan's tile shape, v > 0 = the
  *     compiled tile shape v-1 (see bi_tile_shape).  BI_ERR_SHAPE if out of
  *     range.
- *   pipeline_depth: the streaming kernels only; weight load units in flight per
+ *   pipeline_depth: the streaming kernels: weight load units in flight per
  *     wavefront (0 = the library's choice; otherwise rounded down to a
- *     supported power of two that divides the unit count).
+ *     supported power of two that divides the unit count).  The NVFP4
+ *     ping-pong kernel: memory phases of loads in flight per wavefront (1,
+ *     or 2 for any other value; 0 = 2).
  */
 typedef struct bi_launch_opts {
     int32_t max_workgroups;

@@ -96,11 +96,23 @@ int gemm_variant(int op, int64_t N, int64_t K) {
     // 256 x 192 for 5120 <= N < 12288: one more tile per 768 columns keeps
     // N = 6144 at 256 tiles for 2048 rows (one per compute unit) instead of 192
     if (op == BI_OP_GEMM && N >= 5120 && N < 12288) return bi::kPingPong192Variant;
-    if (N >= 5120)                      // 256 x 256, 8 wavefronts: ping-pong schedule for the
-        return op == BI_OP_GEMM ? bi::kPingPongVariant : 12;  // bf16 GEMM, else 3-deep B ring
+    if (N >= 5120)                      // 256 x 256, 8 wavefronts: ping-pong schedule for the bf16
+        return (op == BI_OP_GEMM || op == BI_OP_NVFP4_GEMM) ? bi::kPingPongVariant : 12;  // and NVFP4
+                                        // GEMMs, else the classic schedule with a 3-deep B ring
     if (N >= 2048) return 9;            // 256 x 128, 8 wavefronts, 3-deep A ring
     if (N >= 512) return 5;             // 128 x 64
     return 6;                           // 64 x 64
+}
+
+// The ping-pong kernels serve their tile shapes for bf16 A with a bf16 weight
+// (256, 192 or 128 columns) or a raw NVFP4 weight (256 columns), batch 1;
+// other operand modes run the classic schedule of the same shape (same bits).
+bool pingpong_ok(int variant, int a_mode, int b_mode, int batch, bool grouped) {
+    if (a_mode != bi::OPND_BF16_ROWS || batch != 1 || grouped) return false;
+    if (b_mode == bi::OPND_BF16_ROWS)
+        return variant == bi::kPingPongVariant || variant == bi::kPingPong192Variant ||
+               variant == bi::kPingPong128Variant;
+    return b_mode == bi::OPND_NVFP4_RAW && variant == bi::kPingPongVariant;
 }
 
 void fill_tile_plan(int op, int variant, bi_plan *out) {
@@ -201,8 +213,7 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
         return {BI_KERNEL_STREAM_REG, M > 32 ? 4 : 2, 0, 0, 16, -1};
     const int v = gemm_variant(op, N, K);
     const bi::TileShape &t = bi::kTileShapes[v];
-    const bool pp = (v == bi::kPingPongVariant || v == bi::kPingPong192Variant || v == bi::kPingPong128Variant) &&
-                    a_mode == bi::OPND_BF16_ROWS && b_mode == bi::OPND_BF16_ROWS && batch == 1 && !grouped;
+    const bool pp = pingpong_ok(v, a_mode, b_mode, batch, grouped);
     return {pp ? BI_KERNEL_TILED_PINGPONG : BI_KERNEL_TILED, t.bm / 16, 0, 0, t.bn, v};
 }
 
@@ -235,13 +246,13 @@ bi_status launch_tiled(int a_mode, int b_mode, int op, int variant, const GemmAr
     int per_cu = bi::kLdsPerCu / bi::tile_lds_bytes(t);
     if (per_cu < 1) per_cu = 1;
     const int grid = default_grid(a.num_tiles, cus, opts, per_cu);
-    const bool pp = (variant == bi::kPingPongVariant || variant == bi::kPingPong192Variant ||
-                     variant == bi::kPingPong128Variant) &&
-                    a_mode == bi::OPND_BF16_ROWS && !a.group_off && b_mode == bi::OPND_BF16_ROWS &&
-                    a.batch == 1;
-    hipError_t e = pp ? bi::launch_pingpong(a, t.bn, grid, static_cast<hipStream_t>(stream))
-                      : bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid,
-                                        static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (!pingpong_ok(variant, a_mode, b_mode, a.batch, a.group_off != nullptr))
+        e = bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid, static_cast<hipStream_t>(stream));
+    else if (b_mode == bi::OPND_NVFP4_RAW)
+        e = bi::launch_pingpong_nvfp4(a, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
+    else
+        e = bi::launch_pingpong(a, t.bn, grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
