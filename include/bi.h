@@ -125,11 +125,9 @@ typedef struct bi_plan {
  *   tile_variant: GEMM family only; 0 = the plan's tile shape, v > 0 = the
  *     compiled tile shape v-1 (see bi_tile_shape).  BI_ERR_SHAPE if out of
  *     range.
- *   pipeline_depth: the streaming kernels: weight load units in flight per
+ *   pipeline_depth: the streaming kernels only; weight load units in flight per
  *     wavefront (0 = the library's choice; otherwise rounded down to a
- *     supported power of two that divides the unit count).  The NVFP4
- *     ping-pong kernel: memory phases of loads in flight per wavefront (1,
- *     or 2 for any other value; 0 = 2).
+ *     supported power of two that divides the unit count).
  */
 typedef struct bi_launch_opts {
     int32_t max_workgroups;
@@ -462,6 +460,27 @@ bi_status bi_plan_regimes(int op, int64_t N, int64_t K, int a_fmt, int cus, bi_r
  * BI_ERR_NULL for a NULL out.  Host-only.
  */
 bi_status bi_tile_shape(int v, bi_plan *out);
+
+/*
+ * Measurement probes.  Not part of the batch-invariant path: they measure
+ * the ceilings its kernels are reported against (the published peaks assume
+ * a clock and a memory efficiency the machine may not reach under load).
+ *
+ * bi_probe_mfma: `grid` workgroups of 8 wavefronts; each wavefront issues
+ *   iters * 8 v_mfma_f32_16x16x32_bf16 (the hot path's instruction) on eight
+ *   independent accumulators, operands in registers.  The call performs
+ *   grid * 8 * iters * 8 * 16384 flops.  out: device uint64 [grid * 8 * 3],
+ *   8-byte aligned; per wavefront: shader-clock cycles of its loop
+ *   (s_memtime), ticks of the constant 100 MHz clock over the same loop
+ *   (s_memrealtime), and a sink word; cycles / (ticks / 1e8) is the clock
+ *   the loop ran at.  iters in [1, 2^40], grid >= 1.
+ * bi_probe_read: reads `bytes` of `src` (device, 16-byte aligned, bytes %
+ *   16 == 0) once, with 16-byte loads from grid * 256 threads, folding them
+ *   into sink (device uint32 [grid * 256], 4-byte aligned, not overlapping
+ *   src).  Time it over a buffer larger than the last-level cache.
+ */
+bi_status bi_probe_mfma(void *out, int64_t iters, int grid, void *stream);
+bi_status bi_probe_read(const void *src, int64_t bytes, void *sink, int grid, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *bi_status_str(bi_status s);

@@ -89,6 +89,8 @@ _SIGS = {
     "bi_mla_decode_workspace_size": [_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_int64)],
     "bi_plan_query": [ctypes.c_int, _i64, _i64, ctypes.POINTER(BiPlan)],
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
+    "bi_probe_mfma": [_p, _i64, ctypes.c_int, _p],
+    "bi_probe_read": [_p, _i64, _p, ctypes.c_int, _p],
     "bi_plan_regimes": [ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(BiRegime),
                         ctypes.c_int, ctypes.POINTER(ctypes.c_int)],
 }
@@ -429,3 +431,29 @@ def bi_mla_decode_noalloc(q, kv, lens, scale, Dv, out):
                                      Dv, _stream(None))
     _raise(st, "bi_mla_decode_noalloc")
     return out
+
+
+PROBE_WAVES = 8
+PROBE_MFMA_FLOPS = 16384  # one v_mfma_f32_16x16x32_bf16
+
+
+def bi_probe_mfma(iters, grid, out=None, *, stream=None):
+    """MFMA-only loop (measurement): returns the device uint64 tensor
+    [grid * 8, 3] of (shader-clock cycles, 100 MHz ticks, sink) per wavefront.
+    The call performs grid * 8 * iters * 8 * 16384 flops."""
+    if out is None:
+        out = torch.empty((grid * PROBE_WAVES, 3), dtype=torch.int64, device="cuda")
+    _raise(lib().bi_probe_mfma(_ptr(out), int(iters), int(grid), _stream(stream)), "bi_probe_mfma")
+    return out
+
+
+def bi_probe_read(src, grid, sink=None, *, stream=None):
+    """Read stream (measurement): reads every byte of the dense device tensor
+    src once; returns the uint32 sink tensor [grid * 256]."""
+    if not src.is_contiguous():
+        raise ValueError("src must be dense")
+    if sink is None:
+        sink = torch.empty((grid * 256,), dtype=torch.int32, device=src.device)
+    _raise(lib().bi_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), int(grid), _stream(stream)),
+           "bi_probe_read")
+    return sink

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "gemm_dispatch.hip", "gemm_bf16.hip", "gemm_kn.hip", "gemm_nvfp4.hip",
            "gemm_nvfp4raw.hip", "gemm_nvfp4a.hip", "gemm_skinny.hip", "gemm_pingpong.hip",
            "rmsnorm.hip", "nvfp4_quant.hip", "bmm.hip",
-           "mla_decode.hip"]
+           "mla_decode.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -250,7 +250,7 @@ bi_status launch_tiled(int a_mode, int b_mode, int op, int variant, const GemmAr
     if (!pingpong_ok(variant, a_mode, b_mode, a.batch, a.group_off != nullptr))
         e = bi::launch_gemm(a_mode, b_mode, GemmRecipe{variant}, a, grid, static_cast<hipStream_t>(stream));
     else if (b_mode == bi::OPND_NVFP4_RAW)
-        e = bi::launch_pingpong_nvfp4(a, grid, opts ? opts->pipeline_depth : 0, static_cast<hipStream_t>(stream));
+        e = bi::launch_pingpong_nvfp4(a, grid, static_cast<hipStream_t>(stream));
     else
         e = bi::launch_pingpong(a, t.bn, grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;
@@ -812,6 +812,28 @@ bi_status bi_mla_decode(const void *q, const void *kv, const int32_t *lens, floa
                         void *stream) {
     return bi_mla_decode_ex(q, kv, lens, scale, out, B, H, Lmax, Dqk, Dv, workspace, workspace_bytes, stream,
                             nullptr);
+}
+
+bi_status bi_probe_mfma(void *out, int64_t iters, int grid, void *stream) {
+    if (iters < 1 || grid < 1 || iters > ((int64_t)1 << 40)) return BI_ERR_SHAPE;
+    if (!out) return BI_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(out) & 7u) return BI_ERR_ALIGN;
+    return bi::launch_mfma_probe(static_cast<uint64_t *>(out), iters, grid, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? BI_OK
+               : BI_ERR_HIP;
+}
+
+bi_status bi_probe_read(const void *src, int64_t bytes, void *sink, int grid, void *stream) {
+    if (bytes <= 0 || bytes % 16 || grid < 1) return BI_ERR_SHAPE;
+    if (!src || !sink) return BI_ERR_NULL;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return BI_ERR_ALIGN;
+    if (overlap(mat_range(sink, 1, (int64_t)grid * 256, 0, 4, 1), mat_range(src, 1, bytes, 0, 1, 1)))
+        return BI_ERR_ALIAS;
+    return bi::launch_read_probe(src, bytes, static_cast<uint32_t *>(sink), grid, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? BI_OK
+               : BI_ERR_HIP;
 }
 
 }  // extern "C"

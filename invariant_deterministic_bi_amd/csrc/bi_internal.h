@@ -106,11 +106,9 @@ hipError_t launch_bmm_short_k(const GemmArgs &args, int grid, hipStream_t stream
 // 256 x 256 tiles, eight wavefronts in a ping-pong schedule; bf16 x bf16, batch 1.
 hipError_t launch_pingpong(const GemmArgs &args, int bn, int grid, hipStream_t stream);
 // The same schedule for bf16 A and a raw NVFP4 weight (K % 64 == 0), 256 x
-// 256 tiles, each wavefront decoding its B fragments from raw LDS stages;
-// `depth` (1 or 2; 0 = kPingPongNvfp4Depth) memory phases of loads in
-// flight per wavefront.
-constexpr int kPingPongNvfp4Depth = 2;
-hipError_t launch_pingpong_nvfp4(const GemmArgs &args, int grid, int depth, hipStream_t stream);
+// 256 tiles: one group decodes the raw B stages and hands the fragments to
+// the other through LDS.
+hipError_t launch_pingpong_nvfp4(const GemmArgs &args, int grid, hipStream_t stream);
 // Direct path for 1 <= M <= 16 * rb, bf16 A and bf16 weight [N, K], batch 1:
 // one 64-thread workgroup per 16-column item, fragments loaded into
 // registers, each weight fragment feeding rb = 1, 2, 4 or 8 16-row blocks of
@@ -204,5 +202,11 @@ constexpr int64_t kMlaScratchBytes = (int64_t)32 << 20;
 constexpr int kMaxDevices = 64;
 hipError_t mla_scratch(float **out);
 hipError_t launch_mla_decode(const MlaArgs &args, int grid, int fold_grid, hipStream_t stream);
+
+// Measurement probes (probe.hip): an MFMA-only loop (eight wavefronts per
+// workgroup; out: three uint64 per wavefront) and a 16-byte read stream
+// (256 threads per workgroup; sink: one uint32 per thread).
+hipError_t launch_mfma_probe(uint64_t *out, int64_t iters, int grid, hipStream_t stream);
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int grid, hipStream_t stream);
 
 }  // namespace bi

@@ -326,55 +326,59 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
 // K/16], K % 64 == 0) in the same ping-pong schedule, 256 x 256 tiles.
 //
 // B reaches LDS raw: per 64-column stage, 256 rows of 32 code bytes and 4
-// scale bytes (9 KB, against 32 KB of bf16), by LDS DMA.  In its memory
-// phase each wavefront reads the raw bytes of its own 64 columns and decodes
-// them straight into its B fragment registers (the exact decode of the tiled
-// kernel: FP4 pair convert with a unit scale, one fp32 multiply by the E4M3
-// scale, top halves), beside the other group's MFMAs.  The decoded fragment
-// holds the same bf16 values the tiled kernel reads from its decoded LDS
-// tile, so every output element's chain -- and its bits -- are the same.
-//
-// The small B stage frees LDS for deeper prefetch: with W memory phases in
-// flight per wavefront, stage s of
-//   A rows 0..127   is issued by group 1 in phase a of step s - 1 - W,
-//   A rows 128..255 by group 0 in phase b of step s - 1 - W,
-//   B rows 0..127   by group 0 in phase b of step s - 2 - W,
-//   B rows 128..255 by group 1 in phase a of step s - 1 - W,
-// and each wavefront, at the end of a memory phase, waits until only its
-// last W phases' loads are in flight.  The A half rings hold W + 1 stages,
-// the raw B ring W + 2 (a slot is reissued only after both groups read it).
+// scale bytes (9 KB, against 32 KB of bf16), by LDS DMA.  The two groups
+// take different shares of the memory work, so that the decode arithmetic
+// never runs beside the other group's decode:
+//   * group 0, in its memory phase (phase b of step s - 1), reads A rows
+//     0..127 and the raw B of stage s, decodes the B fragments of its
+//     wavefront's 64 columns straight into registers (the exact decode of
+//     the tiled kernel: FP4 pair convert with a unit scale, one fp32
+//     multiply by the E4M3 scale, top halves) and writes them to a decoded
+//     B buffer in LDS;
+//   * group 1, in its memory phase (phase a of step s), reads A rows
+//     128..255 and the decoded B fragments of its wavefront's columns (the
+//     same 64 columns), and issues every LDS-DMA load: A rows 0..127, A
+//     rows 128..255 and the raw B of stage s + 2, in phase a of step s.
+// Each compute phase is then 64 MFMAs on fragments in registers.  Group 1
+// waits, at the end of a memory phase, until only that phase's loads are in
+// flight; stage s's loads (issued in phase a of step s - 2) have landed by
+// the end of phase a of step s - 1, before group 0 reads them in phase b of
+// step s - 1.  Rings: A rows 0..127 two stages, A rows 128..255 three (group
+// 1 reads stage s and reissues its slot in the same phase), raw B two, the
+// decoded B one (written in phase b of step s - 1, read in phase a of s).
+// The decoded fragments hold the same bf16 values the tiled kernel reads
+// from its decoded LDS tile, so every output element's chain -- and its
+// bits -- are the same.
 // ---------------------------------------------------------------------------
-template <int W>
 struct Nv4Shape {
     static constexpr int BN = 256, FN = 4;
-    static constexpr int RA = W + 1, RB = W + 2;  // ring depths
+    static constexpr int RA0 = 2, RA1 = 3, RR = 2;  // ring depths
     static constexpr int CodeBytes = BN * 32, RawStage = BN * 36;
-    static constexpr int OffB = 2 * RA * kHalf;   // after the two A half rings
-    static constexpr int Pipe = OffB + RB * RawStage;
+    static constexpr int OffA1 = RA0 * kHalf;
+    static constexpr int OffRaw = OffA1 + RA1 * kHalf;
+    static constexpr int OffDec = OffRaw + RR * RawStage;
+    static constexpr int DecBytes = BN * kRowBytes;   // 32 KB: 8 KB per column strip
+    static constexpr int Pipe = OffDec + DecBytes;
     static constexpr int CStride = BN * 2 + 16;
     static constexpr int CBytes = kBM * CStride;
     static constexpr int Lds = Pipe > CBytes ? Pipe : CBytes;
+    static constexpr int LOADS = 11;  // group 1's DMA instructions per memory phase, per wavefront
     static_assert(Lds <= 160 * 1024, "LDS budget of gfx950");
 };
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int OFF0, int OFF1>
-__device__ __forceinline__ u32x2 rd2x32(uint32_t addr) {
-    u32x2 v;
-    asm volatile("ds_read2_b32 %0, %1 offset0:%2 offset1:%3" : "=v"(v) : "v"(addr), "n"(OFF0), "n"(OFF1) : "memory");
-    return v;
-}
 template <int OFF>
 __device__ __forceinline__ uint32_t rd32(uint32_t addr) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
     return v;
 }
+template <int OFF>
+__device__ __forceinline__ void wr128(uint32_t addr, const u32x4 &v) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "n"(OFF) : "memory");
+}
 
-template <int W>
 __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
-    using S = Nv4Shape<W>;
+    using S = Nv4Shape;
     constexpr int BN = S::BN, FN = S::FN;
     __shared__ __attribute__((aligned(1024))) char lds[S::Lds];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -386,9 +390,6 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
     const bool spread = (G % 8) == 0;
     const int slot = spread ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const uint32_t lds0 = lds_addr(lds);
-    // this wavefront's loads per memory phase: 4 A instructions, 1 code
-    // instruction (32 rows), and for j < 2 one scale instruction (64 rows)
-    const bool scale_wave = j < 2;
 
     for (int base = 0; base < p.num_tiles; base += G) {
         const int L = base + slot;
@@ -405,53 +406,58 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         const i32x4 rs = make_rsrc(Sb, (uint32_t)(rows_b * spr));
         DmaLane dla;
         dla.init(lane, p.lda);
-        // raw B DMA lanes: group g fills rows 128 g .. 128 g + 127 of a stage
-        const int crow = 128 * g + 32 * j + (lane >> 1);        // code row of this lane
-        const int code_off = crow < rows_b ? crow * cpr + (lane & 1) * 16 : (int)0x80000000;
-        const int srow = 128 * g + 64 * j + lane;               // scale row (j < 2)
+        // Raw B DMA lanes (group 1 wavefront j: code rows 64 j .. 64 j + 63 in
+        // two instructions of 32 rows, scale rows 64 j .. 64 j + 63 in one).
+        // A row's 32 code bytes are two 16-byte halves (K chunks 0 and 1 of
+        // the stage); rows whose bit 3 is set store them swapped, so that the
+        // fragment reads of rows r and r + 8 fall in different LDS banks.
+        const int crow = 64 * j + (lane >> 1);                   // code row of instruction 0
+        const int chalf = (lane & 1) ^ ((crow >> 3) & 1);        // the half this lane fetches
+        const int code_off0 = crow < rows_b ? crow * cpr + chalf * 16 : (int)0x80000000;
+        const int code_off1 = crow + 32 < rows_b ? (crow + 32) * cpr + chalf * 16 : (int)0x80000000;
+        const int srow = 64 * j + lane;
         const int scale_off = srow < rows_b ? srow * spr : (int)0x80000000;
 
-        auto dma_raw = [&](int s, bool live) {
-            char *st = lds + S::OffB + (s % S::RB) * S::RawStage;
+        // Group 1's loads of one memory phase (phase a of step u): stage u + 2
+        // of A rows 0..127, A rows 128..255 and raw B.  Stages past the last
+        // issue zero-filling loads into the slot they would use.
+        auto issue = [&](int u) {
+            const int st = u + 2;
+            const bool live = st < nk;
+            char *a0 = lds + (st % S::RA0) * kHalf;
+            char *a1 = lds + S::OffA1 + (st % S::RA1) * kHalf - 128 * kRowBytes;
+            const int r0 = 32 * j, r1 = 128 + 32 * j;
+            dma8<0>(ra, a0, dla, r0, st * kBK, p.K, rows_a, p.lda, live);
+            dma8<1>(ra, a0, dla, r0 + 8, st * kBK, p.K, rows_a, p.lda, live);
+            dma8<0>(ra, a0, dla, r0 + 16, st * kBK, p.K, rows_a, p.lda, live);
+            dma8<1>(ra, a0, dla, r0 + 24, st * kBK, p.K, rows_a, p.lda, live);
+            dma8<0>(ra, a1, dla, r1, st * kBK, p.K, rows_a, p.lda, live);
+            dma8<1>(ra, a1, dla, r1 + 8, st * kBK, p.K, rows_a, p.lda, live);
+            dma8<0>(ra, a1, dla, r1 + 16, st * kBK, p.K, rows_a, p.lda, live);
+            dma8<1>(ra, a1, dla, r1 + 24, st * kBK, p.K, rows_a, p.lda, live);
+            char *raw = lds + S::OffRaw + (st % S::RR) * S::RawStage;
             i32x4 r;
             r.x = __builtin_amdgcn_readfirstlane(rc.x);
             r.y = __builtin_amdgcn_readfirstlane(rc.y);
             r.z = __builtin_amdgcn_readfirstlane(rc.z);
             r.w = __builtin_amdgcn_readfirstlane(rc.w);
-            const int vc = (live && code_off >= 0) ? code_off + s * 32 : (int)0x80000000;
-            bi_raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t *)(st + (128 * g + 32 * j) * 32),
-                                   16, vc, 0, 0, 0);
-            if (scale_wave) {
-                i32x4 q;
-                q.x = __builtin_amdgcn_readfirstlane(rs.x);
-                q.y = __builtin_amdgcn_readfirstlane(rs.y);
-                q.z = __builtin_amdgcn_readfirstlane(rs.z);
-                q.w = __builtin_amdgcn_readfirstlane(rs.w);
-                const int vs = (live && scale_off >= 0) ? scale_off + s * 4 : (int)0x80000000;
-                bi_raw_buffer_load_lds(
-                    q, (__attribute__((address_space(3))) uint32_t *)(st + S::CodeBytes + (128 * g + 64 * j) * 4), 4,
-                    vs, 0, 0, 0);
-            }
-        };
-        // The loads of one memory phase: group 1 in phase a of step u, group
-        // 0 in phase b of step u.
-        auto issue = [&](int u) {
-            const int sa = u + 1 + W, sbb = g ? u + 1 + W : u + 2 + W;
-            const int a_row0 = g ? 0 : 128;   // tile row of the A half this group loads
-            char *a_tile = lds + (g ? 0 : S::RA * kHalf) + (sa % S::RA) * kHalf - a_row0 * kRowBytes;
-            const int ra0 = a_row0 + 32 * j;
-            dma8<0>(ra, a_tile, dla, ra0, sa * kBK, p.K, rows_a, p.lda, sa < nk);
-            dma8<1>(ra, a_tile, dla, ra0 + 8, sa * kBK, p.K, rows_a, p.lda, sa < nk);
-            dma8<0>(ra, a_tile, dla, ra0 + 16, sa * kBK, p.K, rows_a, p.lda, sa < nk);
-            dma8<1>(ra, a_tile, dla, ra0 + 24, sa * kBK, p.K, rows_a, p.lda, sa < nk);
-            dma_raw(sbb, sbb < nk);
-        };
-        auto wait_phases = [&]() {  // only the last W memory phases' loads in flight
-            if (scale_wave) wait_vmcnt<6 * W>();
-            else wait_vmcnt<5 * W>();
+            const int vc0 = (live && code_off0 >= 0) ? code_off0 + st * 32 : (int)0x80000000;
+            const int vc1 = (live && code_off1 >= 0) ? code_off1 + st * 32 : (int)0x80000000;
+            bi_raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t *)(raw + 64 * j * 32), 16, vc0, 0,
+                                   0, 0);
+            bi_raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t *)(raw + (64 * j + 32) * 32), 16,
+                                   vc1, 0, 0, 0);
+            i32x4 q;
+            q.x = __builtin_amdgcn_readfirstlane(rs.x);
+            q.y = __builtin_amdgcn_readfirstlane(rs.y);
+            q.z = __builtin_amdgcn_readfirstlane(rs.z);
+            q.w = __builtin_amdgcn_readfirstlane(rs.w);
+            const int vs = (live && scale_off >= 0) ? scale_off + st * 4 : (int)0x80000000;
+            bi_raw_buffer_load_lds(q, (__attribute__((address_space(3))) uint32_t *)(raw + S::CodeBytes + 64 * j * 4),
+                                   4, vs, 0, 0, 0);
         };
 
-        u32x4 fa[2][8];
+        u32x4 fa[2][8], fb[2][4];
         f32x4 acc[8][FN];
 #pragma unroll
         for (int fm = 0; fm < 8; ++fm)
@@ -459,25 +465,25 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
             for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         const int r16 = lane & 15;
-        const uint32_t a_lane = lds0 + (g ? S::RA * kHalf : 0) + r16 * kRowBytes;
         const uint32_t sw0 = swz(r16, lane >> 4) * 16, sw1 = swz(r16, 4 + (lane >> 4)) * 16;
-        // raw B of this lane: code dwords of chunks (lane >> 4) and 4 + (lane >> 4)
-        // of column 64 j + 16 fn + r16, and that column's scale dword
-        const uint32_t c_lane = lds0 + S::OffB + (64 * j + r16) * 32 + (lane >> 4) * 4;
-        const uint32_t s_lane = lds0 + S::OffB + S::CodeBytes + (64 * j + r16) * 4;
+        // group 0 reads A rows 0..127 from the 2-deep ring, group 1 rows
+        // 128..255 from the 3-deep one
+        const uint32_t a_lane = lds0 + (g ? S::OffA1 : 0) + r16 * kRowBytes;
+        // raw B (group 0): the code dword of 8-element group (lane >> 4) in
+        // K chunk 0 and in K chunk 1 of column 64 j + 16 fn + r16, each in the
+        // half the swizzle put it in, and that column's scale dword
+        const uint32_t c_lane0 = lds0 + S::OffRaw + (64 * j + r16) * 32 + ((r16 >> 3) & 1) * 16 + (lane >> 4) * 4;
+        const uint32_t c_lane1 = c_lane0 ^ 16u;
+        const uint32_t s_lane = lds0 + S::OffRaw + S::CodeBytes + (64 * j + r16) * 4;
         const int sshift = (lane >> 5) * 8;  // the scale byte of K chunk 0 (chunk 1: two bytes up)
-        u32x2 cw[4];
-        uint32_t sv[4];
-        u32x4 bc0, bc1;  // the B fragments of the 16-column block being multiplied
-        // Memory phase: the raw B bytes and A's fragments of stage s.
-#define BI_P4_READ(s)                                                                          \
+        // decoded B: wavefront strip j's fragments, fragment (ks, fn) of lane l
+        // at ((ks * 4 + fn) * 64 + l) * 16
+        const uint32_t d_lane = lds0 + S::OffDec + j * 8192 + lane * 16;
+
+#define BI_P4_READ_A(s)                                                                        \
     do {                                                                                       \
-        const uint32_t cb = c_lane + ((s) % S::RB) * S::RawStage;                              \
-        const uint32_t sb = s_lane + ((s) % S::RB) * S::RawStage;                              \
-        cw[0] = rd2x32<0, 4>(cb); cw[1] = rd2x32<0, 4>(cb + 512);                              \
-        cw[2] = rd2x32<0, 4>(cb + 1024); cw[3] = rd2x32<0, 4>(cb + 1536);                      \
-        sv[0] = rd32<0>(sb); sv[1] = rd32<64>(sb); sv[2] = rd32<128>(sb); sv[3] = rd32<192>(sb); \
-        const uint32_t a0 = a_lane + ((s) % S::RA) * kHalf + sw0, a1 = a_lane + ((s) % S::RA) * kHalf + sw1; \
+        const uint32_t ab = a_lane + (g ? ((s) % S::RA1) : ((s) % S::RA0)) * kHalf;            \
+        const uint32_t a0 = ab + sw0, a1 = ab + sw1;                                           \
         fa[0][0] = rd128<0 * 2048>(a0); fa[0][1] = rd128<1 * 2048>(a0);                      \
         fa[0][2] = rd128<2 * 2048>(a0); fa[0][3] = rd128<3 * 2048>(a0);                      \
         fa[0][4] = rd128<4 * 2048>(a0); fa[0][5] = rd128<5 * 2048>(a0);                      \
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         fa[1][4] = rd128<4 * 2048>(a1); fa[1][5] = rd128<5 * 2048>(a1);                      \
         fa[1][6] = rd128<6 * 2048>(a1); fa[1][7] = rd128<7 * 2048>(a1);                      \
     } while (0)
-#define BI_P4_SETTLE()                                                                         \
+#define BI_P4_SETTLE_A()                                                                       \
     do {                                                                                       \
         asm volatile("s_waitcnt lgkmcnt(0)"                                                   \
                      : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[0][2]), "+v"(fa[0][3]),         \
@@ -495,85 +501,103 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         asm volatile(""                                                                        \
                      : "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fa[1][2]), "+v"(fa[1][3]),         \
                        "+v"(fa[1][4]), "+v"(fa[1][5]), "+v"(fa[1][6]), "+v"(fa[1][7])::"memory"); \
-        asm volatile("" : "+v"(cw[0]), "+v"(cw[1]), "+v"(cw[2]), "+v"(cw[3]), "+v"(sv[0]), "+v"(sv[1]), \
-                     "+v"(sv[2]), "+v"(sv[3])::"memory");                                      \
     } while (0)
-// B fragments of 16-column block fn from the raw bytes (K chunks 0 and 1).
-#define BI_P4_DECODE(fn, b0, b1)                                                               \
+#define BI_P4_SETTLE_B()                                                                       \
     do {                                                                                       \
-        const uint32_t sh = sv[fn] >> sshift;                                                  \
-        const uint4 d0 = decode8(cw[fn].x, e4m3_value<0>(sh));                                 \
-        const uint4 d1 = decode8(cw[fn].y, e4m3_value<2>(sh));                                 \
-        b0 = u32x4{d0.x, d0.y, d0.z, d0.w};                                                    \
-        b1 = u32x4{d1.x, d1.y, d1.z, d1.w};                                                    \
+        asm volatile("" : "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[0][2]), "+v"(fb[0][3])::"memory"); \
+        asm volatile("" : "+v"(fb[1][0]), "+v"(fb[1][1]), "+v"(fb[1][2]), "+v"(fb[1][3])::"memory"); \
     } while (0)
-// Compute phase: block 0's fragments were decoded at the end of the memory
-// phase; block fn + 1's are decoded while block fn's 16 MFMAs run (the
-// group barriers interleave one MFMA with two VALU instructions).  Every
-// accumulator still sees K chunk 0, then chunk 1.
+        // Group 0's memory phase for stage s: raw B first (its decode starts
+        // as soon as it lands), then A; decode; hand the fragments to group 1.
+        auto mem0 = [&](int s) {
+            const uint32_t cb0 = c_lane0 + (s % S::RR) * S::RawStage;
+            const uint32_t cb1 = c_lane1 + (s % S::RR) * S::RawStage;
+            const uint32_t sb = s_lane + (s % S::RR) * S::RawStage;
+            uint32_t c0[4], c1[4], sv[4];
+            c0[0] = rd32<0>(cb0); c1[0] = rd32<0>(cb1);
+            c0[1] = rd32<512>(cb0); c1[1] = rd32<512>(cb1);
+            c0[2] = rd32<1024>(cb0); c1[2] = rd32<1024>(cb1);
+            c0[3] = rd32<1536>(cb0); c1[3] = rd32<1536>(cb1);
+            sv[0] = rd32<0>(sb); sv[1] = rd32<64>(sb); sv[2] = rd32<128>(sb); sv[3] = rd32<192>(sb);
+            BI_P4_READ_A(s);
+            // the 12 raw reads are the oldest of the 28 in flight
+            asm volatile("s_waitcnt lgkmcnt(15)"
+                         : "+v"(c0[0]), "+v"(c0[1]), "+v"(c0[2]), "+v"(c0[3]), "+v"(c1[0]), "+v"(c1[1]),
+                           "+v"(c1[2]), "+v"(c1[3]), "+v"(sv[0]), "+v"(sv[1]), "+v"(sv[2]), "+v"(sv[3])::"memory");
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const uint32_t sh = sv[fn] >> sshift;
+                const uint4 d0 = decode8(c0[fn], e4m3_value<0>(sh));
+                const uint4 d1 = decode8(c1[fn], e4m3_value<2>(sh));
+                fb[0][fn] = u32x4{d0.x, d0.y, d0.z, d0.w};
+                fb[1][fn] = u32x4{d1.x, d1.y, d1.z, d1.w};
+            }
+            wr128<0 * 1024>(d_lane, fb[0][0]); wr128<1 * 1024>(d_lane, fb[0][1]);
+            wr128<2 * 1024>(d_lane, fb[0][2]); wr128<3 * 1024>(d_lane, fb[0][3]);
+            wr128<4 * 1024>(d_lane, fb[1][0]); wr128<5 * 1024>(d_lane, fb[1][1]);
+            wr128<6 * 1024>(d_lane, fb[1][2]); wr128<7 * 1024>(d_lane, fb[1][3]);
+            BI_P4_SETTLE_A();
+            BI_P4_SETTLE_B();
+        };
+        // Group 1's memory phase for stage s: A and the decoded B, then the
+        // loads of stage s + 2.
+        auto mem1 = [&](int s, int u) {
+            BI_P4_READ_A(s);
+            fb[0][0] = rd128<0 * 1024>(d_lane); fb[0][1] = rd128<1 * 1024>(d_lane);
+            fb[0][2] = rd128<2 * 1024>(d_lane); fb[0][3] = rd128<3 * 1024>(d_lane);
+            fb[1][0] = rd128<4 * 1024>(d_lane); fb[1][1] = rd128<5 * 1024>(d_lane);
+            fb[1][2] = rd128<6 * 1024>(d_lane); fb[1][3] = rd128<7 * 1024>(d_lane);
+            issue(u);
+            BI_P4_SETTLE_A();
+            BI_P4_SETTLE_B();
+            wait_vmcnt<S::LOADS>();
+        };
 #define BI_P4_COMPUTE()                                                                        \
     do {                                                                                       \
-        _Pragma("unroll") for (int fn = 0; fn < FN; ++fn) {                                    \
-            u32x4 n0, n1;                                                                      \
-            if (fn + 1 < FN) BI_P4_DECODE(fn + 1, n0, n1);                                     \
-            _Pragma("unroll") for (int fm = 0; fm < 8; ++fm)                                   \
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                         \
-                    __builtin_bit_cast(bf16x8, fa[0][fm]), __builtin_bit_cast(bf16x8, bc0), acc[fm][fn], 0, 0, 0); \
-            _Pragma("unroll") for (int fm = 0; fm < 8; ++fm)                                   \
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                         \
-                    __builtin_bit_cast(bf16x8, fa[1][fm]), __builtin_bit_cast(bf16x8, bc1), acc[fm][fn], 0, 0, 0); \
-            if (fn + 1 < FN) {                                                                 \
-                bc0 = n0;                                                                      \
-                bc1 = n1;                                                                      \
-            }                                                                                  \
-        }                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < 48; ++i) {                                       \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                 \
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                                 \
-        }                                                                                      \
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);                                    \
+        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                       \
+        _Pragma("unroll") for (int fm = 0; fm < 8; ++fm)                                       \
+        _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                      \
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                             \
+                __builtin_bit_cast(bf16x8, fa[ks][fm]), __builtin_bit_cast(bf16x8, fb[ks][fn]), \
+                acc[fm][fn], 0, 0, 0);                                                         \
     } while (0)
 
-        // Prologue: B rows 0..127 of stage 0 (group 0), then the memory
-        // phases of steps -1-W .. -1; everything lands; group 0 reads stage 0.
-        if (g == 0) dma_raw(0, nk > 0);
-#pragma unroll
-        for (int u = -1 - W; u < 0; ++u) issue(u);
+        // Prologue: group 1 issues stages 0 and 1; everything lands; group 0
+        // reads and decodes stage 0 (handing it to group 1); group 1 reads
+        // stage 0 and issues stage 2.
+        if (g == 1) {
+            issue(-2);
+            issue(-1);
+        }
         wait_vmcnt<0>();
         lds_barrier();
-        if (g == 0) {
-            BI_P4_READ(0);
-            BI_P4_SETTLE();
-            BI_P4_DECODE(0, bc0, bc1);
-        }
+        if (g == 0) mem0(0);
         lds_barrier();
         if (g == 1) {
-            BI_P4_READ(0);
-            issue(0);
-            BI_P4_SETTLE();
-            BI_P4_DECODE(0, bc0, bc1);
-            wait_phases();
+            mem1(0, 0);
             lds_barrier();
         }
+        // One loop body serves both groups, group 1 half a step behind: each
+        // iteration is [compute stage t] barrier [memory phase for stage
+        // t + 1] barrier.
         for (int t = 0; t < nk; ++t) {
             __builtin_amdgcn_sched_barrier(0);
             BI_P4_COMPUTE();
             __builtin_amdgcn_sched_barrier(0);
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            BI_P4_READ(t + 1);
-            issue(t + g);
-            BI_P4_SETTLE();
-            BI_P4_DECODE(0, bc0, bc1);
-            wait_phases();
+            if (g == 0)
+                mem0(t + 1);
+            else
+                mem1(t + 1, t + 1);
             __builtin_amdgcn_sched_barrier(0);
             lds_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
         if (g == 0) lds_barrier();
-#undef BI_P4_READ
-#undef BI_P4_SETTLE
-#undef BI_P4_DECODE
+#undef BI_P4_READ_A
+#undef BI_P4_SETTLE_A
+#undef BI_P4_SETTLE_B
 #undef BI_P4_COMPUTE
 
         // Epilogue: every load has landed; fp32 x alpha -> bf16 RNE into a
@@ -616,12 +640,9 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
 
 }  // namespace pingpong
 
-hipError_t launch_pingpong_nvfp4(const GemmArgs &a, int grid, int depth, hipStream_t s) {
+hipError_t launch_pingpong_nvfp4(const GemmArgs &a, int grid, hipStream_t s) {
     if (a.batch != 1 || grid < 1 || a.group_off || a.K % 64 != 0) return hipErrorInvalidValue;
-    if ((depth > 0 ? depth : kPingPongNvfp4Depth) == 1)
-        hipLaunchKernelGGL(pingpong::pingpong_nvfp4_kernel<1>, dim3(grid), dim3(pingpong::kNT), 0, s, a);
-    else
-        hipLaunchKernelGGL(pingpong::pingpong_nvfp4_kernel<2>, dim3(grid), dim3(pingpong::kNT), 0, s, a);
+    hipLaunchKernelGGL(pingpong::pingpong_nvfp4_kernel, dim3(grid), dim3(pingpong::kNT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -339,3 +339,17 @@ def test_plan_regimes_edges_and_errors():
     assert B.lib().bi_plan_regimes(B.BI_OP_RMSNORM, 4096, 0, 0, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_UNSUPPORTED
     assert B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4096, 1, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_SHAPE
     assert B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4100, 0, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_SHAPE
+
+
+def test_probe_validation():
+    """The measurement probes validate their arguments before any launch."""
+    L = B.lib()
+    assert L.bi_probe_mfma(None, 10, 4, None) == B.BI_ERR_NULL
+    assert L.bi_probe_mfma(0x1000, 0, 4, None) == B.BI_ERR_SHAPE
+    assert L.bi_probe_mfma(0x1000, 10, 0, None) == B.BI_ERR_SHAPE
+    assert L.bi_probe_mfma(0x1004, 10, 4, None) == B.BI_ERR_ALIGN
+    assert L.bi_probe_read(0x1000, 0, 0x9000, 4, None) == B.BI_ERR_SHAPE
+    assert L.bi_probe_read(0x1000, 24, 0x9000, 4, None) == B.BI_ERR_SHAPE
+    assert L.bi_probe_read(0x1008, 1024, 0x9000, 4, None) == B.BI_ERR_ALIGN
+    assert L.bi_probe_read(0x1000, 1 << 20, 0x2000, 4, None) == B.BI_ERR_ALIAS
+    assert L.bi_probe_read(None, 1024, 0x9000, 4, None) == B.BI_ERR_NULL
