@@ -160,7 +160,9 @@ def summarize(dirs, out, command, kernel):
             if every:
                 lines.append("# kernel trace, per kernel and grid size (threads), largest total first: "
                              "name | grid | calls | median ns | mean ns | min ns")
-                for (n, g), v in sorted(every.items(), key=lambda kv: -sum(kv[1]))[:60]:
+                for (n, g), v in sorted(every.items(), key=lambda kv: -sum(kv[1])):
+                    if "bi::" not in n:
+                        continue
                     lines.append(f"{n} | {g} | {len(v)} | {statistics.median(v):.0f} | {sum(v) / len(v):.0f} | "
                                  f"{min(v)}")
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -169,9 +171,11 @@ def summarize(dirs, out, command, kernel):
                 acc.setdefault(key, []).append(float(r["Counter_Value"]))
     if acc:
         mean = {k: sum(v) / len(v) for k, v in acc.items()}
-        lines.append("# counters, mean per dispatch: name | grid | counter | value | dispatches")
+        lines.append("# counters, mean per dispatch, for this library's kernels and the two calibration kernels: "
+                     "name | grid | counter | value | dispatches")
         for (n, g, c), m in sorted(mean.items()):
-            lines.append(f"{n} | {g} | {c} | {m:.1f} | {len(acc[(n, g, c)])}")
+            if "bi::" in n or "direct_copy" in n:
+                lines.append(f"{n} | {g} | {c} | {m:.1f} | {len(acc[(n, g, c)])}")
 
         def bytes_of(n, g):
             r32, r64, r128 = (mean.get((n, g, f"TCC_EA0_RDREQ_{s}B")) for s in (32, 64, 128))
