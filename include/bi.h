@@ -19,10 +19,12 @@
  *     avoid (section "implementation breakdown": only the default config with
  *     a persistent scheduler), and the PR #51292 page names size-gated kernel
  *     selection as the bug class (root-cause comment).  Which kernel runs
- *     that arithmetic does depend on M: the tiled kernel of bi_plan_query's
- *     tile shape, or at small M a streaming kernel that spreads column items
- *     of the weight over the whole chip.  bi_plan_regimes lists every such
- *     choice and its row range; all of them give the same bits.
+ *     that arithmetic does depend on M: at small M a streaming kernel that
+ *     spreads column items of the weight over the whole chip, else the tiled
+ *     kernel with a tile shape picked by a cost model of M and N (the fewest
+ *     rounds of tiles over the compute units, weighted by each shape's
+ *     measured round time).  bi_plan_regimes lists every such choice and its
+ *     row range; all of them give the same bits.
  *   - There is no mode switch and no environment variable: invariance is
  *     unconditional (the PR #39912 page lists a cached mode flag as a risk,
  *     section "risks and impact").
@@ -395,10 +397,12 @@ bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, f
  * BI_OP_RMSNORM and BI_OP_REDUCE_RMSNORM pass H as N and 0 as K (the two
  * share one row recipe); for BI_OP_NVFP4_QUANT pass K as N and
  * 0 as K (threads = 256 per workgroup, chunks_per_thread = 1: one thread per
- * 8 elements).  There is deliberately no M
- * argument: the recipe cannot depend on it.  Returns BI_ERR_SHAPE or
- * BI_ERR_UNSUPPORTED for keys the matching entry point would reject.
- * Host-only; makes no HIP call.
+ * 8 elements).  There is no M argument: the per-element recipe does not
+ * depend on it.  For the dense and NVFP4 GEMMs the tile fields describe the
+ * shape of calls with more than 4096 rows; smaller calls may run another
+ * kernel or shape (bi_plan_regimes lists them) with the same bits.  Returns
+ * BI_ERR_SHAPE or BI_ERR_UNSUPPORTED for keys the matching entry point would
+ * reject.  Host-only; makes no HIP call.
  */
 bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out);
 
@@ -423,7 +427,9 @@ typedef enum bi_kernel_kind {
  * `kernel` (m_max = 2^31-1: no bound).  row_blocks: 16-row MFMA blocks of A
  * that each weight fragment feeds (tiled: bm / 16); cols: output columns per
  * work item (tiled: bn); a_pairs: 1 when one load carries A rows 0-7 of two
- * K chunks; a_rows_staged: rows of A the LDS-ring kernel stages (4, 8, 16).
+ * K chunks; a_rows_staged: rows of A the LDS-ring kernel stages (4, 8, 16);
+ * tile_variant: the tiled kernels' shape as bi_launch_opts.tile_variant
+ * numbers it (1 + the bi_tile_shape index), 0 for the streaming kernels.
  */
 typedef struct bi_regime {
     int32_t kernel;
@@ -432,7 +438,7 @@ typedef struct bi_regime {
     int32_t cols;
     int32_t a_pairs;
     int32_t a_rows_staged;
-    int32_t reserved;
+    int32_t tile_variant;
 } bi_regime;
 
 /*
@@ -443,9 +449,10 @@ typedef struct bi_regime {
  * never changes an output bit (every kernel runs the same chain; the
  * bitwise tests cross every edge listed here).
  *   a_fmt: BI_A_BF16, or BI_A_NVFP4 for an NVFP4 A (BI_OP_NVFP4_GEMM only).
- *   cus: compute units of the device the calls run on (one of the edges,
- *     the A-in-LDS limit 10 * M * cus <= 7 * N, depends on it), or 0 for the
- *     current device (one HIP attribute query).
+ *   cus: compute units of the device the calls run on (the edges depend on
+ *     it: the A-in-LDS limit 10 * M * cus <= 7 * N and the cost model's
+ *     rounds of tiles), or 0 for the current device (one HIP attribute
+ *     query).  Above 4096 rows the choice no longer changes with M.
  *   out: room for `capacity` entries; *count = the number of regimes
  *   (BI_ERR_SHAPE, with *count set, when capacity is too small).
  *   Ops other than the GEMM family: BI_ERR_UNSUPPORTED.

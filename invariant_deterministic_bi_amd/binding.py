@@ -42,10 +42,10 @@ class BiPlan(ctypes.Structure):
 
 class BiRegime(ctypes.Structure):
     _fields_ = [("kernel", _i32), ("m_min", _i32), ("m_max", _i32), ("row_blocks", _i32), ("cols", _i32),
-                ("a_pairs", _i32), ("a_rows_staged", _i32), ("reserved", _i32)]
+                ("a_pairs", _i32), ("a_rows_staged", _i32), ("tile_variant", _i32)]
 
     def as_dict(self):
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 KERNEL_KINDS = ("tiled", "tiled_pingpong", "stream_a_lds", "stream_reg", "stream_ring", "bmm_stream")

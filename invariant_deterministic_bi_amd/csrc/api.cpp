@@ -3,10 +3,11 @@
 // Declarations and the contract are in include/bi.h.
 //
 // The per-element recipe -- the MFMA instruction, the K order, the
-// accumulator and the epilogue -- depends on (op, N, K) only.  The kernel
-// that runs it does depend on M: the tiled kernel of bi_plan_query's shape,
-// or, at small M, a streaming kernel (classify() below; the ranges are
-// listed by bi_plan_regimes).  The vLLM PR #39912 summary page (section
+// accumulator and the epilogue -- is the same for every (op, N, K) and M.
+// The kernel that runs it does depend on M: at small M a streaming kernel,
+// else the tiled kernel with a tile shape from a cost model of M and N
+// (classify() below; the ranges are listed by bi_plan_regimes, and
+// bi_plan_query reports the large-M shape).  The vLLM PR #39912 summary page (section
 // "implementation breakdown") pins one default config instead of M-bucketed
 // ones, and the vLLM PR #51292 page's root-cause comment names size-gated
 // selection as the failure mode; here every kernel a shape can take runs the
@@ -68,40 +69,107 @@ bi_status device_cus(int *out) {
 }
 
 // ---------------------------------------------------------------------------
-// Recipe table: (op, N, K) -> index into bi::kTileShapes.  Every output
-// element is computed the same way by every tile shape (16x16x32 bf16 MFMA,
-// K ascending in chunks of 32); the shape is chosen per (N, K) for speed
-// alone: at small M the number of tiles, N / bn, decides how many compute
-// units stream the weight, at large M the tile's bm * bn / (bm + bn) decides
-// the operand traffic per MFMA.
+// Tile shapes.  Every output element is computed the same way by every tile
+// shape (16x16x32 bf16 MFMA, K ascending in chunks of 32, one lane's fp32
+// accumulator); the shape only decides which workgroup computes which
+// outputs, so it is chosen for speed alone.
 // ---------------------------------------------------------------------------
 constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offsets
 
-// The choices below come from sweeping every compiled shape on MI355X at
-// M = 1, 16 and 2048 for each Qwen3-8B-shaped (N, K): at M <= 16 the number
-// of tiles N / bn bounds how many compute units stream the weight (about
-// 50 GB/s each), at M = 2048 a wide tile cuts operand traffic per MFMA.  The
-// shape is the one with the best balance of the two for that N.
-int gemm_variant(int op, int64_t N, int64_t K) {
-    (void)K;
+// Tile shape of the ops that keep one shape per (N, K) at every M: the
+// batched and grouped GEMMs.  (The dense and NVFP4 GEMMs take theirs from
+// the cost model below.)
+int fixed_variant(int op, int64_t N) {
     // Grouped GEMM: every expert adds a partial m-tile, so wide n-tiles (fewer
     // tiles per expert) pay off sooner than for one dense GEMM; every tile
     // shape gives the same bits, so each row is still bitwise bi_gemm's.
     if (op == BI_OP_GROUPED_GEMM) {
         if (N >= 2048) return 12;        // 256 x 256, classic schedule
         if (N >= 512) return 11;         // 128 x 128, 8 wavefronts
-        op = BI_OP_GEMM;
+        return 6;                        // 64 x 64
     }
-    if (op == BI_OP_BMM) return 2;      // 256 x 128, 8 wavefronts
-    // 256 x 192 for 5120 <= N < 12288: one more tile per 768 columns keeps
-    // N = 6144 at 256 tiles for 2048 rows (one per compute unit) instead of 192
-    if (op == BI_OP_GEMM && N >= 5120 && N < 12288) return bi::kPingPong192Variant;
-    if (N >= 5120)                      // 256 x 256, 8 wavefronts: ping-pong schedule for the bf16
-        return (op == BI_OP_GEMM || op == BI_OP_NVFP4_GEMM) ? bi::kPingPongVariant : 12;  // and NVFP4
-                                        // GEMMs, else the classic schedule with a 3-deep B ring
-    if (N >= 2048) return 9;            // 256 x 128, 8 wavefronts, 3-deep A ring
-    if (N >= 512) return 5;             // 128 x 64
-    return 6;                           // 64 x 64
+    return 2;                            // BMM: 256 x 128, 8 wavefronts
+}
+
+// Cost model of the dense and NVFP4 GEMMs' tiled kernel (batch 1).  A launch
+// runs in rounds of one tile per compute unit (every candidate needs more
+// than half of a compute unit's LDS, so one workgroup fits), and a round's
+// time grows with the tile's operand bytes, not with the number of busy
+// compute units: a compute unit streams its tile's A and B at about 45-50
+// GB/s whatever the others do, until the tile is large enough to be
+// MFMA-bound.  So a call's time is ceil(tiles / CUs) x (round cost) x K, and
+// the shape with the least estimate runs (the larger one on a tie).  Round
+// costs are MI355X measurements (microseconds per 4096 of K, every shape
+// forced at M = 32 ... 8192 on N = 4096 ... 24576); each table lists the
+// shapes that won somewhere in that sweep for its operand modes.
+struct TileCost {
+    int variant;  // index into bi::kTileShapes
+    int cost;     // one round, microseconds per 4096 of K
+};
+constexpr TileCost kCostBf16[] = {{6, 24}, {5, 31}, {11, 45}, {2, 60}, {bi::kPingPong192Variant, 85},
+                                  {bi::kPingPongVariant, 100}};
+constexpr TileCost kCostNvfp4W[] = {{11, 50}, {2, 82}, {16, 102}, {bi::kPingPongVariant, 113}};
+constexpr TileCost kCostW4A4[] = {{10, 64}, {2, 92}, {16, 120}, {12, 128}};
+// Above this many rows every shape runs several rounds, and the choice is
+// the shape with the least cost per output row, cost x ceil(N / bn) / bm
+// (the estimate's limit for large M without the round-up), so that the
+// choice stops changing with M.
+constexpr int64_t kModelRows = 4096;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+const TileCost *cost_table(int a_mode, int b_mode, int *n) {
+    if (a_mode == bi::OPND_NVFP4_ROWS) {
+        *n = sizeof kCostW4A4 / sizeof kCostW4A4[0];
+        return kCostW4A4;
+    }
+    if (b_mode == bi::OPND_NVFP4_RAW || b_mode == bi::OPND_NVFP4_ROWS) {
+        *n = sizeof kCostNvfp4W / sizeof kCostNvfp4W[0];
+        return kCostNvfp4W;
+    }
+    *n = sizeof kCostBf16 / sizeof kCostBf16[0];
+    return kCostBf16;
+}
+
+// The tile shape of a dense or NVFP4 GEMM with M rows (M > kModelRows: the
+// large-M limit), and its estimate in microseconds per 4096 of K (0 for the
+// limit).
+int model_variant(int a_mode, int b_mode, int64_t N, int cus, int64_t M, int64_t *est) {
+    int n = 0;
+    const TileCost *tab = cost_table(a_mode, b_mode, &n);
+    int best = -1;
+    int64_t be = 0;
+    double bl = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const bi::TileShape &t = bi::kTileShapes[tab[i].variant];
+        const int64_t tn = ceil_div(N, t.bn);
+        if (M <= kModelRows) {
+            const int64_t e = ceil_div(ceil_div(M, t.bm) * tn, cus) * tab[i].cost;
+            if (best < 0 || e <= be) {
+                best = tab[i].variant;
+                be = e;
+            }
+        } else {
+            const double l = static_cast<double>(tab[i].cost) * static_cast<double>(tn) / t.bm;
+            if (best < 0 || l <= bl) {
+                best = tab[i].variant;
+                bl = l;
+            }
+        }
+    }
+    *est = M <= kModelRows ? be : 0;
+    return best;
+}
+
+// The per-(N, K) plan bi_plan_query reports: the shape every call with more
+// than kModelRows rows runs (the large-M limit does not depend on the number
+// of compute units).
+int plan_variant(int op, int64_t N, int64_t K) {
+    if (op != BI_OP_GEMM && op != BI_OP_NVFP4_GEMM) return fixed_variant(op, N);
+    const int b_mode = op == BI_OP_GEMM ? bi::OPND_BF16_ROWS
+                                        : (K % 64 == 0 ? bi::OPND_NVFP4_RAW : bi::OPND_NVFP4_ROWS);
+    int64_t est = 0;
+    return model_variant(bi::OPND_BF16_ROWS, b_mode, N, 1, kModelRows + 1, &est);
 }
 
 // The ping-pong kernels serve their tile shapes for bf16 A with a bf16 weight
@@ -153,15 +221,18 @@ int default_grid(int tiles, int cus, const bi_launch_opts *opts, int per_cu) {
 // Kernel regimes of the GEMM family.  Every kernel below runs the same
 // per-element chain -- one 16x16x32 bf16 MFMA per 32-wide K chunk, K
 // ascending from +0, one fp32 accumulator per output owned by one lane for
-// the whole K range, (alpha x) then bf16 RNE -- so each gives the tiled
-// kernel's bits.  Which one runs is chosen on the host from the row count M
-// as well as (op, N, K): at M <= 16 (and to 128 rows for bf16 weights of
-// N <= 12288, to 64 for NVFP4 weights) a streaming kernel spreads 8- or
-// 16-column items of the weight over every compute unit, which the per-(N,K)
-// tile cannot do at small M.  This departs from a single tile per (N, K); it
-// is kept safe by that identical chain and by bitwise tests at every regime
-// edge of every configured (N, K).  classify() is the whole rule: run_gemm
-// dispatches on it and bi_plan_regimes() enumerates it.
+// the whole K range, (alpha x) then bf16 RNE -- so each gives the same bits.
+// Which one runs is chosen on the host from the row count M as well as
+// (op, N, K):
+//   * M <= 16: a streaming kernel spreads 8- or 16-column items of the
+//     weight over every compute unit, which no tile can do at so few rows;
+//   * 16 < M <= 128: the register-streaming kernel when its estimate beats
+//     the tiled kernel's (narrow weights, whose tiles cannot fill the chip);
+//   * else the tiled kernel, its tile shape from the cost model above.
+// This departs from a single tile per (N, K); it is kept safe by that
+// identical chain and by bitwise tests at every regime edge of every
+// configured (N, K).  classify() is the whole rule: run_gemm dispatches on it
+// and bi_plan_regimes() enumerates it.
 // ---------------------------------------------------------------------------
 struct Regime {
     int kind;   // bi_kernel_kind
@@ -175,12 +246,18 @@ struct Regime {
     }
 };
 
-constexpr int64_t kStreamMaxRows = 128;  // above this every call takes the tiled kernel
+// Register-streaming kernel (16 < M <= 128): one wavefront per 16-column
+// item, up to 16 per compute unit; each item streams its weight columns once
+// and re-reads A (rb 16-row blocks) from L2, so a round of one item per
+// compute unit costs about 6 + 3.7 rb microseconds per 4096 of K (MI355X,
+// bf16 and NVFP4 weights alike).  In hundredths of a microsecond:
+int64_t stream_round_cost(int rb) { return 600 + 368 * rb; }
 
 Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch, bool grouped, int cus,
                 int64_t M) {
     const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
     const bool stream_modes = a_mode == bi::OPND_BF16_ROWS && (b_mode == bi::OPND_BF16_ROWS || fp4);
+    const bool dense = (op == BI_OP_GEMM || op == BI_OP_NVFP4_GEMM) && batch == 1 && !grouped;
     if ((op == BI_OP_GEMM || op == BI_OP_NVFP4_GEMM) && M <= 16 && stream_modes) {
         // A in LDS when its copy into every compute unit (M * K * 2 bytes
         // each) is at most 0.7 times the weight bytes that unit streams; else
@@ -198,20 +275,22 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
     // BMM with a short reduction: the streaming BMM kernel for every M (its
     // own recipe, chosen from K alone)
     if (op == BI_OP_BMM && bi::bmm_short_k_ok(static_cast<int>(K))) return {BI_KERNEL_BMM_STREAM, 4, 0, 0, 128, -1};
-    // bf16 GEMM with 16 < M <= 128 and N <= 12288: the register-streaming
-    // kernel with two, four or eight 16-row blocks (one weight fragment feeds
-    // each block's chain).  Each item re-reads A from L2 (M * K * 2 bytes),
-    // so wider weights, whose tiles already fill the chip, keep the tiled
-    // kernel.
-    if (op == BI_OP_GEMM && M > 16 && M <= kStreamMaxRows && N <= 12288 && a_mode == bi::OPND_BF16_ROWS &&
-        b_mode == bi::OPND_BF16_ROWS && batch == 1 && !grouped)
-        return {BI_KERNEL_STREAM_REG, M > 64 ? 8 : M > 32 ? 4 : 2, 0, 0, 16, -1};
-    // NVFP4 weight, bf16 A, 16 < M <= 64, K % 128 == 0: the NVFP4 register
-    // kernel with two or four 16-row blocks; each decoded fragment feeds every
-    // block's chain.
-    if (op == BI_OP_NVFP4_GEMM && M > 16 && M <= 64 && K % 128 == 0 && a_mode == bi::OPND_BF16_ROWS && fp4)
-        return {BI_KERNEL_STREAM_REG, M > 32 ? 4 : 2, 0, 0, 16, -1};
-    const int v = gemm_variant(op, N, K);
+    if (!dense) {
+        const int v = fixed_variant(op, N);
+        return {BI_KERNEL_TILED, bi::kTileShapes[v].bm / 16, 0, 0, bi::kTileShapes[v].bn, v};
+    }
+    int64_t est = 0;
+    const int v = model_variant(a_mode, b_mode, N, cus, M, &est);
+    // bf16 A with 16 < M <= 128 and a bf16 weight, or 16 < M <= 64 and a raw
+    // NVFP4 one (K % 128 == 0): the register-streaming kernel with two, four
+    // or eight 16-row blocks (one weight fragment feeds each block's chain)
+    // when it is estimated faster than that tile
+    if (a_mode == bi::OPND_BF16_ROWS &&
+        ((b_mode == bi::OPND_BF16_ROWS && M <= 128) || (fp4 && K % 128 == 0 && M <= 64))) {
+        const int rb = M > 64 ? 8 : M > 32 ? 4 : 2;
+        if (ceil_div(ceil_div(N, 16), cus) * stream_round_cost(rb) < 100 * est)
+            return {BI_KERNEL_STREAM_REG, rb, 0, 0, 16, -1};
+    }
     const bi::TileShape &t = bi::kTileShapes[v];
     const bool pp = pingpong_ok(v, a_mode, b_mode, batch, grouped);
     return {pp ? BI_KERNEL_TILED_PINGPONG : BI_KERNEL_TILED, t.bm / 16, 0, 0, t.bn, v};
@@ -365,7 +444,7 @@ bi_status bi_plan_query(int op, int64_t N, int64_t K, bi_plan *out) {
                 out->threads = 256;
                 return BI_OK;
             }
-            fill_tile_plan(op, gemm_variant(op, N, K), out);
+            fill_tile_plan(op, plan_variant(op, N, K), out);
             return BI_OK;
         }
         case BI_OP_RMSNORM:
@@ -411,11 +490,11 @@ bi_status bi_plan_regimes(int op, int64_t N, int64_t K, int a_fmt, int cus, bi_r
     }
     int a_mode = 0, b_mode = 0;
     op_modes(op, a_fmt, K, &a_mode, &b_mode);
-    // classify() is constant above kStreamMaxRows rows: walk M up to there
-    // and merge equal neighbours into row ranges
+    // classify() is constant above kModelRows rows: walk M up to there and
+    // merge equal neighbours into row ranges
     int n = 0;
     Regime prev{};
-    for (int64_t M = 1; M <= kStreamMaxRows + 1; ++M) {
+    for (int64_t M = 1; M <= kModelRows + 1; ++M) {
         const Regime r = classify(op, a_mode, b_mode, N, K, 1, op == BI_OP_GROUPED_GEMM, cus, M);
         if (M > 1 && r == prev) {
             if (n <= capacity) out[n - 1].m_max = static_cast<int32_t>(M);
@@ -430,6 +509,7 @@ bi_status bi_plan_regimes(int op, int64_t N, int64_t K, int a_fmt, int cus, bi_r
             g.cols = r.cols;
             g.a_pairs = r.ap;
             g.a_rows_staged = r.ma;
+            g.tile_variant = r.variant + 1;
         }
         ++n;
         prev = r;

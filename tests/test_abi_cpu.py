@@ -306,8 +306,11 @@ def test_mla_decode_noalloc_validation():
                                           (B.BI_OP_BMM, 512, 128, 0), (B.BI_OP_GROUPED_GEMM, 4096, 4096, 0)])
 def test_plan_regimes_cover_every_m(op, N, K, a_fmt):
     """The kernel-choice table covers M >= 1 without gaps or overlaps; its
-    last range is the tiled kernel of bi_plan_query's shape (or the
-    streaming BMM kernel), unbounded above; streaming ranges end by 128 rows."""
+    last range starts by 4097 rows and is the tiled kernel of bi_plan_query's
+    shape (or the streaming BMM kernel), unbounded above; streaming ranges
+    end by 128 rows; every tiled range names a compiled shape that matches
+    its row blocks and columns."""
+    shapes = B.tile_shapes()
     for cus in (80, 256, 304):
         regs = B.plan_regimes(op, N, K, a_fmt, cus=cus)
         assert regs[0]["m_min"] == 1 and regs[-1]["m_max"] == 2 ** 31 - 1
@@ -319,11 +322,53 @@ def test_plan_regimes_cover_every_m(op, N, K, a_fmt):
         if last["kind"] != "bmm_stream":
             assert last["kind"] in ("tiled", "tiled_pingpong")
             assert (last["row_blocks"] * 16, last["cols"]) == (plan["bm"], plan["bn"])
-            assert last["m_min"] <= 129
-        for r in regs[:-1]:
-            assert r["kind"].startswith("stream") and r["m_max"] <= 128
-        if a_fmt == 1 or op == B.BI_OP_GROUPED_GEMM:
-            assert len(regs) == 1                     # no streaming kernel serves these
+            assert last["m_min"] <= 4097
+        for r in regs:
+            if r["kind"].startswith("tiled"):
+                t = shapes[r["tile_variant"] - 1]
+                assert (t["bm"], t["bn"]) == (r["row_blocks"] * 16, r["cols"])
+            else:
+                assert r["tile_variant"] == 0
+                assert r["kind"] == "bmm_stream" or r["m_max"] <= 128
+        if op == B.BI_OP_GROUPED_GEMM:
+            assert len(regs) == 1                     # one shape per (N, K)
+        if a_fmt == 1:
+            assert all(r["kind"] == "tiled" for r in regs)   # no streaming kernel for an NVFP4 A
+
+
+def _shape_at(op, N, K, M, a_fmt=0, cus=256):
+    for r in B.plan_regimes(op, N, K, a_fmt, cus=cus):
+        if r["m_min"] <= M <= r["m_max"]:
+            if r["kind"].startswith("tiled"):
+                return (r["row_blocks"] * 16, r["cols"])
+            return r["kind"]
+    raise AssertionError(M)
+
+
+def test_plan_regimes_cost_model_choices():
+    """The tiled kernel's shape at each M of the Qwen3-8B-shaped linears on
+    a 256-CU device is the one the MI355X sweep of every compiled shape
+    found fastest (or within a few percent of it)."""
+    G, F = B.BI_OP_GEMM, B.BI_OP_NVFP4_GEMM
+    want = {
+        (G, 6144, 4096): {32: (64, 64), 128: (64, 64), 256: (128, 64), 512: (128, 128), 1024: (256, 128),
+                          2048: (256, 192), 4096: (256, 192), 8192: (256, 256)},
+        (G, 4096, 4096): {32: "stream_reg", 64: "stream_reg", 128: (64, 64), 256: (64, 64), 512: (128, 64),
+                          1024: (128, 128), 2048: (256, 128), 4096: (256, 256), 8192: (256, 256)},
+        (G, 24576, 4096): {32: (128, 128), 128: (128, 128), 256: (256, 128), 512: (256, 192),
+                           1024: (256, 192), 2048: (256, 256), 4096: (256, 256)},
+        (G, 4096, 12288): {32: "stream_reg", 64: "stream_reg", 128: (64, 64), 256: (64, 64), 512: (128, 64),
+                           1024: (128, 128), 2048: (256, 128), 4096: (256, 256), 8192: (256, 256)},
+        (F, 24576, 4096): {32: (128, 128), 64: (128, 128), 128: (128, 128), 256: (256, 128),
+                           1024: (256, 192), 2048: (256, 256), 4096: (256, 256)},
+    }
+    for (op, N, K), ms in want.items():
+        for M, shape in ms.items():
+            assert _shape_at(op, N, K, M) == shape, (op, N, K, M)
+    w4a4 = {32: (128, 128), 128: (128, 128), 256: (256, 128), 512: (256, 192), 1024: (256, 192),
+            2048: (256, 256), 4096: (256, 256)}
+    for M, shape in w4a4.items():
+        assert _shape_at(F, 24576, 4096, M, a_fmt=1) == shape, M
 
 
 def test_plan_regimes_edges_and_errors():
@@ -335,7 +380,7 @@ def test_plan_regimes_edges_and_errors():
     arr = (B.BiRegime * 1)()
     n = B.ctypes.c_int(0)
     st = B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4096, 0, 256, arr, 1, B.ctypes.byref(n))
-    assert st == B.BI_ERR_SHAPE and n.value == 6
+    assert st == B.BI_ERR_SHAPE and n.value == len(B.plan_regimes(B.BI_OP_GEMM, 4096, 4096, cus=256)) > 1
     assert B.lib().bi_plan_regimes(B.BI_OP_RMSNORM, 4096, 0, 0, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_UNSUPPORTED
     assert B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4096, 1, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_SHAPE
     assert B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4100, 0, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_SHAPE

@@ -163,10 +163,10 @@ def test_w4a4_config_tile_variants_and_grid():
 
 # ------------------------------------------------------------ regime edges
 
-def _regime_ms(op, N, K, a_fmt=B.BI_A_BF16, mmax=300):
+def _regime_ms(op, N, K, a_fmt=B.BI_A_BF16, mmax=4200):
     """M values on both sides of every edge bi_plan_regimes lists for (op,
-    N, K) on this device (the kernel choice changes there), plus 1 and the
-    256-row M-tile edges."""
+    N, K) on this device (the kernel or tile shape changes there), plus 1
+    and the 256-row M-tile edges."""
     ms = {1, 2, 255, 256, 257}
     for r in B.plan_regimes(op, N, K, a_fmt):
         ms |= {r["m_min"], r["m_min"] + 1, r["m_max"], r["m_max"] + 1}
@@ -179,10 +179,10 @@ CONFIG_NK = [(256, 512), (6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288
 @pytest.mark.parametrize("N,K", CONFIG_NK)
 def test_regime_edges_bf16(N, K):
     """Every configuration's (N, K), M walked across every edge of the
-    kernel choice that bi_plan_regimes lists: each M's rows are bitwise the
-    forced tiled kernel's (tile shape 0, 256 x 256) and the M = 300 batch's
-    prefix."""
-    Mmax = 300
+    kernel and tile-shape choice that bi_plan_regimes lists (up to 4200
+    rows, past the last edge): each M's rows are bitwise the forced tiled
+    kernel's (tile shape 0, 256 x 256) and the M = 4200 batch's prefix."""
+    Mmax = 4200
     A = inputs.randn_bf16((Mmax, K), tag=(710, N, K))
     W = inputs.randn_bf16((N, K), 0.02, tag=(711, N, K))
     Ad, Wd = dev(A), dev(W)
@@ -193,26 +193,37 @@ def test_regime_edges_bf16(N, K):
         y = B.bi_gemm(Ad[:M], Wd)
         assert torch.equal(y, yfull[:M]), f"M={M} vs batch"
         assert torch.equal(y, B.bi_gemm(Ad[:M], Wd, tile_variant=1)), f"M={M} vs tiled"
-    ref, s = oracle.gemm(A[[0, 17, 299]], W)
-    assert_within_tol(host(yfull)[[0, 17, 299]], ref, s, f"N={N} K={K}")
+    rows = [0, 17, 299, 2100, Mmax - 1]
+    ref, s = oracle.gemm(A[rows], W)
+    assert_within_tol(host(yfull)[rows], ref, s, f"N={N} K={K}")
 
 
-def test_regime_edges_nvfp4():
-    """The NVFP4 configuration's (24576, 4096), bf16 A: M across every edge
-    bi_plan_regimes lists, bitwise equal to the forced 256 x 256 tiled
-    kernel (the plan's shape) and the batch prefix."""
-    N, K, Mmax = 24576, 4096, 300
+@pytest.mark.parametrize("a_fp4", [False, True], ids=["bf16A", "w4a4"])
+def test_regime_edges_nvfp4(a_fp4):
+    """The NVFP4 configuration's (24576, 4096), bf16 or NVFP4 A: M across
+    every edge bi_plan_regimes lists (up to 4200 rows), bitwise equal to the
+    forced 256 x 256 tiled kernel (classic schedule) and the batch prefix."""
+    N, K, Mmax = 24576, 4096, 4200
     W, Ws, g = _nvfp4_weights(N, K, (125,))
     alpha = float(np.float32(1.0) / g)
     A = inputs.randn_bf16((Mmax, K), tag=(712,))
     Ad, Wd, Wsd = dev(A), dev(W), dev(Ws)
-    note("regime edges nvfp4 M=300")
-    yfull = B.bi_nvfp4_gemm(Ad, Wd, Wsd, alpha)
-    for M in _regime_ms(B.BI_OP_NVFP4_GEMM, N, K):
-        note(f"regime edges nvfp4 M={M}")
-        y = B.bi_nvfp4_gemm(Ad[:M], Wd, Wsd, alpha)
+    if a_fp4:
+        Aq, Aqs = B.bi_nvfp4_quant(Ad, 1.0)
+
+        def run(M, **kw):
+            return B.bi_nvfp4_gemm(Aq[:M], Wd, Wsd, alpha, A_scales=Aqs[:M], **kw)
+    else:
+        def run(M, **kw):
+            return B.bi_nvfp4_gemm(Ad[:M], Wd, Wsd, alpha, **kw)
+    tag = "w4a4" if a_fp4 else "nvfp4"
+    note(f"regime edges {tag} M={Mmax}")
+    yfull = run(Mmax)
+    for M in _regime_ms(B.BI_OP_NVFP4_GEMM, N, K, B.BI_A_NVFP4 if a_fp4 else B.BI_A_BF16):
+        note(f"regime edges {tag} M={M}")
+        y = run(M)
         assert torch.equal(y, yfull[:M]), f"M={M} vs batch"
-        assert torch.equal(y, B.bi_nvfp4_gemm(Ad[:M], Wd, Wsd, alpha, tile_variant=13)), f"M={M} vs tiled"
+        assert torch.equal(y, run(M, tile_variant=13)), f"M={M} vs tiled"
 
 
 # ------------------------------------------------------------ every row alone
