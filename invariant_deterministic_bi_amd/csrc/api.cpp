@@ -272,6 +272,11 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
         const int nb = (N + 15) / 16 >= 2 * static_cast<int64_t>(cus) ? 16 : 8;
         return {BI_KERNEL_STREAM_RING, 1, 0, M <= 4 ? 4 : M <= 8 ? 8 : 16, nb, -1};
     }
+    // NVFP4 A and weight, M <= 16: the same A-in-LDS streaming kernel, A rows
+    // decoded exactly to bf16 into LDS as they are copied
+    if (op == BI_OP_NVFP4_GEMM && M <= 16 && a_mode == bi::OPND_NVFP4_ROWS &&
+        bi::direct_alds_ok(static_cast<int>(M), static_cast<int>(K), true))
+        return {BI_KERNEL_STREAM_A_LDS, 1, 0, 0, 16, -1};
     // BMM with a short reduction: the streaming BMM kernel for every M (its
     // own recipe, chosen from K alone)
     if (op == BI_OP_BMM && bi::bmm_short_k_ok(static_cast<int>(K))) return {BI_KERNEL_BMM_STREAM, 4, 0, 0, 128, -1};
@@ -355,11 +360,12 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
             // a bf16 weight streams best from one wavefront per compute unit
             // (fewer concurrent row streams in HBM), an NVFP4 one from three
             // (its decode needs the SIMDs)
-            const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
+            const bool afp4 = a_mode == bi::OPND_NVFP4_ROWS;
+            const bool fp4 = afp4 || b_mode == bi::OPND_NVFP4_RAW;
             const int items = static_cast<int>((in.N + r.cols - 1) / r.cols);
             int waves = items <= 3 * cus ? items : fp4 ? 3 * cus : cus;
             if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
-            e = bi::launch_direct_alds(in, fp4, r.cols, waves, cus, depth, s);
+            e = bi::launch_direct_alds(in, fp4, afp4, r.cols, waves, cus, depth, s);
             break;
         }
         case BI_KERNEL_STREAM_REG: {

@@ -119,8 +119,9 @@ hipError_t launch_direct(const GemmArgs &args, int rb, int ap, int grid, int dep
 hipError_t launch_direct_nvfp4(const GemmArgs &args, int rb, int ap, int grid, int depth, hipStream_t stream);
 // Direct path with A staged in LDS once per workgroup (bf16 or raw NVFP4
 // weight), for shapes with direct_alds_ok; `waves` streaming wavefronts.
+// afp4 (with fp4): A is NVFP4 rows (lda % 32 == 0), decoded into LDS.
 bool direct_alds_ok(int M, int K, bool fp4);
-hipError_t launch_direct_alds(const GemmArgs &args, bool fp4, int nb, int waves, int cus, int depth,
+hipError_t launch_direct_alds(const GemmArgs &args, bool fp4, bool afp4, int nb, int waves, int cus, int depth,
                               hipStream_t stream);
 
 struct RmsArgs {

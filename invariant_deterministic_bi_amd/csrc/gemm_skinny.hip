@@ -622,8 +622,13 @@ __device__ __forceinline__ void wait_a(i32x4 (&a)[U]) {
 // 128-byte instruction: rows 0..7 of chunk c in lanes 0..7 of each 16-lane
 // row, of chunk c + 1 in lanes 8..15, and a DPP rotation by eight lanes gives
 // chunk c + 1 its place; lanes 8..15 then carry columns that are not stored.
-template <bool FP4, int NB, int D>
+// AFP4 (with FP4): A is NVFP4 too (codes [M, K/2], scales [M, K/16], lda in
+// elements); its rows are decoded exactly to bf16 on the way into LDS -- the
+// same values the tiled kernel's NVFP4 A staging stores -- and the rest is
+// the bf16-A kernel.
+template <bool FP4, int NB, int D, bool AFP4 = false>
 __global__ __launch_bounds__(256) void direct_alds_kernel(GemmArgs p) {
+    static_assert(!AFP4 || FP4, "an NVFP4 A goes with an NVFP4 weight");
     constexpr int U = FP4 ? 4 : 2;      // chunks per unit
     constexpr int LPU = NB == 8 ? 1 : 2; // global loads per unit
     static_assert(NB == 16 || (NB == 8 && !FP4), "8-column items are bf16 only");
@@ -639,8 +644,25 @@ __global__ __launch_bounds__(256) void direct_alds_kernel(GemmArgs p) {
     const int my_items = slot < items ? (items - slot + slots - 1) / slots : 0;
     const int stride = a_stride(p.K);
 
-    // 1. A rows by LDS DMA, 1 KB blocks shared out over the wavefronts
-    {
+    // 1. A rows by LDS DMA, 1 KB blocks shared out over the wavefronts; an
+    // NVFP4 A in 32-element units (16 code bytes, two scale bytes), decoded
+    // and written by every thread
+    if constexpr (AFP4) {
+        const uint8_t *pc = static_cast<const uint8_t *>(p.A);
+        const uint8_t *ps = static_cast<const uint8_t *>(p.A_scales);
+        const int upr = p.K >> 5;
+        for (int q = (int)threadIdx.x; q < p.M * upr; q += (int)blockDim.x) {
+            const int row = q / upr, u = q - row * upr;
+            const uint4 c = *reinterpret_cast<const uint4 *>(pc + (int64_t)row * (p.lda >> 1) + u * 16);
+            const uint32_t sv = *reinterpret_cast<const uint16_t *>(ps + (int64_t)row * (p.lda >> 4) + u * 2);
+            const float s0 = e4m3_value(sv & 0xFFu), s1 = e4m3_value(sv >> 8);
+            char *dst = lds + row * stride + u * 64;
+            lds_write_b128(dst, decode8(c.x, s0));
+            lds_write_b128(dst + 16, decode8(c.y, s0));
+            lds_write_b128(dst + 32, decode8(c.z, s1));
+            lds_write_b128(dst + 48, decode8(c.w, s1));
+        }
+    } else {
         const i32x4 ra = make_rsrc(p.A, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
         const int bpr = (p.K * 2 + 1023) >> 10;
         for (int b = w; b < p.M * bpr; b += nwv) {
@@ -762,7 +784,7 @@ __global__ __launch_bounds__(256) void direct_alds_kernel(GemmArgs p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <bool FP4, int NB>
+template <bool FP4, int NB, bool AFP4 = false>
 hipError_t launch_alds(const GemmArgs &a, int d, int grid, int nwv, hipStream_t s) {
     const dim3 b(64 * nwv);
     switch (d) {
@@ -772,10 +794,10 @@ hipError_t launch_alds(const GemmArgs &a, int d, int grid, int nwv, hipStream_t 
                 break;
             }
             return hipErrorInvalidValue;
-        case 16: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 16>), dim3(grid), b, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 8>), dim3(grid), b, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 4>), dim3(grid), b, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 2>), dim3(grid), b, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 16, AFP4>), dim3(grid), b, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 8, AFP4>), dim3(grid), b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 4, AFP4>), dim3(grid), b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((direct_alds_kernel<FP4, NB, 2, AFP4>), dim3(grid), b, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -803,9 +825,10 @@ bool direct_alds_ok(int M, int K, bool fp4) {
     return M >= 1 && M <= 16 && direct_alds_fits(M, K) && (fp4 ? K % 128 == 0 : true) && nu % 2 == 0;
 }
 
-hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, int nb, int waves, int cus, int depth,
+hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, bool afp4, int nb, int waves, int cus, int depth,
                               hipStream_t s) {
-    if (waves < 1 || cus < 1 || !direct_alds_ok(a.M, a.K, fp4) || (nb != 8 && nb != 16) || (fp4 && nb != 16))
+    if (waves < 1 || cus < 1 || !direct_alds_ok(a.M, a.K, fp4) || (nb != 8 && nb != 16) || (fp4 && nb != 16) ||
+        (afp4 && (!fp4 || a.lda % 32 != 0 || !a.A_scales)))
         return hipErrorInvalidValue;
     const int nu = fp4 ? a.K / 128 : (a.K + 63) / 64;
     const int d = pick_depth(nu, depth == 1 ? 2 : depth, fp4 ? 8 : (nb == 16 || a.K >= 8192) ? 16 : 8,
@@ -815,6 +838,7 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, int nb, int waves, in
     int nwv = (waves + cus - 1) / cus;
     nwv = nwv < 1 ? 1 : nwv > 4 ? 4 : nwv;
     const int grid = (waves + nwv - 1) / nwv;
+    if (afp4) return direct::launch_alds<true, 16, true>(a, d, grid, nwv, s);
     if (fp4) return direct::launch_alds<true, 16>(a, d, grid, nwv, s);
     return nb == 8 ? direct::launch_alds<false, 8>(a, d, grid, nwv, s)
                    : direct::launch_alds<false, 16>(a, d, grid, nwv, s);

@@ -333,7 +333,8 @@ def test_plan_regimes_cover_every_m(op, N, K, a_fmt):
         if op == B.BI_OP_GROUPED_GEMM:
             assert len(regs) == 1                     # one shape per (N, K)
         if a_fmt == 1:
-            assert all(r["kind"] == "tiled" for r in regs)   # no streaming kernel for an NVFP4 A
+            # an NVFP4 A streams only through the A-in-LDS kernel (M <= 16)
+            assert all(r["kind"] == "tiled" or (r["kind"] == "stream_a_lds" and r["m_max"] <= 16) for r in regs)
 
 
 def _shape_at(op, N, K, M, a_fmt=0, cus=256):
@@ -369,6 +370,8 @@ def test_plan_regimes_cost_model_choices():
             2048: (256, 256), 4096: (256, 256)}
     for M, shape in w4a4.items():
         assert _shape_at(F, 24576, 4096, M, a_fmt=1) == shape, M
+    for M in (1, 16):
+        assert _shape_at(F, 24576, 4096, M, a_fmt=1) == "stream_a_lds", M
 
 
 def test_plan_regimes_edges_and_errors():

@@ -157,6 +157,43 @@ def test_nvfp4_activation_rows_quantised_alone():
         assert np.array_equal(yi[0], yfull[i]), f"row {i}"
 
 
+@pytest.mark.parametrize("N,K", [(1000, 1024), (24576, 4096), (300, 4608)])
+def test_w4a4_streaming_small_m(N, K):
+    """W4A4 at M <= 16 streams the weight with A decoded into LDS (at K =
+    4608 the 16-row A no longer fits there, so M = 16 takes the tiled kernel
+    while M <= 15 streams): every M in 1..16 is bitwise the forced tiled
+    kernel and the M = 16 batch's prefix, also with A rows at a padded
+    stride; power-of-two codes give the oracle's exact result; N(0,1) rows
+    agree with the oracle within tolerance."""
+    W, Ws, gw = _nvfp4_weights(N, K, (129, N))
+    x = inputs.rng(12345, 130, N).standard_normal((16, K)).astype(np.float32)
+    ga = inputs.nvfp4_global_scale(x)
+    Aq, Aqs = inputs.nvfp4_quantize(x, ga)
+    alpha = float(np.float32(1.0) / (ga * gw))
+    Wd, Wsd = dev(W), dev(Ws)
+    pad_q = np.zeros((16, K // 2 + 16), np.uint8)
+    pad_s = np.zeros((16, K // 16 + 2), np.uint8)
+    pad_q[:, :K // 2], pad_s[:, :K // 16] = Aq, Aqs
+    Aqd, Aqsd = dev(Aq), dev(Aqs)
+    Pq, Ps = dev(pad_q)[:, :K // 2], dev(pad_s)[:, :K // 16]
+    note(f"w4a4 small M N={N} K={K} M=16")
+    yfull = B.bi_nvfp4_gemm(Aqd, Wd, Wsd, alpha, A_scales=Aqsd)
+    for M in range(1, 17):
+        note(f"w4a4 small M N={N} K={K} M={M}")
+        y = B.bi_nvfp4_gemm(Aqd[:M], Wd, Wsd, alpha, A_scales=Aqsd[:M])
+        assert torch.equal(y, yfull[:M]), f"M={M} vs batch"
+        assert torch.equal(y, B.bi_nvfp4_gemm(Aqd[:M], Wd, Wsd, alpha, A_scales=Aqsd[:M], tile_variant=13)), M
+        assert torch.equal(y, B.bi_nvfp4_gemm(Pq[:M], Wd, Wsd, alpha, A_scales=Ps[:M])), f"M={M} padded"
+    ref, s = oracle.nvfp4_gemm(Aq, Aqs, W, Ws, alpha, K, rows=[0, 7, 15])
+    assert_within_tol(host(yfull)[[0, 7, 15]], ref, s, f"w4a4 N={N} K={K}")
+    W2, Ws2 = inputs.random_nvfp4_pow2((N, K), tag=(131, N))
+    A2, As2 = inputs.random_nvfp4_pow2((7, K), tag=(132, N))
+    ref2, _ = oracle.nvfp4_gemm(A2, As2, W2, Ws2, 0.5, K)
+    note(f"w4a4 small M integer-exact N={N} K={K}")
+    y2 = host(B.bi_nvfp4_gemm(dev(A2), dev(W2), dev(Ws2), 0.5, A_scales=dev(As2)))
+    assert np.array_equal(y2, rne_bf16_of_exact(ref2))
+
+
 # ----------------------------------------------------------------- RMSNorm
 
 
