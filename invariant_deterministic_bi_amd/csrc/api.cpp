@@ -358,12 +358,14 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         case BI_KERNEL_STREAM_A_LDS: {
             // one wavefront per item up to three per compute unit; beyond that
             // a bf16 weight streams best from one wavefront per compute unit
-            // (fewer concurrent row streams in HBM), an NVFP4 one from three
-            // (its decode needs the SIMDs)
+            // (fewer concurrent row streams in HBM), an NVFP4 one from one
+            // wavefront per item up to eight per compute unit: its decode is
+            // VALU work, and a SIMD issues VALU at about half rate for one
+            // wavefront, near full rate for two or more
             const bool afp4 = a_mode == bi::OPND_NVFP4_ROWS;
             const bool fp4 = afp4 || b_mode == bi::OPND_NVFP4_RAW;
             const int items = static_cast<int>((in.N + r.cols - 1) / r.cols);
-            int waves = items <= 3 * cus ? items : fp4 ? 3 * cus : cus;
+            int waves = items <= 3 * cus ? items : fp4 ? (items < 8 * cus ? items : 8 * cus) : cus;
             if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
             e = bi::launch_direct_alds(in, fp4, afp4, r.cols, waves, cus, depth, s);
             break;

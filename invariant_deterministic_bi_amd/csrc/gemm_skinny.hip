@@ -588,7 +588,7 @@ hipError_t launch_nvfp4_ap(const GemmArgs &a, int d, int grid, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Direct path with A in LDS.  The workgroup (1 to 4 wavefronts, each streaming
+// Direct path with A in LDS.  The workgroup (1 to 8 wavefronts, each streaming
 // its own items) first copies A rows 0..M-1 into LDS by DMA, overlapping the
 // first weight prefetch, and every chunk's A fragment is then one LDS read:
 // the only global loads in the loop are the weight's (one 1 KB load per bf16
@@ -596,7 +596,7 @@ hipError_t launch_nvfp4_ap(const GemmArgs &a, int d, int grid, hipStream_t s) {
 // padded A fits kALds bytes.  Row stride: whole 1 KB DMA blocks plus 16 bytes,
 // so the up to 16 rows of a fragment read fall in distinct bank groups.
 // ---------------------------------------------------------------------------
-constexpr int kALds = 144 * 1024;  // one workgroup (up to four wavefronts) per compute unit
+constexpr int kALds = 144 * 1024;  // one workgroup (up to eight wavefronts) per compute unit
 
 __device__ __forceinline__ int a_stride(int K) { return ((K * 2 + 1023) >> 10) * 1024 + 16; }
 
@@ -627,7 +627,7 @@ __device__ __forceinline__ void wait_a(i32x4 (&a)[U]) {
 // same values the tiled kernel's NVFP4 A staging stores -- and the rest is
 // the bf16-A kernel.
 template <bool FP4, int NB, int D, bool AFP4 = false>
-__global__ __launch_bounds__(256) void direct_alds_kernel(GemmArgs p) {
+__global__ __launch_bounds__(512) void direct_alds_kernel(GemmArgs p) {
     static_assert(!AFP4 || FP4, "an NVFP4 A goes with an NVFP4 weight");
     constexpr int U = FP4 ? 4 : 2;      // chunks per unit
     constexpr int LPU = NB == 8 ? 1 : 2; // global loads per unit
@@ -831,12 +831,14 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, bool afp4, int nb, in
         (afp4 && (!fp4 || a.lda % 32 != 0 || !a.A_scales)))
         return hipErrorInvalidValue;
     const int nu = fp4 ? a.K / 128 : (a.K + 63) / 64;
-    const int d = pick_depth(nu, depth == 1 ? 2 : depth, fp4 ? 8 : (nb == 16 || a.K >= 8192) ? 16 : 8,
-                             nb == 8 ? 32 : 16);
-    if (d < 2) return hipErrorInvalidValue;  // the unit count is even (direct_alds_ok)
     // at most one workgroup per compute unit (the A copy takes most of LDS)
     int nwv = (waves + cus - 1) / cus;
-    nwv = nwv < 1 ? 1 : nwv > 4 ? 4 : nwv;
+    nwv = nwv < 1 ? 1 : nwv > 8 ? 8 : nwv;
+    // NVFP4 units in flight: 8, or 4 when two wavefronts share a SIMD (their
+    // decode interleaves, and fewer registers per wavefront are live)
+    const int d = pick_depth(nu, depth == 1 ? 2 : depth,
+                             fp4 ? (nwv > 4 ? 4 : 8) : (nb == 16 || a.K >= 8192) ? 16 : 8, nb == 8 ? 32 : 16);
+    if (d < 2) return hipErrorInvalidValue;  // the unit count is even (direct_alds_ok)
     const int grid = (waves + nwv - 1) / nwv;
     if (afp4) return direct::launch_alds<true, 16, true>(a, d, grid, nwv, s);
     if (fp4) return direct::launch_alds<true, 16>(a, d, grid, nwv, s);
