@@ -259,6 +259,52 @@ def test_tile_shapes_bmm_and_nvfp4():
             assert np.array_equal(host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha, tile_variant=v)), y), (v, rep)
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 2600, 4160), (513, 1300, 2048), (2048, 6144, 4096), (77, 200, 64),
+                                   (300, 256, 128), (260, 5000, 192)])
+def test_nvfp4_pingpong_matches_classic_schedule(M, N, K):
+    """The NVFP4 ping-pong kernel (256 x 256, tile variant 14) against the
+    classic schedule of the same shape (13): ragged M and N, short K (one,
+    two, three 64-column stages), several grid caps, each run repeated (a
+    phase-ordering race would show as a rare mismatch); parity with the
+    oracle on rows of the first and last M-tile."""
+    Wq, Ws, g = _nvfp4_weights(N, K, (144, N))
+    X = inputs.randn_bf16((M, K), tag=(145, M, N))
+    Xd, Wqd, Wsd = dev(X), dev(Wq), dev(Ws)
+    alpha = float(np.float32(1.0) / g)
+    note(f"nvfp4 pingpong M={M} N={N} K={K} classic")
+    y = host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha, tile_variant=13))
+    for mw in (0, 7, 64):
+        for rep in range(2):
+            note(f"nvfp4 pingpong M={M} N={N} K={K} grid cap {mw} rep {rep}")
+            yp = host(B.bi_nvfp4_gemm(Xd, Wqd, Wsd, alpha, tile_variant=14, max_workgroups=mw))
+            assert np.array_equal(yp, y), (M, N, K, mw, rep)
+    rows = sorted({0, min(255, M - 1), M - 1})
+    ref, s = oracle.nvfp4_gemm(X[rows], None, Wq, Ws, alpha, K)
+    assert_within_tol(y[rows], ref, s, "nvfp4 pingpong")
+
+
+def test_nvfp4_pingpong_decodes_every_code_and_scale():
+    """The decode table of the ping-pong kernel: an identity A (bf16, 512
+    rows) picks out single decoded weights, every one of the 16 codes under
+    each of the 254 finite E4M3 scale bytes, through tile variant 14."""
+    K = 512
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    bpr = K // 16
+    N = -(-finite.size // bpr)
+    Ws = np.full(N * bpr, 0x38, np.uint8)
+    Ws[:finite.size] = finite
+    Ws = Ws.reshape(N, bpr)
+    block = np.array([((2 * j + 1) << 4) | (2 * j) for j in range(8)], np.uint8)
+    W = np.tile(block, N * bpr).reshape(N, K // 2)
+    lut, sv = _e2m1_e4m3_table()
+    want = lut[np.arange(K) % 16][:, None] * sv[Ws[:, np.arange(K) // 16]].T + 0.0
+    want_bits = inputs.to_bf16_bits(want)
+    A = inputs.to_bf16_bits(np.eye(K))
+    note("nvfp4 pingpong decode table")
+    y = host(B.bi_nvfp4_gemm(dev(A), dev(W), dev(Ws), 1.0, tile_variant=14))
+    assert np.array_equal(y, want_bits)
+
+
 @pytest.mark.parametrize("H,M,K,N", [(5, 70, 64, 200), (3, 33, 128, 512), (2, 129, 256, 136),
                                      (128, 1, 128, 512), (7, 1000, 128, 264)])
 def test_bmm_short_k_kernel(H, M, K, N):
