@@ -326,33 +326,41 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
 // K/16], K % 64 == 0) in the same ping-pong schedule, 256 x 256 tiles.
 //
 // B reaches LDS raw: per 64-column stage, 256 rows of 32 code bytes and 4
-// scale bytes (9 KB, against 32 KB of bf16), by LDS DMA.  The two groups
-// take different shares of the memory work, so that the decode arithmetic
-// never runs beside the other group's decode:
-//   * group 0, in its memory phase (phase b of step s - 1), reads A rows
-//     0..127 and the raw B of stage s, decodes the B fragments of its
-//     wavefront's 64 columns straight into registers (the exact decode of
-//     the tiled kernel: FP4 pair convert with a unit scale, one fp32
-//     multiply by the E4M3 scale, top halves) and writes them to a decoded
-//     B buffer in LDS;
-//   * group 1, in its memory phase (phase a of step s), reads A rows
-//     128..255 and the decoded B fragments of its wavefront's columns (the
-//     same 64 columns), and issues every LDS-DMA load: A rows 0..127, A
-//     rows 128..255 and the raw B of stage s + 2, in phase a of step s.
-// Each compute phase is then 64 MFMAs on fragments in registers.  Group 1
-// waits, at the end of a memory phase, until only that phase's loads are in
-// flight; stage s's loads (issued in phase a of step s - 2) have landed by
-// the end of phase a of step s - 1, before group 0 reads them in phase b of
-// step s - 1.  Rings: A rows 0..127 two stages, A rows 128..255 three (group
-// 1 reads stage s and reissues its slot in the same phase), raw B two, the
-// decoded B one (written in phase b of step s - 1, read in phase a of s).
-// The decoded fragments hold the same bf16 values the tiled kernel reads
-// from its decoded LDS tile, so every output element's chain -- and its
-// bits -- are the same.
+// scale bytes (9 KB, against 32 KB of bf16), by LDS DMA.  Each B stage is
+// decoded once, half by each group, in their memory phases: a SIMD issues
+// VALU work at about half rate for a lone wavefront, so the decode of a
+// whole stage by one group would outlast the other group's 64 MFMAs.  The
+// decode is the tiled kernel's exact one (FP4 pair convert with a unit
+// scale, one fp32 multiply by the E4M3 scale, top halves).
+//   * group 0, in its memory phase for stage s (phase b of step s - 1),
+//     reads A rows 0..127, the decoded K chunk 1 of stage s and the raw
+//     K chunk 0 of stage s; it decodes chunk 0 of its wavefront's 64
+//     columns straight into registers and writes it to the decoded B
+//     buffer, and issues the LDS-DMA loads of A rows 128..255 of stage s + 2;
+//   * group 1, in its memory phase for stage s (phase a of step s), reads A
+//     rows 128..255 and both decoded chunks of stage s, decodes K chunk 1 of
+//     stage s + 1 from its raw bytes into the decoded B buffer (after its
+//     reads of stage s's chunk 1 from the same slots: one wavefront's LDS
+//     operations execute in order), and issues the LDS-DMA loads of A rows
+//     0..127 and the raw B of stage s + 3 (after its A reads are done: A
+//     stage s + 3 takes stage s's slot).
+// Wavefront j of either group works on columns 64 j .. 64 j + 63, so a
+// decoded fragment goes from one wavefront to its partner on the other
+// group.  Each compute phase is 64 MFMAs on fragments in registers.  Each
+// wavefront waits, at the start of its memory phase, until only its
+// previous memory phase's loads are in flight: group 1's loads of stage
+// s + 1 (issued two memory phases earlier) have then landed, for its own
+// decode of raw chunk 1 of stage s + 1 and, after the barrier, for group
+// 0's reads of stage s + 1; group 0's A rows 128..255 of stage s + 1 have
+// landed before group 1 reads them in the next phase.  Every load so has
+// about two phase pairs to land.  Rings: A rows 0..127, A rows 128..255
+// and raw B three stages each, the decoded B one per K chunk.  The decoded fragments hold the same bf16 values the tiled
+// kernel reads from its decoded LDS tile, so every output element's chain
+// -- and its bits -- are the same.
 // ---------------------------------------------------------------------------
 struct Nv4Shape {
     static constexpr int BN = 256, FN = 4;
-    static constexpr int RA0 = 2, RA1 = 3, RR = 2;  // ring depths
+    static constexpr int RA0 = 3, RA1 = 3, RR = 3;  // ring depths
     static constexpr int CodeBytes = BN * 32, RawStage = BN * 36;
     static constexpr int OffA1 = RA0 * kHalf;
     static constexpr int OffRaw = OffA1 + RA1 * kHalf;
@@ -362,7 +370,8 @@ struct Nv4Shape {
     static constexpr int CStride = BN * 2 + 16;
     static constexpr int CBytes = kBM * CStride;
     static constexpr int Lds = Pipe > CBytes ? Pipe : CBytes;
-    static constexpr int LOADS = 11;  // group 1's DMA instructions per memory phase, per wavefront
+    static constexpr int LOADS0 = 4;  // DMA instructions per memory phase, per wavefront: group 0
+    static constexpr int LOADS1 = 7;  // and group 1
     static_assert(Lds <= 160 * 1024, "LDS budget of gfx950");
 };
 
@@ -418,43 +427,54 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         const int srow = 64 * j + lane;
         const int scale_off = srow < rows_b ? srow * spr : (int)0x80000000;
 
-        // Group 1's loads of one memory phase (phase a of step u): stage u + 2
-        // of A rows 0..127, A rows 128..255 and raw B.  Stages past the last
-        // issue zero-filling loads into the slot they would use.
-        auto issue = [&](int u) {
-            const int st = u + 2;
-            const bool live = st < nk;
+        // LDS-DMA loads.  Each lane's offset within a stage is fixed per
+        // tile (the DmaLane and raw-lane offsets above); the stage's offset
+        // goes in the scalar offset, so an instruction costs no vector
+        // arithmetic.  A stage past the last gets a scalar offset that puts
+        // every lane beyond its buffer, so its loads fill zeros.  Rows past M
+        // (or N) lie beyond their buffer too -- A's range ends with row M - 1,
+        // and a raw lane past N carries an offset of 2^31 -- and K % 64 == 0,
+        // so no other check is needed.  (Offsets stay below 2^32: A lanes
+        // are below 2^26, and raw buffers end below 2^29 < 2^30.)
+        const i32x4 ra_s = {__builtin_amdgcn_readfirstlane(ra.x), __builtin_amdgcn_readfirstlane(ra.y),
+                            __builtin_amdgcn_readfirstlane(ra.z), __builtin_amdgcn_readfirstlane(ra.w)};
+        const i32x4 rc_s = {__builtin_amdgcn_readfirstlane(rc.x), __builtin_amdgcn_readfirstlane(rc.y),
+                            __builtin_amdgcn_readfirstlane(rc.z), __builtin_amdgcn_readfirstlane(rc.w)};
+        const i32x4 rs_s = {__builtin_amdgcn_readfirstlane(rs.x), __builtin_amdgcn_readfirstlane(rs.y),
+                            __builtin_amdgcn_readfirstlane(rs.z), __builtin_amdgcn_readfirstlane(rs.w)};
+        typedef __attribute__((address_space(3))) uint32_t lds_u32;
+        // 8 rows (row0 % 8 == 0) of A stage st into the 128-row tile `tile`
+        // (row0 relative to the tile's first row r_base)
+        auto dma_a = [&](char *tile, int r_base, int row0, int st) {
+            const int soff = st < nk ? (int)((r_base + row0) * p.lda * 2) + st * (kBK * 2) : (int)0x80000000;
+            const int voff = ((row0 >> 3) & 1) ? dla.off[1] : dla.off[0];
+            bi_raw_buffer_load_lds(ra_s, (lds_u32 *)(tile + row0 * kRowBytes), 16, voff, soff, 0, 0);
+        };
+        // A rows 0..127 of stage st (group 1: rows 32 j .. 32 j + 31)
+        auto issue_a0 = [&](int st) {
             char *a0 = lds + (st % S::RA0) * kHalf;
-            char *a1 = lds + S::OffA1 + (st % S::RA1) * kHalf - 128 * kRowBytes;
-            const int r0 = 32 * j, r1 = 128 + 32 * j;
-            dma8<0>(ra, a0, dla, r0, st * kBK, p.K, rows_a, p.lda, live);
-            dma8<1>(ra, a0, dla, r0 + 8, st * kBK, p.K, rows_a, p.lda, live);
-            dma8<0>(ra, a0, dla, r0 + 16, st * kBK, p.K, rows_a, p.lda, live);
-            dma8<1>(ra, a0, dla, r0 + 24, st * kBK, p.K, rows_a, p.lda, live);
-            dma8<0>(ra, a1, dla, r1, st * kBK, p.K, rows_a, p.lda, live);
-            dma8<1>(ra, a1, dla, r1 + 8, st * kBK, p.K, rows_a, p.lda, live);
-            dma8<0>(ra, a1, dla, r1 + 16, st * kBK, p.K, rows_a, p.lda, live);
-            dma8<1>(ra, a1, dla, r1 + 24, st * kBK, p.K, rows_a, p.lda, live);
+            dma_a(a0, 0, 32 * j, st);
+            dma_a(a0, 0, 32 * j + 8, st);
+            dma_a(a0, 0, 32 * j + 16, st);
+            dma_a(a0, 0, 32 * j + 24, st);
+        };
+        // A rows 128..255 of stage st (group 0: rows 128 + 32 j .. + 31)
+        auto issue_a1 = [&](int st) {
+            char *a1 = lds + S::OffA1 + (st % S::RA1) * kHalf;
+            dma_a(a1, 128, 32 * j, st);
+            dma_a(a1, 128, 32 * j + 8, st);
+            dma_a(a1, 128, 32 * j + 16, st);
+            dma_a(a1, 128, 32 * j + 24, st);
+        };
+        // raw B of stage st (group 1: code rows 64 j .. 64 j + 63 in two
+        // instructions of 32 rows, their scale rows in one)
+        auto issue_raw = [&](int st) {
+            const bool live = st < nk;
             char *raw = lds + S::OffRaw + (st % S::RR) * S::RawStage;
-            i32x4 r;
-            r.x = __builtin_amdgcn_readfirstlane(rc.x);
-            r.y = __builtin_amdgcn_readfirstlane(rc.y);
-            r.z = __builtin_amdgcn_readfirstlane(rc.z);
-            r.w = __builtin_amdgcn_readfirstlane(rc.w);
-            const int vc0 = (live && code_off0 >= 0) ? code_off0 + st * 32 : (int)0x80000000;
-            const int vc1 = (live && code_off1 >= 0) ? code_off1 + st * 32 : (int)0x80000000;
-            bi_raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t *)(raw + 64 * j * 32), 16, vc0, 0,
-                                   0, 0);
-            bi_raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t *)(raw + (64 * j + 32) * 32), 16,
-                                   vc1, 0, 0, 0);
-            i32x4 q;
-            q.x = __builtin_amdgcn_readfirstlane(rs.x);
-            q.y = __builtin_amdgcn_readfirstlane(rs.y);
-            q.z = __builtin_amdgcn_readfirstlane(rs.z);
-            q.w = __builtin_amdgcn_readfirstlane(rs.w);
-            const int vs = (live && scale_off >= 0) ? scale_off + st * 4 : (int)0x80000000;
-            bi_raw_buffer_load_lds(q, (__attribute__((address_space(3))) uint32_t *)(raw + S::CodeBytes + 64 * j * 4),
-                                   4, vs, 0, 0, 0);
+            const int sc = live ? st * 32 : 0x40000000, ss = live ? st * 4 : 0x40000000;
+            bi_raw_buffer_load_lds(rc_s, (lds_u32 *)(raw + 64 * j * 32), 16, code_off0, sc, 0, 0);
+            bi_raw_buffer_load_lds(rc_s, (lds_u32 *)(raw + (64 * j + 32) * 32), 16, code_off1, sc, 0, 0);
+            bi_raw_buffer_load_lds(rs_s, (lds_u32 *)(raw + S::CodeBytes + 64 * j * 4), 4, scale_off, ss, 0, 0);
         };
 
         u32x4 fa[2][8], fb[2][4];
@@ -480,18 +500,14 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         // at ((ks * 4 + fn) * 64 + l) * 16
         const uint32_t d_lane = lds0 + S::OffDec + j * 8192 + lane * 16;
 
-#define BI_P4_READ_A(s)                                                                        \
+#define BI_P4_READ_A_KS(s, ks)                                                                 \
     do {                                                                                       \
         const uint32_t ab = a_lane + (g ? ((s) % S::RA1) : ((s) % S::RA0)) * kHalf;            \
-        const uint32_t a0 = ab + sw0, a1 = ab + sw1;                                           \
-        fa[0][0] = rd128<0 * 2048>(a0); fa[0][1] = rd128<1 * 2048>(a0);                      \
-        fa[0][2] = rd128<2 * 2048>(a0); fa[0][3] = rd128<3 * 2048>(a0);                      \
-        fa[0][4] = rd128<4 * 2048>(a0); fa[0][5] = rd128<5 * 2048>(a0);                      \
-        fa[0][6] = rd128<6 * 2048>(a0); fa[0][7] = rd128<7 * 2048>(a0);                      \
-        fa[1][0] = rd128<0 * 2048>(a1); fa[1][1] = rd128<1 * 2048>(a1);                      \
-        fa[1][2] = rd128<2 * 2048>(a1); fa[1][3] = rd128<3 * 2048>(a1);                      \
-        fa[1][4] = rd128<4 * 2048>(a1); fa[1][5] = rd128<5 * 2048>(a1);                      \
-        fa[1][6] = rd128<6 * 2048>(a1); fa[1][7] = rd128<7 * 2048>(a1);                      \
+        const uint32_t ak = ab + ((ks) ? sw1 : sw0);                                           \
+        fa[ks][0] = rd128<0 * 2048>(ak); fa[ks][1] = rd128<1 * 2048>(ak);                    \
+        fa[ks][2] = rd128<2 * 2048>(ak); fa[ks][3] = rd128<3 * 2048>(ak);                    \
+        fa[ks][4] = rd128<4 * 2048>(ak); fa[ks][5] = rd128<5 * 2048>(ak);                    \
+        fa[ks][6] = rd128<6 * 2048>(ak); fa[ks][7] = rd128<7 * 2048>(ak);                    \
     } while (0)
 #define BI_P4_SETTLE_A()                                                                       \
     do {                                                                                       \
@@ -507,50 +523,89 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         asm volatile("" : "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[0][2]), "+v"(fb[0][3])::"memory"); \
         asm volatile("" : "+v"(fb[1][0]), "+v"(fb[1][1]), "+v"(fb[1][2]), "+v"(fb[1][3])::"memory"); \
     } while (0)
-        // Group 0's memory phase for stage s: raw B first (its decode starts
-        // as soon as it lands), then A; decode; hand the fragments to group 1.
-        auto mem0 = [&](int s) {
-            const uint32_t cb0 = c_lane0 + (s % S::RR) * S::RawStage;
-            const uint32_t cb1 = c_lane1 + (s % S::RR) * S::RawStage;
+        // Raw K chunk CH of stage s for this lane: the code dword of its
+        // 8-element group in each of its four columns, and their scale
+        // dwords; and their decode into four fragments.
+        auto read_raw = [&](int s, uint32_t (&c)[4], uint32_t (&sv)[4], auto ch_tag) {
+            constexpr int CH = decltype(ch_tag)::value;
+            const uint32_t cb = (CH ? c_lane1 : c_lane0) + (s % S::RR) * S::RawStage;
             const uint32_t sb = s_lane + (s % S::RR) * S::RawStage;
-            uint32_t c0[4], c1[4], sv[4];
-            c0[0] = rd32<0>(cb0); c1[0] = rd32<0>(cb1);
-            c0[1] = rd32<512>(cb0); c1[1] = rd32<512>(cb1);
-            c0[2] = rd32<1024>(cb0); c1[2] = rd32<1024>(cb1);
-            c0[3] = rd32<1536>(cb0); c1[3] = rd32<1536>(cb1);
+            c[0] = rd32<0>(cb); c[1] = rd32<512>(cb); c[2] = rd32<1024>(cb); c[3] = rd32<1536>(cb);
             sv[0] = rd32<0>(sb); sv[1] = rd32<64>(sb); sv[2] = rd32<128>(sb); sv[3] = rd32<192>(sb);
-            BI_P4_READ_A(s);
-            // the 12 raw reads are the oldest of the 28 in flight
-            asm volatile("s_waitcnt lgkmcnt(15)"
-                         : "+v"(c0[0]), "+v"(c0[1]), "+v"(c0[2]), "+v"(c0[3]), "+v"(c1[0]), "+v"(c1[1]),
-                           "+v"(c1[2]), "+v"(c1[3]), "+v"(sv[0]), "+v"(sv[1]), "+v"(sv[2]), "+v"(sv[3])::"memory");
+        };
+        auto decode_chunk = [&](const uint32_t (&c)[4], const uint32_t (&sv)[4], u32x4 (&out)[4], auto ch_tag) {
+            constexpr int CH = decltype(ch_tag)::value;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const uint32_t sh = sv[fn] >> sshift;
-                const uint4 d0 = decode8(c0[fn], e4m3_value<0>(sh));
-                const uint4 d1 = decode8(c1[fn], e4m3_value<2>(sh));
-                fb[0][fn] = u32x4{d0.x, d0.y, d0.z, d0.w};
-                fb[1][fn] = u32x4{d1.x, d1.y, d1.z, d1.w};
+                const uint4 d = decode8(c[fn], e4m3_value<2 * CH>(sh));
+                out[fn] = u32x4{d.x, d.y, d.z, d.w};
             }
+        };
+        using Ch0 = std::integral_constant<int, 0>;
+        using Ch1 = std::integral_constant<int, 1>;
+        // Group 0's memory phase for stage s: raw chunk 0 and the decoded
+        // chunk 1; decode chunk 0 into registers and hand it to group 1; then
+        // A.  (A is read after the decode so that the decode's temporaries
+        // and the A fragments are never live together.)
+        auto mem0 = [&](int s) {
+            wait_vmcnt<S::LOADS0>();
+            uint32_t c[4], sv[4];
+            read_raw(s, c, sv, Ch0{});
+            fb[1][0] = rd128<4 * 1024>(d_lane); fb[1][1] = rd128<5 * 1024>(d_lane);
+            fb[1][2] = rd128<6 * 1024>(d_lane); fb[1][3] = rd128<7 * 1024>(d_lane);
+            BI_P4_READ_A_KS(s, 0);
+            // the 8 raw reads are the oldest of the 20 in flight
+            asm volatile("s_waitcnt lgkmcnt(12)"
+                         : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(sv[0]), "+v"(sv[1]),
+                           "+v"(sv[2]), "+v"(sv[3])::"memory");
+            decode_chunk(c, sv, fb[0], Ch0{});
             wr128<0 * 1024>(d_lane, fb[0][0]); wr128<1 * 1024>(d_lane, fb[0][1]);
             wr128<2 * 1024>(d_lane, fb[0][2]); wr128<3 * 1024>(d_lane, fb[0][3]);
-            wr128<4 * 1024>(d_lane, fb[1][0]); wr128<5 * 1024>(d_lane, fb[1][1]);
-            wr128<6 * 1024>(d_lane, fb[1][2]); wr128<7 * 1024>(d_lane, fb[1][3]);
+            BI_P4_READ_A_KS(s, 1);
+            issue_a1(s + 2);
             BI_P4_SETTLE_A();
             BI_P4_SETTLE_B();
         };
-        // Group 1's memory phase for stage s: A and the decoded B, then the
-        // loads of stage s + 2.
+        // Group 1's memory phase for stage s: wait for the loads of stage
+        // s + 1 (issued two memory phases ago); both decoded chunks of stage
+        // s and the raw chunk 1 of stage s + 1, decoded into the buffer; A;
+        // then, once its A reads are done (A stage s + 3 reuses their slot),
+        // the loads of step u.
         auto mem1 = [&](int s, int u) {
-            BI_P4_READ_A(s);
+            wait_vmcnt<S::LOADS1>();
+            uint32_t c[4], sv[4];
+            read_raw(s + 1, c, sv, Ch1{});
             fb[0][0] = rd128<0 * 1024>(d_lane); fb[0][1] = rd128<1 * 1024>(d_lane);
             fb[0][2] = rd128<2 * 1024>(d_lane); fb[0][3] = rd128<3 * 1024>(d_lane);
             fb[1][0] = rd128<4 * 1024>(d_lane); fb[1][1] = rd128<5 * 1024>(d_lane);
             fb[1][2] = rd128<6 * 1024>(d_lane); fb[1][3] = rd128<7 * 1024>(d_lane);
-            issue(u);
+            BI_P4_READ_A_KS(s, 0);
+            // the 8 raw reads are the oldest of the 24 in flight
+            asm volatile("s_waitcnt lgkmcnt(15)"
+                         : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(sv[0]), "+v"(sv[1]),
+                           "+v"(sv[2]), "+v"(sv[3])::"memory");
+            u32x4 nd[4];
+            decode_chunk(c, sv, nd, Ch1{});
+            wr128<4 * 1024>(d_lane, nd[0]); wr128<5 * 1024>(d_lane, nd[1]);
+            wr128<6 * 1024>(d_lane, nd[2]); wr128<7 * 1024>(d_lane, nd[3]);
+            BI_P4_READ_A_KS(s, 1);
             BI_P4_SETTLE_A();
             BI_P4_SETTLE_B();
-            wait_vmcnt<S::LOADS>();
+            issue_a0(u + 3);
+            issue_raw(u + 3);
+        };
+        // Group 1 alone, before the first step: chunk 1 of stage 0.
+        auto dec1_first = [&]() {
+            uint32_t c[4], sv[4];
+            read_raw(0, c, sv, Ch1{});
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(sv[0]), "+v"(sv[1]),
+                           "+v"(sv[2]), "+v"(sv[3])::"memory");
+            u32x4 nd[4];
+            decode_chunk(c, sv, nd, Ch1{});
+            wr128<4 * 1024>(d_lane, nd[0]); wr128<5 * 1024>(d_lane, nd[1]);
+            wr128<6 * 1024>(d_lane, nd[2]); wr128<7 * 1024>(d_lane, nd[3]);
         };
 #define BI_P4_COMPUTE()                                                                        \
     do {                                                                                       \
@@ -562,14 +617,22 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
                 acc[fm][fn], 0, 0, 0);                                                         \
     } while (0)
 
-        // Prologue: group 1 issues stages 0 and 1; everything lands; group 0
-        // reads and decodes stage 0 (handing it to group 1); group 1 reads
-        // stage 0 and issues stage 2.
+        // Prologue: group 1 issues stages 0..2; everything lands; group 1
+        // decodes chunk 1 of stage 0; group 0 reads stage 0 and decodes its
+        // chunk 0; group 1 reads stage 0, decodes chunk 1 of stage 1 and
+        // issues stage 3.
         if (g == 1) {
-            issue(-2);
-            issue(-1);
+#pragma unroll
+            for (int st = 0; st < 3; ++st) {
+                issue_a0(st);
+                issue_raw(st);
+            }
+            issue_a1(0);
+            issue_a1(1);
         }
         wait_vmcnt<0>();
+        lds_barrier();
+        if (g == 1) dec1_first();
         lds_barrier();
         if (g == 0) mem0(0);
         lds_barrier();
@@ -595,7 +658,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         if (g == 0) lds_barrier();
-#undef BI_P4_READ_A
+#undef BI_P4_READ_A_KS
 #undef BI_P4_SETTLE_A
 #undef BI_P4_SETTLE_B
 #undef BI_P4_COMPUTE
