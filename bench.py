@@ -73,7 +73,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--m", type=int, default=2048, help="tokens per step")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -321,12 +321,20 @@ def main():
                 fn()
         return g
 
-    def graph_us(fn, reps, replays=3):
+    def graph_us(fn, reps, replays=3, warm_ms=40.0):
         """Mean time of one call, from HIP events around `replays` replays of
-        a graph of `reps` calls (no host launch cost between the kernels)."""
+        a graph of `reps` calls (no host launch cost between the kernels).
+        The graph is first replayed, untimed, for at least `warm_ms`: the
+        GPU's clock settles over the first tens of milliseconds of a new
+        sustained load (a qkv call measured 106 us in the second replay and
+        85-90 us from the fifth on)."""
         g = capture(fn, reps)
-        g.replay()
-        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        n_w = 0
+        while n_w < 2 or (time.perf_counter() - t_w) * 1e3 < warm_ms:
+            g.replay()
+            torch.cuda.synchronize()
+            n_w += 1
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(replays):
