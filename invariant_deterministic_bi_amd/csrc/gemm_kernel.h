@@ -754,7 +754,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, char *lds, int m0, i
                 if (col + j < p.N) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
         }
     }
-    __syncthreads();  // the LDS tile is reused by the next tile's prologue
+    // the LDS is reused by the next tile's prologue: its reads are done
+    // (the global stores may still be in flight; a __syncthreads() would
+    // wait for them too)
+    lds_barrier();
 }
 
 template <int BM, int BN, int WGM, int WGN, int SA, int SB, int AMODE, int BMODE>

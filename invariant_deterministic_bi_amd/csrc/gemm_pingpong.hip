@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
         _Pragma("unroll") for (int fm = 0; fm < 8; ++fm)                                       \
         _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                      \
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                             \
-                __builtin_bit_cast(bf16x8, fa[ks][fm]), __builtin_bit_cast(bf16x8, fb[ks][fn]), \
+                __builtin_bit_cast(bf16x8, fb[ks][fn]), __builtin_bit_cast(bf16x8, fa[ks][fm]), \
                 acc[fm][fn], 0, 0, 0);                                                         \
     } while (0)
 
@@ -282,9 +282,16 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
 #undef BI_PP_SETTLE
 #undef BI_PP_COMPUTE
 
-        // Epilogue: every load has landed (the zero-filling ones included),
-        // then fp32 -> bf16 RNE into a padded LDS tile and 16-byte row chunks
-        // to global memory.
+        // Epilogue.  The MFMA takes the weight fragment first, so each
+        // accumulator block is transposed: lane l of block (fm, fn) holds
+        // output row 16 fm + (l & 15) of its group and the four consecutive
+        // columns 16 fn + 4 (l >> 4) .. + 3.  (Operand order changes no bit:
+        // each element is the same sum of the same exact products in the same
+        // K order.)  They are rounded (RNE) to four bf16 and written to a
+        // padded LDS tile as one 8-byte write -- with a 528-byte row stride
+        // the 32 lanes of a half-wavefront hit all 64 banks once -- then
+        // 16-byte row chunks go to global memory.  First every load has landed
+        // (the zero-filling ones included).
         wait_vmcnt<0>();
         lds_barrier();
         char *ct = lds;
@@ -292,13 +299,11 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
         for (int fm = 0; fm < 8; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int col = (BN / 4) * j + fn * 16 + (lane & 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 128 * g + fm * 16 + (lane >> 4) * 4 + i;
-                    *reinterpret_cast<uint16_t *>(ct + row * S::CStride + col * 2) =
-                        (uint16_t)f32_to_bf16_rne(acc[fm][fn][i]);
-                }
+                const int row = 128 * g + fm * 16 + (lane & 15);
+                const int col = (BN / 4) * j + fn * 16 + (lane >> 4) * 4;
+                const uint32_t e0 = f32_to_bf16_rne(acc[fm][fn][0]), e1 = f32_to_bf16_rne(acc[fm][fn][1]);
+                const uint32_t e2 = f32_to_bf16_rne(acc[fm][fn][2]), e3 = f32_to_bf16_rne(acc[fm][fn][3]);
+                *reinterpret_cast<uint2 *>(ct + row * S::CStride + col * 2) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
             }
         __syncthreads();
         constexpr int CPR = BN / 8;
@@ -317,7 +322,10 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_kernel(GemmArgs p) {
                     if (col + e < p.N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
             }
         }
-        __syncthreads();  // the LDS is reused by the next tile's prologue
+        // the LDS is reused by the next tile's prologue: its reads are done
+        // (the global stores may still be in flight; a __syncthreads() would
+        // wait for them too)
+        lds_barrier();
     }
 }
 
@@ -613,7 +621,7 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         _Pragma("unroll") for (int fm = 0; fm < 8; ++fm)                                       \
         _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                      \
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                             \
-                __builtin_bit_cast(bf16x8, fa[ks][fm]), __builtin_bit_cast(bf16x8, fb[ks][fn]), \
+                __builtin_bit_cast(bf16x8, fb[ks][fn]), __builtin_bit_cast(bf16x8, fa[ks][fm]), \
                 acc[fm][fn], 0, 0, 0);                                                         \
     } while (0)
 
@@ -664,7 +672,11 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
 #undef BI_P4_COMPUTE
 
         // Epilogue: every load has landed; fp32 x alpha -> bf16 RNE into a
-        // padded LDS tile, then 16-byte row chunks to global memory.
+        // padded LDS tile, then 16-byte row chunks to global memory.  The
+        // accumulator blocks are transposed, as in the bf16 kernel (the MFMA
+        // takes the weight fragment first): lane l of block (fm, fn) holds
+        // row 16 fm + (l & 15) of its group and the four consecutive columns
+        // 16 fn + 4 (l >> 4) .. + 3, written as one 8-byte LDS store.
         wait_vmcnt<0>();
         lds_barrier();
         char *ct = lds;
@@ -672,13 +684,13 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
         for (int fm = 0; fm < 8; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int col = 64 * j + fn * 16 + (lane & 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 128 * g + fm * 16 + (lane >> 4) * 4 + i;
-                    *reinterpret_cast<uint16_t *>(ct + row * S::CStride + col * 2) =
-                        (uint16_t)f32_to_bf16_rne(acc[fm][fn][i] * p.alpha);
-                }
+                const int row = 128 * g + fm * 16 + (lane & 15);
+                const int col = 64 * j + fn * 16 + (lane >> 4) * 4;
+                const uint32_t e0 = f32_to_bf16_rne(acc[fm][fn][0] * p.alpha);
+                const uint32_t e1 = f32_to_bf16_rne(acc[fm][fn][1] * p.alpha);
+                const uint32_t e2 = f32_to_bf16_rne(acc[fm][fn][2] * p.alpha);
+                const uint32_t e3 = f32_to_bf16_rne(acc[fm][fn][3] * p.alpha);
+                *reinterpret_cast<uint2 *>(ct + row * S::CStride + col * 2) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
             }
         __syncthreads();
         constexpr int CPR = BN / 8;
@@ -697,7 +709,10 @@ __global__ __launch_bounds__(kNT, 1) void pingpong_nvfp4_kernel(GemmArgs p) {
                     if (col + e < p.N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
             }
         }
-        __syncthreads();  // the LDS is reused by the next tile's prologue
+        // the LDS is reused by the next tile's prologue: its reads are done
+        // (the global stores may still be in flight; a __syncthreads() would
+        // wait for them too)
+        lds_barrier();
     }
 }
 
