@@ -419,7 +419,8 @@ typedef enum bi_kernel_kind {
     BI_KERNEL_STREAM_A_LDS = 2,    /* weight streamed into registers in column items, A staged in LDS */
     BI_KERNEL_STREAM_REG = 3,      /* weight and A fragments streamed into registers, column items */
     BI_KERNEL_STREAM_RING = 4,     /* weight streamed through a per-wavefront LDS ring, column items */
-    BI_KERNEL_BMM_STREAM = 5       /* BMM: a 128-column B block kept in LDS, A streamed in 64-row tiles */
+    BI_KERNEL_BMM_STREAM = 5,      /* BMM: a 128-column B block kept in LDS, A streamed in 64-row tiles */
+    BI_KERNEL_STREAM_A_CHUNKS = 6  /* weight streamed into registers in column items, A in LDS in K chunks */
 } bi_kernel_kind;
 
 /*

@@ -48,7 +48,8 @@ class BiRegime(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-KERNEL_KINDS = ("tiled", "tiled_pingpong", "stream_a_lds", "stream_reg", "stream_ring", "bmm_stream")
+KERNEL_KINDS = ("tiled", "tiled_pingpong", "stream_a_lds", "stream_reg", "stream_ring", "bmm_stream",
+                "stream_a_chunks")
 
 
 class BiLaunchOpts(ctypes.Structure):

@@ -253,6 +253,19 @@ struct Regime {
 // bf16 and NVFP4 weights alike).  In hundredths of a microsecond:
 int64_t stream_round_cost(int rb) { return 600 + 368 * rb; }
 
+// The chunked-A kernel (A staged in LDS 2048 / rb columns at a time, one
+// 16-column item per wavefront, up to eight per compute unit): with w items
+// per compute unit (w > 1) a call costs about a + b w microseconds per 4096
+// of K (MI355X, N = 6144 ... 24576, M = 17 ... 64).  A bf16 weight is bound
+// by the stream (b large); an NVFP4 one by its decode, which two items share
+// a SIMD for only above four per compute unit.  In hundredths of a
+// microsecond:
+int64_t achunk_cost(bool fp4, int rb, int64_t items, int cus) {
+    const int64_t w100 = items * 100 / cus;  // items per compute unit, x 100
+    if (fp4) return (rb == 2 ? 1350 : 1900) + (rb == 2 ? 125 : 130) * w100 / 100;
+    return (rb == 2 ? 1220 : 1660) + (rb == 2 ? 470 : 430) * w100 / 100;
+}
+
 Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch, bool grouped, int cus,
                 int64_t M) {
     const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
@@ -288,14 +301,30 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
     const int v = model_variant(a_mode, b_mode, N, cus, M, &est);
     // bf16 A with 16 < M <= 128 and a bf16 weight, or 16 < M <= 64 and a raw
     // NVFP4 one (K % 128 == 0): the register-streaming kernel with two, four
-    // or eight 16-row blocks (one weight fragment feeds each block's chain)
-    // when it is estimated faster than that tile
+    // or eight 16-row blocks (one weight fragment feeds each block's chain);
+    // with M <= 64 and more 16-column items than compute units, also the
+    // kernel that keeps A in LDS in K chunks.  The one with the least
+    // estimate runs if it is below the tile's.
+    const int64_t items = ceil_div(N, 16);
+    int64_t best = 100 * est;
+    Regime pick{BI_KERNEL_TILED, 0, 0, 0, 0, -1};
     if (a_mode == bi::OPND_BF16_ROWS &&
         ((b_mode == bi::OPND_BF16_ROWS && M <= 128) || (fp4 && K % 128 == 0 && M <= 64))) {
         const int rb = M > 64 ? 8 : M > 32 ? 4 : 2;
-        if (ceil_div(ceil_div(N, 16), cus) * stream_round_cost(rb) < 100 * est)
-            return {BI_KERNEL_STREAM_REG, rb, 0, 0, 16, -1};
+        const int64_t e = ceil_div(items, cus) * stream_round_cost(rb);
+        if (e < best) {
+            best = e;
+            pick = {BI_KERNEL_STREAM_REG, rb, 0, 0, 16, -1};
+        }
+        if (M <= 64 && items > cus && bi::direct_achunk_ok(static_cast<int>(M), static_cast<int>(K), rb, fp4)) {
+            const int64_t ec = achunk_cost(fp4, rb, items, cus);
+            if (ec < best) {
+                best = ec;
+                pick = {BI_KERNEL_STREAM_A_CHUNKS, rb, 0, 0, 16, -1};
+            }
+        }
     }
+    if (pick.kind != BI_KERNEL_TILED) return pick;
     const bi::TileShape &t = bi::kTileShapes[v];
     const bool pp = pingpong_ok(v, a_mode, b_mode, batch, grouped);
     return {pp ? BI_KERNEL_TILED_PINGPONG : BI_KERNEL_TILED, t.bm / 16, 0, 0, t.bn, v};
@@ -368,6 +397,15 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
             int waves = items <= 3 * cus ? items : fp4 ? (items < 8 * cus ? items : 8 * cus) : cus;
             if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
             e = bi::launch_direct_alds(in, fp4, afp4, r.cols, waves, cus, depth, s);
+            break;
+        }
+        case BI_KERNEL_STREAM_A_CHUNKS: {
+            // one wavefront per 16-column item, up to eight per compute unit
+            const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
+            const int items = static_cast<int>((in.N + 15) / 16);
+            int waves = items < 8 * cus ? items : 8 * cus;
+            if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
+            e = bi::launch_direct_achunk(in, fp4, r.rb, waves, cus, depth, s);
             break;
         }
         case BI_KERNEL_STREAM_REG: {

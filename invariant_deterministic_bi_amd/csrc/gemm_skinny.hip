@@ -803,6 +803,238 @@ hipError_t launch_alds(const GemmArgs &a, int d, int grid, int nwv, hipStream_t 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Direct path for 16 < M <= 64 with A staged in LDS in K chunks.  A of up to
+// 16 RB rows no longer fits the LDS whole, so it goes in chunks of
+// CK = 2048 / RB columns (64 KB), two buffers: chunk c + 1 is copied by LDS
+// DMA while chunk c is read.  Each wavefront streams one 16-column item of
+// the weight through its register window (as the A-in-LDS kernel does) over
+// the whole K range, and each weight fragment feeds the RB row blocks'
+// chains; the wavefronts of a workgroup share the A chunks.  One barrier per
+// chunk.  The per-element chain is the tiled kernel's: one MFMA per 32-wide
+// K chunk, ascending from +0.  FP4: NVFP4 weight (four-chunk units, K %
+// 128 == 0); else bf16 (chunk pairs).  D: units in flight, a divisor of the
+// units per A chunk.  Needs K % CK == 0 (checked by the host).
+// ---------------------------------------------------------------------------
+// Waits until at most N LDS reads are outstanding; the NF fragment
+// registers are operands of the wait, so none of them is used before it.
+template <int N, int NF>
+__device__ __forceinline__ void wait_frags(i32x4 *a) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt field is 4 bits");
+    if constexpr (NF == 4)
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(N) : "memory");
+    else if constexpr (NF == 8)
+        asm volatile("s_waitcnt lgkmcnt(%8)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+                     : "n"(N)
+                     : "memory");
+    else {
+        static_assert(NF == 16, "4, 8 or 16 fragments");
+        asm volatile("s_waitcnt lgkmcnt(%16)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]),
+                       "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]),
+                       "+v"(a[15])
+                     : "n"(N)
+                     : "memory");
+    }
+}
+
+template <int RB>
+struct AChunk {
+    static constexpr int CK = 2048 / RB;          // K columns per staged chunk
+    static constexpr int ROWS = 16 * RB;
+    static constexpr int AS = CK * 2 + 16;        // padded LDS row stride (bank spread)
+    static constexpr int BUF = ROWS * AS;
+    static constexpr int BPR = CK * 2 / 1024;     // 1 KB DMA blocks per row and chunk
+    static_assert(RB == 2 || RB == 4, "two or four row blocks");
+    static_assert(2 * BUF <= 160 * 1024, "two chunk buffers fit the LDS");
+};
+
+template <bool FP4, int RB, int D>
+__global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
+    using AC = AChunk<RB>;
+    constexpr int U = FP4 ? 4 : 2;                 // 32-wide chunks per unit
+    constexpr int UPC = AC::CK / (32 * U);         // units per A chunk
+    constexpr int LPU = 2;                         // weight loads per unit
+    static_assert(UPC % D == 0, "the window steps within a chunk");
+    static_assert(FP4 || D % 2 == 0, "bf16: units alternate between two fragment sets");
+    static_assert(UPC * LPU < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[2 * AC::BUF];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nwv = (int)(blockDim.x >> 6);
+    const int r = lane & 15, sub = lane >> 4;
+    const int items = (p.N + 15) >> 4;
+    const int nch = p.K / AC::CK;
+    const int nu = nch * UPC;                      // units per item
+    const i32x4 ra = make_rsrc(p.A, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
+    const int cpr = p.K >> 1, spr = p.K >> 4;
+    const int sshift = 8 * (sub >> 1);
+    uint16_t *Y = static_cast<uint16_t *>(p.Y);
+    const uint32_t lds0 = lds_addr(lds);
+
+    // A chunk c into buffer c & 1: rows 0..M-1, 1 KB blocks shared out over
+    // the wavefronts (rows beyond M are never read: fragment reads clamp)
+    auto stage = [&](int c) {
+        char *buf = lds + (c & 1) * AC::BUF;
+        for (int b = w; b < p.M * AC::BPR; b += nwv) {
+            const int row = b / AC::BPR, part = b - row * AC::BPR;
+            const int k = c * AC::CK + part * 512 + lane * 8;
+            bi_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) uint32_t *)(buf + row * AC::AS + part * 1024),
+                                   16, (int)(row * p.lda * 2) + k * 2, 0, 0, 0);
+        }
+    };
+
+    for (int round = 0; (int)blockIdx.x * nwv + round * (int)gridDim.x * nwv < items; ++round) {
+        const int item = (int)blockIdx.x * nwv + w + round * (int)gridDim.x * nwv;
+        const int n0 = item * 16;
+        const int rows_b = item < items ? min(16, p.N - n0) : 0;
+        const int64_t b0 = rows_b > 0 ? n0 : 0;
+        i32x4 rb, rs;
+        int w_lane, s_lane = kMark;
+        if constexpr (FP4) {
+            rb = make_rsrc(static_cast<const uint8_t *>(p.B) + b0 * cpr, rows_b > 0 ? (uint32_t)(rows_b * cpr) : 0u);
+            rs = make_rsrc(static_cast<const uint8_t *>(p.B_scales) + b0 * spr,
+                           rows_b > 0 ? (uint32_t)(rows_b * spr) : 0u);
+            w_lane = r < rows_b ? r * cpr + 16 * sub : kMark;
+            s_lane = r < rows_b ? r * spr : kMark;
+        } else {
+            rb = make_rsrc(static_cast<const uint16_t *>(p.B) + b0 * p.ldb,
+                           rows_b > 0 ? (uint32_t)(((int64_t)(rows_b - 1) * p.ldb + p.K) * 2) : 0u);
+            rs = rb;
+            w_lane = r < rows_b ? (int)(r * p.ldb * 2) + 16 * sub : kMark;
+        }
+        // unit u of this wavefront's item into (x0, x1); units past the last
+        // read zeros (a wavefront past the last item reads only zeros)
+        auto issue = [&](int u, i32x4 &x0, i32x4 &x1) {
+            const bool live = u < nu;
+            if constexpr (FP4) {
+                x0 = bi_raw_buffer_load_b128(rb, live ? w_lane + 64 * u : kMark, 0, 0);
+                const i32x2 sv = bi_raw_buffer_load_b64(rs, live ? s_lane + 8 * u : kMark, 0, 0);
+                x1 = i32x4{sv.x, sv.y, 0, 0};
+            } else {
+                x0 = bi_raw_buffer_load_b128(rb, live ? w_lane + 128 * u : kMark, 0, 0);
+                x1 = bi_raw_buffer_load_b128(rb, live ? w_lane + 128 * u + 64 : kMark, 0, 0);
+            }
+        };
+
+        // chunk 0, then the weight window; chunk 0's copies are older than
+        // the window's D * LPU loads
+        stage(0);
+        asm volatile("" ::: "memory");
+        i32x4 ws0[D], ws1[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(d, ws0[d], ws1[d]);
+        wait_vmcnt<D * LPU>();
+        lds_barrier();
+
+        f32x4 acc[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // this lane's A row in each block, clamped to a staged row
+        uint32_t a_row[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) a_row[b] = (uint32_t)(min(16 * b + r, p.M - 1) * AC::AS) + 16 * sub;
+        for (int c = 0; c < nch; ++c) {
+            // the next chunk's copies go out before this chunk's weight loads,
+            // so waiting for all but those UPC * LPU loads covers them
+            if (c + 1 < nch) stage(c + 1);
+            asm volatile("" ::: "memory");
+            const uint32_t cb = lds0 + (uint32_t)((c & 1) * AC::BUF);
+            // bf16: the A fragments of unit 0 (set 0); each unit then reads the
+            // next unit's into the other set before its own MFMAs
+            i32x4 af[2][RB * U];
+            if constexpr (!FP4) {
+#pragma unroll
+                for (int b = 0; b < RB; ++b)
+#pragma unroll
+                    for (int j = 0; j < U; ++j) af[0][b * U + j] = rd_a(cb + a_row[b] + 64 * j);
+            }
+            for (int ub = 0; ub < UPC; ub += D) {
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    const int ul = ub + d;                 // unit within the chunk
+                    constexpr int NF = RB * U;
+                    i32x4 wv[U];
+                    i32x4 *a = af[FP4 ? 0 : (d & 1)];
+                    if constexpr (FP4) {
+                        // fragment reads first: the decode covers their latency
+#pragma unroll
+                        for (int b = 0; b < RB; ++b)
+#pragma unroll
+                            for (int j = 0; j < U; ++j) a[b * U + j] = rd_a(cb + a_row[b] + 64 * (ul * U + j));
+                        uint32_t y[4] = {(uint32_t)ws0[d].x, (uint32_t)ws0[d].y, (uint32_t)ws0[d].z, (uint32_t)ws0[d].w};
+                        transpose4(y[0], y[1], y[2], y[3]);
+                        const uint32_t s01 = (uint32_t)ws1[d].x >> sshift, s23 = (uint32_t)ws1[d].y >> sshift;
+                        const float sc[4] = {e4m3_value<0>(s01), e4m3_value<2>(s01), e4m3_value<0>(s23),
+                                             e4m3_value<2>(s23)};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint4 q = decode8(y[j], sc[j]);
+                            wv[j] = i32x4{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+                        }
+                        wait_frags<0, NF>(a);
+                    } else {
+                        wv[0] = ws0[d];
+                        wv[1] = ws1[d];
+                        if (ul + 1 < UPC) {
+                            i32x4 *an = af[(d + 1) & 1];
+#pragma unroll
+                            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                                for (int j = 0; j < U; ++j)
+                                    an[b * U + j] = rd_a(cb + a_row[b] + 64 * ((ul + 1) * U + j));
+                            wait_frags<NF, NF>(a);
+                        } else {
+                            wait_frags<0, NF>(a);
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < U; ++j)
+#pragma unroll
+                        for (int b = 0; b < RB; ++b)
+                            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[b * U + j]),
+                                                                             __builtin_bit_cast(bf16x8, wv[j]), acc[b],
+                                                                             0, 0, 0);
+                    issue(c * UPC + ul + D, ws0[d], ws1[d]);
+                }
+            }
+            // chunk c + 1 has landed (its copies are older than this chunk's
+            // UPC * LPU weight loads), and every wavefront is done with chunk
+            // c, whose buffer chunk c + 2 reuses
+            wait_vmcnt<UPC * LPU>();
+            lds_barrier();
+        }
+        const int col = n0 + r;
+        if (r < rows_b) {
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * b + 4 * sub + i;
+                    float v = acc[b][i];
+                    if constexpr (FP4) v = v * p.alpha;
+                    if (row < p.M) Y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+                }
+        }
+        wait_vmcnt<0>();  // the window's trailing zero loads land before the next round
+        lds_barrier();
+    }
+}
+
+template <bool FP4, int RB>
+hipError_t launch_achunk_rb(const GemmArgs &a, int d, int grid, int nwv, hipStream_t s) {
+    constexpr int UPC = AChunk<RB>::CK / (32 * (FP4 ? 4 : 2));
+    const dim3 b(64 * nwv);
+    switch (d) {
+        case 8: if constexpr (UPC % 8 == 0) { hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 8>), dim3(grid), b, 0, s, a); break; } return hipErrorInvalidValue;
+        case 4: if constexpr (UPC % 4 == 0) { hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 4>), dim3(grid), b, 0, s, a); break; } return hipErrorInvalidValue;
+        case 2: hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 2>), dim3(grid), b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace direct
 
 // A power of two <= dmax dividing `units`: `depth` if given, else `dflt`.
@@ -844,6 +1076,37 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, bool afp4, int nb, in
     if (fp4) return direct::launch_alds<true, 16>(a, d, grid, nwv, s);
     return nb == 8 ? direct::launch_alds<false, 8>(a, d, grid, nwv, s)
                    : direct::launch_alds<false, 16>(a, d, grid, nwv, s);
+}
+
+// K-chunked A in LDS (16 < M <= 64): rb = 2 or 4 row blocks, K % (2048 / rb)
+// == 0 (and K % 128 == 0 for an NVFP4 weight); `waves` streaming wavefronts,
+// one 16-column item each per round.
+bool direct_achunk_ok(int M, int K, int rb, bool fp4) {
+    if (rb != 2 && rb != 4) return false;
+    const int ck = 2048 / rb;
+    return M > 16 * (rb / 2) && M <= 16 * rb && K % ck == 0 && (!fp4 || K % 128 == 0);
+}
+
+hipError_t launch_direct_achunk(const GemmArgs &a, bool fp4, int rb, int waves, int cus, int depth, hipStream_t s) {
+    if (waves < 1 || cus < 1 || a.M < 1 || a.M > 16 * rb || (rb != 2 && rb != 4) || a.K % (2048 / rb) != 0 ||
+        (fp4 && a.K % 128 != 0))
+        return hipErrorInvalidValue;
+    // one workgroup per compute unit (two 64 KB chunk buffers), up to eight
+    // wavefronts
+    int nwv = (waves + cus - 1) / cus;
+    nwv = nwv < 1 ? 1 : nwv > 8 ? 8 : nwv;
+    const int grid = (waves + nwv - 1) / nwv;
+    const int upc = (2048 / rb) / (32 * (fp4 ? 4 : 2));
+    // depth 1 is taken as 2: two units are the least the window holds
+    int d = depth > 1 ? depth : depth == 1 ? 2 : fp4 ? 4 : 8;
+    d = d > 8 ? 8 : d;
+    while (d & (d - 1)) d &= d - 1;
+    while (d > 2 && upc % d) d >>= 1;
+    if (d < 2 || upc % d) return hipErrorInvalidValue;
+    if (fp4) return rb == 2 ? direct::launch_achunk_rb<true, 2>(a, d, grid, nwv, s)
+                            : direct::launch_achunk_rb<true, 4>(a, d, grid, nwv, s);
+    return rb == 2 ? direct::launch_achunk_rb<false, 2>(a, d, grid, nwv, s)
+                   : direct::launch_achunk_rb<false, 4>(a, d, grid, nwv, s);
 }
 
 hipError_t launch_direct_nvfp4(const GemmArgs &a, int rb, int ap, int grid, int depth, hipStream_t s) {

@@ -347,20 +347,21 @@ def _shape_at(op, N, K, M, a_fmt=0, cus=256):
 
 
 def test_plan_regimes_cost_model_choices():
-    """The tiled kernel's shape at each M of the Qwen3-8B-shaped linears on
-    a 256-CU device is the one the MI355X sweep of every compiled shape
-    found fastest (or within a few percent of it)."""
+    """The kernel at each M of the Qwen3-8B-shaped linears on a 256-CU
+    device (the tiled kernel's shape, or a streaming kernel) is the one the
+    MI355X sweeps of every compiled shape and of the streaming kernels found
+    fastest (or within a few percent of it)."""
     G, F = B.BI_OP_GEMM, B.BI_OP_NVFP4_GEMM
     want = {
-        (G, 6144, 4096): {32: (64, 64), 128: (64, 64), 256: (128, 64), 512: (128, 128), 1024: (256, 128),
+        (G, 6144, 4096): {32: "stream_a_chunks", 64: "stream_a_chunks", 128: (64, 64), 256: (128, 64), 512: (128, 128), 1024: (256, 128),
                           2048: (256, 192), 4096: (256, 192), 8192: (256, 256)},
         (G, 4096, 4096): {32: "stream_reg", 64: "stream_reg", 128: (64, 64), 256: (64, 64), 512: (128, 64),
                           1024: (128, 128), 2048: (256, 128), 4096: (256, 256), 8192: (256, 256)},
-        (G, 24576, 4096): {32: (128, 128), 128: (128, 128), 256: (256, 128), 512: (256, 192),
+        (G, 24576, 4096): {32: "stream_a_chunks", 64: "stream_a_chunks", 128: (128, 128), 256: (256, 128), 512: (256, 192),
                            1024: (256, 192), 2048: (256, 256), 4096: (256, 256)},
         (G, 4096, 12288): {32: "stream_reg", 64: "stream_reg", 128: (64, 64), 256: (64, 64), 512: (128, 64),
                            1024: (128, 128), 2048: (256, 128), 4096: (256, 256), 8192: (256, 256)},
-        (F, 24576, 4096): {32: (128, 128), 64: (128, 128), 128: (128, 128), 256: (256, 128),
+        (F, 24576, 4096): {32: "stream_a_chunks", 64: "stream_a_chunks", 128: (128, 128), 256: (256, 128),
                            1024: (256, 192), 2048: (256, 256), 4096: (256, 256)},
     }
     for (op, N, K), ms in want.items():

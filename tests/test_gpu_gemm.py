@@ -240,6 +240,56 @@ def test_pingpong_schedule_matches_classic_schedule(pp, classic, bn):
             assert_within_tol(host(gemm(Ad, Wd, tile_variant=pp))[[0, 511, 2047]], ref, s, "pingpong")
 
 
+@pytest.mark.parametrize("N,K,fp4", [(6144, 4096, False), (8200, 2048, False), (24576, 4096, True),
+                                     (6144, 4096, True), (8200, 2048, True)])
+def test_chunked_a_path_matches_tiled_kernel(N, K, fp4):
+    """16 < M <= 64 with A staged in LDS in K chunks (more 16-column items
+    than compute units; bf16 and NVFP4 weights, ragged N): every M in {17,
+    20, 32, 33, 48, 63, 64} bitwise equal to the forced tiled kernel and to
+    the M = 64 batch, under wavefront caps {1, 7, #CU} and pipeline depths
+    {1, 2, 4, 8}; parity with the oracle."""
+    Mmax = 64
+    A = inputs.randn_bf16((Mmax, K), tag=(90, N, K))
+    if fp4:
+        x = inputs.rng(12345, 91, N, K).standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
+        g = inputs.nvfp4_global_scale(x)
+        W, Ws = inputs.nvfp4_quantize(x, g)
+        alpha = float(np.float32(1.0) / g)
+        Ad, Wd, Wsd = dev(A), dev(W), dev(Ws)
+
+        def run(M, **kw):
+            return host(B.bi_nvfp4_gemm(Ad[:M], Wd, Wsd, alpha, **kw))
+        tiled = 13
+    else:
+        W = inputs.randn_bf16((N, K), 0.02, tag=(92, N, K))
+        Ad, Wd = dev(A), dev(W)
+
+        def run(M, **kw):
+            return host(gemm(Ad[:M], Wd, **kw))
+        tiled = 1
+    plan = B.plan_regimes(B.BI_OP_NVFP4_GEMM if fp4 else B.BI_OP_GEMM, N, K)
+    chunked = [r for r in plan if r["kind"] == "stream_a_chunks"]
+    assert chunked and chunked[0]["m_min"] == 17, plan
+    note(f"chunked A N={N} K={K} fp4={fp4} M=64")
+    yfull = run(Mmax)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for M in (17, 20, 32, 33, 48, 63, 64):
+        note(f"chunked A N={N} K={K} fp4={fp4} M={M}")
+        y = run(M)
+        assert np.array_equal(y, yfull[:M]), f"M={M} vs batch"
+        assert np.array_equal(y, run(M, tile_variant=tiled)), f"M={M} vs tiled"
+        for mw in (1, 7, cus):
+            assert np.array_equal(run(M, max_workgroups=mw), y), (M, mw)
+        for depth in (1, 2, 4, 8):
+            assert np.array_equal(run(M, pipeline_depth=depth), y), (M, depth)
+    rows = [0, 17, 63]
+    if fp4:
+        ref, s = oracle.nvfp4_gemm(A[rows], None, W, Ws, alpha, K)
+    else:
+        ref, s = oracle.gemm(A[rows], W)
+    assert_within_tol(yfull[rows], ref, s, f"chunked A N={N} K={K}")
+
+
 @pytest.mark.parametrize("N,K", [(200, 544), (4100, 4128), (256, 96), (6144, 4096), (8200, 512)])
 def test_small_m_path_matches_tiled_kernel(N, K):
     """M <= 64 runs the direct kernels (8- or 16-column items streamed into
