@@ -265,6 +265,12 @@ int64_t achunk_cost(bool fp4, int rb, int64_t items, int cus) {
     if (fp4) return (rb == 2 ? 1350 : 1900) + (rb == 2 ? 125 : 130) * w100 / 100;
     return (rb == 2 ? 1220 : 1660) + (rb == 2 ? 470 : 430) * w100 / 100;
 }
+// With an NVFP4 A, whose rows each workgroup (of at least four wavefronts)
+// decodes into LDS as well (N = 1000 ... 24576, K = 4096 and 12288):
+int64_t achunk_cost_w4a4(int rb, int64_t items, int cus) {
+    const int64_t w100 = items * 100 / cus;
+    return rb == 2 ? 1600 + 110 * w100 / 100 : 2350 + 150 * w100 / 100;
+}
 
 Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch, bool grouped, int cus,
                 int64_t M) {
@@ -318,6 +324,19 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
         }
         if (M <= 64 && items > cus && bi::direct_achunk_ok(static_cast<int>(M), static_cast<int>(K), rb, fp4)) {
             const int64_t ec = achunk_cost(fp4, rb, items, cus);
+            if (ec < best) {
+                best = ec;
+                pick = {BI_KERNEL_STREAM_A_CHUNKS, rb, 0, 0, 16, -1};
+            }
+        }
+    }
+    // NVFP4 A and weight, 16 < M <= 64 (K % 128 == 0): the chunked-A kernel
+    // with A's rows decoded into LDS chunk by chunk (at any N: there is no
+    // register-streaming kernel for an NVFP4 A)
+    if (a_mode == bi::OPND_NVFP4_ROWS && M <= 64 && K % 128 == 0) {
+        const int rb = M > 32 ? 4 : 2;
+        if (bi::direct_achunk_ok(static_cast<int>(M), static_cast<int>(K), rb, true)) {
+            const int64_t ec = achunk_cost_w4a4(rb, items, cus);
             if (ec < best) {
                 best = ec;
                 pick = {BI_KERNEL_STREAM_A_CHUNKS, rb, 0, 0, 16, -1};
@@ -401,11 +420,12 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         }
         case BI_KERNEL_STREAM_A_CHUNKS: {
             // one wavefront per 16-column item, up to eight per compute unit
-            const bool fp4 = b_mode == bi::OPND_NVFP4_RAW;
+            const bool afp4 = a_mode == bi::OPND_NVFP4_ROWS;
+            const bool fp4 = afp4 || b_mode == bi::OPND_NVFP4_RAW;
             const int items = static_cast<int>((in.N + 15) / 16);
             int waves = items < 8 * cus ? items : 8 * cus;
             if (opts && opts->max_workgroups > 0 && opts->max_workgroups < waves) waves = opts->max_workgroups;
-            e = bi::launch_direct_achunk(in, fp4, r.rb, waves, cus, depth, s);
+            e = bi::launch_direct_achunk(in, fp4, afp4, r.rb, waves, cus, depth, s);
             break;
         }
         case BI_KERNEL_STREAM_REG: {

@@ -122,9 +122,11 @@ hipError_t launch_direct_nvfp4(const GemmArgs &args, int rb, int ap, int grid, i
 // afp4 (with fp4): A is NVFP4 rows (lda % 32 == 0), decoded into LDS.
 bool direct_alds_ok(int M, int K, bool fp4);
 // Direct path with A staged in LDS in K chunks (16 < M <= 64): rb = 2 or 4
-// row blocks; bf16 A, bf16 or raw NVFP4 weight; `waves` wavefronts.
+// row blocks; bf16 A, bf16 or raw NVFP4 weight; `waves` wavefronts.  afp4
+// (with fp4): A is NVFP4 rows (lda % 32 == 0), decoded into LDS chunk by
+// chunk.
 bool direct_achunk_ok(int M, int K, int rb, bool fp4);
-hipError_t launch_direct_achunk(const GemmArgs &args, bool fp4, int rb, int waves, int cus, int depth,
+hipError_t launch_direct_achunk(const GemmArgs &args, bool fp4, bool afp4, int rb, int waves, int cus, int depth,
                                 hipStream_t stream);
 hipError_t launch_direct_alds(const GemmArgs &args, bool fp4, bool afp4, int nb, int waves, int cus, int depth,
                               hipStream_t stream);

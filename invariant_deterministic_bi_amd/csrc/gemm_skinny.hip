@@ -815,6 +815,11 @@ hipError_t launch_alds(const GemmArgs &a, int d, int grid, int nwv, hipStream_t 
 // K chunk, ascending from +0.  FP4: NVFP4 weight (four-chunk units, K %
 // 128 == 0); else bf16 (chunk pairs).  D: units in flight, a divisor of the
 // units per A chunk.  Needs K % CK == 0 (checked by the host).
+// AFP4 (with FP4): A is NVFP4 rows (codes [M, K/2], scales [M, K/16], lda
+// in elements, lda % 32 == 0), decoded exactly to bf16 as each chunk is
+// staged -- the values the tiled kernel's NVFP4 A staging stores.  Chunk
+// c + 1's first loads go out at the start of chunk c and are decoded and
+// written at its end, before the barrier.
 // ---------------------------------------------------------------------------
 // Waits until at most N LDS reads are outstanding; the NF fragment
 // registers are operands of the wait, so none of them is used before it.
@@ -850,8 +855,9 @@ struct AChunk {
     static_assert(2 * BUF <= 160 * 1024, "two chunk buffers fit the LDS");
 };
 
-template <bool FP4, int RB, int D>
+template <bool FP4, int RB, int D, bool AFP4 = false>
 __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
+    static_assert(!AFP4 || FP4, "an NVFP4 A goes with an NVFP4 weight");
     using AC = AChunk<RB>;
     constexpr int U = FP4 ? 4 : 2;                 // 32-wide chunks per unit
     constexpr int UPC = AC::CK / (32 * U);         // units per A chunk
@@ -876,12 +882,53 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
     // A chunk c into buffer c & 1: rows 0..M-1, 1 KB blocks shared out over
     // the wavefronts (rows beyond M are never read: fragment reads clamp)
     auto stage = [&](int c) {
+        if constexpr (AFP4) return;
         char *buf = lds + (c & 1) * AC::BUF;
         for (int b = w; b < p.M * AC::BPR; b += nwv) {
             const int row = b / AC::BPR, part = b - row * AC::BPR;
             const int k = c * AC::CK + part * 512 + lane * 8;
             bi_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) uint32_t *)(buf + row * AC::AS + part * 1024),
                                    16, (int)(row * p.lda * 2) + k * 2, 0, 0, 0);
+        }
+    };
+    // NVFP4 A: chunk c in 32-element units (16 code bytes, two scale bytes),
+    // AG per thread per group; group g's loads, then its decode and writes
+    constexpr int AG = 4;
+    constexpr int UPR = AC::CK / 32;               // units per row and chunk
+    const int a4_units = AFP4 ? p.M * UPR : 0;
+    const int a4_groups = (a4_units + AG * (int)blockDim.x - 1) / (AG * (int)blockDim.x);
+    uint4 qa[AG];
+    uint32_t qs[AG];
+    auto a4_load = [&](int c, int g) {
+        if constexpr (AFP4) {
+            const uint8_t *pc = static_cast<const uint8_t *>(p.A);
+            const uint8_t *ps = static_cast<const uint8_t *>(p.A_scales);
+#pragma unroll
+            for (int i = 0; i < AG; ++i) {
+                const int q = (g * AG + i) * (int)blockDim.x + (int)threadIdx.x;
+                if (q < a4_units) {
+                    const int row = q / UPR, u = c * UPR + (q - row * UPR);
+                    qa[i] = *reinterpret_cast<const uint4 *>(pc + (int64_t)row * (p.lda >> 1) + u * 16);
+                    qs[i] = *reinterpret_cast<const uint16_t *>(ps + (int64_t)row * (p.lda >> 4) + u * 2);
+                }
+            }
+        }
+    };
+    auto a4_write = [&](int c, int g) {
+        if constexpr (AFP4) {
+#pragma unroll
+            for (int i = 0; i < AG; ++i) {
+                const int q = (g * AG + i) * (int)blockDim.x + (int)threadIdx.x;
+                if (q < a4_units) {
+                    const int row = q / UPR, u = q - row * UPR;
+                    const float s0 = e4m3_value(qs[i] & 0xFFu), s1 = e4m3_value(qs[i] >> 8);
+                    char *dst = lds + (c & 1) * AC::BUF + row * AC::AS + u * 64;
+                    lds_write_b128(dst, decode8(qa[i].x, s0));
+                    lds_write_b128(dst + 16, decode8(qa[i].y, s0));
+                    lds_write_b128(dst + 32, decode8(qa[i].z, s1));
+                    lds_write_b128(dst + 48, decode8(qa[i].w, s1));
+                }
+            }
         }
     };
 
@@ -921,6 +968,10 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
         // chunk 0, then the weight window; chunk 0's copies are older than
         // the window's D * LPU loads
         stage(0);
+        for (int g = 0; g < a4_groups; ++g) {
+            a4_load(0, g);
+            a4_write(0, g);
+        }
         asm volatile("" ::: "memory");
         i32x4 ws0[D], ws1[D];
 #pragma unroll
@@ -938,7 +989,10 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
         for (int c = 0; c < nch; ++c) {
             // the next chunk's copies go out before this chunk's weight loads,
             // so waiting for all but those UPC * LPU loads covers them
-            if (c + 1 < nch) stage(c + 1);
+            if (c + 1 < nch) {
+                stage(c + 1);
+                if (a4_groups > 0) a4_load(c + 1, 0);
+            }
             asm volatile("" ::: "memory");
             const uint32_t cb = lds0 + (uint32_t)((c & 1) * AC::BUF);
             // bf16: the A fragments of unit 0 (set 0); each unit then reads the
@@ -999,9 +1053,19 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
                     issue(c * UPC + ul + D, ws0[d], ws1[d]);
                 }
             }
+            // NVFP4 A: chunk c + 1 decoded into the other buffer (read last in
+            // chunk c - 1, before the previous barrier)
+            if (AFP4 && c + 1 < nch) {
+                a4_write(c + 1, 0);
+                for (int g = 1; g < a4_groups; ++g) {
+                    a4_load(c + 1, g);
+                    a4_write(c + 1, g);
+                }
+            }
             // chunk c + 1 has landed (its copies are older than this chunk's
-            // UPC * LPU weight loads), and every wavefront is done with chunk
-            // c, whose buffer chunk c + 2 reuses
+            // UPC * LPU weight loads; its LDS writes end at the barrier), and
+            // every wavefront is done with chunk c, whose buffer chunk c + 2
+            // reuses
             wait_vmcnt<UPC * LPU>();
             lds_barrier();
         }
@@ -1022,14 +1086,14 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
     }
 }
 
-template <bool FP4, int RB>
+template <bool FP4, int RB, bool AFP4 = false>
 hipError_t launch_achunk_rb(const GemmArgs &a, int d, int grid, int nwv, hipStream_t s) {
     constexpr int UPC = AChunk<RB>::CK / (32 * (FP4 ? 4 : 2));
     const dim3 b(64 * nwv);
     switch (d) {
-        case 8: if constexpr (UPC % 8 == 0) { hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 8>), dim3(grid), b, 0, s, a); break; } return hipErrorInvalidValue;
-        case 4: if constexpr (UPC % 4 == 0) { hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 4>), dim3(grid), b, 0, s, a); break; } return hipErrorInvalidValue;
-        case 2: hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 2>), dim3(grid), b, 0, s, a); break;
+        case 8: if constexpr (UPC % 8 == 0) { hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 8, AFP4>), dim3(grid), b, 0, s, a); break; } return hipErrorInvalidValue;
+        case 4: if constexpr (UPC % 4 == 0) { hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 4, AFP4>), dim3(grid), b, 0, s, a); break; } return hipErrorInvalidValue;
+        case 2: hipLaunchKernelGGL((direct_achunk_kernel<FP4, RB, 2, AFP4>), dim3(grid), b, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1080,21 +1144,26 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, bool afp4, int nb, in
 
 // K-chunked A in LDS (16 < M <= 64): rb = 2 or 4 row blocks, K % (2048 / rb)
 // == 0 (and K % 128 == 0 for an NVFP4 weight); `waves` streaming wavefronts,
-// one 16-column item each per round.
+// one 16-column item each per round.  afp4 (with fp4): A is NVFP4 rows
+// (lda % 32 == 0, A_scales set).
 bool direct_achunk_ok(int M, int K, int rb, bool fp4) {
     if (rb != 2 && rb != 4) return false;
     const int ck = 2048 / rb;
     return M > 16 * (rb / 2) && M <= 16 * rb && K % ck == 0 && (!fp4 || K % 128 == 0);
 }
 
-hipError_t launch_direct_achunk(const GemmArgs &a, bool fp4, int rb, int waves, int cus, int depth, hipStream_t s) {
+hipError_t launch_direct_achunk(const GemmArgs &a, bool fp4, bool afp4, int rb, int waves, int cus, int depth,
+                                hipStream_t s) {
     if (waves < 1 || cus < 1 || a.M < 1 || a.M > 16 * rb || (rb != 2 && rb != 4) || a.K % (2048 / rb) != 0 ||
-        (fp4 && a.K % 128 != 0))
+        (fp4 && a.K % 128 != 0) || (afp4 && (!fp4 || a.lda % 32 != 0 || !a.A_scales)))
         return hipErrorInvalidValue;
     // one workgroup per compute unit (two 64 KB chunk buffers), up to eight
-    // wavefronts
+    // wavefronts; an NVFP4 A takes at least four (its decode is shared by
+    // the workgroup's wavefronts, so fewer workgroups with more wavefronts
+    // beat one wavefront each)
     int nwv = (waves + cus - 1) / cus;
     nwv = nwv < 1 ? 1 : nwv > 8 ? 8 : nwv;
+    if (afp4 && nwv < 4) nwv = waves < 4 ? waves : 4;
     const int grid = (waves + nwv - 1) / nwv;
     const int upc = (2048 / rb) / (32 * (fp4 ? 4 : 2));
     // depth 1 is taken as 2: two units are the least the window holds
@@ -1103,6 +1172,8 @@ hipError_t launch_direct_achunk(const GemmArgs &a, bool fp4, int rb, int waves, 
     while (d & (d - 1)) d &= d - 1;
     while (d > 2 && upc % d) d >>= 1;
     if (d < 2 || upc % d) return hipErrorInvalidValue;
+    if (afp4) return rb == 2 ? direct::launch_achunk_rb<true, 2, true>(a, d, grid, nwv, s)
+                             : direct::launch_achunk_rb<true, 4, true>(a, d, grid, nwv, s);
     if (fp4) return rb == 2 ? direct::launch_achunk_rb<true, 2>(a, d, grid, nwv, s)
                             : direct::launch_achunk_rb<true, 4>(a, d, grid, nwv, s);
     return rb == 2 ? direct::launch_achunk_rb<false, 2>(a, d, grid, nwv, s)
