@@ -256,19 +256,27 @@ int64_t stream_round_cost(int rb) { return 600 + 368 * rb; }
 // The chunked-A kernel (A staged in LDS 2048 / rb columns at a time, one
 // 16-column item per wavefront, up to eight per compute unit): with w items
 // per compute unit (w > 1) a call costs about a + b w microseconds per 4096
-// of K (MI355X, N = 6144 ... 24576, M = 17 ... 64).  A bf16 weight is bound
+// of K (MI355X, N = 6144 ... 24576, M = 17 ... 128).  A bf16 weight is bound
 // by the stream (b large); an NVFP4 one by its decode, which two items share
-// a SIMD for only above four per compute unit.  In hundredths of a
-// microsecond:
+// a SIMD for only above four per compute unit.  Eight row blocks (M > 64)
+// re-read 128 rows of A from LDS per weight fragment: they beat the tile
+// only for an NVFP4 weight with at least four items per compute unit.  In
+// hundredths of a microsecond (kNever: not a candidate):
+constexpr int64_t kNever = INT64_MAX / 4;
 int64_t achunk_cost(bool fp4, int rb, int64_t items, int cus) {
     const int64_t w100 = items * 100 / cus;  // items per compute unit, x 100
-    if (fp4) return (rb == 2 ? 1350 : 1900) + (rb == 2 ? 125 : 130) * w100 / 100;
+    if (fp4) {
+        if (rb == 8) return items >= 4 * static_cast<int64_t>(cus) ? 4000 + 120 * w100 / 100 : kNever;
+        return (rb == 2 ? 1350 : 1900) + (rb == 2 ? 125 : 130) * w100 / 100;
+    }
+    if (rb == 8) return kNever;
     return (rb == 2 ? 1220 : 1660) + (rb == 2 ? 470 : 430) * w100 / 100;
 }
 // With an NVFP4 A, whose rows each workgroup (of at least four wavefronts)
 // decodes into LDS as well (N = 1000 ... 24576, K = 4096 and 12288):
 int64_t achunk_cost_w4a4(int rb, int64_t items, int cus) {
     const int64_t w100 = items * 100 / cus;
+    if (rb == 8) return 4200 + 150 * w100 / 100;
     return rb == 2 ? 1600 + 110 * w100 / 100 : 2350 + 150 * w100 / 100;
 }
 
@@ -308,21 +316,22 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
     // bf16 A with 16 < M <= 128 and a bf16 weight, or 16 < M <= 64 and a raw
     // NVFP4 one (K % 128 == 0): the register-streaming kernel with two, four
     // or eight 16-row blocks (one weight fragment feeds each block's chain);
-    // with M <= 64 and more 16-column items than compute units, also the
-    // kernel that keeps A in LDS in K chunks.  The one with the least
-    // estimate runs if it is below the tile's.
+    // with M <= 128 (either weight) and more 16-column items than compute
+    // units, also the kernel that keeps A in LDS in K chunks.  The one with
+    // the least estimate runs if it is below the tile's.
     const int64_t items = ceil_div(N, 16);
     int64_t best = 100 * est;
     Regime pick{BI_KERNEL_TILED, 0, 0, 0, 0, -1};
-    if (a_mode == bi::OPND_BF16_ROWS &&
-        ((b_mode == bi::OPND_BF16_ROWS && M <= 128) || (fp4 && K % 128 == 0 && M <= 64))) {
+    if (a_mode == bi::OPND_BF16_ROWS && M <= 128 && (b_mode == bi::OPND_BF16_ROWS || (fp4 && K % 128 == 0))) {
         const int rb = M > 64 ? 8 : M > 32 ? 4 : 2;
-        const int64_t e = ceil_div(items, cus) * stream_round_cost(rb);
-        if (e < best) {
-            best = e;
-            pick = {BI_KERNEL_STREAM_REG, rb, 0, 0, 16, -1};
+        if (b_mode == bi::OPND_BF16_ROWS || M <= 64) {
+            const int64_t e = ceil_div(items, cus) * stream_round_cost(rb);
+            if (e < best) {
+                best = e;
+                pick = {BI_KERNEL_STREAM_REG, rb, 0, 0, 16, -1};
+            }
         }
-        if (M <= 64 && items > cus && bi::direct_achunk_ok(static_cast<int>(M), static_cast<int>(K), rb, fp4)) {
+        if (items > cus && bi::direct_achunk_ok(static_cast<int>(M), static_cast<int>(K), rb, fp4)) {
             const int64_t ec = achunk_cost(fp4, rb, items, cus);
             if (ec < best) {
                 best = ec;
@@ -330,11 +339,11 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
             }
         }
     }
-    // NVFP4 A and weight, 16 < M <= 64 (K % 128 == 0): the chunked-A kernel
-    // with A's rows decoded into LDS chunk by chunk (at any N: there is no
-    // register-streaming kernel for an NVFP4 A)
-    if (a_mode == bi::OPND_NVFP4_ROWS && M <= 64 && K % 128 == 0) {
-        const int rb = M > 32 ? 4 : 2;
+    // NVFP4 A and weight, 16 < M <= 128 (K % 128 == 0): the chunked-A
+    // kernel with A's rows decoded into LDS chunk by chunk (at any N: there
+    // is no register-streaming kernel for an NVFP4 A)
+    if (a_mode == bi::OPND_NVFP4_ROWS && M <= 128 && K % 128 == 0) {
+        const int rb = M > 64 ? 8 : M > 32 ? 4 : 2;
         if (bi::direct_achunk_ok(static_cast<int>(M), static_cast<int>(K), rb, true)) {
             const int64_t ec = achunk_cost_w4a4(rb, items, cus);
             if (ec < best) {

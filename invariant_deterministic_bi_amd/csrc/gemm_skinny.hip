@@ -850,8 +850,8 @@ struct AChunk {
     static constexpr int ROWS = 16 * RB;
     static constexpr int AS = CK * 2 + 16;        // padded LDS row stride (bank spread)
     static constexpr int BUF = ROWS * AS;
-    static constexpr int BPR = CK * 2 / 1024;     // 1 KB DMA blocks per row and chunk
-    static_assert(RB == 2 || RB == 4, "two or four row blocks");
+    static constexpr int BPR = CK * 2 / 1024;     // 1 KB DMA blocks per row and chunk (0: a 512-byte row)
+    static_assert(RB == 2 || RB == 4 || RB == 8, "two, four or eight row blocks");
     static_assert(2 * BUF <= 160 * 1024, "two chunk buffers fit the LDS");
 };
 
@@ -884,6 +884,16 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
     auto stage = [&](int c) {
         if constexpr (AFP4) return;
         char *buf = lds + (c & 1) * AC::BUF;
+        if constexpr (AC::BPR == 0) {
+            // 512-byte rows: one row per instruction, lanes 0..31
+            for (int row = w; row < p.M; row += nwv) {
+                const int k = c * AC::CK + (lane & 31) * 8;
+                if (lane < 32)
+                    bi_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) uint32_t *)(buf + row * AC::AS), 16,
+                                           (int)(row * p.lda * 2) + k * 2, 0, 0, 0);
+            }
+            return;
+        }
         for (int b = w; b < p.M * AC::BPR; b += nwv) {
             const int row = b / AC::BPR, part = b - row * AC::BPR;
             const int k = c * AC::CK + part * 512 + lane * 8;
@@ -893,7 +903,7 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
     };
     // NVFP4 A: chunk c in 32-element units (16 code bytes, two scale bytes),
     // AG per thread per group; group g's loads, then its decode and writes
-    constexpr int AG = 4;
+    constexpr int AG = RB == 8 ? 2 : 4;            // (eight row blocks: registers are short)
     constexpr int UPR = AC::CK / 32;               // units per row and chunk
     const int a4_units = AFP4 ? p.M * UPR : 0;
     const int a4_groups = (a4_units + AG * (int)blockDim.x - 1) / (AG * (int)blockDim.x);
@@ -995,10 +1005,17 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
             }
             asm volatile("" ::: "memory");
             const uint32_t cb = lds0 + (uint32_t)((c & 1) * AC::BUF);
-            // bf16: the A fragments of unit 0 (set 0); each unit then reads the
-            // next unit's into the other set before its own MFMAs
-            i32x4 af[2][RB * U];
-            if constexpr (!FP4) {
+            // bf16 with at most eight fragments per unit: the A fragments of
+            // unit 0 (set 0); each unit then reads the next unit's into the
+            // other set before its own MFMAs (sixteen would overrun the LDS
+            // counter, so eight row blocks read each unit's own)
+            constexpr bool PF = !FP4 && RB * U <= 8;
+            // NVFP4 with eight row blocks: two halves of four blocks, each
+            // read, waited for and multiplied in turn (registers are short)
+            constexpr int H = FP4 && RB * U > 16 ? 2 : 1;
+            constexpr int RBH = RB / H;
+            i32x4 af[PF ? 2 : 1][RBH * U];
+            if constexpr (PF) {
 #pragma unroll
                 for (int b = 0; b < RB; ++b)
 #pragma unroll
@@ -1008,25 +1025,47 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
 #pragma unroll
                 for (int d = 0; d < D; ++d) {
                     const int ul = ub + d;                 // unit within the chunk
-                    constexpr int NF = RB * U;
+                    constexpr int NF = RBH * U;
                     i32x4 wv[U];
-                    i32x4 *a = af[FP4 ? 0 : (d & 1)];
+                    i32x4 *a = af[PF ? (d & 1) : 0];
                     if constexpr (FP4) {
-                        // fragment reads first: the decode covers their latency
+#pragma unroll
+                        for (int h = 0; h < H; ++h) {
+                            // fragment reads first: the decode covers their latency
+#pragma unroll
+                            for (int b = 0; b < RBH; ++b)
+#pragma unroll
+                                for (int j = 0; j < U; ++j)
+                                    a[b * U + j] = rd_a(cb + a_row[h * RBH + b] + 64 * (ul * U + j));
+                            if (h == 0) {
+                                uint32_t y[4] = {(uint32_t)ws0[d].x, (uint32_t)ws0[d].y, (uint32_t)ws0[d].z,
+                                                 (uint32_t)ws0[d].w};
+                                transpose4(y[0], y[1], y[2], y[3]);
+                                const uint32_t s01 = (uint32_t)ws1[d].x >> sshift, s23 = (uint32_t)ws1[d].y >> sshift;
+                                const float sc[4] = {e4m3_value<0>(s01), e4m3_value<2>(s01), e4m3_value<0>(s23),
+                                                     e4m3_value<2>(s23)};
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    const uint4 q = decode8(y[j], sc[j]);
+                                    wv[j] = i32x4{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+                                }
+                            }
+                            wait_frags<0, NF>(a);
+#pragma unroll
+                            for (int j = 0; j < U; ++j)
+#pragma unroll
+                                for (int b = 0; b < RBH; ++b)
+                                    acc[h * RBH + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        __builtin_bit_cast(bf16x8, a[b * U + j]), __builtin_bit_cast(bf16x8, wv[j]),
+                                        acc[h * RBH + b], 0, 0, 0);
+                        }
+                    } else if constexpr (!PF) {
+                        wv[0] = ws0[d];
+                        wv[1] = ws1[d];
 #pragma unroll
                         for (int b = 0; b < RB; ++b)
 #pragma unroll
                             for (int j = 0; j < U; ++j) a[b * U + j] = rd_a(cb + a_row[b] + 64 * (ul * U + j));
-                        uint32_t y[4] = {(uint32_t)ws0[d].x, (uint32_t)ws0[d].y, (uint32_t)ws0[d].z, (uint32_t)ws0[d].w};
-                        transpose4(y[0], y[1], y[2], y[3]);
-                        const uint32_t s01 = (uint32_t)ws1[d].x >> sshift, s23 = (uint32_t)ws1[d].y >> sshift;
-                        const float sc[4] = {e4m3_value<0>(s01), e4m3_value<2>(s01), e4m3_value<0>(s23),
-                                             e4m3_value<2>(s23)};
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint4 q = decode8(y[j], sc[j]);
-                            wv[j] = i32x4{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-                        }
                         wait_frags<0, NF>(a);
                     } else {
                         wv[0] = ws0[d];
@@ -1043,13 +1082,15 @@ __global__ __launch_bounds__(512) void direct_achunk_kernel(GemmArgs p) {
                             wait_frags<0, NF>(a);
                         }
                     }
+                    if constexpr (!FP4) {
 #pragma unroll
-                    for (int j = 0; j < U; ++j)
+                        for (int j = 0; j < U; ++j)
 #pragma unroll
-                        for (int b = 0; b < RB; ++b)
-                            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[b * U + j]),
-                                                                             __builtin_bit_cast(bf16x8, wv[j]), acc[b],
-                                                                             0, 0, 0);
+                            for (int b = 0; b < RB; ++b)
+                                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, a[b * U + j]), __builtin_bit_cast(bf16x8, wv[j]),
+                                    acc[b], 0, 0, 0);
+                    }
                     issue(c * UPC + ul + D, ws0[d], ws1[d]);
                 }
             }
@@ -1147,14 +1188,14 @@ hipError_t launch_direct_alds(const GemmArgs &a, bool fp4, bool afp4, int nb, in
 // one 16-column item each per round.  afp4 (with fp4): A is NVFP4 rows
 // (lda % 32 == 0, A_scales set).
 bool direct_achunk_ok(int M, int K, int rb, bool fp4) {
-    if (rb != 2 && rb != 4) return false;
+    if (rb != 2 && rb != 4 && rb != 8) return false;
     const int ck = 2048 / rb;
     return M > 16 * (rb / 2) && M <= 16 * rb && K % ck == 0 && (!fp4 || K % 128 == 0);
 }
 
 hipError_t launch_direct_achunk(const GemmArgs &a, bool fp4, bool afp4, int rb, int waves, int cus, int depth,
                                 hipStream_t s) {
-    if (waves < 1 || cus < 1 || a.M < 1 || a.M > 16 * rb || (rb != 2 && rb != 4) || a.K % (2048 / rb) != 0 ||
+    if (waves < 1 || cus < 1 || a.M < 1 || a.M > 16 * rb || (rb != 2 && rb != 4 && rb != 8) || a.K % (2048 / rb) != 0 ||
         (fp4 && a.K % 128 != 0) || (afp4 && (!fp4 || a.lda % 32 != 0 || !a.A_scales)))
         return hipErrorInvalidValue;
     // one workgroup per compute unit (two 64 KB chunk buffers), up to eight
@@ -1172,12 +1213,15 @@ hipError_t launch_direct_achunk(const GemmArgs &a, bool fp4, bool afp4, int rb, 
     while (d & (d - 1)) d &= d - 1;
     while (d > 2 && upc % d) d >>= 1;
     if (d < 2 || upc % d) return hipErrorInvalidValue;
-    if (afp4) return rb == 2 ? direct::launch_achunk_rb<true, 2, true>(a, d, grid, nwv, s)
-                             : direct::launch_achunk_rb<true, 4, true>(a, d, grid, nwv, s);
-    if (fp4) return rb == 2 ? direct::launch_achunk_rb<true, 2>(a, d, grid, nwv, s)
-                            : direct::launch_achunk_rb<true, 4>(a, d, grid, nwv, s);
-    return rb == 2 ? direct::launch_achunk_rb<false, 2>(a, d, grid, nwv, s)
-                   : direct::launch_achunk_rb<false, 4>(a, d, grid, nwv, s);
+    if (afp4) return rb == 2   ? direct::launch_achunk_rb<true, 2, true>(a, d, grid, nwv, s)
+                     : rb == 4 ? direct::launch_achunk_rb<true, 4, true>(a, d, grid, nwv, s)
+                               : direct::launch_achunk_rb<true, 8, true>(a, d, grid, nwv, s);
+    if (fp4) return rb == 2   ? direct::launch_achunk_rb<true, 2>(a, d, grid, nwv, s)
+                    : rb == 4 ? direct::launch_achunk_rb<true, 4>(a, d, grid, nwv, s)
+                              : direct::launch_achunk_rb<true, 8>(a, d, grid, nwv, s);
+    return rb == 2   ? direct::launch_achunk_rb<false, 2>(a, d, grid, nwv, s)
+           : rb == 4 ? direct::launch_achunk_rb<false, 4>(a, d, grid, nwv, s)
+                     : direct::launch_achunk_rb<false, 8>(a, d, grid, nwv, s);
 }
 
 hipError_t launch_direct_nvfp4(const GemmArgs &a, int rb, int ap, int grid, int depth, hipStream_t s) {

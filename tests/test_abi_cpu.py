@@ -334,9 +334,9 @@ def test_plan_regimes_cover_every_m(op, N, K, a_fmt):
             assert len(regs) == 1                     # one shape per (N, K)
         if a_fmt == 1:
             # an NVFP4 A streams only through the A-in-LDS kernel (M <= 16)
-            # and the chunked-A kernel (16 < M <= 64)
+            # and the chunked-A kernel (16 < M <= 128)
             assert all(r["kind"] == "tiled" or (r["kind"] == "stream_a_lds" and r["m_max"] <= 16) or
-                       (r["kind"] == "stream_a_chunks" and 17 <= r["m_min"] and r["m_max"] <= 64) for r in regs)
+                       (r["kind"] == "stream_a_chunks" and 17 <= r["m_min"] and r["m_max"] <= 128) for r in regs)
 
 
 def _shape_at(op, N, K, M, a_fmt=0, cus=256):
@@ -363,13 +363,13 @@ def test_plan_regimes_cost_model_choices():
                            1024: (256, 192), 2048: (256, 256), 4096: (256, 256)},
         (G, 4096, 12288): {32: "stream_reg", 64: "stream_reg", 128: (64, 64), 256: (64, 64), 512: (128, 64),
                            1024: (128, 128), 2048: (256, 128), 4096: (256, 256), 8192: (256, 256)},
-        (F, 24576, 4096): {32: "stream_a_chunks", 64: "stream_a_chunks", 128: (128, 128), 256: (256, 128),
+        (F, 24576, 4096): {32: "stream_a_chunks", 64: "stream_a_chunks", 128: "stream_a_chunks", 256: (256, 128),
                            1024: (256, 192), 2048: (256, 256), 4096: (256, 256)},
     }
     for (op, N, K), ms in want.items():
         for M, shape in ms.items():
             assert _shape_at(op, N, K, M) == shape, (op, N, K, M)
-    w4a4 = {32: "stream_a_chunks", 64: "stream_a_chunks", 128: (128, 128), 256: (256, 128), 512: (256, 192), 1024: (256, 192),
+    w4a4 = {32: "stream_a_chunks", 64: "stream_a_chunks", 128: "stream_a_chunks", 256: (256, 128), 512: (256, 192), 1024: (256, 192),
             2048: (256, 256), 4096: (256, 256)}
     for M, shape in w4a4.items():
         assert _shape_at(F, 24576, 4096, M, a_fmt=1) == shape, M

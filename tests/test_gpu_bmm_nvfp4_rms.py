@@ -196,31 +196,32 @@ def test_w4a4_streaming_small_m(N, K):
 
 @pytest.mark.parametrize("N,K", [(24576, 4096), (6144, 4096), (8200, 2048), (1000, 4096)])
 def test_w4a4_chunked_a_mid_m(N, K):
-    """W4A4 at 16 < M <= 64 streams the weight with A's rows decoded into LDS
-    chunk by chunk (at least four wavefronts per workgroup, also when N
-    gives fewer items than compute units): every M in
-    {17, 20, 32, 33, 48, 63, 64} is bitwise the forced tiled kernel and the
-    M = 64 batch's prefix, also with A rows at a padded stride, under
-    wavefront caps {1, 7, #CU} and pipeline depths {1, 2, 4, 8}; N(0,1) rows
-    agree with the oracle within tolerance; power-of-two codes give its
-    exact result."""
+    """W4A4 at 16 < M <= 128 streams the weight with A's rows decoded into
+    LDS chunk by chunk (two, four or eight row blocks; at least four
+    wavefronts per workgroup, also when N gives fewer items than compute
+    units): every M in {17, 20, 32, 33, 48, 63, 64, 65, 100, 127, 128} is
+    bitwise the forced tiled kernel and the M = 128 batch's prefix, also with
+    A rows at a padded stride, under wavefront caps {1, 7, #CU} and pipeline
+    depths {1, 2, 4, 8}; N(0,1) rows agree with the oracle within tolerance;
+    power-of-two codes give its exact result."""
     plan = B.plan_regimes(B.BI_OP_NVFP4_GEMM, N, K, 1)
-    assert [r["m_min"] for r in plan if r["kind"] == "stream_a_chunks"][:1] == [17], plan
+    chunked = [r for r in plan if r["kind"] == "stream_a_chunks"]
+    assert chunked and chunked[0]["m_min"] == 17 and chunked[-1]["m_max"] == 128, plan
     W, Ws, gw = _nvfp4_weights(N, K, (133, N))
-    x = inputs.rng(12345, 134, N).standard_normal((64, K)).astype(np.float32)
+    x = inputs.rng(12345, 134, N).standard_normal((128, K)).astype(np.float32)
     ga = inputs.nvfp4_global_scale(x)
     Aq, Aqs = inputs.nvfp4_quantize(x, ga)
     alpha = float(np.float32(1.0) / (ga * gw))
     Wd, Wsd = dev(W), dev(Ws)
-    pad_q = np.zeros((64, K // 2 + 16), np.uint8)
-    pad_s = np.zeros((64, K // 16 + 2), np.uint8)
+    pad_q = np.zeros((128, K // 2 + 16), np.uint8)
+    pad_s = np.zeros((128, K // 16 + 2), np.uint8)
     pad_q[:, :K // 2], pad_s[:, :K // 16] = Aq, Aqs
     Aqd, Aqsd = dev(Aq), dev(Aqs)
     Pq, Ps = dev(pad_q)[:, :K // 2], dev(pad_s)[:, :K // 16]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    note(f"w4a4 mid M N={N} K={K} M=64")
+    note(f"w4a4 mid M N={N} K={K} M=128")
     yfull = B.bi_nvfp4_gemm(Aqd, Wd, Wsd, alpha, A_scales=Aqsd)
-    for M in (17, 20, 32, 33, 48, 63, 64):
+    for M in (17, 20, 32, 33, 48, 63, 64, 65, 100, 127, 128):
         note(f"w4a4 mid M N={N} K={K} M={M}")
         y = B.bi_nvfp4_gemm(Aqd[:M], Wd, Wsd, alpha, A_scales=Aqsd[:M])
         assert torch.equal(y, yfull[:M]), f"M={M} vs batch"
@@ -232,14 +233,16 @@ def test_w4a4_chunked_a_mid_m(N, K):
         for depth in (1, 2, 4, 8):
             assert torch.equal(y, B.bi_nvfp4_gemm(Aqd[:M], Wd, Wsd, alpha, A_scales=Aqsd[:M],
                                                   pipeline_depth=depth)), (M, depth)
-    ref, s = oracle.nvfp4_gemm(Aq, Aqs, W, Ws, alpha, K, rows=[0, 17, 63])
-    assert_within_tol(host(yfull)[[0, 17, 63]], ref, s, f"w4a4 mid M N={N} K={K}")
+    ref, s = oracle.nvfp4_gemm(Aq, Aqs, W, Ws, alpha, K, rows=[0, 17, 63, 127])
+    assert_within_tol(host(yfull)[[0, 17, 63, 127]], ref, s, f"w4a4 mid M N={N} K={K}")
     W2, Ws2 = inputs.random_nvfp4_pow2((N, K), tag=(135, N))
-    A2, As2 = inputs.random_nvfp4_pow2((40, K), tag=(136, N))
-    ref2, _ = oracle.nvfp4_gemm(A2, As2, W2, Ws2, 0.5, K, rows=[0, 20, 39])
-    note(f"w4a4 mid M integer-exact N={N} K={K}")
-    y2 = host(B.bi_nvfp4_gemm(dev(A2), dev(W2), dev(Ws2), 0.5, A_scales=dev(As2)))
-    assert np.array_equal(y2[[0, 20, 39]], rne_bf16_of_exact(ref2))
+    for mi in (40, 100):
+        A2, As2 = inputs.random_nvfp4_pow2((mi, K), tag=(136, N, mi))
+        rr = [0, mi // 2, mi - 1]
+        ref2, _ = oracle.nvfp4_gemm(A2, As2, W2, Ws2, 0.5, K, rows=rr)
+        note(f"w4a4 mid M integer-exact N={N} K={K} M={mi}")
+        y2 = host(B.bi_nvfp4_gemm(dev(A2), dev(W2), dev(Ws2), 0.5, A_scales=dev(As2)))
+        assert np.array_equal(y2[rr], rne_bf16_of_exact(ref2))
 
 
 # ----------------------------------------------------------------- RMSNorm

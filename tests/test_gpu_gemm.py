@@ -244,11 +244,18 @@ def test_pingpong_schedule_matches_classic_schedule(pp, classic, bn):
                                      (6144, 4096, True), (8200, 2048, True)])
 def test_chunked_a_path_matches_tiled_kernel(N, K, fp4):
     """16 < M <= 64 with A staged in LDS in K chunks (more 16-column items
-    than compute units; bf16 and NVFP4 weights, ragged N): every M in {17,
-    20, 32, 33, 48, 63, 64} bitwise equal to the forced tiled kernel and to
-    the M = 64 batch, under wavefront caps {1, 7, #CU} and pipeline depths
-    {1, 2, 4, 8}; parity with the oracle."""
-    Mmax = 64
+    than compute units; bf16 and NVFP4 weights, ragged N), and 64 < M <= 128
+    (eight row blocks) for an NVFP4 weight with at least four items per
+    compute unit: every M in {17, 20, 32, 33, 48, 63, 64} (and {65, 100,
+    127, 128}) bitwise equal to the forced tiled kernel and to the full
+    batch, under wavefront caps {1, 7, #CU} and pipeline depths {1, 2, 4, 8};
+    parity with the oracle."""
+    plan = B.plan_regimes(B.BI_OP_NVFP4_GEMM if fp4 else B.BI_OP_GEMM, N, K)
+    chunked = [r for r in plan if r["kind"] == "stream_a_chunks"]
+    assert chunked and chunked[0]["m_min"] == 17, plan
+    wide = chunked[-1]["m_max"] >= 128
+    assert wide == (fp4 and N == 24576), plan
+    Mmax = 128 if wide else 64
     A = inputs.randn_bf16((Mmax, K), tag=(90, N, K))
     if fp4:
         x = inputs.rng(12345, 91, N, K).standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
@@ -267,13 +274,10 @@ def test_chunked_a_path_matches_tiled_kernel(N, K, fp4):
         def run(M, **kw):
             return host(gemm(Ad[:M], Wd, **kw))
         tiled = 1
-    plan = B.plan_regimes(B.BI_OP_NVFP4_GEMM if fp4 else B.BI_OP_GEMM, N, K)
-    chunked = [r for r in plan if r["kind"] == "stream_a_chunks"]
-    assert chunked and chunked[0]["m_min"] == 17, plan
-    note(f"chunked A N={N} K={K} fp4={fp4} M=64")
+    note(f"chunked A N={N} K={K} fp4={fp4} M={Mmax}")
     yfull = run(Mmax)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for M in (17, 20, 32, 33, 48, 63, 64):
+    for M in (17, 20, 32, 33, 48, 63, 64) + ((65, 100, 127, 128) if wide else ()):
         note(f"chunked A N={N} K={K} fp4={fp4} M={M}")
         y = run(M)
         assert np.array_equal(y, yfull[:M]), f"M={M} vs batch"
@@ -282,7 +286,7 @@ def test_chunked_a_path_matches_tiled_kernel(N, K, fp4):
             assert np.array_equal(run(M, max_workgroups=mw), y), (M, mw)
         for depth in (1, 2, 4, 8):
             assert np.array_equal(run(M, pipeline_depth=depth), y), (M, depth)
-    rows = [0, 17, 63]
+    rows = [0, 17, 63] + ([127] if wide else [])
     if fp4:
         ref, s = oracle.nvfp4_gemm(A[rows], None, W, Ws, alpha, K)
     else:
