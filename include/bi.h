@@ -284,7 +284,9 @@ bi_status bi_reduce_rmsnorm(const void *const *partials, int n_partials, int64_t
  *   E >= 1 experts; sW >= (N-1)*ldw + K when E > 1; K % 8 == 0.  T == 0 is
  *   a no-op.  The kernel enumerates only the experts' non-empty tiles (at most
  *   (ceil(T/bm) + E) * ceil(N/bn)), so any routing spreads evenly over the
- *   persistent grid.
+ *   persistent grid.  The tile shape follows N and the average rows per
+ *   expert, ceil(T / E) (bi_plan_regimes lists the ranges); every shape
+ *   gives the same bits.
  */
 bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int64_t sW, void *Y,
                           int64_t ldy, const int64_t *group_offsets, int64_t E, int64_t T, int64_t N,
@@ -399,8 +401,9 @@ bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, f
  * 0 as K (threads = 256 per workgroup, chunks_per_thread = 1: one thread per
  * 8 elements).  There is no M argument: the per-element recipe does not
  * depend on it.  For the dense and NVFP4 GEMMs the tile fields describe the
- * shape of calls with more than 4096 rows; smaller calls may run another
- * kernel or shape (bi_plan_regimes lists them) with the same bits.  Returns
+ * shape of calls with more than 4096 rows (for the grouped GEMM, more than
+ * 4096 rows per expert on average); smaller calls may run another kernel or
+ * shape (bi_plan_regimes lists them) with the same bits.  Returns
  * BI_ERR_SHAPE or BI_ERR_UNSUPPORTED for keys the matching entry point would
  * reject.  Host-only; makes no HIP call.
  */
@@ -454,6 +457,8 @@ typedef struct bi_regime {
  *     it: the A-in-LDS limit 10 * M * cus <= 7 * N and the cost model's
  *     rounds of tiles), or 0 for the current device (one HIP attribute
  *     query).  Above 4096 rows the choice no longer changes with M.
+ *   BI_OP_GROUPED_GEMM: M stands for the average rows per expert,
+ *     ceil(T / E).
  *   out: room for `capacity` entries; *count = the number of regimes
  *   (BI_ERR_SHAPE, with *count set, when capacity is too small).
  *   Ops other than the GEMM family: BI_ERR_UNSUPPORTED.

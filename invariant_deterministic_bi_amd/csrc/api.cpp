@@ -76,19 +76,23 @@ bi_status device_cus(int *out) {
 // ---------------------------------------------------------------------------
 constexpr int64_t kMaxLd = (int64_t)1 << 22;  // keeps 32-bit in-tile byte offsets
 
-// Tile shape of the ops that keep one shape per (N, K) at every M: the
-// batched and grouped GEMMs.  (The dense and NVFP4 GEMMs take theirs from
-// the cost model below.)
-int fixed_variant(int op, int64_t N) {
-    // Grouped GEMM: every expert adds a partial m-tile, so wide n-tiles (fewer
-    // tiles per expert) pay off sooner than for one dense GEMM; every tile
-    // shape gives the same bits, so each row is still bitwise bi_gemm's.
-    if (op == BI_OP_GROUPED_GEMM) {
-        if (N >= 2048) return 12;        // 256 x 256, classic schedule
-        if (N >= 512) return 11;         // 128 x 128, 8 wavefronts
-        return 6;                        // 64 x 64
-    }
-    return 2;                            // BMM: 256 x 128, 8 wavefronts
+// Tile shape of the batched GEMM: 256 x 128, 8 wavefronts, at every M.
+int fixed_variant(int /*op*/, int64_t /*N*/) { return 2; }
+
+// Tile shape of the grouped GEMM from N and the average rows per expert
+// (T / E, rounded up; the group sizes themselves are on the device).  Every
+// expert adds a partial m-tile, and sizes spread around the average, so an
+// m-tile just above the average would double the tiles: the bands sit below
+// the multiples of bm.  MI355X, 8 experts of 4096 x 4096 (µs, this choice
+// against the best forced tile): 64 rows 47 (47), 128 rows 57 (57), 256 rows
+// 91 (91), 512 rows 171 (171), 1024 rows 316 (315).  Every tile shape gives
+// the same bits, so each row is still bitwise bi_gemm's.
+int grouped_variant(int64_t N, int64_t rows) {
+    if (N < 512) return 6;               // 64 x 64
+    if (N < 2048 || rows <= 96) return 11;  // 128 x 128, 8 wavefronts
+    if (rows <= 192) return 9;           // 256 x 128, 8 wavefronts, 3-deep A ring
+    if (rows <= 768) return 16;          // 256 x 192, classic schedule
+    return 12;                           // 256 x 256, classic schedule
 }
 
 // Cost model of the dense and NVFP4 GEMMs' tiled kernel (batch 1).  A launch
@@ -165,6 +169,7 @@ int model_variant(int a_mode, int b_mode, int64_t N, int cus, int64_t M, int64_t
 // than kModelRows rows runs (the large-M limit does not depend on the number
 // of compute units).
 int plan_variant(int op, int64_t N, int64_t K) {
+    if (op == BI_OP_GROUPED_GEMM) return grouped_variant(N, kModelRows + 1);
     if (op != BI_OP_GEMM && op != BI_OP_NVFP4_GEMM) return fixed_variant(op, N);
     const int b_mode = op == BI_OP_GEMM ? bi::OPND_BF16_ROWS
                                         : (K % 64 == 0 ? bi::OPND_NVFP4_RAW : bi::OPND_NVFP4_ROWS);
@@ -308,7 +313,8 @@ Regime classify(int op, int a_mode, int b_mode, int64_t N, int64_t K, int batch,
     // own recipe, chosen from K alone)
     if (op == BI_OP_BMM && bi::bmm_short_k_ok(static_cast<int>(K))) return {BI_KERNEL_BMM_STREAM, 4, 0, 0, 128, -1};
     if (!dense) {
-        const int v = fixed_variant(op, N);
+        // grouped: M is the average rows per expert
+        const int v = grouped ? grouped_variant(N, M) : fixed_variant(op, N);
         return {BI_KERNEL_TILED, bi::kTileShapes[v].bm / 16, 0, 0, bi::kTileShapes[v].bn, v};
     }
     int64_t est = 0;
@@ -409,7 +415,9 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;
         return launch_tiled(a_mode, b_mode, op, opts->tile_variant - 1, in, stream, opts, cus);
     }
-    const Regime r = classify(op, a_mode, b_mode, in.N, in.K, in.batch, in.group_off != nullptr, cus, in.M);
+    // grouped: classify() takes the average rows per expert
+    const int64_t m_cls = in.group_off ? (in.M + in.batch - 1) / in.batch : in.M;
+    const Regime r = classify(op, a_mode, b_mode, in.N, in.K, in.batch, in.group_off != nullptr, cus, m_cls);
     hipError_t e = hipSuccess;
     switch (r.kind) {
         case BI_KERNEL_STREAM_A_LDS: {

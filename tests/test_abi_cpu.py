@@ -213,14 +213,25 @@ def test_reduce_rmsnorm_validation():
 
 def test_grouped_gemm_plan_shares_the_gemm_chain():
     """The grouped GEMM's tile may differ from the dense one (every tile shape
-    gives the same bits), but the MFMA block and K step are the same, and the
-    plan is a function of (N, K) alone."""
+    gives the same bits), but the MFMA block and K step are the same.  The
+    tile follows N and the average rows per expert: 128 x 128 up to 96 rows,
+    256 x 128 to 192, 256 x 192 to 768, then 256 x 256 (N >= 2048); 128 x 128
+    for 512 <= N < 2048 and 64 x 64 below."""
     for N, K in ((6144, 4096), (4096, 4096), (1536, 4096), (256, 1024)):
         g, q = B.plan_query(B.BI_OP_GEMM, N, K), B.plan_query(B.BI_OP_GROUPED_GEMM, N, K)
         for key in ("mfma_m", "mfma_n", "mfma_k", "bk"):
             assert g[key] == q[key]
         assert q == B.plan_query(B.BI_OP_GROUPED_GEMM, N, K)
     assert B.plan_query(B.BI_OP_GROUPED_GEMM, 4096, 4096)["bn"] == 256
+    shapes = B.tile_shapes()
+
+    def bands(N):
+        return [(r["m_min"], r["m_max"], shapes[r["tile_variant"] - 1]["bm"], shapes[r["tile_variant"] - 1]["bn"])
+                for r in B.plan_regimes(B.BI_OP_GROUPED_GEMM, N, 4096, cus=256)]
+    big = 2 ** 31 - 1
+    assert bands(4096) == [(1, 96, 128, 128), (97, 192, 256, 128), (193, 768, 256, 192), (769, big, 256, 256)]
+    assert bands(1536) == [(1, big, 128, 128)]
+    assert bands(256) == [(1, big, 64, 64)]
 
 
 def test_grouped_gemm_validation():
@@ -331,7 +342,7 @@ def test_plan_regimes_cover_every_m(op, N, K, a_fmt):
                 assert r["tile_variant"] == 0
                 assert r["kind"] == "bmm_stream" or r["m_max"] <= 128
         if op == B.BI_OP_GROUPED_GEMM:
-            assert len(regs) == 1                     # one shape per (N, K)
+            assert all(r["kind"] == "tiled" for r in regs)   # shapes by rows per expert
         if a_fmt == 1:
             # an NVFP4 A streams only through the A-in-LDS kernel (M <= 16)
             # and the chunked-A kernel (16 < M <= 128)

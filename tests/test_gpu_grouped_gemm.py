@@ -22,7 +22,12 @@ def offsets_dev(off):
                                          (4, 6144, 4096, [1, 129, 0, 70]),
                                          (1, 6144, 512, [33]),
                                          (3, 200, 544, [5, 16, 1]),
-                                         (64, 256, 512, [0] * 20 + [1, 2000] + [0] * 30 + [5] + [0] * 11)])
+                                         (64, 256, 512, [0] * 20 + [1, 2000] + [0] * 30 + [5] + [0] * 11),
+                                         # the tile bands by rows per expert at N = 4096: 256 x 128,
+                                         # 256 x 192, 256 x 256
+                                         (4, 4096, 1024, [150, 100, 170, 180]),
+                                         (4, 4096, 1024, [300, 250, 0, 650]),
+                                         (2, 4096, 512, [900, 1300])])
 def test_grouped_parity_and_rows_alone(E, N, K, sizes):
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     T = int(off[-1])
