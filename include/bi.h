@@ -323,8 +323,9 @@ bi_status bi_grouped_gemm(const void *A, int64_t lda, const void *W, int64_t ldw
  *     nothing else (BI_ERR_SHAPE if too small).  With it, and when the
  *     (request, 16-head group) pairs are fewer than the device's compute
  *     units, every 1024-token chunk of every request gets its own workgroup
- *     and a second kernel folds the chunks: the same bits, more of the chip
- *     busy.  Its contents need no initialisation and are clobbered.
+ *     (first chunks first) and a second kernel folds the chunks: the same
+ *     bits, more of the chip busy.  Its contents need no initialisation and
+ *     are clobbered.
  *   Dqk % 8 == 0, Dqk <= 1024; Dv % 8 == 0, Dv <= Dqk, Dv <= 1024;
  *   Lmax <= 16384.  q, kv, out 16-byte aligned.  scale finite
  *   (BI_ERR_VALUE otherwise).  B == 0 or H == 0 is a no-op.

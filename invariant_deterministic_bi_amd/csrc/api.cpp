@@ -936,13 +936,15 @@ bi_status bi_mla_decode_ex(const void *q, const void *kv, const int32_t *lens, f
     a.ws = split ? static_cast<float *>(workspace) : nullptr;
     a.nchunk = split ? (int)((Lmax + bi::kMlaChunk - 1) / bi::kMlaChunk) : 0;
     // work units: (request, 16-head group[, chunk]) for the MFMA kernel, one
-    // workgroup per compute unit; (request, head) for the VALU kernel
+    // workgroup each (a compute unit takes the next as it finishes one, which
+    // evens out requests of unequal length); (request, head) for the VALU
+    // kernel
     const bool mfma = bi::mla_mfma_variant(a.Dqk, a.Dv) != 0;
     const int64_t units = mfma ? bi::mla_mfma_units(B * (split ? a.nchunk : 1), (int)((H + 15) / 16)) : B * H;
     if (units > kI32Max) return BI_ERR_UNSUPPORTED;
-    const int per_cu = mfma ? 1 : (bi::mla_token_capacity(a.Lmax) == 4096 ? 4 : 1);
+    const int per_cu = mfma ? (int)((units + cus - 1) / cus) : (bi::mla_token_capacity(a.Lmax) == 4096 ? 4 : 1);
     const int grid = default_grid((int)units, cus, opts, per_cu);
-    const int64_t fold_blocks = (groups * 16 * Dv + 255) / 256;  // one thread per output element
+    const int64_t fold_blocks = (groups * 4 * Dv + 255) / 256;  // one thread per four output elements
     const int fold_grid = (int)(fold_blocks < (int64_t)cus * 8 ? fold_blocks : (int64_t)cus * 8);
     hipError_t e = bi::launch_mla_decode(a, grid, fold_grid < 1 ? 1 : fold_grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? BI_OK : BI_ERR_HIP;

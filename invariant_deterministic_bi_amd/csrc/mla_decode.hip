@@ -9,25 +9,30 @@
 // (Dqk, Dv) only:
 //
 // MFMA kernel (Dqk <= 32*KC, Dv <= 128*VB for a compiled (KC, VB)): a
-// request's tokens form chunks of kMlaChunk.  Within chunk c, wavefront w of
-// four takes the chunk's 32-token blocks w, w+4, w+8, ... ascending and
-// keeps, per head of a group of 16, a running max m, a weight sum l and an
-// fp32 value accumulator O:
+// request's tokens form chunks of kMlaChunk.  Within chunk c the 32-token
+// blocks are taken in ascending order, with one running max m, weight sum l
+// and fp32 value accumulator O per head of a group of 16:
 //   S^T = K . Q^T        16x16x32 bf16 MFMA, tokens as rows, heads as
-//                        columns, Dqk in ascending 32-wide chunks; times scale;
+//                        columns; Dqk in two parts (32-wide chunks 0 ..
+//                        KC/2 - 1 and KC/2 .. KC - 1), each an ascending
+//                        MFMA chain from zero, added part 0 + part 1; times
+//                        scale;
 //   m' = max(m, block max);  alpha = exp2((m - m') * log2 e);
 //   p_t = exp2((s_t - m') * log2 e)  (hardware exp2; 0 past L_b);
-//   l = alpha * l + the lane's p_t in a fixed order;
+//   l = alpha * l + the lane's p_t in a fixed order (a head's four lane
+//                        sums added in a fixed butterfly at the chunk's end);
 //   O^T = alpha * O^T + V^T . P_hi^T + V^T . P_lo^T, where P_hi = bf16(p)
 //                        and P_lo = bf16(p - P_hi) (the pair carries p to
 //                        about 2^-18 relative), V^T transposed in registers.
-// The four waves' (m, l, O) are merged in wave order with the factors
-// exp2((m_w - M) * log2 e), M the largest m_w, giving the chunk's
-// (m_c, l_c, O_c).  The chunks are folded in ascending order (fold_head,
-// fold_elem) and o = bf16_rne(O / l).  Either one workgroup per (request,
-// head group) walks all chunks and folds them in LDS, or, given a workspace,
-// one workgroup per chunk writes (m_c, l_c, O_c) and mla_fold_kernel folds
-// them: the same operations, so the same bits.
+// That gives the chunk's (m_c, l_c, O_c).  The chunks are folded in
+// ascending order (fold_head, fold_elem) and o = bf16_rne(O / l).  Either
+// one workgroup per (request, head group) walks all chunks and folds them
+// in registers, or, given a workspace, one workgroup per chunk writes
+// (m_c, l_c, O_c) and mla_fold_kernel folds them: the same operations, so
+// the same bits.  A workgroup has four computing wavefronts (wavefront w
+// takes score part w >> 1 of token half w & 1 and value dims 128 w ..) and
+// four copying wavefronts that stream the blocks into a ring of LDS buffers
+// by LDS DMA, two barriers per block.
 
 // VALU kernel (other shapes): one workgroup per (request, head); one thread
 // per token computes the score as an fp32 fma chain over d ascending, the
@@ -50,6 +55,14 @@ __device__ __forceinline__ uint32_t to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
+}
+
+// Two floats rounded to bf16 (nearest even), packed low then high: the
+// hardware conversion.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -165,7 +178,8 @@ __global__ __launch_bounds__(kNT) void mla_valu_kernel(MlaArgs a) {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kNW = 4;                    // wavefronts per workgroup (MFMA kernel)
+constexpr int kNW = 4;                    // computing wavefronts per workgroup (MFMA kernel)
+constexpr int kNCopy = 4;                 // copying wavefronts per workgroup (MFMA kernel)
 constexpr int kQStride = kMlaMaxDqk + 8;  // LDS row of Q, padded: 16 rows conflict-free
 
 constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range: loads read zeros
@@ -197,17 +211,85 @@ __device__ __forceinline__ float fold_elem(int c, float o_c, float os, float fa,
     return c == 0 ? o_c : __builtin_fmaf(o_c, fb, os * fa);
 }
 
+// LDS geometry of the MFMA kernel for KC: a staged 32-token block is 32 rows
+// of 4 KC 16-byte chunks (Dqk padded to 32 KC; zeros past Dqk), unpadded,
+// with chunk c of row r at slot c ^ (r & 7) of the row, so that the 16 rows
+// a fragment read touches spread over the banks.  The block is one
+// contiguous range of the cache, copied as 2 KC 1 KB LDS-DMA pieces.
+template <int KC>
+struct MlaStage {
+    static constexpr int CPR = 4 * KC;            // 16-byte chunks per row
+    static constexpr int ROWB = 16 * CPR;         // bytes per row
+    static constexpr int BUF = 32 * ROWB;         // one 32-token block
+    static constexpr int PIECES = BUF / 1024;     // LDS-DMA instructions per block
+    static constexpr int NBUF = 4;                // ring of blocks: three in flight
+    static constexpr int PW = PIECES / kNCopy;    // pieces per copying wavefront and block
+    static constexpr int PA = PW / 3;             // of them issued while the scores run
+    static constexpr int KH = KC / 2;             // score chunks per computing wavefront
+    static_assert(CPR % 8 == 0 && BUF % 1024 == 0 && PIECES % kNCopy == 0 && KC % 2 == 0,
+                  "whole swizzle groups, pieces and score halves");
+};
+__device__ __forceinline__ uint32_t mla_slot(int row, int c) { return (uint32_t)(c ^ (row & 7)) * 16u; }
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16v(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4_t lds16(const char *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+// Wait until at most n (0, 1 or 2) blocks of PER LDS-DMA instructions each
+// are still in flight from this wavefront.
+template <int PER>
+__device__ __forceinline__ void wait_blocks(int n) {
+    if (n >= 2) gemm_detail::wait_vmcnt<2 * PER>();
+    else if (n == 1) gemm_detail::wait_vmcnt<PER>();
+    else gemm_detail::wait_vmcnt<0>();
+}
+constexpr int kScoreAhead = 4;  // score fragments in flight
+// The largest x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane
+// groups of one MFMA column), by lane swaps between the 16- and 32-lane
+// halves (max is exact and symmetric, so the order does not matter).
+__device__ __forceinline__ float max_lane_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int KC, int VB>
-__global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t qs[16 * kQStride];
-    __shared__ float ob[VB * 128][17];  // this chunk's merged O^T: [dim][head], padded
-    __shared__ float os[VB * 128][17];  // the running fold over chunks (one-workgroup path)
-    __shared__ float mred[kNW][16], lred[kNW][16], mch[16], lch[16], fah[16], fbh[16], Mr[16], Lr[16];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__global__ __launch_bounds__((kNW + kNCopy) * 64, 1) void mla_mfma_kernel(MlaArgs a) {
+    using S = MlaStage<KC>;
+    constexpr int NB = S::NBUF, PW = S::PW, PA = S::PA;
+    constexpr int NT = (kNW + kNCopy) * 64;
+    constexpr int VBW = (VB + kNW - 1) / kNW;  // value blocks per computing wavefront
+    static_assert(2 * PW < 64, "two blocks in flight fit the vmcnt field");
+    static_assert(VB * 128 * 17 * 4 <= NB * S::BUF, "the output tile fits in the ring");
+    __shared__ __attribute__((aligned(1024))) char kvs[NB * S::BUF];
+    // partial scores: [part p][half h] at ss[2 p + h], part p over the score
+    // chunks p KH .. p KH + KH - 1
+    __shared__ __attribute__((aligned(16))) f32x4_t ss[4][64];
+    // a chunk's O^T (or the final fold), [dim][head] padded, in the ring: it
+    // is written only once every copy into the ring has landed and been read
+    float(*ob)[17] = reinterpret_cast<float(*)[17]>(kvs);
+    __shared__ float Lr[16];  // the heads' weight sums, for the output
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool copier = w >= kNW;  // wavefronts kNW.. copy, the others compute
+    const int dw = w - kNW;
     const int r16 = lane & 15, g = lane >> 4;
     const int Dqk = a.Dqk, Dv = a.Dv, H = a.H;
     const int HG = (H + 15) >> 4;
-    const int qrow = (Dqk + 31) & ~31;  // Q columns staged (zero past Dqk)
+    // Per-lane fragment offsets.  Score reads (row 16 h + r16 of a block,
+    // chunk 4 cc + g): slot (4 cc + g) ^ (r16 & 7) is byte 64 cc + koff[cc &
+    // 1] of the row.  Value reads (row 16 (k >> 2) + 4 g +
+    // m, m = k & 3; chunk 16 vb + r16, wrapped into a shorter row): byte
+    // voff[m] + 16 ROWB (k >> 2) + 256 vb of the block.
+    const int r7 = r16 & 7, kb2 = (r7 >> 2) & 1, kg = 16 * ((g ^ r7) & 3);
+    const int koff[2] = {kg + 64 * kb2, kg - 64 * kb2};
+    const int rr = (S::CPR < 16 ? r16 & 7 : r16) ^ (4 * (g & 1));
+    int voff[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) voff[m] = (4 * g + m) * S::ROWB + 16 * (rr ^ m);
     // A key is a request (or a request's chunk); its head groups read the same
     // cache rows.  Units are ordered so that a key's head groups get the same
     // unit index mod 8 -- the same XCD, and so one L2, when the grid is a
@@ -221,201 +303,289 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
         const int64_t key = grp * 8 + (r & 7);
         if (key >= keys) continue;  // padding of the last group of 8 keys (uniform per workgroup)
         const int hg = r >> 3;
-        const int b = (int)(key / ncu), h0 = hg * 16;
+        // (chunks key: chunk key / B of request key % B, so that the first
+        // chunks, the longest, come first)
+        const int b = (int)(a.ws ? key % a.B : key), h0 = hg * 16;
         int L = a.lens[b];
         L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
         const int nc = (L + kMlaChunk - 1) / kMlaChunk;
-        const int c0 = a.ws ? (int)(key % ncu) : 0, c1 = a.ws ? c0 + 1 : nc;
+        const int c0 = a.ws ? (int)(key / a.B) : 0, c1 = a.ws ? c0 + 1 : nc;
         if (c0 >= nc && a.ws) continue;  // a chunk past the request's end (uniform per workgroup)
         const uint16_t *kvb = static_cast<const uint16_t *>(a.kv) + (int64_t)b * a.Lmax * Dqk;
         const uint16_t *qb = static_cast<const uint16_t *>(a.q) + ((int64_t)b * H + h0) * Dqk;
 
-        __syncthreads();  // the previous unit's readers of qs, ob, os and the head arrays are done
-        for (int i = tid; i < 16 * (qrow >> 3); i += kNW * 64) {
-            const int h = i / (qrow >> 3), d = (i % (qrow >> 3)) * 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (h0 + h < H && d < Dqk) v = *reinterpret_cast<const uint4 *>(qb + (int64_t)h * Dqk + d);
-            *reinterpret_cast<uint4 *>(qs + h * kQStride + d) = v;
+        __syncthreads();  // the previous unit's readers of the LDS are done
+        // the score B fragments of computing wavefront w: head r16, dims
+        // 32 cc + 8 g .. + 7 for its chunks cc = (w >> 1) KH + i (zeros past
+        // Dqk or H); their loads overlap the first copies
+        u32x4_t qreg[S::KH];
+        if (!copier) {
+#pragma unroll
+            for (int i = 0; i < S::KH; ++i) {
+                const int d = 32 * ((w >> 1) * S::KH + i) + 8 * g;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (h0 + r16 < H && d < Dqk) v = *reinterpret_cast<const uint4 *>(qb + (int64_t)r16 * Dqk + d);
+                qreg[i] = u32x4_t{v.x, v.y, v.z, v.w};
+            }
         }
-        __syncthreads();
 
         const int nblk = (L + 31) >> 5;
         // the request's L cached rows; rows at or past L read as zeros
-        const gemm_detail::i32x4 rkv = gemm_detail::make_rsrc(kvb, (uint32_t)L * (uint32_t)Dqk * 2u);
-        for (int c = c0; c < c1; ++c) {
-            f32x4_t o[VB][8];
+        gemm_detail::i32x4 rkv = gemm_detail::make_rsrc(kvb, (uint32_t)L * (uint32_t)Dqk * 2u);
+        rkv.x = __builtin_amdgcn_readfirstlane(rkv.x);
+        rkv.y = __builtin_amdgcn_readfirstlane(rkv.y);
+        rkv.z = __builtin_amdgcn_readfirstlane(rkv.z);
+        rkv.w = __builtin_amdgcn_readfirstlane(rkv.w);
+        // pieces dw + kNCopy j, J0 <= j < J1, of block kb into buffer bi by
+        // LDS DMA (copying wavefronts): lane l of piece i lands at position
+        // 64 i + l of the block, row p / CPR, slot p % CPR, and reads its
+        // chunk's bytes
+        auto stage = [&](auto j0c, auto j1c, int kb, int bi) {
+            constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
+            char *dst = kvs + bi * S::BUF + 1024 * dw;
+            // recomputed per call (kept out of the loop-invariant registers)
+            int p0 = 64 * dw + lane;
+            asm volatile("" : "+v"(p0));
+            const int tb = kb * 32 * Dqk * 2;
 #pragma unroll
-            for (int vb = 0; vb < VB; ++vb)
+            for (int j = J0; j < J1; ++j) {
+                const int pos = p0 + 64 * kNCopy * j;
+                const int row = pos / S::CPR, slot = pos - row * S::CPR;
+                const int c = slot ^ (row & 7);
+                const int off = tb + row * Dqk * 2 + 16 * c;
+                bi_raw_buffer_load_lds(rkv, (__attribute__((address_space(3))) uint32_t *)(dst + 1024 * kNCopy * j), 16,
+                                       16 * c < Dqk * 2 ? off : kOutOfRange, 0, 0, 0);
+            }
+        };
+        using C0 = std::integral_constant<int, 0>;
+        using CA = std::integral_constant<int, PA>;
+        using CW = std::integral_constant<int, PW>;
+
+        // this wavefront's running fold over chunks (one-workgroup path):
+        // O in os_r, the head's (M, L) in Mh, Lh (every computing lane of a
+        // head holds the same values)
+        f32x4_t os_r[VBW][8];
+        float Mh = 0.f, Lh = 0.f;
+        // the unit's blocks kbu0 .. kbu_end - 1 (its chunks' blocks in order)
+        // stream through the ring without a break: block kb in buffer
+        // (kb - kbu0) % NB
+        const int kbu0 = c0 * (kMlaChunk / 32), kbu_end = min(nblk, c1 * (kMlaChunk / 32));
+        if (kbu_end > kbu0) {
+            // the first two blocks, then the wait for the first; the rest of
+            // the ring fills in the first block's two phases (an earlier
+            // unit's stores are out of the count first)
+            if (copier) {
+                gemm_detail::wait_vmcnt<0>();
+                stage(C0{}, CW{}, kbu0, 0);
+                if (kbu0 + 1 < kbu_end) {
+                    stage(C0{}, CW{}, kbu0 + 1, 1);
+                    wait_blocks<PW>(1);
+                } else {
+                    wait_blocks<PW>(0);
+                }
+            }
+            gemm_detail::lds_barrier();  // block kbu0 is in LDS
+        }
+        // the blocks in ascending order, two barriers each (the copying and
+        // the computing wavefronts run loops of their own with the same
+        // barriers): computing wavefront w takes part w >> 1 of the scores
+        // of half w & 1, and value blocks w, w + kNW, ...; the copying
+        // wavefronts copy block kb + NB - 1 in two parts, one beside the
+        // scores, one beside the values
+        if (copier) {
+            static_assert(NB == 4, "the first block's phases fill the ring");
+            for (int kb = kbu0; kb < kbu_end; ++kb) {
+                const int bn = (kb - kbu0 + NB - 1) % NB;
+                const bool more = kb + NB - 1 < kbu_end;
+                if (kb == kbu0) {
+                    if (kbu0 + 2 < kbu_end) stage(C0{}, CW{}, kbu0 + 2, 2);
+                } else if (more) {
+                    stage(C0{}, CA{}, kb + NB - 1, bn);
+                }
+                gemm_detail::lds_barrier();
+                // the rest; then block kb + 1 has landed (the blocks after it
+                // may still be in flight)
+                if (kb == kbu0) {
+                    if (more) stage(C0{}, CW{}, kb + NB - 1, bn);
+                } else if (more) {
+                    stage(CA{}, CW{}, kb + NB - 1, bn);
+                }
+                wait_blocks<PW>(max(0, min(kbu_end - 1, kb + NB - 1) - (kb + 1)));
+                gemm_detail::lds_barrier();
+            }
+        } else {
+            for (int c = c0; c < c1; ++c) {
+                f32x4_t o[VBW][8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) o[vb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            float m_run = -INFINITY, l_part = 0.f;
-            const int kb_end = min(nblk, (c + 1) * (kMlaChunk / 32));
-            for (int kb = c * (kMlaChunk / 32) + w; kb < kb_end; kb += kNW) {
-                const int t0 = kb * 32;
-                // scores: lane holds tokens t0 + 16hb + 4g + i of head r16
-                f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-                uint4 kk[2][KC];
+                for (int vi = 0; vi < VBW; ++vi)
 #pragma unroll
-                for (int hb = 0; hb < 2; ++hb) {
-                    const int t = t0 + 16 * hb + r16;
+                    for (int j = 0; j < 8; ++j) o[vi][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                float m_run = -INFINITY, l_part = 0.f;
+                const int kb0 = c * (kMlaChunk / 32), kb_end = min(nblk, (c + 1) * (kMlaChunk / 32));
+                for (int kb = kb0; kb < kb_end; ++kb) {
+                    const char *kbase = kvs + ((kb - kbu0) % NB) * S::BUF;
+                    const int t0 = kb * 32;
+                    // this wavefront's first value block: lane (r16, g) reads
+                    // tokens 16 (k >> 2) + 4 g + (k & 3), chunk 16 vb + r16
+                    // (wrapped into the row where the block has fewer chunks:
+                    // rows past Dv)
+                    u32x4_t vv[8];
+                    if (w < VB) {
 #pragma unroll
-                    for (int cc = 0; cc < KC; ++cc) {
-                        const int d = 32 * cc + 8 * g;
-                        kk[hb][cc] = rload16(rkv, d < Dqk ? (t * Dqk + d) * 2 : kOutOfRange);
+                        for (int k = 0; k < 8; ++k) vv[k] = lds16(kbase + voff[k & 3] + 16 * S::ROWB * (k >> 2) + 256 * w);
                     }
-                }
-                // the first value block's loads go out before the score MFMAs
-                uint32_t wv0[8][4];
+                    {
+                        // part w >> 1 of S^T half w & 1: lane (token r16 of the
+                        // half, group g), chunks c0s .. c0s + KH - 1 ascending;
+                        // the K fragment of a chunk read kScoreAhead - 1 ahead
+                        f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        const char *krow = kbase + (16 * (w & 1) + r16) * S::ROWB;
+                        const int c0s = (w >> 1) * S::KH;
+                        u32x4_t kf[kScoreAhead];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
-                    const uint4 v = rload16(rkv, 8 * r16 < Dv ? (t * Dqk + 8 * r16) * 2 : kOutOfRange);
-                    wv0[k][0] = v.x; wv0[k][1] = v.y; wv0[k][2] = v.z; wv0[k][3] = v.w;
-                }
-                // each Q chunk is read from LDS once and feeds both halves' chains
+                        for (int i = 0; i < kScoreAhead - 1 && i < S::KH; ++i)
+                            kf[i] = lds16(krow + koff[(c0s + i) & 1] + 64 * (c0s + i));
 #pragma unroll
-                for (int cc = 0; cc < KC; ++cc) {
-                    const uint4 qq = *reinterpret_cast<const uint4 *>(qs + r16 * kQStride + 32 * cc + 8 * g);
-                    sacc[0] = mfma16(kk[0][cc], qq, sacc[0]);
-                    sacc[1] = mfma16(kk[1][cc], qq, sacc[1]);
-                }
-                float sv[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
-                    sv[k] = t < L ? sacc[k >> 2][k & 3] * a.scale : -INFINITY;
-                }
-                float bm = sv[0];
-#pragma unroll
-                for (int k = 1; k < 8; ++k) bm = fmaxf(bm, sv[k]);
-                bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-                bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-                const float m_new = fmaxf(m_run, bm);  // finite: token t0 < L is in the block
-                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-                m_run = m_new;
-                float pv[8];
-                l_part *= alpha;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    pv[k] = __builtin_amdgcn_exp2f((sv[k] - m_new) * kLog2e);
-                    l_part += pv[k];
-                }
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t h0b = to_bf16_rne(pv[2 * q]), h1b = to_bf16_rne(pv[2 * q + 1]);
-                    const uint32_t l0b = to_bf16_rne(pv[2 * q] - __uint_as_float(h0b << 16));
-                    const uint32_t l1b = to_bf16_rne(pv[2 * q + 1] - __uint_as_float(h1b << 16));
-                    hi[q] = h0b | (h1b << 16);
-                    lo[q] = l0b | (l1b << 16);
-                }
-                const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-                const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-#pragma unroll
-                for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) o[vb][j] *= alpha;
-                // values: lane loads its group's 8 tokens x 8 dims (128 vb + 8 r16 ..);
-                // block vb + 1's loads go out before block vb's MFMAs
-                uint32_t wcur[8][4];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) wcur[k][e] = wv0[k][e];
-#pragma unroll
-                for (int vb = 0; vb < VB; ++vb) {
-                    uint32_t wnext[8][4];
-                    if (vb + 1 < VB) {
-                        const int dn = 128 * (vb + 1) + 8 * r16;
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            const int t = t0 + 16 * (k >> 2) + 4 * g + (k & 3);
-                            const uint4 v = rload16(rkv, dn < Dv ? (t * Dqk + dn) * 2 : kOutOfRange);
-                            wnext[k][0] = v.x; wnext[k][1] = v.y; wnext[k][2] = v.z; wnext[k][3] = v.w;
+                        for (int i = 0; i < S::KH; ++i) {
+                            const int in = i + kScoreAhead - 1;
+                            if (in < S::KH) kf[in % kScoreAhead] = lds16(krow + koff[(c0s + in) & 1] + 64 * (c0s + in));
+                            __builtin_amdgcn_sched_barrier(0);  // keeps the reads this far ahead
+                            sacc = mfma16v(kf[i % kScoreAhead], qreg[i], sacc);
                         }
+                        ss[w][lane] = sacc;
                     }
+                    gemm_detail::lds_barrier();  // the partial scores are in LDS
+                    // half h: part 0 + part 1; tokens at or past L weigh 0
+                    const f32x4_t sraw[2] = {ss[0][lane] + ss[2][lane], ss[1][lane] + ss[3][lane]};
+                    float sv[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        // V^T row (dim 128 vb + 8 r16 + j) over the 8 tokens, in the order of pv
-                        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                        const int wd = j >> 1;
-                        const uint4 av = make_uint4(__builtin_amdgcn_perm(wcur[1][wd], wcur[0][wd], sel),
-                                                    __builtin_amdgcn_perm(wcur[3][wd], wcur[2][wd], sel),
-                                                    __builtin_amdgcn_perm(wcur[5][wd], wcur[4][wd], sel),
-                                                    __builtin_amdgcn_perm(wcur[7][wd], wcur[6][wd], sel));
-                        o[vb][j] = mfma16(av, phi, o[vb][j]);
-                        o[vb][j] = mfma16(av, plo, o[vb][j]);
-                    }
-                    if (vb + 1 < VB) {
+                    for (int k = 0; k < 8; ++k) sv[k] = sraw[k >> 2][k & 3] * a.scale;
+                    if (t0 + 32 > L) {
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) wcur[k][e] = wnext[k][e];
+                            if (t0 + 16 * (k >> 2) + 4 * g + (k & 3) >= L) sv[k] = -INFINITY;
                     }
+                    float bm = sv[0];
+#pragma unroll
+                    for (int k = 1; k < 8; ++k) bm = fmaxf(bm, sv[k]);
+                    bm = max_lane_groups(bm);
+                    const float m_new = fmaxf(m_run, bm);  // finite: token t0 < L is in the block
+                    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+                    m_run = m_new;
+                    float pv[8];
+                    l_part *= alpha;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        pv[k] = __builtin_amdgcn_exp2f((sv[k] - m_new) * kLog2e);
+                        l_part += pv[k];
+                    }
+                    // P_hi = bf16(p), P_lo = bf16(p - P_hi), round to nearest even
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        hi[q] = bf16_pair(pv[2 * q], pv[2 * q + 1]);
+                        lo[q] = bf16_pair(pv[2 * q] - __uint_as_float(hi[q] << 16),
+                                          pv[2 * q + 1] - __uint_as_float(hi[q] & 0xFFFF0000u));
+                    }
+                    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                    // values (dims past Dv compute rows that are never stored)
+#pragma unroll
+                    for (int vi = 0; vi < VBW; ++vi) {
+                        const int vb = w + kNW * vi;
+                        if (vb >= VB) break;
+                        // (a factor of 1 in every lane, the common case once
+                        // the maximum settles, leaves O as it is)
+                        if (__any(alpha != 1.f)) {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) o[vi][j] *= alpha;
+                        }
+                        if (vi > 0) {
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) vv[k] = lds16(kbase + voff[k & 3] + 16 * S::ROWB * (k >> 2) + 256 * vb);
+                        }
+                        uint32_t wcur[8][4];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            wcur[k][0] = vv[k].x; wcur[k][1] = vv[k].y; wcur[k][2] = vv[k].z; wcur[k][3] = vv[k].w;
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            // V^T row (dim 128 vb + 8 r16 + j) over the 8 tokens, in the order of pv
+                            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                            const int wd = j >> 1;
+                            const uint4 av = make_uint4(__builtin_amdgcn_perm(wcur[1][wd], wcur[0][wd], sel),
+                                                        __builtin_amdgcn_perm(wcur[3][wd], wcur[2][wd], sel),
+                                                        __builtin_amdgcn_perm(wcur[5][wd], wcur[4][wd], sel),
+                                                        __builtin_amdgcn_perm(wcur[7][wd], wcur[6][wd], sel));
+                            o[vi][j] = mfma16(av, phi, o[vi][j]);
+                            o[vi][j] = mfma16(av, plo, o[vi][j]);
+                        }
+                    }
+                    // every wavefront is done with this block's buffer (which
+                    // block kb + NB reuses) and with the scores; block kb + 1
+                    // has landed
+                    gemm_detail::lds_barrier();
                 }
-            }
 
-            // merge the chunk's waves in wave order (the chunk holds token c * chunk < L)
-            float lw = l_part;
-            lw += __shfl_xor(lw, 16, 64);
-            lw += __shfl_xor(lw, 32, 64);
-            if (g == 0) {
-                mred[w][r16] = m_run;
-                lred[w][r16] = lw;
-            }
-            __syncthreads();
-            float M = mred[0][r16];
+                // the chunk's (m_c, l_c, O_c): every computing wavefront holds
+                // the same m and l, its O^T rows are its value blocks' dims
+                float lw = l_part;
+                lw += __shfl_xor(lw, 16, 64);
+                lw += __shfl_xor(lw, 32, 64);
+                if (a.ws) {
+                    // this chunk's partial m[16], l[16], O[16][Dv], from the
+                    // registers: lane (r16, g) holds head r16's dims 128 vb +
+                    // 32 g + 8 i + j at o[vi][j][i]
+                    float *pw = a.ws + (((int64_t)b * HG + hg) * ncu + c) * (32 + 16 * (int64_t)Dv);
+                    if (w == 0 && g == 0) {
+                        pw[r16] = m_run;
+                        pw[16 + r16] = lw;
+                    }
 #pragma unroll
-            for (int v = 1; v < kNW; ++v) M = fmaxf(M, mred[v][r16]);
-            const float f = __builtin_amdgcn_exp2f((m_run - M) * kLog2e);
-            if (tid < 16) {
-                float lt = __builtin_amdgcn_exp2f((mred[0][tid] - M) * kLog2e) * lred[0][tid];
+                    for (int vi = 0; vi < VBW; ++vi) {
+                        const int vb = w + kNW * vi;
+                        if (vb >= VB) break;
 #pragma unroll
-                for (int v = 1; v < kNW; ++v)
-                    lt = __builtin_fmaf(__builtin_amdgcn_exp2f((mred[v][tid] - M) * kLog2e), lred[v][tid], lt);
-                mch[tid] = M;
-                lch[tid] = lt;
-            }
-            for (int v = 0; v < kNW; ++v) {
-                if (w == v) {
+                        for (int i = 0; i < 4; ++i) {
+                            const int d = 128 * vb + 32 * g + 8 * i;
+                            if (d >= Dv) continue;
+                            float4 *dst = reinterpret_cast<float4 *>(pw + 32 + (int64_t)r16 * Dv + d);
+                            dst[0] = make_float4(o[vi][0][i], o[vi][1][i], o[vi][2][i], o[vi][3][i]);
+                            dst[1] = make_float4(o[vi][4][i], o[vi][5][i], o[vi][6][i], o[vi][7][i]);
+                        }
+                    }
+                } else {
+                    // the fold, in the lanes
+                    float fa, fb;
+                    fold_head(c, m_run, lw, Mh, Lh, fa, fb);
 #pragma unroll
-                    for (int vb = 0; vb < VB; ++vb)
+                    for (int vi = 0; vi < VBW; ++vi)
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                float &dst = ob[128 * vb + 8 * (4 * g + i) + j][r16];
-                                dst = v == 0 ? f * o[vb][j][i] : __builtin_fmaf(f, o[vb][j][i], dst);
-                            }
+                            for (int i = 0; i < 4; ++i)
+                                os_r[vi][j][i] = fold_elem(c, o[vi][j][i], os_r[vi][j][i], fa, fb);
                 }
-                __syncthreads();
-            }
-            if (a.ws) {
-                // this chunk's partial: m[16], l[16], O[Dv][16]
-                float *pw = a.ws + (((int64_t)b * HG + hg) * ncu + c) * (32 + 16 * (int64_t)Dv);
-                if (tid < 16) {
-                    pw[tid] = mch[tid];
-                    pw[16 + tid] = lch[tid];
-                }
-                for (int i = tid; i < 16 * Dv; i += kNW * 64) pw[32 + i] = ob[i >> 4][i & 15];
-            } else {
-                if (tid < 16) {
-                    float Mh = Mr[tid], Lh = Lr[tid], fa, fb;
-                    fold_head(c, mch[tid], lch[tid], Mh, Lh, fa, fb);
-                    Mr[tid] = Mh; Lr[tid] = Lh; fah[tid] = fa; fbh[tid] = fb;
-                }
-                __syncthreads();
-                for (int i = tid; i < 16 * Dv; i += kNW * 64) {
-                    const int d = i >> 4, h = i & 15;
-                    os[d][h] = fold_elem(c, ob[d][h], os[d][h], fah[h], fbh[h]);
-                }
-                __syncthreads();
             }
         }
         if (a.ws) continue;
-        // out[b][h0 + h][8c .. 8c + 7]
+        // the fold into ob, then out[b][h0 + h][8c .. 8c + 7]
+        if (L > 0) {
+            if (w == 0 && g == 0) Lr[r16] = Lh;
+#pragma unroll
+            for (int vi = 0; vi < VBW; ++vi) {
+                const int vb = w + kNW * vi;
+                if (vb >= VB) break;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ob[128 * vb + 8 * (4 * g + i) + j][r16] = os_r[vi][j][i];
+            }
+        }
+        __syncthreads();
         uint16_t *ob_out = static_cast<uint16_t *>(a.out) + ((int64_t)b * H + h0) * Dv;
-        for (int i = tid; i < 16 * (Dv >> 3); i += kNW * 64) {
+        for (int i = tid; i < 16 * (Dv >> 3); i += NT) {
             const int h = i / (Dv >> 3), cq = i % (Dv >> 3);
             if (h0 + h >= H) continue;
             uint32_t r[4] = {0u, 0u, 0u, 0u};
@@ -423,38 +593,66 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_mfma_kernel(MlaArgs a) {
                 const float l = Lr[h];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    r[q] = to_bf16_rne(os[8 * cq + 2 * q][h] / l) | (to_bf16_rne(os[8 * cq + 2 * q + 1][h] / l) << 16);
+                    r[q] = to_bf16_rne(ob[8 * cq + 2 * q][h] / l) | (to_bf16_rne(ob[8 * cq + 2 * q + 1][h] / l) << 16);
             }
             *reinterpret_cast<uint4 *>(ob_out + (int64_t)h * Dv + 8 * cq) = make_uint4(r[0], r[1], r[2], r[3]);
         }
     }
 }
 
-// The fold of the chunk partials, one thread per output element (request,
-// head group, dim, head): it folds chunks 0, 1, ... of its head in order,
-// recomputing the head's scalars by the same operations.
+// The fold of the chunk partials, one thread per four output elements
+// (request, head group, head, dims 4q .. 4q + 3): it folds chunks 0, 1, ...
+// of its head in order, recomputing the head's scalars by the same
+// operations; the partials of up to kFoldBatch chunks are loaded before
+// they are folded.
+constexpr int kFoldBatch = 8;
 __global__ __launch_bounds__(256) void mla_fold_kernel(MlaArgs a) {
-    const int Dv = a.Dv, H = a.H, HG = (H + 15) >> 4;
-    const int64_t per = 16 * (int64_t)Dv;
+    const int Dv = a.Dv, H = a.H, HG = (H + 15) >> 4, DQ = Dv >> 2;
+    const int64_t per = 16 * (int64_t)DQ;
     const int64_t total = (int64_t)a.B * HG * per;
-    const int64_t pstride = 32 + per;
+    const int64_t pstride = 32 + 16 * (int64_t)Dv;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
         const int64_t u = idx / per;
         const int i = (int)(idx - u * per);
-        const int d = i >> 4, h = i & 15;
+        const int h = i / DQ, d = 4 * (i - h * DQ);
         const int b = (int)(u / HG), h0 = (int)(u % HG) * 16;
         if (h0 + h >= H) continue;
         int L = a.lens[b];
         L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
         const int nc = (L + kMlaChunk - 1) / kMlaChunk;
         const float *pw = a.ws + u * a.nchunk * pstride;
-        float M = 0.f, Ls = 0.f, Os = 0.f, fa, fb;
-        for (int c = 0; c < nc; ++c) {
-            const float *pc = pw + c * pstride;
-            fold_head(c, pc[h], pc[16 + h], M, Ls, fa, fb);
-            Os = fold_elem(c, pc[32 + i], Os, fa, fb);
+        float M = 0.f, Ls = 0.f, Os[4] = {0.f, 0.f, 0.f, 0.f}, fa, fb;
+        for (int cb = 0; cb < nc; cb += kFoldBatch) {
+            float mv[kFoldBatch], lv[kFoldBatch];
+            float4 ov[kFoldBatch];
+#pragma unroll
+            for (int k = 0; k < kFoldBatch; ++k) {
+                if (cb + k < nc) {
+                    const float *pc = pw + (cb + k) * pstride;
+                    mv[k] = pc[h];
+                    lv[k] = pc[16 + h];
+                    ov[k] = *reinterpret_cast<const float4 *>(pc + 32 + (int64_t)h * Dv + d);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kFoldBatch; ++k) {
+                if (cb + k < nc) {
+                    const int c = cb + k;
+                    fold_head(c, mv[k], lv[k], M, Ls, fa, fb);
+                    Os[0] = fold_elem(c, ov[k].x, Os[0], fa, fb);
+                    Os[1] = fold_elem(c, ov[k].y, Os[1], fa, fb);
+                    Os[2] = fold_elem(c, ov[k].z, Os[2], fa, fb);
+                    Os[3] = fold_elem(c, ov[k].w, Os[3], fa, fb);
+                }
+            }
         }
-        static_cast<uint16_t *>(a.out)[((int64_t)b * H + h0 + h) * Dv + d] = (uint16_t)(nc > 0 ? to_bf16_rne(Os / Ls) : 0u);
+        uint32_t r[2] = {0u, 0u};
+        if (nc > 0) {
+            r[0] = to_bf16_rne(Os[0] / Ls) | (to_bf16_rne(Os[1] / Ls) << 16);
+            r[1] = to_bf16_rne(Os[2] / Ls) | (to_bf16_rne(Os[3] / Ls) << 16);
+        }
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + ((int64_t)b * H + h0 + h) * Dv + d) =
+            make_uint2(r[0], r[1]);
     }
 }
 
@@ -512,9 +710,9 @@ hipError_t launch_mla_decode(const MlaArgs &a, int grid, int fold_grid, hipStrea
     if (v) {
         if (a.ws && (a.nchunk < 1 || fold_grid < 1)) return hipErrorInvalidValue;
         switch (v) {
-            case 1: hipLaunchKernelGGL((mla_mfma_kernel<18, 4>), dim3(grid), dim3(kNW * 64), 0, st, a); break;
-            case 2: hipLaunchKernelGGL((mla_mfma_kernel<4, 1>), dim3(grid), dim3(kNW * 64), 0, st, a); break;
-            default: hipLaunchKernelGGL((mla_mfma_kernel<2, 1>), dim3(grid), dim3(kNW * 64), 0, st, a); break;
+            case 1: hipLaunchKernelGGL((mla_mfma_kernel<18, 4>), dim3(grid), dim3((kNW + kNCopy) * 64), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((mla_mfma_kernel<4, 1>), dim3(grid), dim3((kNW + kNCopy) * 64), 0, st, a); break;
+            default: hipLaunchKernelGGL((mla_mfma_kernel<2, 1>), dim3(grid), dim3((kNW + kNCopy) * 64), 0, st, a); break;
         }
         if (a.ws) {
             hipError_t e = hipGetLastError();
