@@ -79,6 +79,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     p.add_argument("--only-step", action="store_true", help="run the timed steps only (for profiler passes)")
+    p.add_argument("--only-mla", action="store_true",
+                   help="run the MLA decode next-row workload only (workspace schedule; for profiler passes)")
     p.add_argument("--calib", action="store_true",
                    help="after the steps, read 512 MiB three times and copy 512 MiB three times "
                         "(counter calibration)")
@@ -211,6 +213,39 @@ def summarize(dirs, out, command, kernel):
 
 # ------------------------------------------------------------------ main
 
+def mla_only(args, B, inputs, np, torch, dev):
+    """The MLA decode next row's workload (64 requests of 1024-4096 tokens,
+    16 heads, 576/512, with the workspace), the same seeded inputs as the
+    sweep, called `steps` times after `warmup` calls; one JSON line with the
+    mean of HIP events around the timed calls."""
+    gen = torch.Generator(device=dev)
+
+    def randn(shape, std, seed):
+        gen.manual_seed(seed)
+        return torch.randn(shape, generator=gen, device=dev).mul_(std).to(torch.bfloat16)
+
+    Bq, Hq, Dqk, Dv, Lmx = 64, 16, 576, 512, 4096
+    lens_np = inputs.rng(12345, 21).integers(1024, Lmx + 1, Bq).astype(np.int32)
+    qa = randn((Bq, Hq, Dqk), 1.0, 90)
+    kva = randn((Bq, Lmx, Dqk), 1.0, 91)
+    lens_d = torch.from_numpy(lens_np).to(dev)
+    wsa = torch.empty(B.mla_decode_workspace_size(Bq, Hq, Lmx, Dqk, Dv), dtype=torch.uint8, device=dev)
+    sc = 1.0 / 192 ** 0.5
+    oa = B.bi_mla_decode(qa, kva, lens_d, sc, Dv, workspace=wsa)
+    for _ in range(args.warmup):
+        B.bi_mla_decode(qa, kva, lens_d, sc, Dv, oa, workspace=wsa)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        B.bi_mla_decode(qa, kva, lens_d, sc, Dv, oa, workspace=wsa)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    print(json.dumps({"metric": "mla_decode", "us_per_call": round(us, 2), "tokens": int(lens_np.sum()),
+                      "GB/s": round((2.0 * int(lens_np.sum()) * Dqk) / (us * 1e-6) / 1e9, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -231,6 +266,9 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if args.only_mla:
+        mla_only(args, B, inputs, np, torch, dev)
+        return
     M = args.m
     Mb = min(M, 1024)
     H, Nqkv, No, Ngu, Kdn, heads, dk, dn = 4096, 6144, 4096, 24576, 12288, 128, 128, 512
