@@ -180,14 +180,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kNW = 4;                    // computing wavefronts per workgroup (MFMA kernel)
 constexpr int kNCopy = 4;                 // copying wavefronts per workgroup (MFMA kernel)
-constexpr int kQStride = kMlaMaxDqk + 8;  // LDS row of Q, padded: 16 rows conflict-free
 
 constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range: loads read zeros
-
-// 16 bytes at byte offset `off` of the buffer `r`, or zeros past its range.
-__device__ __forceinline__ uint4 rload16(gemm_detail::i32x4 r, int off) {
-    return __builtin_bit_cast(uint4, bi_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -229,7 +223,6 @@ struct MlaStage {
     static_assert(CPR % 8 == 0 && BUF % 1024 == 0 && PIECES % kNCopy == 0 && KC % 2 == 0,
                   "whole swizzle groups, pieces and score halves");
 };
-__device__ __forceinline__ uint32_t mla_slot(int row, int c) { return (uint32_t)(c ^ (row & 7)) * 16u; }
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma16v(u32x4_t a, u32x4_t b, f32x4_t c) {

@@ -67,6 +67,36 @@ def test_mla_decode_parity_and_requests_alone(lens, H, Dqk, Dv, Lmax):
     assert len(outs) == 1
 
 
+def test_mla_decode_chunk_boundaries_and_schedules():
+    """Requests ending on, just before and just after the 1024-token chunk
+    boundaries and the 32-token block boundaries: parity; the chunked
+    schedule (workspace, first chunks first), the one-workgroup schedule
+    (its copy stream running across the chunks), both under grid caps that
+    make a workgroup take several units, and the no-allocation entry point
+    all give the same bits."""
+    lens = [1024, 1025, 2047, 2048, 2049, 3072, 32, 31, 0, 1]
+    Bn, H, Dqk, Dv, Lmax = len(lens), 16, 576, 512, 3100
+    scale = 1.0 / math.sqrt(192.0)
+    q = inputs.randn_bf16((Bn, H, Dqk), 1.0, tag=(505, Lmax))
+    kv = inputs.randn_bf16((Bn, Lmax, Dqk), 1.0, tag=(506, Lmax))
+    qd, kvd = dev(q), dev(kv)
+    note("mla_decode chunk boundaries and schedules")
+    o = host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv))
+    pick = [0, 1, 3, 4, 6, 7]
+    check_parity(o[pick], q[pick], kv[pick], [lens[i] for i in pick], scale, Dv, "mla_decode chunk boundaries")
+    assert not o[8].any()
+    ws = torch.empty(B.mla_decode_workspace_size(Bn, H, Lmax, Dqk, Dv), dtype=torch.uint8, device="cuda")
+    assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, workspace=ws)), o)
+    for mw in (1, 3, 100):
+        assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, workspace=ws,
+                                                   max_workgroups=mw)), o), mw
+    for mw in (2, 5):
+        assert np.array_equal(host(B.bi_mla_decode(qd, kvd, lens_dev(lens), scale, Dv, max_workgroups=mw)), o), mw
+    on = torch.empty((Bn, H, Dv), dtype=torch.bfloat16, device="cuda")
+    B.bi_mla_decode_noalloc(qd, kvd, lens_dev(lens), scale, Dv, on)
+    assert np.array_equal(host(on), o)
+
+
 def test_mla_decode_batch_composition_and_capacity():
     """A request's output is the same bits inside batches of other requests of
     other lengths, and whether the dense cache layout holds 4096 or 5000 rows
