@@ -182,6 +182,7 @@ constexpr int kNW = 4;                    // computing wavefronts per workgroup 
 constexpr int kNCopy = 4;                 // copying wavefronts per workgroup (MFMA kernel)
 
 constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range: loads read zeros
+constexpr int kReadOnce = 2;  // cache policy of the cache-row copies: non-temporal (each row is read once)
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -218,7 +219,7 @@ struct MlaStage {
     static constexpr int PIECES = BUF / 1024;     // LDS-DMA instructions per block
     static constexpr int NBUF = 4;                // ring of blocks: three in flight
     static constexpr int PW = PIECES / kNCopy;    // pieces per copying wavefront and block
-    static constexpr int PA = PW / 3;             // of them issued while the scores run
+    static constexpr int PA = PW / 2 + 1;         // of them issued while the scores run
     static constexpr int KH = KC / 2;             // score chunks per computing wavefront
     static_assert(CPR % 8 == 0 && BUF % 1024 == 0 && PIECES % kNCopy == 0 && KC % 2 == 0,
                   "whole swizzle groups, pieces and score halves");
@@ -347,7 +348,7 @@ __global__ __launch_bounds__((kNW + kNCopy) * 64, 1) void mla_mfma_kernel(MlaArg
                 const int c = slot ^ (row & 7);
                 const int off = tb + row * Dqk * 2 + 16 * c;
                 bi_raw_buffer_load_lds(rkv, (__attribute__((address_space(3))) uint32_t *)(dst + 1024 * kNCopy * j), 16,
-                                       16 * c < Dqk * 2 ? off : kOutOfRange, 0, 0, 0);
+                                       16 * c < Dqk * 2 ? off : kOutOfRange, 0, 0, kReadOnce);
             }
         };
         using C0 = std::integral_constant<int, 0>;
