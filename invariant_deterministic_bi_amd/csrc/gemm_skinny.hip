@@ -707,7 +707,9 @@ __global__ __launch_bounds__(512) void direct_alds_kernel(GemmArgs p) {
         } else if constexpr (NB == 8) {
             int o = w_lane + 128 * is_u;
             if (is_u >= kfull && 64 * is_u + 32 * (r >> 3) + 8 * sub >= p.K) o = kMark;
-            x0 = bi_raw_buffer_load_b128(rb, o, 0, 0);
+            // non-temporal: faster here (qkv 6144x4096 at M = 1 ... 16 by 12%,
+            // down 4096x12288 at M = 1 by 10%), slower on the other streams
+            x0 = bi_raw_buffer_load_b128(rb, o, 0, 2);
         } else {
             int o0 = w_lane + 128 * is_u, o1 = o0 + 64;
             if (is_u >= kfull) {
