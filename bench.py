@@ -428,7 +428,7 @@ def main():
         return
 
     # ---------------------------------------------------------------- ceilings
-    log("ceilings: MFMA loop and read stream")
+    log("ceilings: MFMA loop, read stream and LDS reads")
     mgrid, iters = 2 * cus, 20000
     pout = torch.empty((mgrid * B.PROBE_WAVES, 3), dtype=torch.int64, device=dev)
     runs = []
@@ -442,19 +442,30 @@ def main():
     sink = torch.empty(cus * 16 * 256, dtype=torch.int32, device=dev)
     read_gbs = rbuf.numel() / graph_us(lambda: B.bi_probe_read(rbuf, cus * 16, sink), 5) / 1e3
     del rbuf
+    lds_iters = 2000
+    lout = torch.empty((cus * B.PROBE_WAVES, 2), dtype=torch.int64, device=dev)
+    for _ in range(2):
+        B.bi_probe_lds(lds_iters, cus, lout)
+    torch.cuda.synchronize()
+    lcyc = lout.cpu().numpy()[:, 0].astype(np.float64).reshape(cus, B.PROBE_WAVES).max(axis=1)
+    lds_bpc = float(np.median(B.PROBE_WAVES * lds_iters * B.PROBE_LDS_BYTES / lcyc))
     ceilings = {"mfma_loop_tflops": round(mfma_tf, 1), "mfma_loop_clock_mhz": round(mfma_clk),
                 "mfma_loop_frac_of_spec": round(mfma_tf / PEAK_BF16_TFLOPS, 4),
                 "read_stream_2GiB_gbs": round(read_gbs, 1),
                 "read_stream_frac_of_spec": round(read_gbs / PEAK_HBM_GBS, 4),
+                "lds_read_bytes_per_cycle_per_cu": round(lds_bpc, 1),
                 "how": "bi_probe_mfma: grid 2x#CU x 8 waves x 20000 x 8 v_mfma_f32_16x16x32_bf16, median of 3, "
-                       "clock = s_memtime cycles / s_memrealtime ticks; bi_probe_read: 2 GiB, 16-byte loads, mean of 5"}
+                       "clock = s_memtime cycles / s_memrealtime ticks; bi_probe_read: 2 GiB, 16-byte loads, mean of 5; "
+                       "bi_probe_lds: #CU workgroups x 8 waves x 2000 x 16 conflict-free ds_read_b128, median over "
+                       "workgroups of 8 x 2000 x 16 KB / the workgroup's largest cycle count"}
     try:
         r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
         if r.returncode == 0:
             ceilings["amd_smi_clock"] = json.loads(r.stdout)
     except Exception:  # amd-smi missing or slow: the probe's clock stands
         pass
-    log(f"MFMA loop {mfma_tf:.0f} TFLOP/s at {mfma_clk:.0f} MHz; read stream {read_gbs:.0f} GB/s")
+    log(f"MFMA loop {mfma_tf:.0f} TFLOP/s at {mfma_clk:.0f} MHz; read stream {read_gbs:.0f} GB/s; "
+        f"LDS reads {lds_bpc:.0f} B/cycle/CU")
 
     def frac_entry(name, us, work, launches):
         nbytes, flops = work

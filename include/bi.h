@@ -492,9 +492,18 @@ bi_status bi_tile_shape(int v, bi_plan *out);
  *   16 == 0) once, with 16-byte loads from grid * 256 threads, folding them
  *   into sink (device uint32 [grid * 256], 4-byte aligned, not overlapping
  *   src).  Time it over a buffer larger than the last-level cache.
+ * bi_probe_lds: `grid` workgroups of 8 wavefronts; each fills a 64 KB LDS
+ *   buffer, then every wavefront issues iters * 16 ds_read_b128 over it
+ *   (64 consecutive 16-byte slots per instruction: no bank conflict), i.e.
+ *   iters * 16 KB per wavefront.  out: device uint64 [grid * 8 * 2], 8-byte
+ *   aligned; per wavefront: shader-clock cycles of its loop (s_memtime) and a
+ *   sink word.  8 * iters * 16 KB / (the workgroup's largest cycle count) is
+ *   the LDS read rate of one compute unit in bytes per cycle.  iters in
+ *   [1, 2^40], grid >= 1.
  */
 bi_status bi_probe_mfma(void *out, int64_t iters, int grid, void *stream);
 bi_status bi_probe_read(const void *src, int64_t bytes, void *sink, int grid, void *stream);
+bi_status bi_probe_lds(void *out, int64_t iters, int grid, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *bi_status_str(bi_status s);

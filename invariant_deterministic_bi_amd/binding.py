@@ -92,6 +92,7 @@ _SIGS = {
     "bi_tile_shape": [ctypes.c_int, ctypes.POINTER(BiPlan)],
     "bi_probe_mfma": [_p, _i64, ctypes.c_int, _p],
     "bi_probe_read": [_p, _i64, _p, ctypes.c_int, _p],
+    "bi_probe_lds": [_p, _i64, ctypes.c_int, _p],
     "bi_plan_regimes": [ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(BiRegime),
                         ctypes.c_int, ctypes.POINTER(ctypes.c_int)],
 }
@@ -445,6 +446,19 @@ def bi_probe_mfma(iters, grid, out=None, *, stream=None):
     if out is None:
         out = torch.empty((grid * PROBE_WAVES, 3), dtype=torch.int64, device="cuda")
     _raise(lib().bi_probe_mfma(_ptr(out), int(iters), int(grid), _stream(stream)), "bi_probe_mfma")
+    return out
+
+
+PROBE_LDS_BYTES = 16 * 1024  # LDS bytes one wavefront reads per iteration
+
+
+def bi_probe_lds(iters, grid, out=None, *, stream=None):
+    """LDS read loop (measurement): returns the device uint64 tensor
+    [grid * 8, 2] of (shader-clock cycles, sink) per wavefront; each
+    wavefront reads iters * 16 KB from LDS."""
+    if out is None:
+        out = torch.empty((grid * PROBE_WAVES, 2), dtype=torch.int64, device="cuda")
+    _raise(lib().bi_probe_lds(_ptr(out), int(iters), int(grid), _stream(stream)), "bi_probe_lds")
     return out
 
 

@@ -989,6 +989,16 @@ bi_status bi_probe_mfma(void *out, int64_t iters, int grid, void *stream) {
                : BI_ERR_HIP;
 }
 
+bi_status bi_probe_lds(void *out, int64_t iters, int grid, void *stream) {
+    if (iters < 1 || grid < 1 || iters > ((int64_t)1 << 40)) return BI_ERR_SHAPE;
+    if (!out) return BI_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(out) & 7u) return BI_ERR_ALIGN;
+    return bi::launch_lds_probe(static_cast<uint64_t *>(out), iters, grid, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? BI_OK
+               : BI_ERR_HIP;
+}
+
 bi_status bi_probe_read(const void *src, int64_t bytes, void *sink, int grid, void *stream) {
     if (bytes <= 0 || bytes % 16 || grid < 1) return BI_ERR_SHAPE;
     if (!src || !sink) return BI_ERR_NULL;

@@ -212,9 +212,12 @@ hipError_t mla_scratch(float **out);
 hipError_t launch_mla_decode(const MlaArgs &args, int grid, int fold_grid, hipStream_t stream);
 
 // Measurement probes (probe.hip): an MFMA-only loop (eight wavefronts per
-// workgroup; out: three uint64 per wavefront) and a 16-byte read stream
-// (256 threads per workgroup; sink: one uint32 per thread).
+// workgroup; out: three uint64 per wavefront), a 16-byte read stream (256
+// threads per workgroup; sink: one uint32 per thread) and an LDS read loop.
 hipError_t launch_mfma_probe(uint64_t *out, int64_t iters, int grid, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int grid, hipStream_t stream);
+// LDS read probe: eight wavefronts per workgroup, each issuing iters * 16
+// conflict-free ds_read_b128; out: two uint64 per wavefront (cycles, sink).
+hipError_t launch_lds_probe(uint64_t *out, int64_t iters, int grid, hipStream_t stream);
 
 }  // namespace bi

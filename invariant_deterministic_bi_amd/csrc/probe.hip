@@ -8,6 +8,9 @@
 //     clock the matrix cores actually ran at is measured, not assumed.
 //   * Read stream: 16-byte loads over a caller buffer, every byte once,
 //     folded into a per-thread XOR so no load can be dropped.
+//   * LDS read stream: every wavefront reads a 64 KB LDS buffer with 16-byte
+//     reads (ds_read_b128), consecutive lanes on consecutive 16-byte slots
+//     (no bank conflict), recording its shader-clock cycles over the loop.
 // Neither is part of the batch-invariant path; the library exports them so
 // that a benchmark can report its kernels against measured ceilings.
 
@@ -75,7 +78,41 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *src, int64
     sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+constexpr int kLdsProbeSlots = 4096;  // 16-byte slots: 64 KB
+constexpr int kLdsProbeReads = 16;    // reads per wavefront per iteration
+
+__global__ __launch_bounds__(kProbeWaves * 64, 1) void lds_probe_kernel(uint64_t *out, int64_t iters) {
+    __shared__ u32x4 buf[kLdsProbeSlots];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kLdsProbeSlots; i += kProbeWaves * 64)
+        buf[i] = u32x4{(uint32_t)i, (uint32_t)i * 3u, 7u, 9u};
+    __syncthreads();
+    u32x4 x = {0u, 0u, 0u, 0u};
+    // slot base + 256 r: base < 256, so every index is below 4096; the reads
+    // of one instruction are 64 consecutive slots
+    int base = (wave * 64 + lane) & 255;
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < kLdsProbeReads; ++r) x += buf[base + r * 256];
+        base = (base + 64) & 255;
+    }
+    // the sum is used (so no read is dropped) before the second timestamp
+    asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    if (lane == 0) {
+        uint64_t *o = out + ((int64_t)blockIdx.x * kProbeWaves + wave) * 2;
+        o[0] = t1 - t0;
+        o[1] = (uint64_t)(x.x ^ x.y ^ x.z ^ x.w);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_lds_probe(uint64_t *out, int64_t iters, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(lds_probe_kernel, dim3(grid), dim3(kProbeWaves * 64), 0, s, out, iters);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(uint64_t *out, int64_t iters, int grid, hipStream_t s) {
     hipLaunchKernelGGL(mfma_probe_kernel, dim3(grid), dim3(kProbeWaves * 64), 0, s, out, iters);

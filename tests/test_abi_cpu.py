@@ -415,3 +415,7 @@ def test_probe_validation():
     assert L.bi_probe_read(0x1008, 1024, 0x9000, 4, None) == B.BI_ERR_ALIGN
     assert L.bi_probe_read(0x1000, 1 << 20, 0x2000, 4, None) == B.BI_ERR_ALIAS
     assert L.bi_probe_read(None, 1024, 0x9000, 4, None) == B.BI_ERR_NULL
+    assert L.bi_probe_lds(None, 10, 4, None) == B.BI_ERR_NULL
+    assert L.bi_probe_lds(0x1000, 0, 4, None) == B.BI_ERR_SHAPE
+    assert L.bi_probe_lds(0x1000, 10, 0, None) == B.BI_ERR_SHAPE
+    assert L.bi_probe_lds(0x1004, 10, 4, None) == B.BI_ERR_ALIGN
