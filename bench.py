@@ -147,7 +147,9 @@ def summarize(dirs, out, command, kernel):
     -- and the ratio is reported.  traffic_bytes_per_launch is the read +
     write bytes of the dispatches of `kernel` with the largest grid.
     """
-    lines = [f"# rocprofv3 summary written by: python bench.py --summarize {' '.join(dirs)}"
+    # the profiler's output folders, named by their last component
+    lines = [f"# rocprofv3 summary written by: python bench.py --summarize "
+             f"{' '.join('<out>/' + os.path.basename(os.path.normpath(d)) for d in dirs)}"
              + (f" --kernel {kernel}" if kernel else ""),
              f"# profiled command(s): {command}" if command else "#",
              f"kernel_source_sha: {kernel_source_sha()}"]
