@@ -549,6 +549,7 @@ def main():
 
     if not args.no_sweep:
         sweep = []
+        fixed = []   # the fixed-plan option at a few M: context, not sweep points
         gen = torch.Generator(device=dev)
 
         def randn(shape, std, seed):
@@ -568,7 +569,7 @@ def main():
             """copies of the weight covering >= 1 GiB when m_small, else one"""
             return w_list if m_small else w_list[:1]
 
-        def gemm_sweep(cfg, op, N, K, ms, wstd=0.02, seed=0):
+        def gemm_sweep(cfg, op, N, K, ms, wstd=0.02, seed=0, fixed_ms=()):
             W = randn((N, K), wstd, 1000 + seed)
             A = randn((max(ms), K), 1.0, 2000 + seed)
             Yfull = B.bi_gemm(A, W)
@@ -588,6 +589,18 @@ def main():
                 ok = torch.equal(Y, Yfull[:m])
                 check(ok, f"{cfg} {op} M={m}")
                 point(cfg, op, m, us, gemm_work(m, N, K), N=N, K=K, cold=m <= 256, bits_equal_full=ok)
+                if m in fixed_ms:
+                    # the same call with one tile shape per (N, K) at every M
+                    def ff():
+                        B.bi_gemm(A[:m], ws[k[0] % len(ws)], Y, fixed_plan=True)
+                        k[0] += 1
+                    fus = graph_us(ff, reps)
+                    B.bi_gemm(A[:m], W, Y, fixed_plan=True)
+                    okf = torch.equal(Y, Yfull[:m])
+                    check(okf, f"{cfg} {op} M={m} fixed plan")
+                    t_roof, _ = roof(*gemm_work(m, N, K))
+                    fixed.append({"op": op, "M": m, "us": round(fus, 2), "default_us": round(us, 2),
+                                  "frac": float(f"{t_roof / fus:.4g}"), "bits_equal_default": okf})
             del copies
             torch.cuda.empty_cache()
 
@@ -609,7 +622,7 @@ def main():
         check(torch.equal(ys, Yfull), "tiny every row alone")
         pow2 = [1 << i for i in range(12)]                      # 1 .. 2048
         for op, N in (("qkv", Nqkv), ("o_proj", No), ("gate_up", Ngu)):
-            gemm_sweep("C2 Qwen3-8B linears", op, N, H, pow2, seed=N)
+            gemm_sweep("C2 Qwen3-8B linears", op, N, H, pow2, seed=N, fixed_ms=(1, 16, 128, 512))
         gemm_sweep("C3 down_proj long-K", "down", H, Kdn, sorted(set([1 << i for i in range(14)] + [7, 129, 1000])),
                    seed=7)
 
@@ -748,6 +761,7 @@ def main():
             if small:
                 summary[cfg]["hbm_frac_at_M_le_16"] = gmean(small)
         result["sweep_summary"] = summary
+        result["fixed_plan"] = fixed
     result["invariance"] = {"checked": inv["checked"], "passed": inv["passed"],
                             "pass_pct": round(100.0 * inv["passed"] / max(1, inv["checked"]), 2),
                             "failed": inv["failed"]}

@@ -130,12 +130,21 @@ typedef struct bi_plan {
  *   pipeline_depth: the streaming kernels only; weight load units in flight per
  *     wavefront (0 = the library's choice; otherwise rounded down to a
  *     supported power of two that divides the unit count).
+ *   fixed_plan: GEMM family; nonzero = the tiled kernel with one tile shape
+ *     for the operation, its operand formats and (N, K) at every M -- for a
+ *     dense or NVFP4 GEMM with a bf16 A the shape bi_plan_query reports, for
+ *     the grouped GEMM its many-rows shape -- so neither the kernel nor the
+ *     tile is chosen from M.  For callers that require that by construction;
+ *     the default choice (which also uses M) gives the same bits, faster at
+ *     small and middle M.  tile_variant, when set, takes precedence; the
+ *     BMM's plan never depends on M.
  */
 typedef struct bi_launch_opts {
     int32_t max_workgroups;
     int32_t tile_variant;
     int32_t pipeline_depth;
-    int32_t reserved[5];
+    int32_t fixed_plan;
+    int32_t reserved[4];
 } bi_launch_opts;
 
 /*

@@ -54,7 +54,7 @@ KERNEL_KINDS = ("tiled", "tiled_pingpong", "stream_a_lds", "stream_reg", "stream
 
 class BiLaunchOpts(ctypes.Structure):
     _fields_ = [("max_workgroups", _i32), ("tile_variant", _i32), ("pipeline_depth", _i32),
-                ("reserved", _i32 * 5)]
+                ("fixed_plan", _i32), ("reserved", _i32 * 4)]
 
 
 class BiError(RuntimeError):
@@ -173,13 +173,14 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _opts(max_workgroups=0, tile_variant=0, pipeline_depth=0):
-    if not max_workgroups and not tile_variant and not pipeline_depth:
+def _opts(max_workgroups=0, tile_variant=0, pipeline_depth=0, fixed_plan=False):
+    if not max_workgroups and not tile_variant and not pipeline_depth and not fixed_plan:
         return None
     o = BiLaunchOpts()
     o.max_workgroups = int(max_workgroups)
     o.tile_variant = int(tile_variant)
     o.pipeline_depth = int(pipeline_depth)
+    o.fixed_plan = 1 if fixed_plan else 0
     return ctypes.byref(o)
 
 
@@ -199,7 +200,7 @@ def _raise(st, what):
         raise BiError(st, what)
 
 
-def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0, pipeline_depth=0):
+def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0, pipeline_depth=0, fixed_plan=False):
     """Y[M,N] = A[M,K] . B[N,K]^T (bf16); allocates Y with torch if not given."""
     _check2d(A, "A")
     _check2d(B, "B")
@@ -213,7 +214,7 @@ def bi_gemm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0, pipe
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y must be [M, N]")
     st = lib().bi_gemm_ex(_ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(Y), Y.stride(0),
-                          M, N, K, _stream(stream), _opts(max_workgroups, tile_variant, pipeline_depth))
+                          M, N, K, _stream(stream), _opts(max_workgroups, tile_variant, pipeline_depth, fixed_plan))
     _raise(st, "bi_gemm")
     return Y
 
@@ -238,7 +239,7 @@ def bi_bmm(A, B, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
 
 
 def bi_nvfp4_gemm(A, W, W_scales, alpha, Y=None, *, A_scales=None, K=None, stream=None,
-                  max_workgroups=0, tile_variant=0, pipeline_depth=0):
+                  max_workgroups=0, tile_variant=0, pipeline_depth=0, fixed_plan=False):
     """Y[M,N] = alpha * A . W^T with NVFP4 W (codes [N,K/2] uint8, scales [N,K/16] uint8).
 
     A is bf16 [M,K] when A_scales is None, else NVFP4 codes [M,K/2] with
@@ -270,7 +271,7 @@ def bi_nvfp4_gemm(A, W, W_scales, alpha, Y=None, *, A_scales=None, K=None, strea
     _check2d(Y, "Y")
     st = lib().bi_nvfp4_gemm_ex(_ptr(A), _ptr(A_scales), a_fmt, lda, _ptr(W), _ptr(W_scales),
                                 float(alpha), _ptr(Y), Y.stride(0), M, N, K, _stream(stream),
-                                _opts(max_workgroups, tile_variant, pipeline_depth))
+                                _opts(max_workgroups, tile_variant, pipeline_depth, fixed_plan))
     _raise(st, "bi_nvfp4_gemm")
     return Y
 
@@ -349,7 +350,7 @@ def bi_reduce_rmsnorm(partials, gamma, eps, residual=None, R=None, Y=None, *, st
     return R, Y
 
 
-def bi_grouped_gemm(A, W, offsets, Y=None, *, stream=None, max_workgroups=0, tile_variant=0):
+def bi_grouped_gemm(A, W, offsets, Y=None, *, stream=None, max_workgroups=0, tile_variant=0, fixed_plan=False):
     """Mixture-of-experts grouped GEMM: rows offsets[e] .. offsets[e+1]-1 of
     A [T,K] use W[e] [N,K]; offsets is a device int64 tensor [E+1]."""
     _check2d(A, "A")
@@ -366,7 +367,7 @@ def bi_grouped_gemm(A, W, offsets, Y=None, *, stream=None, max_workgroups=0, til
     _check2d(Y, "Y")
     st = lib().bi_grouped_gemm_ex(_ptr(A), A.stride(0), _ptr(W), W.stride(1), W.stride(0), _ptr(Y),
                                   Y.stride(0), _ptr(offsets), E, T, N, K, _stream(stream),
-                                  _opts(max_workgroups, tile_variant))
+                                  _opts(max_workgroups, tile_variant, 0, fixed_plan))
     _raise(st, "bi_grouped_gemm")
     return Y
 

@@ -415,6 +415,14 @@ bi_status run_gemm(int a_mode, int b_mode, int op, const GemmArgs &in, void *str
         if (opts->tile_variant < 0 || opts->tile_variant > bi::kNumTileShapes) return BI_ERR_SHAPE;
         return launch_tiled(a_mode, b_mode, op, opts->tile_variant - 1, in, stream, opts, cus);
     }
+    // fixed_plan: one tile shape for (op, operand modes, N, K) at every M --
+    // the cost model's many-rows choice, which no longer depends on M
+    if (opts && opts->fixed_plan && op != BI_OP_BMM) {
+        int64_t est = 0;
+        const int v = op == BI_OP_GROUPED_GEMM ? grouped_variant(in.N, kModelRows + 1)
+                                               : model_variant(a_mode, b_mode, in.N, 1, kModelRows + 1, &est);
+        return launch_tiled(a_mode, b_mode, op, v, in, stream, opts, cus);
+    }
     // grouped: classify() takes the average rows per expert
     const int64_t m_cls = in.group_off ? (in.M + in.batch - 1) / in.batch : in.M;
     const Regime r = classify(op, a_mode, b_mode, in.N, in.K, in.batch, in.group_off != nullptr, cus, m_cls);

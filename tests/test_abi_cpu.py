@@ -403,6 +403,14 @@ def test_plan_regimes_edges_and_errors():
     assert B.lib().bi_plan_regimes(B.BI_OP_GEMM, 4096, 4100, 0, 256, arr, 1, B.ctypes.byref(n)) == B.BI_ERR_SHAPE
 
 
+def test_launch_opts_layout():
+    """bi_launch_opts keeps its 32-byte layout (fixed_plan took a reserved
+    slot), with the fields at the offsets bi.h gives them."""
+    O = B.BiLaunchOpts
+    assert B.ctypes.sizeof(O) == 32
+    assert [O.max_workgroups.offset, O.tile_variant.offset, O.pipeline_depth.offset, O.fixed_plan.offset] == [0, 4, 8, 12]
+
+
 def test_probe_validation():
     """The measurement probes validate their arguments before any launch."""
     L = B.lib()
